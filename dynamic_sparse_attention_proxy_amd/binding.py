@@ -1,0 +1,238 @@
+"""ctypes binding of libcrisp.so (the C ABI declared in include/crisp.h).
+
+Argument marshalling only: every function here forwards device pointers,
+sizes and torch's current HIP stream to the library, and raises CrispError
+on a non-zero status.  Nothing is computed on the host, and there is no
+fallback: if the library is missing, every call fails loudly.
+
+Functions keep the C names.  Tensors must be contiguous and live on the GPU
+that is current.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libcrisp.so")
+
+CRISP_OK = 0
+STATUS_NAMES = {0: "CRISP_OK", 1: "CRISP_ERR_NULL", 2: "CRISP_ERR_SHAPE", 3: "CRISP_ERR_PARAM",
+                4: "CRISP_ERR_ALIGN", 5: "CRISP_ERR_WORKSPACE", 6: "CRISP_ERR_DEVICE", 7: "CRISP_ERR_LAUNCH"}
+
+ROUTE_PE, ROUTE_VS = 0, 1
+ROUTE_AUTO, ROUTE_FORCE_VS, ROUTE_FORCE_PE = 0, 1, 2
+NF_MEDIAN, NF_MEAN = 0, 1
+
+
+class CrispError(RuntimeError):
+    def __init__(self, fn: str, status: int, message: str):
+        super().__init__(f"{fn}: {STATUS_NAMES.get(status, status)} ({message})")
+        self.status = status
+
+
+class crisp_dims(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32), ("seq_len", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("block", ctypes.c_int32), ("scale", ctypes.c_float)]
+
+
+class crisp_cfg(ctypes.Structure):
+    _fields_ = [("tau", ctypes.c_float), ("alpha", ctypes.c_float), ("gamma_pe", ctypes.c_float),
+                ("kmin_blocks", ctypes.c_int32), ("sink_width", ctypes.c_int32), ("recency_width", ctypes.c_int32),
+                ("nf_stat", ctypes.c_int32), ("route_override", ctypes.c_int32)]
+
+
+class crisp_blocks(ctypes.Structure):
+    _fields_ = [("count", ctypes.c_void_p), ("idx", ctypes.c_void_p), ("v_score", ctypes.c_void_p),
+                ("s_score", ctypes.c_void_p), ("floor_v", ctypes.c_void_p), ("floor_s", ctypes.c_void_p),
+                ("v_mask", ctypes.c_void_p), ("s_mask", ctypes.c_void_p), ("n_v", ctypes.c_void_p),
+                ("n_s", ctypes.c_void_p)]
+
+
+_lib = None
+
+_P = ctypes.c_void_p
+_SIGS = {
+    "crisp_proxy": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "crisp_proxy_scratch_bytes": (ctypes.c_size_t, [ctypes.POINTER(crisp_dims)]),
+    "crisp_route": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), _P, _P, _P, _P]),
+    "crisp_select": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), _P, _P, _P, _P,
+                                    ctypes.POINTER(crisp_blocks), _P, ctypes.c_size_t, _P]),
+    "crisp_select_gamma": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), ctypes.c_float, _P,
+                                          _P, _P, _P, ctypes.POINTER(crisp_blocks), _P, ctypes.c_size_t, _P]),
+    "crisp_select_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(crisp_dims)]),
+    "crisp_list_capacity": (ctypes.c_size_t, [ctypes.POINTER(crisp_dims)]),
+    "crisp_sparse_attn": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P,
+                                         _P]),
+    "crisp_dense_attn": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, ctypes.c_int32, _P, _P]),
+    "crisp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "crisp_abi_version": (ctypes.c_int32, []),
+}
+
+
+def lib() -> ctypes.CDLL:
+    """Load libcrisp.so (built in-tree by __graft_entry__.build())."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libcrisp.so not found at {LIB_PATH}: build it with "
+                               "`python -m dynamic_sparse_attention_proxy_amd.build`")
+        handle = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(handle, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = handle
+    return _lib
+
+
+def _check(fn: str, status: int):
+    if status != CRISP_OK:
+        raise CrispError(fn, status, lib().crisp_status_string(status).decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    if t is None:
+        return None
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to libcrisp must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def make_dims(num_q_heads: int, num_kv_heads: int, seq_len: int, head_dim: int = 128, block: int = 128,
+              scale: Optional[float] = None) -> crisp_dims:
+    if scale is None:
+        scale = 1.0 / math.sqrt(head_dim)
+    return crisp_dims(num_q_heads, num_kv_heads, seq_len, head_dim, block, scale)
+
+
+def make_cfg(tau: float = 0.5, alpha: float = 1.25, gamma_pe: float = 0.95, kmin_blocks: int = 8,
+             sink_width: int = 128, recency_width: int = 128, nf_stat: int = NF_MEDIAN,
+             route_override: int = ROUTE_AUTO) -> crisp_cfg:
+    return crisp_cfg(tau, alpha, gamma_pe, kmin_blocks, sink_width, recency_width, nf_stat, route_override)
+
+
+def crisp_proxy_scratch_bytes(dims: crisp_dims) -> int:
+    return int(lib().crisp_proxy_scratch_bytes(ctypes.byref(dims)))
+
+
+def crisp_select_workspace_bytes(dims: crisp_dims) -> int:
+    return int(lib().crisp_select_workspace_bytes(ctypes.byref(dims)))
+
+
+def crisp_list_capacity(dims: crisp_dims) -> int:
+    return int(lib().crisp_list_capacity(ctypes.byref(dims)))
+
+
+def crisp_abi_version() -> int:
+    return int(lib().crisp_abi_version())
+
+
+def crisp_proxy(dims: crisp_dims, q, k, attn_map, row_lse=None, partials=None, stream=None):
+    nbytes = partials.numel() * partials.element_size() if partials is not None else 0
+    _check("crisp_proxy", lib().crisp_proxy(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(attn_map), _ptr(row_lse),
+                                            _ptr(partials), nbytes, _stream(stream)))
+
+
+def crisp_route(dims: crisp_dims, cfg: crisp_cfg, attn_map, c_struct, route, stream=None):
+    _check("crisp_route", lib().crisp_route(ctypes.byref(dims), ctypes.byref(cfg), _ptr(attn_map), _ptr(c_struct),
+                                            _ptr(route), _stream(stream)))
+
+
+def _blocks(out: dict) -> crisp_blocks:
+    b = crisp_blocks()
+    for name, _ in crisp_blocks._fields_:
+        t = out.get(name)
+        setattr(b, name, None if t is None else _ptr(t).value)
+    return b
+
+
+def crisp_select(dims: crisp_dims, cfg: crisp_cfg, q, k, attn_map, route, out: dict, workspace, stream=None):
+    b = _blocks(out)
+    _check("crisp_select", lib().crisp_select(ctypes.byref(dims), ctypes.byref(cfg), _ptr(q), _ptr(k),
+                                              _ptr(attn_map), _ptr(route), ctypes.byref(b), _ptr(workspace),
+                                              workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def crisp_select_gamma(dims: crisp_dims, cfg: crisp_cfg, gamma: float, q, k, attn_map, route, out: dict,
+                       workspace, stream=None):
+    b = _blocks(out)
+    _check("crisp_select_gamma", lib().crisp_select_gamma(ctypes.byref(dims), ctypes.byref(cfg), gamma, _ptr(q),
+                                                          _ptr(k), _ptr(attn_map), _ptr(route), ctypes.byref(b),
+                                                          _ptr(workspace),
+                                                          workspace.numel() * workspace.element_size(),
+                                                          _stream(stream)))
+
+
+def crisp_sparse_attn(dims: crisp_dims, q, k, v, count, idx, out, lse=None, stream=None):
+    out_fp32 = 1 if out.dtype == torch.float32 else 0
+    _check("crisp_sparse_attn", lib().crisp_sparse_attn(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(count),
+                                                        _ptr(idx), _ptr(out), out_fp32, _ptr(lse), _stream(stream)))
+
+
+def crisp_dense_attn(dims: crisp_dims, q, k, v, out, lse=None, stream=None):
+    out_fp32 = 1 if out.dtype == torch.float32 else 0
+    _check("crisp_dense_attn", lib().crisp_dense_attn(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
+                                                      out_fp32, _ptr(lse), _stream(stream)))
+
+
+# --------------------------------------------------------------------------
+# Buffer bundle for one layer (device memory from torch; no computation).
+# --------------------------------------------------------------------------
+
+
+class CrispBuffers:
+    """Device buffers of one layer's CRISP chain, allocated once and reused."""
+
+    def __init__(self, dims: crisp_dims, device=None, out_dtype=torch.bfloat16, diagnostics: bool = True):
+        dev = torch.device("cuda") if device is None else torch.device(device)
+        hq, n = dims.num_q_heads, dims.seq_len
+        N = n // dims.block
+        f32, i32 = torch.float32, torch.int32
+        self.dims = dims
+        self.attn_map = torch.empty((hq, dims.block, n), dtype=f32, device=dev)
+        self.row_lse = torch.empty((hq, dims.block), dtype=f32, device=dev)
+        self.partials = torch.empty(crisp_proxy_scratch_bytes(dims), dtype=torch.uint8, device=dev)
+        self.c_struct = torch.empty((hq,), dtype=f32, device=dev)
+        self.route = torch.empty((hq,), dtype=i32, device=dev)
+        self.workspace = torch.empty(crisp_select_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+        self.blocks = {"count": torch.empty((hq, N), dtype=i32, device=dev),
+                       "idx": torch.empty((crisp_list_capacity(dims),), dtype=i32, device=dev)}
+        if diagnostics:
+            self.blocks.update({
+                "v_score": torch.empty((hq, N), dtype=f32, device=dev),
+                "s_score": torch.empty((hq, N), dtype=f32, device=dev),
+                "floor_v": torch.empty((hq,), dtype=f32, device=dev),
+                "floor_s": torch.empty((hq,), dtype=f32, device=dev),
+                "v_mask": torch.empty((hq, N), dtype=i32, device=dev),
+                "s_mask": torch.empty((hq, N), dtype=i32, device=dev),
+                "n_v": torch.empty((hq,), dtype=i32, device=dev),
+                "n_s": torch.empty((hq,), dtype=i32, device=dev),
+            })
+        self.out = torch.empty((hq, n, dims.head_dim), dtype=out_dtype, device=dev)
+        self.lse = torch.empty((hq, n), dtype=f32, device=dev)
+
+
+def crisp_prefill(dims: crisp_dims, cfg: crisp_cfg, q, k, v, bufs: CrispBuffers, gamma: Optional[float] = None,
+                  stream=None):
+    """One layer's path: proxy -> route -> select (or the gamma comparison
+    chain when `gamma` is given) -> block-sparse attention, all on `stream`."""
+    crisp_proxy(dims, q, k, bufs.attn_map, bufs.row_lse, bufs.partials, stream)
+    crisp_route(dims, cfg, bufs.attn_map, bufs.c_struct, bufs.route, stream)
+    if gamma is None:
+        crisp_select(dims, cfg, q, k, bufs.attn_map, bufs.route, bufs.blocks, bufs.workspace, stream)
+    else:
+        crisp_select_gamma(dims, cfg, gamma, q, k, bufs.attn_map, bufs.route, bufs.blocks, bufs.workspace, stream)
+    crisp_sparse_attn(dims, q, k, v, bufs.blocks["count"], bufs.blocks["idx"], bufs.out, bufs.lse, stream)
+    return bufs.out

@@ -1,0 +1,222 @@
+// C ABI of the CRISP library: argument validation, workspace carving and
+// kernel dispatch.  Declarations and the contract of every entry point are
+// in include/crisp.h.
+
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <string.h>
+
+#include "../../include/crisp.h"
+#include "common.h"
+#include "internal.h"
+
+namespace {
+
+constexpr int kMaxSeqLen = 524288;  // LDS sizing of the selection kernels (N <= 4096)
+constexpr int kMaxDevices = 64;
+
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+crisp_status check_dims(const crisp_dims* d) {
+  if (d == nullptr) return CRISP_ERR_NULL;
+  if (d->head_dim != 128 || d->block != 128) return CRISP_ERR_SHAPE;
+  if (d->num_q_heads <= 0 || d->num_kv_heads <= 0) return CRISP_ERR_SHAPE;
+  if (d->num_q_heads % d->num_kv_heads != 0) return CRISP_ERR_SHAPE;
+  if (d->seq_len < 2 * d->block || d->seq_len % d->block != 0 || d->seq_len > kMaxSeqLen) return CRISP_ERR_SHAPE;
+  // grid sizes (Hq * N workgroups) must fit the launch limits comfortably
+  if ((long long)d->num_q_heads * (d->seq_len / d->block) > (1LL << 30)) return CRISP_ERR_SHAPE;
+  if (!(d->scale > 0.f) || !isfinite(d->scale)) return CRISP_ERR_PARAM;
+  return CRISP_OK;
+}
+
+crisp_status check_cfg(const crisp_dims* d, const crisp_cfg* c) {
+  if (c == nullptr) return CRISP_ERR_NULL;
+  if (!(c->tau >= 0.f && c->tau <= 1.f)) return CRISP_ERR_PARAM;
+  if (!(c->alpha > 0.f) || !isfinite(c->alpha)) return CRISP_ERR_PARAM;
+  if (!(c->gamma_pe > 0.f && c->gamma_pe <= 1.f)) return CRISP_ERR_PARAM;
+  if (c->kmin_blocks < 1) return CRISP_ERR_PARAM;
+  if (c->sink_width < 1 || c->sink_width > d->seq_len / 2) return CRISP_ERR_PARAM;
+  if (c->recency_width < 1 || c->recency_width > d->seq_len / 2) return CRISP_ERR_PARAM;
+  if (c->nf_stat != CRISP_NF_MEDIAN && c->nf_stat != CRISP_NF_MEAN) return CRISP_ERR_PARAM;
+  if (c->route_override < CRISP_ROUTE_AUTO || c->route_override > CRISP_ROUTE_FORCE_PE) return CRISP_ERR_PARAM;
+  return CRISP_OK;
+}
+
+crisp_status check_ptr(const void* p) {
+  if (p == nullptr) return CRISP_ERR_NULL;
+  if (!aligned16(p)) return CRISP_ERR_ALIGN;
+  return CRISP_OK;
+}
+
+crisp_status check_opt(const void* p) { return (p == nullptr || aligned16(p)) ? CRISP_OK : CRISP_ERR_ALIGN; }
+
+#define CRISP_TRY(expr)              \
+  do {                               \
+    crisp_status s_ = (expr);        \
+    if (s_ != CRISP_OK) return s_;   \
+  } while (0)
+
+// 0 = unknown, 1 = gfx950, 2 = other
+int g_device_kind[kMaxDevices];
+
+crisp_status check_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return CRISP_ERR_DEVICE;
+  if (dev >= kMaxDevices) return CRISP_ERR_DEVICE;
+  int kind = __atomic_load_n(&g_device_kind[dev], __ATOMIC_ACQUIRE);
+  if (kind == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return CRISP_ERR_DEVICE;
+    kind = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    __atomic_store_n(&g_device_kind[dev], kind, __ATOMIC_RELEASE);
+  }
+  return kind == 1 ? CRISP_OK : CRISP_ERR_DEVICE;
+}
+
+crisp_status launched(hipError_t e) { return e == hipSuccess ? CRISP_OK : CRISP_ERR_LAUNCH; }
+
+crisp_status select_common(const crisp_dims* dims, const crisp_cfg* cfg, bool use_gamma, float gamma, const void* q,
+                           const void* k, const float* attn_map, const int32_t* route, const crisp_blocks* out,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  CRISP_TRY(check_dims(dims));
+  CRISP_TRY(check_cfg(dims, cfg));
+  if (use_gamma && !(gamma > 0.f && gamma <= 1.f)) return CRISP_ERR_PARAM;
+  if (out == nullptr) return CRISP_ERR_NULL;
+  CRISP_TRY(check_ptr(q));
+  CRISP_TRY(check_ptr(k));
+  CRISP_TRY(check_ptr(attn_map));
+  CRISP_TRY(check_ptr(route));
+  CRISP_TRY(check_ptr(out->count));
+  CRISP_TRY(check_ptr(out->idx));
+  CRISP_TRY(check_opt(out->v_score));
+  CRISP_TRY(check_opt(out->s_score));
+  CRISP_TRY(check_opt(out->floor_v));
+  CRISP_TRY(check_opt(out->floor_s));
+  CRISP_TRY(check_opt(out->v_mask));
+  CRISP_TRY(check_opt(out->s_mask));
+  CRISP_TRY(check_opt(out->n_v));
+  CRISP_TRY(check_opt(out->n_s));
+  CRISP_TRY(check_ptr(workspace));
+  const int hq = dims->num_q_heads, hkv = dims->num_kv_heads, n = dims->seq_len;
+  if (workspace_bytes < crisp::select_workspace_bytes(hq, hkv, n)) return CRISP_ERR_WORKSPACE;
+  CRISP_TRY(check_device());
+  crisp::SelectBuffers b = crisp::carve_select_workspace(workspace, hq, hkv, n);
+  if (out->v_score) b.vscore = out->v_score;
+  if (out->s_score) b.sscore = out->s_score;
+  if (out->floor_v) b.floor_v = out->floor_v;
+  if (out->floor_s) b.floor_s = out->floor_s;
+  if (out->v_mask) b.vmask = out->v_mask;
+  if (out->s_mask) b.smask = out->s_mask;
+  if (out->n_v) b.n_v = out->n_v;
+  if (out->n_s) b.n_s = out->n_s;
+  return launched(crisp::launch_select((const __bf16*)q, (const __bf16*)k, attn_map, route, b, out->count, out->idx,
+                                       hq, hkv, n, dims->scale, cfg->alpha, cfg->gamma_pe, cfg->kmin_blocks,
+                                       cfg->nf_stat, use_gamma, gamma, (hipStream_t)stream));
+}
+
+crisp_status attn_common(const crisp_dims* dims, const void* q, const void* k, const void* v, const int32_t* count,
+                         const int32_t* idx, void* out, int32_t out_is_fp32, float* lse, bool dense, void* stream) {
+  CRISP_TRY(check_dims(dims));
+  CRISP_TRY(check_ptr(q));
+  CRISP_TRY(check_ptr(k));
+  CRISP_TRY(check_ptr(v));
+  if (!dense) {
+    CRISP_TRY(check_ptr(count));
+    CRISP_TRY(check_ptr(idx));
+  }
+  CRISP_TRY(check_ptr(out));
+  CRISP_TRY(check_opt(lse));
+  if (out_is_fp32 != 0 && out_is_fp32 != 1) return CRISP_ERR_PARAM;
+  CRISP_TRY(check_device());
+  return launched(crisp::launch_attention((const __bf16*)q, (const __bf16*)k, (const __bf16*)v, count, idx, out,
+                                          out_is_fp32, lse, dims->num_q_heads, dims->num_kv_heads, dims->seq_len,
+                                          dims->scale, dense, (hipStream_t)stream));
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t crisp_proxy_scratch_bytes(const crisp_dims* dims) {
+  if (check_dims(dims) != CRISP_OK) return 0;
+  return crisp::proxy_scratch_bytes(dims->num_q_heads, dims->seq_len);
+}
+
+crisp_status crisp_proxy(const crisp_dims* dims, const void* q, const void* k, float* attn_map, float* row_lse,
+                         void* partials, size_t partials_bytes, void* stream) {
+  CRISP_TRY(check_dims(dims));
+  CRISP_TRY(check_ptr(q));
+  CRISP_TRY(check_ptr(k));
+  CRISP_TRY(check_ptr(attn_map));
+  CRISP_TRY(check_opt(row_lse));
+  CRISP_TRY(check_ptr(partials));
+  if (partials_bytes < crisp::proxy_scratch_bytes(dims->num_q_heads, dims->seq_len)) return CRISP_ERR_WORKSPACE;
+  CRISP_TRY(check_device());
+  return launched(crisp::launch_proxy((const __bf16*)q, (const __bf16*)k, attn_map, row_lse, partials,
+                                      dims->num_q_heads, dims->num_kv_heads, dims->seq_len, dims->scale,
+                                      (hipStream_t)stream));
+}
+
+crisp_status crisp_route(const crisp_dims* dims, const crisp_cfg* cfg, const float* attn_map, float* c_struct,
+                         int32_t* route, void* stream) {
+  CRISP_TRY(check_dims(dims));
+  CRISP_TRY(check_cfg(dims, cfg));
+  CRISP_TRY(check_ptr(attn_map));
+  CRISP_TRY(check_ptr(c_struct));
+  CRISP_TRY(check_ptr(route));
+  CRISP_TRY(check_device());
+  return launched(crisp::launch_route(attn_map, c_struct, route, dims->num_q_heads, dims->seq_len, cfg->sink_width,
+                                      cfg->recency_width, cfg->tau, cfg->route_override, (hipStream_t)stream));
+}
+
+crisp_status crisp_select(const crisp_dims* dims, const crisp_cfg* cfg, const void* q, const void* k,
+                          const float* attn_map, const int32_t* route, const crisp_blocks* out, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return select_common(dims, cfg, false, 0.f, q, k, attn_map, route, out, workspace, workspace_bytes, stream);
+}
+
+crisp_status crisp_select_gamma(const crisp_dims* dims, const crisp_cfg* cfg, float gamma, const void* q,
+                                const void* k, const float* attn_map, const int32_t* route, const crisp_blocks* out,
+                                void* workspace, size_t workspace_bytes, void* stream) {
+  return select_common(dims, cfg, true, gamma, q, k, attn_map, route, out, workspace, workspace_bytes, stream);
+}
+
+size_t crisp_select_workspace_bytes(const crisp_dims* dims) {
+  if (check_dims(dims) != CRISP_OK) return 0;
+  return crisp::select_workspace_bytes(dims->num_q_heads, dims->num_kv_heads, dims->seq_len);
+}
+
+size_t crisp_list_capacity(const crisp_dims* dims) {
+  if (check_dims(dims) != CRISP_OK) return 0;
+  const size_t N = (size_t)dims->seq_len / dims->block;
+  return (size_t)dims->num_q_heads * (N * (N + 1) / 2);
+}
+
+crisp_status crisp_sparse_attn(const crisp_dims* dims, const void* q, const void* k, const void* v,
+                               const int32_t* count, const int32_t* idx, void* out, int32_t out_is_fp32, float* lse,
+                               void* stream) {
+  return attn_common(dims, q, k, v, count, idx, out, out_is_fp32, lse, false, stream);
+}
+
+crisp_status crisp_dense_attn(const crisp_dims* dims, const void* q, const void* k, const void* v, void* out,
+                              int32_t out_is_fp32, float* lse, void* stream) {
+  return attn_common(dims, q, k, v, nullptr, nullptr, out, out_is_fp32, lse, true, stream);
+}
+
+const char* crisp_status_string(crisp_status status) {
+  switch (status) {
+    case CRISP_OK: return "ok";
+    case CRISP_ERR_NULL: return "a required pointer is NULL";
+    case CRISP_ERR_SHAPE: return "unsupported dimensions (need d = 128, block = 128, n % 128 == 0, 256 <= n <= 524288, Hq % Hkv == 0)";
+    case CRISP_ERR_PARAM: return "a method parameter is out of range";
+    case CRISP_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case CRISP_ERR_WORKSPACE: return "workspace or scratch buffer too small";
+    case CRISP_ERR_DEVICE: return "no gfx950 device is current";
+    case CRISP_ERR_LAUNCH: return "kernel launch failed";
+  }
+  return "unknown status";
+}
+
+int32_t crisp_abi_version(void) { return (1 << 16) | 0; }
+
+}  // extern "C"

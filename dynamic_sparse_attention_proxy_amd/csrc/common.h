@@ -1,0 +1,286 @@
+// Device-side helpers shared by the CRISP kernels (gfx950 / CDNA4 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace crisp {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kBlock = 128;    // query/key block (B)
+constexpr int kHeadDim = 128;  // d
+constexpr int kNumXcd = 8;     // MI355X: 8 accelerator dies, workgroups dealt round-robin
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+
+// 32x32x16 bf16 MFMA: C[32x32] += A[32x16] * B[16x32].
+// Lane l holds row (A) / column (B) l % 32 and the 8 k-values of k-group l / 32;
+// the accumulator lane l holds column l % 32, rows 8*(v/4) + 4*(l/32) + v%4.
+__device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 u) { return __builtin_bit_cast(bf16x8, u); }
+
+// Round-to-nearest-even fp32 -> bf16 of 8 values (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ bf16x8 pack_bf16x8(float a0, float a1, float a2, float a3, float a4, float a5,
+                                              float a6, float a7) {
+  bf16x8 r;
+  r[0] = (__bf16)a0; r[1] = (__bf16)a1; r[2] = (__bf16)a2; r[3] = (__bf16)a3;
+  r[4] = (__bf16)a4; r[5] = (__bf16)a5; r[6] = (__bf16)a6; r[7] = (__bf16)a7;
+  return r;
+}
+
+__device__ __forceinline__ float wave_max(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+
+__device__ __forceinline__ float wave_sum(float x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+__device__ __forceinline__ int wave_sum_i(int x) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x += __shfl_xor(x, o);
+  return x;
+}
+
+// Order-preserving key for non-negative floats with index tie-break:
+// ascending key = descending value, then ascending index.
+__device__ __forceinline__ uint64_t desc_key(float x, uint32_t idx) {
+  uint32_t b = __float_as_uint(x);
+  return ((uint64_t)(~b) << 32) | (uint64_t)idx;
+}
+__device__ __forceinline__ uint32_t key_index(uint64_t k) { return (uint32_t)(k & 0xffffffffu); }
+__device__ __forceinline__ float key_value(uint64_t k) { return __uint_as_float(~(uint32_t)(k >> 32)); }
+
+// In-LDS bitonic sort (ascending) of `P` (power of two) 64-bit keys by a
+// whole workgroup of `nthreads` threads.  Caller syncs before and after.
+__device__ inline void bitonic_sort_lds(uint64_t* keys, int P, int tid, int nthreads) {
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int t = tid; t < (P >> 1); t += nthreads) {
+        int lo = 2 * t - (t & (stride - 1));
+        int hi = lo + stride;
+        bool up = ((lo & size) == 0);
+        uint64_t a = keys[lo], b = keys[hi];
+        if ((a > b) == up) {
+          keys[lo] = b;
+          keys[hi] = a;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Exclusive prefix sum of one int per thread over a workgroup (<= 1024
+// threads); returns the exclusive prefix and writes the total.
+__device__ inline int block_exclusive_scan(int x, int* lds_tmp, int tid, int nthreads, int* total) {
+  const int lane = tid & 63, wid = tid >> 6, nw = (nthreads + 63) >> 6;
+  int incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) lds_tmp[wid] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int w = 0; w < nw; ++w) {
+      int t = lds_tmp[w];
+      lds_tmp[w] = acc;
+      acc += t;
+    }
+    lds_tmp[nw] = acc;
+  }
+  __syncthreads();
+  int res = lds_tmp[wid] + incl - x;
+  *total = lds_tmp[nw];
+  __syncthreads();
+  return res;
+}
+
+// Inclusive prefix sum of one float per thread in a fixed order
+// (wave scan, then a serial pass over wave totals) - deterministic.
+__device__ inline float block_inclusive_scan_f(float x, float* lds_tmp, int tid, int nthreads) {
+  const int lane = tid & 63, wid = tid >> 6, nw = (nthreads + 63) >> 6;
+  float incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    float y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  if (lane == 63) lds_tmp[wid] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    float acc = 0.f;
+    for (int w = 0; w < nw; ++w) {
+      float t = lds_tmp[w];
+      lds_tmp[w] = acc;
+      acc += t;
+    }
+  }
+  __syncthreads();
+  float res = lds_tmp[wid] + incl;
+  __syncthreads();
+  return res;
+}
+
+// Exclusive prefix sum of one float per thread in a fixed order.
+__device__ inline float block_exclusive_scan_f(float x, float* lds_tmp, int tid, int nthreads) {
+  const int lane = tid & 63, wid = tid >> 6, nw = (nthreads + 63) >> 6;
+  float incl = x;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    float y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  float excl_w = __shfl_up(incl, 1);
+  if (lane == 0) excl_w = 0.f;
+  if (lane == 63) lds_tmp[wid] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    float acc = 0.f;
+    for (int w = 0; w < nw; ++w) {
+      float t = lds_tmp[w];
+      lds_tmp[w] = acc;
+      acc += t;
+    }
+  }
+  __syncthreads();
+  float res = lds_tmp[wid] + excl_w;
+  __syncthreads();
+  return res;
+}
+
+__device__ inline int block_min_i(int x, int* lds_tmp, int tid, int nthreads) {
+  const int lane = tid & 63, wid = tid >> 6, nw = (nthreads + 63) >> 6;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) x = min(x, __shfl_xor(x, o));
+  if (lane == 0) lds_tmp[wid] = x;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = lds_tmp[0];
+    for (int w = 1; w < nw; ++w) acc = min(acc, lds_tmp[w]);
+    lds_tmp[nw] = acc;
+  }
+  __syncthreads();
+  int r = lds_tmp[nw];
+  __syncthreads();
+  return r;
+}
+
+__device__ inline int block_sum_i(int x, int* lds_tmp, int tid, int nthreads) {
+  const int lane = tid & 63, wid = tid >> 6, nw = (nthreads + 63) >> 6;
+  x = wave_sum_i(x);
+  if (lane == 0) lds_tmp[wid] = x;
+  __syncthreads();
+  if (tid == 0) {
+    int acc = 0;
+    for (int w = 0; w < nw; ++w) acc += lds_tmp[w];
+    lds_tmp[nw] = acc;
+  }
+  __syncthreads();
+  int r = lds_tmp[nw];
+  __syncthreads();
+  return r;
+}
+
+__device__ __forceinline__ float bf16lo_to_f(uint32_t u) { return __uint_as_float(u << 16); }
+__device__ __forceinline__ float bf16hi_to_f(uint32_t u) { return __uint_as_float(u & 0xffff0000u); }
+
+// Sum of one float per thread over a workgroup in a fixed order.
+__device__ inline float block_sum_f(float x, float* lds_tmp, int tid, int nthreads) {
+  const int lane = tid & 63, wid = tid >> 6, nw = (nthreads + 63) >> 6;
+  float s = wave_sum(x);
+  if (lane == 0) lds_tmp[wid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    float acc = 0.f;
+    for (int w = 0; w < nw; ++w) acc += lds_tmp[w];
+    lds_tmp[nw] = acc;
+  }
+  __syncthreads();
+  float r = lds_tmp[nw];
+  __syncthreads();
+  return r;
+}
+
+__device__ inline float block_max_f(float x, float* lds_tmp, int tid, int nthreads) {
+  const int lane = tid & 63, wid = tid >> 6, nw = (nthreads + 63) >> 6;
+  float s = wave_max(x);
+  if (lane == 0) lds_tmp[wid] = s;
+  __syncthreads();
+  if (tid == 0) {
+    float acc = -INFINITY;
+    for (int w = 0; w < nw; ++w) acc = fmaxf(acc, lds_tmp[w]);
+    lds_tmp[nw] = acc;
+  }
+  __syncthreads();
+  float r = lds_tmp[nw];
+  __syncthreads();
+  return r;
+}
+
+// Workgroup -> (head, query block) map shared by the attention kernels.
+// Work is dealt heaviest first (query block N-1 first, since causal rows
+// grow with qb) and so that all workgroups on one XCD - which share that
+// die's L2 - read the same KV group.
+struct RowMap {
+  int mode;  // 1: Hkv % 8 == 0, 2: 8 % Hkv == 0, 0: plain order
+  int hq, hkv, qpg, nblk;
+};
+
+inline RowMap make_row_map(int hq, int hkv, int nblk) {
+  RowMap m;
+  m.hq = hq;
+  m.hkv = hkv;
+  m.qpg = hq / hkv;
+  m.nblk = nblk;
+  const long long total = (long long)hq * nblk;
+  if (hkv % kNumXcd == 0 && hq % kNumXcd == 0)
+    m.mode = 1;
+  else if (kNumXcd % hkv == 0 && ((long long)m.qpg * nblk) % (kNumXcd / hkv) == 0 && total % kNumXcd == 0)
+    m.mode = 2;
+  else
+    m.mode = 0;
+  return m;
+}
+
+__host__ __device__ inline void map_row(const RowMap& m, int id, int* h_out, int* qb_out) {
+  if (m.mode == 1) {
+    const int xcd = id % kNumXcd, s = id / kNumXcd;
+    const int hpx = m.hq / kNumXcd;
+    const int l = s % hpx;
+    const int grp = xcd + kNumXcd * (l / m.qpg);
+    *h_out = grp * m.qpg + l % m.qpg;
+    *qb_out = m.nblk - 1 - s / hpx;
+  } else if (m.mode == 2) {
+    const int xcd = id % kNumXcd, s = id / kNumXcd;
+    const int xpg = kNumXcd / m.hkv;
+    const int g = xcd % m.hkv, sub = xcd / m.hkv;
+    const int t = s * xpg + sub;
+    *h_out = g * m.qpg + t % m.qpg;
+    *qb_out = m.nblk - 1 - t / m.qpg;
+  } else {
+    *h_out = id % m.hq;
+    *qb_out = m.nblk - 1 - id / m.hq;
+  }
+}
+
+}  // namespace crisp

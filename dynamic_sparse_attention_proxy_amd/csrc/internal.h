@@ -1,0 +1,54 @@
+// Launchers of the CRISP kernels, called by the C ABI layer after argument
+// validation.  All take device pointers and enqueue on `stream`.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace crisp {
+
+// Proxy: keys per workgroup of the two proxy passes.
+constexpr int kProxyChunk = 512;
+inline int proxy_chunks(int n) { return (n + kProxyChunk - 1) / kProxyChunk; }
+inline size_t proxy_scratch_bytes(int hq, int n) {
+  // per (head, chunk, row): running max and sum; per (head, row): log2-sum-exp
+  return (size_t)hq * proxy_chunks(n) * 128 * 2 * sizeof(float) + (size_t)hq * 128 * sizeof(float);
+}
+
+hipError_t launch_proxy(const __bf16* q, const __bf16* k, float* amap, float* row_lse, void* scratch, int hq,
+                        int hkv, int n, float scale, hipStream_t stream);
+
+hipError_t launch_route(const float* amap, float* c_struct, int32_t* route, int hq, int n, int sink_width,
+                        int recency_width, float tau, int route_override, hipStream_t stream);
+
+struct SelectBuffers {
+  float* lo;      // [Hq][N] lower-triangle tile sums of the proxy map
+  float* up;      // [Hq][N] strict upper-triangle tile sums
+  float* vscore;  // [Hq][N]
+  float* sscore;  // [Hq][N]
+  float* floor_v; // [Hq]
+  float* floor_s; // [Hq]
+  int32_t* vmask; // [Hq][N]
+  int32_t* smask; // [Hq][N]
+  int32_t* n_v;   // [Hq]
+  int32_t* n_s;   // [Hq]
+  float* qbar;    // [Hq][N][128]
+  float* kbar;    // [Hkv][N][128]
+};
+
+size_t select_workspace_bytes(int hq, int hkv, int n);
+SelectBuffers carve_select_workspace(void* ws, int hq, int hkv, int n);
+
+// use_gamma = false: noise floor on VS heads, gamma_pe on PE heads.
+// use_gamma = true: gamma-cumulative on VS heads and `gamma` on PE heads.
+hipError_t launch_select(const __bf16* q, const __bf16* k, const float* amap, const int32_t* route,
+                         const SelectBuffers& b, int32_t* count, int32_t* idx, int hq, int hkv, int n, float scale,
+                         float alpha, float gamma_pe, int kmin, int nf_stat, bool use_gamma, float gamma,
+                         hipStream_t stream);
+
+hipError_t launch_attention(const __bf16* q, const __bf16* k, const __bf16* v, const int32_t* count,
+                            const int32_t* idx, void* out, int out_fp32, float* lse, int hq, int hkv, int n,
+                            float scale, bool dense, hipStream_t stream);
+
+}  // namespace crisp

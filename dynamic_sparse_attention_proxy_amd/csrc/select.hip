@@ -1,0 +1,458 @@
+// Block selection of CRISP on gfx950.
+//
+// Vertical-Slash heads (ai.info summary, "Methodology in Plain English";
+// ai-feeds summary, method module 2):
+//   tile_sums  - one streaming pass over the proxy map: per (head, key block)
+//                the mass on and below the tile diagonal (row >= column) and
+//                above it.  Proxy row r sits at position 128(N-1)+r, so key
+//                128kb+c is at offset 128(N-1-kb)+(r-c): the lower triangle
+//                falls in slash block N-1-kb, the upper one in N-2-kb.  The
+//                vertical score of kb is the tile total.
+//   vs_select  - per (head, direction): sort the block scores in LDS, floor =
+//                alpha x lower median (or mean) of blocks 1..N-1, keep blocks
+//                above it plus block 0, top up to k_min; or, for the
+//                comparison chain, the shortest gamma-coverage prefix.
+//   vs_expand  - per (head, query block): kept vertical blocks <= qb and the
+//                two key blocks covered by each kept slash band, compacted in
+//                ascending order.
+// Pooled-Estimation heads ("Key Contributions" item 2; gamma = 0.95 on PE):
+//   pe_pool    - mean of each 128-row block of q (PE heads) and k.
+//   pe_select  - per (head, query block): pooled logits against kb <= qb,
+//                softmax, LDS sort, shortest prefix reaching gamma, plus qb.
+
+#include "common.h"
+#include "internal.h"
+
+namespace crisp {
+
+namespace {
+
+constexpr int kAlign = 256;
+
+__device__ __forceinline__ int pow2_ceil(int x) { return x <= 1 ? 1 : 1 << (32 - __clz(x - 1)); }
+
+__global__ __launch_bounds__(256) void tile_sums_kernel(const float* amap, float* lo_out, float* up_out, int n,
+                                                        int nblk) {
+  __shared__ float red[8];
+  const int kb = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float* base = amap + (size_t)h * kBlock * n + (size_t)kb * kBlock;
+  const int c0 = 4 * (lane & 31), rs = lane >> 5;
+  f32x4 x[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) x[i] = *(const f32x4*)(base + (size_t)(32 * w + 2 * i + rs) * n + c0);
+  float lo = 0.f, up = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int r = 32 * w + 2 * i + rs;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      if (r >= c0 + e)
+        lo += x[i][e];
+      else
+        up += x[i][e];
+    }
+  }
+  lo = block_sum_f(lo, red, tid, 256);
+  up = block_sum_f(up, red, tid, 256);
+  if (tid == 0) {
+    lo_out[(size_t)h * nblk + kb] = lo;
+    up_out[(size_t)h * nblk + kb] = up;
+  }
+}
+
+struct VsArgs {
+  const float* lo;
+  const float* up;
+  const int32_t* route;
+  float* vscore;
+  float* sscore;
+  float* floor_v;
+  float* floor_s;
+  int32_t* vmask;
+  int32_t* smask;
+  int32_t* n_v;
+  int32_t* n_s;
+  int nblk;
+  int pw2;  // power of two >= nblk
+  float alpha;
+  float gamma;
+  int kmin;
+  int nf_stat;
+  int use_gamma;
+};
+
+constexpr int kVsThreads = 1024;
+
+__global__ __launch_bounds__(kVsThreads) void vs_select_kernel(VsArgs p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int N = p.nblk, P = p.pw2;
+  uint64_t* keys = (uint64_t*)smem;
+  float* xl = (float*)(keys + P);
+  uint8_t* mask = (uint8_t*)(xl + N);
+  __shared__ float redf[20];
+  __shared__ int redi[20];
+  const int h = blockIdx.x, dir = blockIdx.y, tid = threadIdx.x;
+  const float* lo = p.lo + (size_t)h * N;
+  const float* up = p.up + (size_t)h * N;
+  float* xs = (dir == 0 ? p.vscore : p.sscore) + (size_t)h * N;
+  for (int b = tid; b < N; b += kVsThreads) {
+    float x;
+    if (dir == 0)
+      x = (lo[b] + up[b]) * (1.f / kBlock);
+    else
+      x = (lo[N - 1 - b] + (b <= N - 2 ? up[N - 2 - b] : 0.f)) * (1.f / kBlock);
+    xl[b] = x;
+    xs[b] = x;
+    mask[b] = 0;
+  }
+  int32_t* mask_out = (dir == 0 ? p.vmask : p.smask) + (size_t)h * N;
+  float* floor_out = dir == 0 ? p.floor_v : p.floor_s;
+  int32_t* nsel_out = dir == 0 ? p.n_v : p.n_s;
+  if (p.route[h] != 1) {
+    for (int b = tid; b < N; b += kVsThreads) mask_out[b] = 0;
+    if (tid == 0) {
+      floor_out[h] = 0.f;
+      nsel_out[h] = 0;
+    }
+    return;
+  }
+  __syncthreads();
+  const int want = min(p.kmin, N);
+  if (!p.use_gamma) {
+    // Noise floor over the candidates 1..N-1 (block 0 always kept).
+    const int m = N - 1;
+    for (int i = tid; i < P; i += kVsThreads) keys[i] = i < m ? desc_key(xl[i + 1], i + 1) : ~0ull;
+    __syncthreads();
+    bitonic_sort_lds(keys, P, tid, kVsThreads);
+    float mu;
+    if (p.nf_stat == 0) {
+      const int kidx = (m - 1) / 2;          // lower median, ascending index
+      mu = key_value(keys[m - 1 - kidx]);    // same value in descending order
+    } else {
+      float s = 0.f;
+      for (int b = 1 + tid; b < N; b += kVsThreads) s += xl[b];
+      mu = block_sum_f(s, redf, tid, kVsThreads) / (float)m;
+    }
+    const float T = p.alpha * mu;
+    int above = 0;
+    for (int i = tid; i < m; i += kVsThreads) above += key_value(keys[i]) > T ? 1 : 0;
+    above = block_sum_i(above, redi, tid, kVsThreads);
+    const int take = max(above, want - 1);
+    for (int i = tid; i < take; i += kVsThreads) mask[key_index(keys[i])] = 1;
+    if (tid == 0) {
+      mask[0] = 1;
+      floor_out[h] = T;
+      nsel_out[h] = take + 1;
+    }
+  } else {
+    // gamma-cumulative coverage over all N blocks, then block 0 and k_min.
+    for (int i = tid; i < P; i += kVsThreads) keys[i] = i < N ? desc_key(xl[i], i) : ~0ull;
+    __syncthreads();
+    bitonic_sort_lds(keys, P, tid, kVsThreads);
+    const int per = (N + kVsThreads - 1) / kVsThreads;
+    const int beg = min(N, tid * per), end = min(N, beg + per);
+    float local = 0.f;
+    for (int i = beg; i < end; ++i) local += key_value(keys[i]);
+    float run = block_exclusive_scan_f(local, redf, tid, kVsThreads);
+    int cut = 0x7fffffff;
+    for (int i = beg; i < end; ++i) {
+      run += key_value(keys[i]);
+      if (run >= p.gamma) {
+        cut = i;
+        break;
+      }
+    }
+    cut = block_min_i(cut, redi, tid, kVsThreads);
+    if (cut == 0x7fffffff) cut = N - 1;
+    for (int i = tid; i <= cut; i += kVsThreads) mask[key_index(keys[i])] = 1;
+    __syncthreads();
+    if (tid == 0) {
+      int cnt = cut + 1;
+      if (!mask[0]) {
+        mask[0] = 1;
+        ++cnt;
+      }
+      for (int pos = cut + 1; cnt < want && pos < N; ++pos) {
+        const uint32_t b = key_index(keys[pos]);
+        if (!mask[b]) {
+          mask[b] = 1;
+          ++cnt;
+        }
+      }
+      floor_out[h] = key_value(keys[cut]);
+      nsel_out[h] = cnt;
+    }
+  }
+  __syncthreads();
+  for (int b = tid; b < N; b += kVsThreads) mask_out[b] = mask[b];
+}
+
+__global__ __launch_bounds__(256) void pe_pool_kernel(const __bf16* q, const __bf16* k, const int32_t* route,
+                                                      float* qbar, float* kbar, int hq, int n) {
+  __shared__ float part[16][kHeadDim];
+  const int kb = blockIdx.x, which = blockIdx.y, tid = threadIdx.x;
+  const int nblk = n / kBlock;
+  const __bf16* src;
+  float* dst;
+  if (which < hq) {
+    if (route[which] != 0) return;
+    src = q + (size_t)which * n * kHeadDim;
+    dst = qbar + (size_t)which * nblk * kHeadDim;
+  } else {
+    const int g = which - hq;
+    src = k + (size_t)g * n * kHeadDim;
+    dst = kbar + (size_t)g * nblk * kHeadDim;
+  }
+  const int dc = tid & 15, rg = tid >> 4;
+  float acc[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+  u32x4 x[8];
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr)
+    x[rr] = *(const u32x4*)(src + (size_t)(kb * kBlock + rg * 8 + rr) * kHeadDim + 8 * dc);
+#pragma unroll
+  for (int rr = 0; rr < 8; ++rr)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      acc[2 * j] += bf16lo_to_f(x[rr][j]);
+      acc[2 * j + 1] += bf16hi_to_f(x[rr][j]);
+    }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[rg][8 * dc + e] = acc[e];
+  __syncthreads();
+  if (tid < kHeadDim) {
+    float s = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s += part[r][tid];
+    dst[(size_t)kb * kHeadDim + tid] = s * (1.f / kBlock);
+  }
+}
+
+struct PeArgs {
+  const float* qbar;
+  const float* kbar;
+  const int32_t* route;
+  int32_t* count;
+  int32_t* idx;
+  int hq;
+  int qpg;
+  int nblk;
+  float scale_log2;
+  float gamma;
+};
+
+constexpr int kPeThreads = 256;
+
+__global__ __launch_bounds__(kPeThreads) void pe_select_kernel(PeArgs p) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  __shared__ float redf[8];
+  __shared__ int redi[8];
+  const int N = p.nblk;
+  const int id = blockIdx.x;
+  const int h = id % p.hq, qb = N - 1 - id / p.hq;
+  if (p.route[h] != 0) return;
+  const int L = qb + 1, P = pow2_ceil(L);
+  uint64_t* keys = (uint64_t*)smem;
+  float* pr = (float*)(keys + pow2_ceil(N));
+  uint8_t* flags = (uint8_t*)(pr + N);
+  const int tid = threadIdx.x, l16 = tid & 15, grp = tid >> 4;
+  const int g = h / p.qpg;
+
+  // pooled logits (base 2): 16 lanes per key block, 8 dims each
+  const float* qv = p.qbar + ((size_t)h * N + qb) * kHeadDim + 8 * l16;
+  const f32x4 qa = *(const f32x4*)qv, qc = *(const f32x4*)(qv + 4);
+  const float* kbase = p.kbar + (size_t)g * N * kHeadDim + 8 * l16;
+  for (int kb0 = 0; kb0 < L; kb0 += 16) {
+    const int kb = kb0 + grp;
+    float dot = 0.f;
+    if (kb < L) {
+      const f32x4 ka = *(const f32x4*)(kbase + (size_t)kb * kHeadDim);
+      const f32x4 kc = *(const f32x4*)(kbase + (size_t)kb * kHeadDim + 4);
+      dot = qa[0] * ka[0] + qa[1] * ka[1] + qa[2] * ka[2] + qa[3] * ka[3] + qc[0] * kc[0] + qc[1] * kc[1] +
+            qc[2] * kc[2] + qc[3] * kc[3];
+    }
+    dot += __shfl_xor(dot, 1);
+    dot += __shfl_xor(dot, 2);
+    dot += __shfl_xor(dot, 4);
+    dot += __shfl_xor(dot, 8);
+    if (kb < L && l16 == 0) pr[kb] = dot * p.scale_log2;
+  }
+  __syncthreads();
+  float mx = -INFINITY;
+  for (int kb = tid; kb < L; kb += kPeThreads) mx = fmaxf(mx, pr[kb]);
+  mx = block_max_f(mx, redf, tid, kPeThreads);
+  float loc = 0.f;
+  for (int kb = tid; kb < L; kb += kPeThreads) {
+    const float e = fast_exp2(pr[kb] - mx);
+    pr[kb] = e;
+    loc += e;
+  }
+  const float sum = block_sum_f(loc, redf, tid, kPeThreads);
+  for (int i = tid; i < P; i += kPeThreads) {
+    if (i < L) {
+      const float pv = pr[i] / sum;
+      keys[i] = desc_key(pv, i);
+      flags[i] = 0;
+    } else {
+      keys[i] = ~0ull;
+    }
+  }
+  __syncthreads();
+  bitonic_sort_lds(keys, P, tid, kPeThreads);
+
+  const int per = (L + kPeThreads - 1) / kPeThreads;
+  const int beg = min(L, tid * per), end = min(L, beg + per);
+  float local = 0.f;
+  for (int i = beg; i < end; ++i) local += key_value(keys[i]);
+  float run = block_exclusive_scan_f(local, redf, tid, kPeThreads);
+  int cut = 0x7fffffff;
+  for (int i = beg; i < end; ++i) {
+    run += key_value(keys[i]);
+    if (run >= p.gamma) {
+      cut = i;
+      break;
+    }
+  }
+  cut = block_min_i(cut, redi, tid, kPeThreads);
+  if (cut == 0x7fffffff) cut = L - 1;
+  for (int i = tid; i <= cut; i += kPeThreads) flags[key_index(keys[i])] = 1;
+  if (tid == 0) flags[qb] = 1;
+  __syncthreads();
+
+  // ascending compaction
+  int c = 0;
+  for (int kb = beg; kb < end; ++kb) c += flags[kb];
+  int total;
+  int pos = block_exclusive_scan(c, redi, tid, kPeThreads, &total);
+  int32_t* out = p.idx + (size_t)h * ((size_t)N * (N + 1) / 2) + (size_t)qb * (qb + 1) / 2;
+  for (int kb = beg; kb < end; ++kb)
+    if (flags[kb]) out[pos++] = kb;
+  if (tid == 0) p.count[(size_t)h * N + qb] = total;
+}
+
+__global__ __launch_bounds__(256) void vs_expand_kernel(const int32_t* route, const int32_t* vmask,
+                                                        const int32_t* smask, int32_t* count, int32_t* idx, int hq,
+                                                        int nblk) {
+  __shared__ int redi[8];
+  const int N = nblk, id = blockIdx.x;
+  const int h = id % hq, qb = N - 1 - id / hq;
+  if (route[h] != 1) return;
+  const int tid = threadIdx.x;
+  const int L = qb + 1;
+  const int32_t* vm = vmask + (size_t)h * N;
+  const int32_t* sm = smask + (size_t)h * N;
+  const int per = (L + 255) / 256;
+  const int beg = min(L, tid * per), end = min(L, beg + per);
+  int c = 0;
+  for (int kb = beg; kb < end; ++kb) c += (vm[kb] | sm[qb - kb] | (kb < qb ? sm[qb - kb - 1] : 0)) ? 1 : 0;
+  int total;
+  int pos = block_exclusive_scan(c, redi, tid, 256, &total);
+  int32_t* out = idx + (size_t)h * ((size_t)N * (N + 1) / 2) + (size_t)qb * (qb + 1) / 2;
+  for (int kb = beg; kb < end; ++kb)
+    if (vm[kb] | sm[qb - kb] | (kb < qb ? sm[qb - kb - 1] : 0)) out[pos++] = kb;
+  if (tid == 0) count[(size_t)h * N + qb] = total;
+}
+
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+inline int host_pow2_ceil(int x) {
+  int p = 1;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+}  // namespace
+
+size_t select_workspace_bytes(int hq, int hkv, int n) {
+  const size_t N = (size_t)n / kBlock;
+  size_t b = 0;
+  b += 4 * align_up(hq * N * sizeof(float));        // lo, up, vscore, sscore
+  b += 2 * align_up(hq * sizeof(float));            // floors
+  b += 2 * align_up(hq * N * sizeof(int32_t));      // masks
+  b += 2 * align_up(hq * sizeof(int32_t));          // kept counts
+  b += align_up(hq * N * kHeadDim * sizeof(float)); // qbar
+  b += align_up(hkv * N * kHeadDim * sizeof(float));// kbar
+  return b;
+}
+
+SelectBuffers carve_select_workspace(void* ws, int hq, int hkv, int n) {
+  const size_t N = (size_t)n / kBlock;
+  char* p = (char*)ws;
+  SelectBuffers b;
+  auto take = [&](size_t bytes) {
+    char* r = p;
+    p += align_up(bytes);
+    return (void*)r;
+  };
+  b.lo = (float*)take(hq * N * sizeof(float));
+  b.up = (float*)take(hq * N * sizeof(float));
+  b.vscore = (float*)take(hq * N * sizeof(float));
+  b.sscore = (float*)take(hq * N * sizeof(float));
+  b.floor_v = (float*)take(hq * sizeof(float));
+  b.floor_s = (float*)take(hq * sizeof(float));
+  b.vmask = (int32_t*)take(hq * N * sizeof(int32_t));
+  b.smask = (int32_t*)take(hq * N * sizeof(int32_t));
+  b.n_v = (int32_t*)take(hq * sizeof(int32_t));
+  b.n_s = (int32_t*)take(hq * sizeof(int32_t));
+  b.qbar = (float*)take(hq * N * kHeadDim * sizeof(float));
+  b.kbar = (float*)take(hkv * N * kHeadDim * sizeof(float));
+  return b;
+}
+
+hipError_t launch_select(const __bf16* q, const __bf16* k, const float* amap, const int32_t* route,
+                         const SelectBuffers& b, int32_t* count, int32_t* idx, int hq, int hkv, int n, float scale,
+                         float alpha, float gamma_pe, int kmin, int nf_stat, bool use_gamma, float gamma,
+                         hipStream_t stream) {
+  const int N = n / kBlock;
+  hipError_t e;
+  hipLaunchKernelGGL(tile_sums_kernel, dim3(N, hq), dim3(256), 0, stream, amap, b.lo, b.up, n, N);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  VsArgs va;
+  va.lo = b.lo;
+  va.up = b.up;
+  va.route = route;
+  va.vscore = b.vscore;
+  va.sscore = b.sscore;
+  va.floor_v = b.floor_v;
+  va.floor_s = b.floor_s;
+  va.vmask = b.vmask;
+  va.smask = b.smask;
+  va.n_v = b.n_v;
+  va.n_s = b.n_s;
+  va.nblk = N;
+  va.pw2 = host_pow2_ceil(N);
+  va.alpha = alpha;
+  va.gamma = gamma;
+  va.kmin = kmin;
+  va.nf_stat = nf_stat;
+  va.use_gamma = use_gamma ? 1 : 0;
+  const size_t vs_lds = (size_t)va.pw2 * 8 + (size_t)N * 4 + (size_t)N;
+  hipLaunchKernelGGL(vs_select_kernel, dim3(hq, 2), dim3(kVsThreads), vs_lds, stream, va);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  hipLaunchKernelGGL(pe_pool_kernel, dim3(N, hq + hkv), dim3(256), 0, stream, q, k, route, b.qbar, b.kbar, hq, n);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  PeArgs pa;
+  pa.qbar = b.qbar;
+  pa.kbar = b.kbar;
+  pa.route = route;
+  pa.count = count;
+  pa.idx = idx;
+  pa.hq = hq;
+  pa.qpg = hq / hkv;
+  pa.nblk = N;
+  pa.scale_log2 = scale * kLog2e;
+  pa.gamma = use_gamma ? gamma : gamma_pe;
+  const size_t pe_lds = (size_t)host_pow2_ceil(N) * 8 + (size_t)N * 4 + (size_t)N;
+  hipLaunchKernelGGL(pe_select_kernel, dim3(hq * N), dim3(kPeThreads), pe_lds, stream, pa);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  hipLaunchKernelGGL(vs_expand_kernel, dim3(hq * N), dim3(256), 0, stream, route, b.vmask, b.smask, count, idx, hq,
+                     N);
+  return hipGetLastError();
+}
+
+}  // namespace crisp

@@ -1,0 +1,201 @@
+/*
+ * crisp.h - C ABI of the CRISP sparse prefill attention library (gfx950).
+ *
+ * Method: "CRISP: Cliff-awaRe Input-adaptive Sparse Prefilling with
+ * Structural-Mass-Motivated Routing" (arXiv 2609.01925).  Per attention head
+ * the prefill path makes two runtime decisions, which sparse pattern to use
+ * and how many blocks to keep (ai.info summary, "Methodology in Plain
+ * English"), then runs exact softmax attention over what it kept (ai.info
+ * summary, "Why This Matters").  The four calls below are those steps, in
+ * order, plus a dense causal kernel (the speedup denominator) and a
+ * gamma-cumulative selector (the FlexPrefill-style budget rule the paper
+ * compares against, "Main Findings").
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are device pointers to contiguous, head-major arrays:
+ *       q        [Hq][n][d]   bf16, rotary embedding already applied
+ *       k, v     [Hkv][n][d]  bf16, rotary embedding already applied (k)
+ *     Query head h reads KV head h / (Hq / Hkv) (consecutive heads share).
+ *   - Supported shapes: d = 128, block = 128, n a multiple of 128 with
+ *     n >= 256, Hq a multiple of Hkv.  Anything else is CRISP_ERR_SHAPE.
+ *   - Every pointer must be 16-byte aligned (CRISP_ERR_ALIGN otherwise).
+ *   - The caller owns every buffer; the library allocates nothing.  Its only
+ *     global state is a write-once per-device record of whether the device
+ *     is a gfx950, so calls are reentrant.
+ *   - Arguments are validated on the host before anything is launched; a
+ *     failed validation returns an error and leaves all outputs untouched.
+ *   - Work is enqueued asynchronously on `stream` (a hipStream_t, NULL for
+ *     the default stream).  No call synchronises; outputs are valid once
+ *     the stream has completed.  A launch error is CRISP_ERR_LAUNCH.
+ *   - The device must be a gfx950 (CRISP_ERR_DEVICE otherwise).
+ */
+#ifndef CRISP_H
+#define CRISP_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define CRISP_API __attribute__((visibility("default")))
+#else
+#define CRISP_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum crisp_status {
+  CRISP_OK = 0,
+  CRISP_ERR_NULL = 1,      /* a required pointer is NULL */
+  CRISP_ERR_SHAPE = 2,     /* unsupported dimensions */
+  CRISP_ERR_PARAM = 3,     /* a method parameter is out of range */
+  CRISP_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned */
+  CRISP_ERR_WORKSPACE = 5, /* workspace smaller than crisp_select_workspace_bytes */
+  CRISP_ERR_DEVICE = 6,    /* no device, or the current device is not gfx950 */
+  CRISP_ERR_LAUNCH = 7     /* a kernel launch failed */
+} crisp_status;
+
+/* Route codes written by crisp_route (per query head). */
+#define CRISP_ROUTE_PE 0 /* Pooled-Estimation path */
+#define CRISP_ROUTE_VS 1 /* Vertical-Slash path */
+
+/* crisp_cfg.route_override */
+#define CRISP_ROUTE_AUTO 0     /* C_struct >= tau picks VS, else PE */
+#define CRISP_ROUTE_FORCE_VS 1 /* every head VS (exercises the noise floor) */
+#define CRISP_ROUTE_FORCE_PE 2 /* every head PE */
+
+/* crisp_cfg.nf_stat: statistic of the background block mass */
+#define CRISP_NF_MEDIAN 0 /* lower median of the non-retained blocks (default) */
+#define CRISP_NF_MEAN 1   /* their mean (the literal "expected background mass") */
+
+typedef struct crisp_dims {
+  int32_t num_q_heads;  /* Hq */
+  int32_t num_kv_heads; /* Hkv, divides Hq */
+  int32_t seq_len;      /* n, multiple of block, >= 2 * block */
+  int32_t head_dim;     /* d, must be 128 */
+  int32_t block;        /* B, must be 128 */
+  float scale;          /* softmax scale applied to q.k, > 0 (normally 1/sqrt(d)) */
+} crisp_dims;
+
+/* Method parameters (ai.info summary, "Methodology in Plain English":
+ * block 128, k_min = 8 blocks per direction, gamma = 0.95 on PE only,
+ * alpha in {1.0, 1.25} on VS; "Key Contributions": 128-token sink and
+ * recency windows). */
+typedef struct crisp_cfg {
+  float tau;             /* route threshold on C_struct, in [0, 1] */
+  float alpha;           /* noise-floor multiple, > 0 */
+  float gamma_pe;        /* coverage target on PE heads, in (0, 1] */
+  int32_t kmin_blocks;   /* minimum blocks kept per VS direction, >= 1 */
+  int32_t sink_width;    /* first columns counted by C_struct, 1..n/2 */
+  int32_t recency_width; /* last columns counted by C_struct, 1..n/2 */
+  int32_t nf_stat;       /* CRISP_NF_MEDIAN or CRISP_NF_MEAN */
+  int32_t route_override;/* CRISP_ROUTE_AUTO / _FORCE_VS / _FORCE_PE */
+} crisp_cfg;
+
+/* Selection output.  With N = n / 128 blocks, the key-block list of query
+ * block qb of head h is idx[h * N(N+1)/2 + qb(qb+1)/2 + t], t < count[h*N+qb],
+ * ascending, always holding qb (the diagonal).  Optional diagnostics may be
+ * NULL; for PE heads the VS diagnostics are written as zeros. */
+typedef struct crisp_blocks {
+  int32_t* count;   /* [Hq][N], required */
+  int32_t* idx;     /* [Hq][N(N+1)/2], required (crisp_list_capacity entries) */
+  float* v_score;   /* [Hq][N] pooled vertical mass, optional */
+  float* s_score;   /* [Hq][N] pooled slash mass, optional */
+  float* floor_v;   /* [Hq] threshold used on v (alpha * statistic), optional */
+  float* floor_s;   /* [Hq] threshold used on s, optional */
+  int32_t* v_mask;  /* [Hq][N] 1 = vertical block kept, optional */
+  int32_t* s_mask;  /* [Hq][N] 1 = slash block kept, optional */
+  int32_t* n_v;     /* [Hq] kept vertical blocks, optional */
+  int32_t* n_s;     /* [Hq] kept slash blocks, optional */
+} crisp_blocks;
+
+/* Step 1 - proxy attention map (ai.info summary, "Key Contributions" item 2:
+ * C_struct is read off a proxy attention map the method already computes).
+ * The proxy rows are the last 128 query positions of each head, attending
+ * causally to all keys:
+ *   attn_map[h][r][j] = softmax_j(scale * q[h][n-128+r] . k[g(h)][j]), j <= n-128+r,
+ *   and 0 for j > n-128+r.                                 [Hq][128][n] fp32
+ * row_lse (optional, [Hq][128] fp32): natural log of each row's sum of
+ * exp(scale * q.k).  `partials` is scratch of crisp_proxy_scratch_bytes
+ * bytes (caller-owned device memory). */
+CRISP_API crisp_status crisp_proxy(const crisp_dims* dims, const void* q, const void* k, float* attn_map,
+                         float* row_lse, void* partials, size_t partials_bytes, void* stream);
+
+CRISP_API size_t crisp_proxy_scratch_bytes(const crisp_dims* dims);
+
+/* Step 2 - structural-mass routing (ai.info summary, "Key Contributions"
+ * item 2 and "Methodology in Plain English"; ai-feeds summary, method
+ * module 1).  C_struct[h] is the mass of the proxy map on the first
+ * sink_width and the last recency_width key columns, averaged over the 128
+ * proxy rows, so it lies in [0, 1]; route[h] = VS when C_struct >= tau, PE
+ * otherwise, unless cfg->route_override forces one path.
+ * c_struct [Hq] fp32, route [Hq] int32. */
+CRISP_API crisp_status crisp_route(const crisp_dims* dims, const crisp_cfg* cfg, const float* attn_map,
+                         float* c_struct, int32_t* route, void* stream);
+
+/* Step 3 - block selection (ai.info summary, "Methodology in Plain English";
+ * ai-feeds summary, method module 2).
+ *   VS heads: pooled vertical scores v[kb] (column mass of key block kb) and
+ *   slash scores s[b] (mass at query-key offsets 128b..128b+127) from the
+ *   proxy map; per direction the floor is alpha times the lower median (or
+ *   mean) of blocks 1..N-1 (block 0 - the sink, or the local window - is
+ *   always kept and excluded from the estimate); every block above the floor
+ *   is kept, topped up to kmin_blocks by score (ties to the lower index).
+ *   The list of qb is {kept vertical kb <= qb} U {qb-b, qb-b-1 : kept slash b},
+ *   clipped to [0, qb].
+ *   PE heads: mean-pool q and k over 128-token blocks, softmax of
+ *   scale * qbar[qb] . kbar[kb] over kb <= qb, keep the shortest prefix of the
+ *   descending order whose mass reaches gamma_pe, plus qb.
+ * q, k, attn_map: as above; route: [Hq] from crisp_route.  `workspace` must
+ * hold crisp_select_workspace_bytes(dims) bytes of device memory. */
+CRISP_API crisp_status crisp_select(const crisp_dims* dims, const crisp_cfg* cfg, const void* q, const void* k,
+                          const float* attn_map, const int32_t* route, const crisp_blocks* out,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/* Comparison chain - gamma-cumulative coverage on both paths (ai.info
+ * summary, "Main Findings": the budget rule CRISP replaces on VS heads,
+ * and the routing-only ablation).  Same as crisp_select except that each VS
+ * direction keeps the shortest prefix of its blocks (block 0 included) in
+ * descending score order whose mass reaches `gamma`, then block 0 and the
+ * kmin top-up; PE heads use `gamma` instead of cfg->gamma_pe.
+ * gamma in (0, 1]. */
+CRISP_API crisp_status crisp_select_gamma(const crisp_dims* dims, const crisp_cfg* cfg, float gamma, const void* q,
+                                const void* k, const float* attn_map, const int32_t* route,
+                                const crisp_blocks* out, void* workspace, size_t workspace_bytes,
+                                void* stream);
+
+CRISP_API size_t crisp_select_workspace_bytes(const crisp_dims* dims);
+
+/* Number of int32 entries crisp_blocks.idx must hold: Hq * N(N+1)/2. */
+CRISP_API size_t crisp_list_capacity(const crisp_dims* dims);
+
+/* Step 4 - exact block-sparse causal attention (ai.info summary, "Why This
+ * Matters": exact softmax attention over the selected blocks).  For a query
+ * i in block qb the keys are every j <= i lying in a key block of qb's list:
+ *   out[h][i] = sum_j softmax_j(scale * q[h][i] . k[g][j]) v[g][j]
+ * count/idx: the lists produced by crisp_select (entries must satisfy
+ * 0 <= kb <= qb, strictly ascending, last entry qb; count >= 1).
+ * out: [Hq][n][d], bf16 when out_is_fp32 = 0, fp32 otherwise.
+ * lse (optional, [Hq][n] fp32): natural log of each row's sum of exp. */
+CRISP_API crisp_status crisp_sparse_attn(const crisp_dims* dims, const void* q, const void* k, const void* v,
+                               const int32_t* count, const int32_t* idx, void* out, int32_t out_is_fp32,
+                               float* lse, void* stream);
+
+/* Dense causal attention with the same kernel and output conventions
+ * (every key block 0..qb): the exact baseline the speedups are measured
+ * against (ai.info summary, "Main Findings"). */
+CRISP_API crisp_status crisp_dense_attn(const crisp_dims* dims, const void* q, const void* k, const void* v, void* out,
+                              int32_t out_is_fp32, float* lse, void* stream);
+
+/* Static description of a status code. */
+CRISP_API const char* crisp_status_string(crisp_status status);
+
+/* ABI version, (major << 16) | minor. */
+CRISP_API int32_t crisp_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* CRISP_H */

@@ -1,0 +1,120 @@
+"""Comparators between the HIP path and the fp64 oracle.
+
+Tolerances (applied element by element):
+  * route: exact, unless C_struct is within 1e-3 relative of tau;
+  * C_struct: 1e-4 relative;
+  * selected sets: exact, except blocks whose oracle score lies within 1e-3
+    relative of the decision boundary (the floor, the k_min cut, or the
+    gamma cut); a gamma prefix may differ in length by one when the oracle's
+    running sum crosses gamma within 1e-3 relative;
+  * attention: max-abs 1e-2 and mean-abs 1e-3 against fp64, on identical lists.
+"""
+from __future__ import annotations
+
+import math
+from typing import List, Sequence
+
+import numpy as np
+import torch
+
+from oracle import crisp_oracle as O
+
+REL_SEL = 1e-3
+REL_CSTRUCT = 1e-4
+ATTN_MAXABS = 1e-2
+ATTN_MEANABS = 1e-3
+
+
+def to64(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to("cpu").to(torch.float64).numpy()
+
+
+def gpu_lists(count: np.ndarray, idx: np.ndarray, h: int, N: int) -> List[List[int]]:
+    base = h * (N * (N + 1) // 2)
+    out = []
+    for qb in range(N):
+        s = base + qb * (qb + 1) // 2
+        out.append(idx[s:s + int(count[h, qb])].tolist())
+    return out
+
+
+def near(x: float, ref: float, rel: float = REL_SEL) -> bool:
+    return abs(x - ref) <= rel * abs(ref)
+
+
+def check_route(c_oracle: float, tau: float, route_gpu: int, route_oracle: int):
+    if route_gpu != route_oracle:
+        assert near(c_oracle, tau), f"route differs with C_struct={c_oracle} far from tau={tau}"
+
+
+def check_noise_floor_mask(x: np.ndarray, alpha: float, kmin: int, stat: int, mask_gpu: np.ndarray,
+                           floor_gpu: float):
+    mask_o, T = O.noise_floor_select(x, alpha, kmin, stat)
+    assert near(floor_gpu, T), f"floor {floor_gpu} vs oracle {T}"
+    N = x.shape[0]
+    cand = list(range(1, N))
+    order = O._order_desc(x, cand)
+    bounds = [T]
+    want = min(kmin, N)
+    if want - 1 >= 1:
+        bounds.append(float(x[order[want - 2]]))
+    diff = np.nonzero(mask_o != mask_gpu.astype(bool))[0]
+    for b in diff:
+        assert b != 0, "block 0 must always be kept"
+        assert any(near(float(x[b]), t) for t in bounds), (
+            f"block {b} (score {x[b]}) differs away from the boundaries {bounds}")
+    return mask_o
+
+
+def gamma_candidates(x: np.ndarray, items: Sequence[int], gamma: float):
+    """Prefix lengths the GPU may legitimately take, with the cut score of each."""
+    order = O._order_desc(x, list(items))
+    cums = np.cumsum(x[order])
+    K = len(O.gamma_prefix(x, gamma, items))
+    ks = {K}
+    if K >= 2 and cums[K - 2] >= gamma * (1 - REL_SEL):
+        ks.add(K - 1)
+    if K < len(order) and cums[K - 1] <= gamma * (1 + REL_SEL):
+        ks.add(K + 1)
+    return order, sorted(ks)
+
+
+def check_gamma_set(x: np.ndarray, items: Sequence[int], gamma: float, got: set, always: set,
+                    extra_fill: int = 0):
+    """`got` must equal some admissible prefix (plus `always`, plus a k_min
+    fill to `extra_fill` blocks) up to swaps of near-equal scores at the cut."""
+    order, ks = gamma_candidates(x, items, gamma)
+    errs = []
+    for K in ks:
+        ref = set(order[:K]) | set(always)
+        pos = K
+        while len(ref) < extra_fill and pos < len(order):
+            ref.add(order[pos])
+            pos += 1
+        cut_scores = [float(x[order[K - 1]])]
+        if pos > K:
+            cut_scores.append(float(x[order[pos - 1]]))
+        diff = (ref ^ got) - set(always)
+        bad = [b for b in diff if not any(near(float(x[b]), c) for c in cut_scores)]
+        if not bad:
+            return
+        errs.append((K, sorted(bad)[:8]))
+    raise AssertionError(f"gamma set differs beyond the near-cut exemption: {errs}")
+
+
+def check_pe_lists(qbar: np.ndarray, kbar: np.ndarray, scale: float, gamma: float, lists_gpu, qbs=None):
+    N = qbar.shape[0]
+    qbs = range(N) if qbs is None else qbs
+    for qb in qbs:
+        p = O.pe_row_probs(qbar, kbar, qb, scale)
+        got = set(lists_gpu[qb])
+        assert lists_gpu[qb] == sorted(got), "lists must be ascending without repeats"
+        assert qb in got
+        check_gamma_set(p, range(qb + 1), gamma, got, {qb})
+
+
+def check_attention(out_gpu: np.ndarray, out_ref: np.ndarray, what: str = ""):
+    err = np.abs(out_gpu - out_ref)
+    assert err.max() <= ATTN_MAXABS, f"{what} max-abs {err.max()}"
+    assert err.mean() <= ATTN_MEANABS, f"{what} mean-abs {err.mean()}"
+    return float(err.max()), float(err.mean())

@@ -1,0 +1,150 @@
+"""Host-side tests of the C ABI (no GPU): the library loads, exports every
+declared entry point, sizes its buffers as documented and rejects invalid
+arguments before touching the device."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from dynamic_sparse_attention_proxy_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "crisp.h")
+
+# Fake device addresses: never dereferenced, every case fails validation first.
+P16 = 0x10000
+P8 = 0x10008
+
+
+def _declared():
+    text = open(HEADER).read()
+    return re.findall(r"CRISP_API\s+[\w\s\*]+?\b(crisp_\w+)\s*\(", text)
+
+
+def test_library_exports_every_declared_symbol():
+    names = _declared()
+    assert len(names) == 11
+    lib = B.lib()
+    for n in names:
+        assert hasattr(lib, n), n
+    if shutil.which("nm"):
+        out = subprocess.run(["nm", "-D", "--defined-only", B.LIB_PATH], capture_output=True, text=True).stdout
+        exported = set(re.findall(r"\bT (crisp_\w+)", out))
+        assert set(names) == exported
+
+
+def test_abi_version_and_status_strings():
+    assert B.crisp_abi_version() >> 16 == 1
+    lib = B.lib()
+    for s in range(8):
+        assert lib.crisp_status_string(s)
+    assert lib.crisp_status_string(99) == b"unknown status"
+
+
+def test_sizes():
+    d = B.make_dims(32, 8, 524288)
+    N = 524288 // 128
+    assert B.crisp_list_capacity(d) == 32 * N * (N + 1) // 2
+    ws = B.crisp_select_workspace_bytes(d)
+    assert ws >= (32 + 8) * N * 128 * 4 + 4 * 32 * N * 4
+    assert B.crisp_proxy_scratch_bytes(d) >= 32 * 128 * 4
+    bad = B.make_dims(32, 8, 1000)
+    assert B.crisp_list_capacity(bad) == 0
+    assert B.crisp_select_workspace_bytes(bad) == 0
+
+
+def _dense(dims, q=P16, k=P16, v=P16, out=P16, fp32=0, lse=None):
+    return B.lib().crisp_dense_attn(ctypes.byref(dims), q, k, v, out, fp32, lse, None)
+
+
+@pytest.mark.parametrize("hq,hkv,n,d,blk,status", [
+    (32, 8, 1000, 128, 128, 2),    # n not a multiple of the block
+    (32, 8, 128, 128, 128, 2),     # n below two blocks
+    (32, 8, 4096, 64, 128, 2),     # head_dim
+    (32, 8, 4096, 128, 64, 2),     # block
+    (30, 8, 4096, 128, 128, 2),    # Hq % Hkv
+    (32, 0, 4096, 128, 128, 2),
+    (32, 8, 1 << 21, 128, 128, 2), # beyond the supported length
+])
+def test_shape_errors(hq, hkv, n, d, blk, status):
+    dims = B.crisp_dims(hq, hkv, n, d, blk, 0.088)
+    assert _dense(dims) == status
+
+
+def test_pointer_and_param_errors():
+    dims = B.make_dims(4, 2, 1024)
+    assert _dense(dims, q=None) == 1
+    assert _dense(dims, out=P8) == 4
+    assert _dense(dims, lse=P8) == 4
+    assert _dense(dims, fp32=2) == 3
+    bad_scale = B.crisp_dims(4, 2, 1024, 128, 128, -1.0)
+    assert _dense(bad_scale) == 3
+    lib = B.lib()
+    assert lib.crisp_sparse_attn(ctypes.byref(dims), P16, P16, P16, None, P16, P16, 0, None, None) == 1
+    # proxy scratch too small
+    assert lib.crisp_proxy(ctypes.byref(dims), P16, P16, P16, None, P16, 16, None) == 5
+    assert lib.crisp_proxy(None, P16, P16, P16, None, P16, 1 << 30, None) == 1
+
+
+@pytest.mark.parametrize("field,value", [
+    ("tau", 1.5), ("tau", -0.1), ("alpha", 0.0), ("gamma_pe", 0.0), ("gamma_pe", 1.01), ("kmin_blocks", 0),
+    ("sink_width", 0), ("recency_width", 600), ("nf_stat", 2), ("route_override", 3),
+])
+def test_cfg_errors(field, value):
+    dims = B.make_dims(4, 2, 1024)
+    cfg = B.make_cfg()
+    setattr(cfg, field, value)
+    lib = B.lib()
+    assert lib.crisp_route(ctypes.byref(dims), ctypes.byref(cfg), P16, P16, P16, None) == 3
+    blocks = B.crisp_blocks()
+    blocks.count = P16
+    blocks.idx = P16
+    assert lib.crisp_select(ctypes.byref(dims), ctypes.byref(cfg), P16, P16, P16, P16, ctypes.byref(blocks), P16,
+                            1 << 40, None) == 3
+
+
+def test_select_errors():
+    dims = B.make_dims(4, 2, 1024)
+    cfg = B.make_cfg()
+    lib = B.lib()
+    blocks = B.crisp_blocks()
+    blocks.count = P16
+    blocks.idx = None
+    assert lib.crisp_select(ctypes.byref(dims), ctypes.byref(cfg), P16, P16, P16, P16, ctypes.byref(blocks), P16,
+                            1 << 40, None) == 1
+    blocks.idx = P16
+    blocks.v_score = P8
+    assert lib.crisp_select(ctypes.byref(dims), ctypes.byref(cfg), P16, P16, P16, P16, ctypes.byref(blocks), P16,
+                            1 << 40, None) == 4
+    blocks.v_score = None
+    assert lib.crisp_select(ctypes.byref(dims), ctypes.byref(cfg), P16, P16, P16, P16, ctypes.byref(blocks), P16,
+                            64, None) == 5
+    assert lib.crisp_select_gamma(ctypes.byref(dims), ctypes.byref(cfg), 0.0, P16, P16, P16, P16,
+                                  ctypes.byref(blocks), P16, 1 << 40, None) == 3
+    assert lib.crisp_select_gamma(ctypes.byref(dims), ctypes.byref(cfg), 1.2, P16, P16, P16, P16,
+                                  ctypes.byref(blocks), P16, 1 << 40, None) == 3
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(B, "_lib", None)
+    monkeypatch.setattr(B, "LIB_PATH", str(tmp_path / "missing.so"))
+    with pytest.raises(RuntimeError, match="libcrisp.so not found"):
+        B.lib()
+
+
+@pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
+                    reason="needs hipcc for a host build")
+@pytest.mark.parametrize("hq,hkv,nblk,mode", [
+    (32, 8, 4096, 1), (28, 4, 1024, 2), (1, 1, 32, 2), (32, 8, 256, 1), (3, 1, 5, 0), (16, 16, 64, 1), (4, 2, 3, 0),
+])
+def test_row_map_is_a_bijection(tmp_path_factory, hq, hkv, nblk, mode):
+    exe = tmp_path_factory.getbasetemp() / "row_map_check"
+    if not exe.exists():
+        hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+        subprocess.run([hipcc, "-O2", "-std=c++17", os.path.join(ROOT, "tests", "cpp", "row_map_check.cpp"),
+                        "-o", str(exe)], check=True, capture_output=True)
+    r = subprocess.run([str(exe), str(hq), str(hkv), str(nblk), str(mode)], capture_output=True, text=True)
+    assert r.returncode == 0, r.stdout

@@ -1,0 +1,275 @@
+"""GPU parity of the HIP path against the fp64 oracle (needs an MI355X).
+
+Every call goes through the C ABI (libcrisp.so via the ctypes binding);
+the oracle sees the same bf16 bits, generated on the GPU and copied back.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from dynamic_sparse_attention_proxy_amd import binding as B
+from dynamic_sparse_attention_proxy_amd import synth
+from oracle import crisp_oracle as O
+from parity import (REL_CSTRUCT, check_attention, check_gamma_set, check_noise_floor_mask, check_pe_lists,
+                    check_route, gpu_lists, near, to64)
+
+pytestmark = pytest.mark.gpu
+
+BLK = 128
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _cfg_oracle(cfg: B.crisp_cfg) -> O.OracleConfig:
+    return O.OracleConfig(tau=cfg.tau, alpha=cfg.alpha, gamma_pe=cfg.gamma_pe, kmin_blocks=cfg.kmin_blocks,
+                          sink_width=cfg.sink_width, recency_width=cfg.recency_width, nf_stat=cfg.nf_stat,
+                          route_override=cfg.route_override)
+
+
+_INPUTS = {}
+
+
+def inputs(widx, seq_len=None):
+    key = (widx, seq_len)
+    if key not in _INPUTS:
+        print(f"[gen] workload {widx} n={seq_len}", flush=True)
+        _INPUTS[key] = synth.make_inputs(synth.workload(widx), device="cuda", seq_len=seq_len)
+    return _INPUTS[key]
+
+
+def run_chain(x, cfg, gamma=None, out_dtype=torch.float32):
+    hq, hkv, n = x.q.shape[0], x.k.shape[0], x.q.shape[1]
+    dims = B.make_dims(hq, hkv, n)
+    bufs = B.CrispBuffers(dims, out_dtype=out_dtype)
+    B.crisp_prefill(dims, cfg, x.q, x.k, x.v, bufs, gamma=gamma)
+    torch.cuda.synchronize()
+    return dims, bufs
+
+
+# ---------------------------------------------------------------------------
+# attention kernels on given lists
+# ---------------------------------------------------------------------------
+
+
+def test_dense_attention_single_head_4k():
+    x = inputs(0)
+    dims = B.make_dims(1, 1, 4096)
+    out = torch.empty((1, 4096, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((1, 4096), dtype=torch.float32, device="cuda")
+    B.crisp_dense_attn(dims, x.q, x.k, x.v, out, lse)
+    torch.cuda.synchronize()
+    q, k, v = to64(x.q[0]), to64(x.k[0]), to64(x.v[0])
+    ref = O.attention_rows(q, k, v, O.dense_lists(32), dims.scale, range(32))
+    og, lg = out[0].cpu().numpy(), lse[0].cpu().numpy()
+    for qb in range(32):
+        check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"qb {qb}")
+        np.testing.assert_allclose(lg[qb * BLK:(qb + 1) * BLK], ref[qb][1], rtol=2e-5, atol=2e-5)
+    # bf16 output is the fp32 result rounded once
+    outb = torch.empty((1, 4096, 128), dtype=torch.bfloat16, device="cuda")
+    B.crisp_dense_attn(dims, x.q, x.k, x.v, outb)
+    torch.cuda.synchronize()
+    np.testing.assert_array_equal(outb.float().cpu().numpy(), out.to(torch.bfloat16).float().cpu().numpy())
+
+
+def _random_lists(rng, N, kind):
+    lists = []
+    for qb in range(N):
+        if kind == "diag":
+            l = [qb]
+        elif kind == "full":
+            l = list(range(qb + 1))
+        else:
+            l = sorted(set(rng.choice(qb + 1, size=int(rng.integers(1, qb + 2)), replace=False).tolist()) | {qb})
+        lists.append(l)
+    return lists
+
+
+def _pack_lists(all_lists, hq, N):
+    count = np.zeros((hq, N), np.int32)
+    idx = np.zeros(hq * N * (N + 1) // 2, np.int32)
+    for h in range(hq):
+        base = h * N * (N + 1) // 2
+        for qb, l in enumerate(all_lists[h]):
+            count[h, qb] = len(l)
+            s = base + qb * (qb + 1) // 2
+            idx[s:s + len(l)] = l
+    return torch.from_numpy(count).cuda(), torch.from_numpy(idx).cuda()
+
+
+@pytest.mark.parametrize("hq,hkv,n,kind", [
+    (1, 1, 256, "random"),     # smallest length, mode-2 map
+    (3, 1, 640, "random"),     # plain map (3 * 5 blocks)
+    (4, 2, 1024, "diag"),      # local window only
+    (7, 1, 384, "full"),       # 7:1 GQA, full lists = dense
+    (8, 8, 1024, "random"),    # one KV head per query head
+])
+def test_sparse_attention_matches_oracle_on_given_lists(hq, hkv, n, kind):
+    rng = np.random.default_rng(hq * 1000 + n)
+    w = synth.custom(hq, hkv, n, seed=hq + n, needles=2)
+    x = synth.make_inputs(w, device="cuda")
+    N = n // BLK
+    lists = [_random_lists(rng, N, kind) for _ in range(hq)]
+    count, idx = _pack_lists(lists, hq, N)
+    dims = B.make_dims(hq, hkv, n)
+    out = torch.empty((hq, n, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    print(f"[sparse] hq={hq} hkv={hkv} n={n} kind={kind}", flush=True)
+    B.crisp_sparse_attn(dims, x.q, x.k, x.v, count, idx, out, lse)
+    torch.cuda.synchronize()
+    for h in range(hq):
+        g = h * hkv // hq
+        ref = O.attention_rows(to64(x.q[h]), to64(x.k[g]), to64(x.v[g]), lists[h], dims.scale, range(N))
+        og, lg = out[h].cpu().numpy(), lse[h].cpu().numpy()
+        for qb in range(N):
+            check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"h {h} qb {qb}")
+            np.testing.assert_allclose(lg[qb * BLK:(qb + 1) * BLK], ref[qb][1], rtol=2e-5, atol=2e-5)
+    if kind == "full":
+        dense = torch.empty_like(out)
+        B.crisp_dense_attn(dims, x.q, x.k, x.v, dense)
+        torch.cuda.synchronize()
+        assert torch.equal(dense, out)
+
+
+# ---------------------------------------------------------------------------
+# proxy, route, selection on the single-head 4k workload
+# ---------------------------------------------------------------------------
+
+
+def test_proxy_and_route_single_head_4k():
+    x = inputs(0)
+    cfg = B.make_cfg()
+    dims, bufs = run_chain(x, cfg)
+    q, k = to64(x.q[0]), to64(x.k[0])
+    A_o, lse_o = O.proxy_map(q[-BLK:], k, dims.scale)
+    A_g = bufs.attn_map[0].cpu().numpy().astype(np.float64)
+    assert np.abs(A_g - A_o).max() <= 1e-6
+    np.testing.assert_allclose(A_g.sum(axis=1), 1.0, atol=1e-4)
+    for r in range(BLK):
+        assert np.all(A_g[r, 4096 - BLK + r + 1:] == 0.0)
+    np.testing.assert_allclose(bufs.row_lse[0].cpu().numpy(), lse_o, rtol=1e-5, atol=1e-5)
+    c_o = O.c_struct(A_o)
+    c_g = float(bufs.c_struct[0])
+    assert abs(c_g - c_o) <= REL_CSTRUCT * c_o
+    check_route(c_o, cfg.tau, int(bufs.route[0]), O.route(c_o, cfg.tau))
+
+
+@pytest.mark.parametrize("alpha,stat", [(1.25, B.NF_MEDIAN), (1.0, B.NF_MEDIAN), (1.25, B.NF_MEAN)])
+def test_noise_floor_selection_single_head_4k(alpha, stat):
+    x = inputs(0)
+    cfg = B.make_cfg(route_override=B.ROUTE_FORCE_VS, alpha=alpha, nf_stat=stat)
+    dims, bufs = run_chain(x, cfg)
+    hr = O.select_head(to64(x.q[0]), to64(x.k[0]), _cfg_oracle(cfg), dims.scale)
+    N = 32
+    vg = bufs.blocks["v_score"][0].cpu().numpy()
+    sg = bufs.blocks["s_score"][0].cpu().numpy()
+    np.testing.assert_allclose(vg, hr.v, rtol=1e-4, atol=1e-9)
+    np.testing.assert_allclose(sg, hr.sl, rtol=1e-4, atol=1e-9)
+    vm = bufs.blocks["v_mask"][0].cpu().numpy()
+    sm = bufs.blocks["s_mask"][0].cpu().numpy()
+    check_noise_floor_mask(hr.v, alpha, 8, stat, vm, float(bufs.blocks["floor_v"][0]))
+    check_noise_floor_mask(hr.sl, alpha, 8, stat, sm, float(bufs.blocks["floor_s"][0]))
+    assert int(bufs.blocks["n_v"][0]) == int(vm.sum())
+    assert int(bufs.blocks["n_s"][0]) == int(sm.sum())
+    lists_g = gpu_lists(bufs.blocks["count"].cpu().numpy(), bufs.blocks["idx"].cpu().numpy(), 0, N)
+    assert lists_g == O.vs_lists(vm.astype(bool), sm.astype(bool))
+    ref = O.attention_rows(to64(x.q[0]), to64(x.k[0]), to64(x.v[0]), lists_g, dims.scale, range(N))
+    og = bufs.out[0].cpu().numpy()
+    for qb in range(N):
+        check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"qb {qb}")
+
+
+def test_pe_selection_single_head_4k():
+    x = inputs(0)
+    cfg = B.make_cfg(route_override=B.ROUTE_FORCE_PE)
+    dims, bufs = run_chain(x, cfg)
+    q, k = to64(x.q[0]), to64(x.k[0])
+    lists_g = gpu_lists(bufs.blocks["count"].cpu().numpy(), bufs.blocks["idx"].cpu().numpy(), 0, 32)
+    check_pe_lists(O.pe_pool(q), O.pe_pool(k), dims.scale, cfg.gamma_pe, lists_g)
+    assert bufs.blocks["v_mask"].sum().item() == 0
+    ref = O.attention_rows(q, k, to64(x.v[0]), lists_g, dims.scale, range(32))
+    og = bufs.out[0].cpu().numpy()
+    for qb in range(32):
+        check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"qb {qb}")
+
+
+@pytest.mark.parametrize("gamma", [0.95, 0.97])
+def test_gamma_comparison_chain_single_head_4k(gamma):
+    x = inputs(0)
+    cfg = B.make_cfg(route_override=B.ROUTE_FORCE_VS)
+    dims, bufs = run_chain(x, cfg, gamma=gamma)
+    hr = O.select_head(to64(x.q[0]), to64(x.k[0]), _cfg_oracle(cfg), dims.scale, gamma=gamma)
+    for key, xs in (("v_mask", hr.v), ("s_mask", hr.sl)):
+        got = set(np.nonzero(bufs.blocks[key][0].cpu().numpy())[0].tolist())
+        check_gamma_set(xs, range(32), gamma, got, {0}, extra_fill=8)
+
+
+# ---------------------------------------------------------------------------
+# Llama-3.1-8B-shaped 32k layer: every head through proxy/route/select,
+# attention on sampled query blocks
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("override", [B.ROUTE_AUTO, B.ROUTE_FORCE_VS])
+def test_llama_32k_layer(override):
+    x = inputs(1)
+    cfg = B.make_cfg(route_override=override)
+    print(f"[chain] llama 32k override={override}", flush=True)
+    dims, bufs = run_chain(x, cfg)
+    hq, N = 32, 256
+    ocfg = _cfg_oracle(cfg)
+    count = bufs.blocks["count"].cpu().numpy()
+    idx = bufs.blocks["idx"].cpu().numpy()
+    cs = bufs.c_struct.cpu().numpy()
+    rt = bufs.route.cpu().numpy()
+    rng = np.random.default_rng(5)
+    heads = sorted({0, 21, 22, 31} | set(rng.choice(hq, 2, replace=False).tolist()))
+    for h in range(hq):
+        g = h // 4
+        q, k = to64(x.q[h]), to64(x.k[g])
+        A, _ = O.proxy_map(q[-BLK:], k, dims.scale)
+        c_o = O.c_struct(A)
+        assert abs(cs[h] - c_o) <= REL_CSTRUCT * c_o, (h, cs[h], c_o)
+        r_o = O.route(c_o, cfg.tau, override)
+        check_route(c_o, cfg.tau, int(rt[h]), r_o)
+        lists_g = gpu_lists(count, idx, h, N)
+        if rt[h] == O.ROUTE_VS:
+            ct, dg = O.token_scores(A)
+            v, sl = O.pooled_scores(ct, dg)
+            vm = bufs.blocks["v_mask"][h].cpu().numpy()
+            sm = bufs.blocks["s_mask"][h].cpu().numpy()
+            check_noise_floor_mask(v, cfg.alpha, 8, 0, vm, float(bufs.blocks["floor_v"][h]))
+            check_noise_floor_mask(sl, cfg.alpha, 8, 0, sm, float(bufs.blocks["floor_s"][h]))
+            assert lists_g == O.vs_lists(vm.astype(bool), sm.astype(bool))
+        elif h in heads:
+            check_pe_lists(O.pe_pool(q), O.pe_pool(k), dims.scale, cfg.gamma_pe, lists_g,
+                           qbs=[0, 1, 2, 100, 254, 255])
+        if h in heads:
+            qbs = [0, 1, 128, 254, 255]
+            ref = O.attention_rows(q, k, to64(x.v[g]), lists_g, dims.scale, qbs)
+            og = bufs.out[h].cpu().numpy()
+            for qb in qbs:
+                check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"h {h} qb {qb}")
+
+
+def test_chain_is_deterministic():
+    x = inputs(1)
+    cfg = B.make_cfg(route_override=B.ROUTE_FORCE_VS)
+    _, b1 = run_chain(x, cfg)
+    _, b2 = run_chain(x, cfg)
+    assert torch.equal(b1.attn_map, b2.attn_map)
+    for key in ("count", "v_score", "s_score", "v_mask", "s_mask", "floor_v", "floor_s"):
+        assert torch.equal(b1.blocks[key], b2.blocks[key]), key
+    c, i1, i2 = b1.blocks["count"].cpu().numpy(), b1.blocks["idx"].cpu().numpy(), b2.blocks["idx"].cpu().numpy()
+    for h in (0, 13, 31):
+        assert gpu_lists(c, i1, h, 256) == gpu_lists(c, i2, h, 256)
+    assert torch.equal(b1.out, b2.out)
+    assert torch.equal(b1.lse, b2.lse)
