@@ -1,0 +1,287 @@
+"""Prefill attention benchmark: CRISP layer ms and speedup over the dense kernel.
+
+One step = one layer's whole path (proxy -> route -> select -> block-sparse
+attention) on one batch of seeded synthetic inputs already resident in HBM.
+The headline workload is the Llama-3.1-8B-shaped 512k-token layer (32 query
+heads, 8 KV heads, head dim 128); the Qwen2.5-7B-shaped 128k layer is
+reported beside it.  The dense causal kernel, the forced Vertical-Slash
+chain and the gamma-cumulative comparison chains are timed separately.
+
+Prints one JSON line (rank 0, N = 1).
+"""
+import argparse
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+TILE_FLOP = 4 * 128 * 128 * 128  # QK^T + PV of one 128x128 (query block, key block) tile
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+METRIC = "prefill attn ms/layer + speedup vs own dense kernel at 128k/512k, 1 GPU"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--workload", default="llama3.1-8b-512k")
+    ap.add_argument("--secondary", default="qwen2.5-7b-128k", help="extra workload reported beside ('' for none)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-compare", action="store_true", help="skip the gamma comparison chains")
+    ap.add_argument("--only-crisp", action="store_true", help="time the CRISP chain only (profiling runs)")
+    ap.add_argument("--route", choices=["auto", "vs", "pe"], default="auto",
+                    help="route override of the timed CRISP chain (the reported value uses auto)")
+    return ap.parse_args()
+
+
+def kernel_sha():
+    h = hashlib.sha256()
+    for f in ("attn.hip", "common.h"):
+        with open(os.path.join(ROOT, "dynamic_sparse_attention_proxy_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+class Timer:
+    """HIP events on torch's current stream, which is the stream every
+    libcrisp call is enqueued on."""
+
+    def __init__(self, torch):
+        self.torch = torch
+        self.pairs = []
+
+    def __enter__(self):
+        self.a = self.torch.cuda.Event(enable_timing=True)
+        self.b = self.torch.cuda.Event(enable_timing=True)
+        self.a.record()
+        return self
+
+    def __exit__(self, *exc):
+        self.b.record()
+        self.pairs.append((self.a, self.b))
+
+    def ms(self):
+        return [a.elapsed_time(b) for a, b in self.pairs]
+
+
+def run_workload(torch, B, synth, wname, args, cfg_kw, compare):
+    w = synth.workload(wname)
+    log(f"generating {w.name} on the GPU")
+    t0 = time.time()
+    x = synth.make_inputs(w, device="cuda")
+    torch.cuda.synchronize()
+    log(f"generated in {time.time() - t0:.1f}s")
+    dims = B.make_dims(w.num_q_heads, w.num_kv_heads, w.seq_len)
+    N = w.seq_len // 128
+    bufs = B.CrispBuffers(dims, out_dtype=torch.bfloat16)
+    override = {"auto": B.ROUTE_AUTO, "vs": B.ROUTE_FORCE_VS, "pe": B.ROUTE_FORCE_PE}[args.route]
+    cfg = B.make_cfg(**dict(cfg_kw, route_override=override))
+    res = {"workload": w.name}
+
+    def chain(c, gamma, attn_timer=None):
+        B.crisp_proxy(dims, x.q, x.k, bufs.attn_map, bufs.row_lse, bufs.partials)
+        B.crisp_route(dims, c, bufs.attn_map, bufs.c_struct, bufs.route)
+        if gamma is None:
+            B.crisp_select(dims, c, x.q, x.k, bufs.attn_map, bufs.route, bufs.blocks, bufs.workspace)
+        else:
+            B.crisp_select_gamma(dims, c, gamma, x.q, x.k, bufs.attn_map, bufs.route, bufs.blocks, bufs.workspace)
+        if attn_timer is None:
+            B.crisp_sparse_attn(dims, x.q, x.k, x.v, bufs.blocks["count"], bufs.blocks["idx"], bufs.out, bufs.lse)
+        else:
+            with attn_timer:
+                B.crisp_sparse_attn(dims, x.q, x.k, x.v, bufs.blocks["count"], bufs.blocks["idx"], bufs.out,
+                                    bufs.lse)
+
+    def timed_chain(c, gamma, steps, warmup):
+        for _ in range(warmup):
+            chain(c, gamma)
+        torch.cuda.synchronize()
+        at = Timer(torch)
+        t0 = time.perf_counter()
+        ev0 = torch.cuda.Event(enable_timing=True)
+        ev1 = torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        for _ in range(steps):
+            chain(c, gamma, at)
+        ev1.record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - t0) * 1e3 / steps
+        step_ms = ev0.elapsed_time(ev1) / steps
+        tiles = int(bufs.blocks["count"].sum().item())
+        routes = bufs.route.cpu().tolist()
+        attn = at.ms()
+        return {"ms_per_layer": step_ms, "wall_ms_per_layer": wall, "attn_ms": sum(attn) / len(attn),
+                "attn_ms_all": attn, "tiles": tiles, "tile_frac": tiles / (w.num_q_heads * N * (N + 1) / 2),
+                "heads_vs": int(sum(routes)), "heads_pe": len(routes) - int(sum(routes))}
+
+    log(f"{w.name}: CRISP chain (route {args.route}), warmup {args.warmup}, steps {args.steps}")
+    res["crisp"] = timed_chain(cfg, None, args.steps, args.warmup)
+    res["crisp"]["c_struct"] = [round(float(c), 6) for c in bufs.c_struct.cpu().tolist()]
+    log(f"{w.name}: crisp {res['crisp']['ms_per_layer']:.2f} ms")
+    if args.only_crisp:
+        return res, x, dims
+    # dense baseline
+    for _ in range(args.warmup):
+        B.crisp_dense_attn(dims, x.q, x.k, x.v, bufs.out)
+    torch.cuda.synchronize()
+    dt = Timer(torch)
+    for _ in range(args.steps):
+        with dt:
+            B.crisp_dense_attn(dims, x.q, x.k, x.v, bufs.out)
+    torch.cuda.synchronize()
+    d_ms = dt.ms()
+    res["dense"] = {"ms_per_layer": sum(d_ms) / len(d_ms), "ms_all": d_ms,
+                    "tiles": w.num_q_heads * N * (N + 1) // 2}
+    log(f"{w.name}: dense {res['dense']['ms_per_layer']:.2f} ms")
+    # forced Vertical-Slash: the noise-floor selection on every head
+    for alpha in (1.25, 1.0):
+        c = B.make_cfg(**dict(cfg_kw, route_override=B.ROUTE_FORCE_VS, alpha=alpha))
+        r = timed_chain(c, None, args.steps, 1)
+        r["n_v_mean"] = float(bufs.blocks["n_v"].float().mean())
+        r["n_s_mean"] = float(bufs.blocks["n_s"].float().mean())
+        res[f"forced_vs_alpha{alpha}"] = r
+        log(f"{w.name}: forced-VS alpha {alpha}: {r['ms_per_layer']:.2f} ms, {r['tiles']} tiles")
+    if compare:
+        for gamma in (0.95, 0.97):
+            c = B.make_cfg(**dict(cfg_kw, route_override=B.ROUTE_FORCE_VS))
+            r = timed_chain(c, gamma, max(1, args.steps - 1), 0)
+            r["n_v_mean"] = float(bufs.blocks["n_v"].float().mean())
+            r["n_s_mean"] = float(bufs.blocks["n_s"].float().mean())
+            res[f"gamma{gamma}_forced_vs"] = r
+            log(f"{w.name}: gamma {gamma} (VS heads): {r['ms_per_layer']:.2f} ms, {r['tiles']} tiles")
+    dense_ms = res["dense"]["ms_per_layer"]
+    for key in list(res):
+        if isinstance(res[key], dict) and "ms_per_layer" in res[key] and key != "dense":
+            res[key]["speedup_vs_dense"] = dense_ms / res[key]["ms_per_layer"]
+    return res, x, dims
+
+
+def cpu_baseline(q, k, v, dims, res, cfg_kw):
+    """The fp64 oracle on a bounded sample of the same layer (head 0), scaled
+    to ms/layer: per-head proxy/route/scores x Hq, pooled-estimation rows by
+    their length, attention by the tiles the GPU chain computed."""
+    from oracle import crisp_oracle as O
+
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    hq, n = dims.num_q_heads, dims.seq_len
+    N = n // 128
+    ocfg = O.OracleConfig(**{kk: vv for kk, vv in cfg_kw.items() if kk in ("tau", "alpha", "gamma_pe")})
+    t0 = time.perf_counter()
+    A, _ = O.proxy_map(q[-128:], k, dims.scale)
+    c = O.c_struct(A)
+    O.route(c, ocfg.tau)
+    ct, dg = O.token_scores(A)
+    O.pooled_scores(ct, dg)
+    t_head = time.perf_counter() - t0
+    del A
+    t0 = time.perf_counter()
+    qbar, kbar = O.pe_pool(q), O.pe_pool(k)
+    rows = [N - 1 - 7 * i for i in range(24)]
+    lists = {qb: O.pe_row_select(qbar, kbar, qb, dims.scale, ocfg.gamma_pe) for qb in rows}
+    t_rows = time.perf_counter() - t0
+    t_pe_head = t_rows / sum(qb + 1 for qb in rows) * (N * (N + 1) / 2)
+    att_rows = rows[:2]
+    t0 = time.perf_counter()
+    O.attention_rows(q, k, v, lists, dims.scale, att_rows)
+    t_att = time.perf_counter() - t0
+    tiles_sampled = sum(len(lists[qb]) for qb in att_rows)
+    tiles = res["crisp"]["tiles"]
+    total_s = t_head * hq + t_pe_head * res["crisp"]["heads_pe"] + t_att / tiles_sampled * tiles
+    return {"value": round(total_s * 1e3, 1), "unit": "ms", "cores": int(threads), "kind": "oracle",
+            "sample": (f"head 0 of {res['workload']}: proxy map, C_struct and vertical/slash scores in full, "
+                       f"{len(rows)} pooled-estimation rows, attention of query blocks {att_rows} "
+                       f"({tiles_sampled} tiles); scaled to {hq} heads, N(N+1)/2 pooled pairs per PE head "
+                       f"and the {tiles} tiles the GPU chain computed"),
+            "measured_s": round(t_head + t_rows + t_att, 2)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: the CRISP layer is timed on a single MI355X "
+              "(a multi-GPU run would shard whole KV groups with no communication; not built).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+
+    from dynamic_sparse_attention_proxy_amd import binding as B
+    from dynamic_sparse_attention_proxy_amd import synth
+
+    B.lib()
+    torch.cuda.set_device(0)
+    cfg_kw = dict(tau=0.5, alpha=1.25, gamma_pe=0.95)
+    t_start = time.time()
+    main_res, x, dims = run_workload(torch, B, synth, args.workload, args, cfg_kw, compare=not args.no_compare)
+    crisp = main_res["crisp"]
+    value = crisp["ms_per_layer"]
+    achieved = TILE_FLOP * crisp["tiles"] / (crisp["attn_ms"] * 1e-3) / 1e12
+    traffic = None
+    tfile = os.path.join(ROOT, "profiles", "sparse_attn_traffic.json")
+    if os.path.exists(tfile):
+        with open(tfile) as f:
+            t = json.load(f)
+        if t.get("kernel_sha") == kernel_sha() and t.get("workload") == main_res["workload"]:
+            traffic = t.get("hbm_bytes_per_launch")
+    roofline = {"bound": "mfma", "achieved": round(achieved, 2), "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
+                "kernel": "fa_fwd_kernel<false> (crisp_sparse_attn)", "kernel_ms": round(crisp["attn_ms"], 3),
+                "flop_per_launch": TILE_FLOP * crisp["tiles"]}
+    cpu_inputs = None
+    if not args.no_cpu_baseline and not args.only_crisp:
+        g0 = 0
+        cpu_inputs = tuple(t.double().cpu().numpy() for t in (x.q[0], x.k[g0], x.v[g0]))
+    secondary = None
+    if args.secondary and not args.only_crisp:
+        del x
+        torch.cuda.empty_cache()
+        sres, sx, _ = run_workload(torch, B, synth, args.secondary, args, cfg_kw, compare=False)
+        del sx
+        secondary = sres
+    cpu = None
+    if cpu_inputs is not None:
+        log("timing the CPU oracle on a bounded sample")
+        cpu = cpu_baseline(*cpu_inputs, dims, main_res, cfg_kw)
+    speed = main_res.get("dense", {}).get("ms_per_layer")
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "ms",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(value, 3),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Gaussians with planted sink and needles, RoPE; shapes of the named model)",
+        "config": {"workload": main_res["workload"], "num_q_heads": dims.num_q_heads,
+                   "num_kv_heads": dims.num_kv_heads, "seq_len": dims.seq_len, "head_dim": 128, "block": 128,
+                   "route": args.route, **cfg_kw},
+        "speedup_vs_dense": round(speed / value, 4) if speed else None,
+        "dense_ms": round(speed, 3) if speed else None,
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "detail": main_res,
+        "secondary": secondary,
+        "wall_s": round(time.time() - t_start, 1),
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()
