@@ -27,6 +27,7 @@ FLAGS = [
     "-fvisibility=hidden",
     "-Wall",
     "-Wno-unused-command-line-argument",
+    "-fno-honor-nans",  # inputs are finite; lets fmaxf map to v_max3 without canonicalisation
     # packed fp32 ops stay off: ordinary float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE,

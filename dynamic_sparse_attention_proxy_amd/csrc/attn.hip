@@ -17,6 +17,8 @@
 // accumulator registers 0..7 / 8..15 of lane group g hold keys 8g..8g+7 and
 // 16+8g..16+8g+7, the 8 contiguous keys each PV k-group needs.
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -27,6 +29,7 @@ namespace {
 constexpr int kStep = 64;              // keys per pipeline step
 constexpr int kKsStride = kHeadDim + 8; // bf16 per K row in LDS (16 B pad)
 constexpr int kVtStride = kStep + 8;    // bf16 per V^T row in LDS (16 B pad)
+constexpr float kHeadroom = 8.f;        // log2 slack before the running max is raised
 
 struct AttnArgs {
   const __bf16* q;
@@ -138,11 +141,11 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   const int ia = l32 >> 3, ig = (l32 >> 2) & 1, ib = l32 & 3;
   const int krow = 16 * (ia >> 1) + 8 * ig + 4 * (ia & 1) + ib;
 
-  load_step(0);
-  store_step(0);
-  __syncthreads();
-
-  for (int step = 0; step < nsteps; ++step) {
+  // One pipeline step: keys key0 .. key0+63 from LDS stage `cur`, while the
+  // next step's tiles are in flight to registers.  kMasked is only used for
+  // the two steps of the diagonal block, which sorted lists put last.
+  auto do_step = [&](int step, auto masked_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
     const int cur = step & 1;
     const bool more = step + 1 < nsteps;
     if (more) load_step(step + 1);
@@ -163,30 +166,37 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
       }
     }
 
-    // Online softmax, base 2.  The causal mask only touches the diagonal block.
-    const bool diag = (key0 >> 7) == qb;
-    float mx = -INFINITY;
+    if (kMasked) {
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        float t = s[kb2][v] * p.scale_log2;
-        if (diag && (key0 + 32 * kb2 + acc_key(v, lg)) > qpos) t = -INFINITY;
-        s[kb2][v] = t;
-        mx = fmaxf(mx, t);
-      }
+        for (int v = 0; v < 16; ++v)
+          if (key0 + 32 * kb2 + acc_key(v, lg) > qpos) s[kb2][v] = -INFINITY;
+    }
+
+    // Online softmax in base 2 on raw scores: t = s * scale_log2 (> 0 keeps
+    // the order, so the row max is taken before scaling).  The running max
+    // is only raised when a score exceeds it by more than kHeadroom, so
+    // rescaling the accumulator is rare; probabilities stay below
+    // 2^kHeadroom, well inside bf16 and fp32 range.
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int v = 2; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[0][v], s[0][v + 1]));
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[1][v], s[1][v + 1]));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-    if (__any(m_new > m_run)) {
-      const float alpha = fast_exp2(m_run - m_use);
+    const float mxs = mx * p.scale_log2;
+    if (__any(mxs > m_run + kHeadroom)) {
+      const float m_new = fmaxf(m_run, mxs);
+      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
       l_run *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
         for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+      m_run = m_new;
     }
-    m_run = m_new;
+    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
 
     bf16x8 pb[2][2];
 #pragma unroll
@@ -194,7 +204,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
       float e[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        e[v] = fast_exp2(s[kb2][v] - m_use);
+        e[v] = fast_exp2(fmaf(s[kb2][v], p.scale_log2, neg_m));
         l_run += e[v];
       }
       pb[kb2][0] = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
@@ -215,7 +225,15 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
 
     if (more) store_step(cur ^ 1);
     __syncthreads();
-  }
+  };
+
+  load_step(0);
+  store_step(0);
+  __syncthreads();
+  // every block but the last (the diagonal) is fully visible to all rows
+  for (int step = 0; step < nsteps - 2; ++step) do_step(step, std::false_type{});
+  do_step(nsteps - 2, std::true_type{});
+  do_step(nsteps - 1, std::true_type{});
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / l_tot;
