@@ -40,6 +40,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-compare", action="store_true", help="skip the gamma comparison chains")
     ap.add_argument("--only-crisp", action="store_true", help="time the CRISP chain only (profiling runs)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run one 1 GiB device-to-device copy first (HBM counter calibration)")
     ap.add_argument("--route", choices=["auto", "vs", "pe"], default="auto",
                     help="route override of the timed CRISP chain (the reported value uses auto)")
     return ap.parse_args()
@@ -223,6 +225,13 @@ def main():
 
     B.lib()
     torch.cuda.set_device(0)
+    if args.calibrate_copy:
+        src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log("calibration copy: 1 GiB read + 1 GiB written")
+        del src, dst
     cfg_kw = dict(tau=0.5, alpha=1.25, gamma_pe=0.95)
     t_start = time.time()
     main_res, x, dims = run_workload(torch, B, synth, args.workload, args, cfg_kw, compare=not args.no_compare)
