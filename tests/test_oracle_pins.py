@@ -499,7 +499,7 @@ def test_diagonal_only_is_local_window():
 
 
 # --------------------------------------------------------------------------
-# spec check 4 on structured inputs through the whole selection
+# the O(n) claim on structured inputs through the whole selection
 # --------------------------------------------------------------------------
 
 
