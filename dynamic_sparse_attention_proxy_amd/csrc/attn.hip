@@ -27,9 +27,10 @@ namespace crisp {
 namespace {
 
 constexpr int kStep = 64;              // keys per pipeline step
-constexpr int kKsStride = kHeadDim + 8; // bf16 per K row in LDS (16 B pad)
-constexpr int kVtStride = kStep + 8;    // bf16 per V^T row in LDS (16 B pad)
+typedef __bf16 gcc_bf16x4 __attribute__((__vector_size__(8)));
+typedef __attribute__((address_space(3))) gcc_bf16x4 lds_bf16x4;
 constexpr float kHeadroom = 8.f;        // log2 slack before the running max is raised
+constexpr int kBufferFlags = 0x00020000; // buffer resource word 3: raw 32-bit data, no swizzle
 
 struct AttnArgs {
   const __bf16* q;
@@ -47,13 +48,16 @@ struct AttnArgs {
   RowMap map;
 };
 
+// LDS chunk swizzle of row r: bits (r3, r0, r1) into chunk bits (0, 1, 2).
+__device__ __forceinline__ int swz(int r) { return ((r >> 3) & 1) | ((r & 3) << 1); }
+
 // Key index (0..31) held by accumulator register v of lane group lg.
 __device__ __forceinline__ int acc_key(int v, int lg) { return (v < 8) ? (8 * lg + v) : (16 + 8 * lg + (v - 8)); }
 
 template <bool kDense>
 __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
-  __shared__ __attribute__((aligned(16))) __bf16 ks[2][kStep * kKsStride];
-  __shared__ __attribute__((aligned(16))) __bf16 vt[2][kHeadDim * kVtStride];
+  __shared__ __attribute__((aligned(1024))) __bf16 ks[2][kStep * kHeadDim];
+  __shared__ __attribute__((aligned(1024))) __bf16 vs[2][kStep * kHeadDim];
 
   int h, qb;
   map_row(p.map, blockIdx.x, &h, &qb);
@@ -92,86 +96,105 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
     for (int v = 0; v < 16; ++v) o[db][v] = 0.f;
   float m_run = -INFINITY, l_run = 0.f;
 
-  // Global -> register staging of one step.
-  // K: 64 rows x 16 chunks of 16 B; thread takes chunks tid + 256 i.
-  // V: thread takes a 4-key x 8-d sub-block (keys 4*kq.., d 8*dc..).
-  const int kq = tid >> 4, dc = tid & 15;
-  u32x4 kreg[4], vreg[4];
+  // Global -> LDS by DMA (buffer_load ... lds): each wave instruction fills
+  // 1 KiB of LDS, lane L at byte 16 L.  K and V tiles are stored row-major
+  // (a 64-key step is 64 rows of 256 B) with the 16-byte chunk c of row r at
+  // chunk position c ^ swz(r).  swz spreads the two read patterns over the
+  // banks: the K operand (8 lanes read one chunk of rows {0..3, 8..11} + 4k)
+  // and the transposing V^T read (16 lanes read 2 chunks of 4 consecutive
+  // rows).  Wave w fills rows 16w .. 16w+15 with 4 instructions; lane L of
+  // instruction i writes row r = 16w + 4i + L/16 at position L & 15, so it
+  // loads global chunk (L & 15) ^ swz(r) of that row.
+  const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kg, 0, (int)(nd * 2), kBufferFlags);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vg, 0, (int)(nd * 2), kBufferFlags);
+  int dma_off[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * w + 4 * i + (lane >> 4);
+    dma_off[i] = r * 256 + (((lane & 15) ^ swz(r)) << 4);
+  }
 
   auto step_key0 = [&](int step) -> int {
     const int kb = kDense ? (step >> 1) : min(max(list[step >> 1], 0), qb);
     return kb * kBlock + (step & 1) * kStep;
   };
 
-  auto load_step = [&](int step) {
-    const int key0 = step_key0(step);
+  auto dma = [&](__amdgpu_buffer_rsrc_t rs, __bf16* stage, int step) {
+    const int soff = step_key0(step) * (kHeadDim * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 4, col = (c & 15) * 8;
-      kreg[i] = *(const u32x4*)(kg + (size_t)(key0 + row) * kHeadDim + col);
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i) vreg[i] = *(const u32x4*)(vg + (size_t)(key0 + 4 * kq + i) * kHeadDim + 8 * dc);
-  };
-
-  auto store_step = [&](int stage) {
-    __bf16* kdst = ks[stage];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int c = tid + 256 * i;
-      const int row = c >> 4, col = (c & 15) * 8;
-      *(u32x4*)(kdst + row * kKsStride + col) = kreg[i];
-    }
-    __bf16* vdst = vt[stage];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      // d = 8dc + 2j (low halves) and 8dc + 2j + 1 (high halves) of keys 4kq..4kq+3
-      u32x2 ev, od;
-      ev[0] = (vreg[0][j] & 0xffffu) | (vreg[1][j] << 16);
-      ev[1] = (vreg[2][j] & 0xffffu) | (vreg[3][j] << 16);
-      od[0] = (vreg[0][j] >> 16) | (vreg[1][j] & 0xffff0000u);
-      od[1] = (vreg[2][j] >> 16) | (vreg[3][j] & 0xffff0000u);
-      *(u32x2*)(vdst + (8 * dc + 2 * j) * kVtStride + 4 * kq) = ev;
-      *(u32x2*)(vdst + (8 * dc + 2 * j + 1) * kVtStride + 4 * kq) = od;
-    }
+    for (int i = 0; i < 4; ++i)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + (16 * w + 4 * i) * kHeadDim),
+                                               16, dma_off[i], soff, 0, 0);
   };
 
   // Row of the K operand fed by this lane: a permutation of 0..31 (see top).
   const int ia = l32 >> 3, ig = (l32 >> 2) & 1, ib = l32 & 3;
   const int krow = 16 * (ia >> 1) + 8 * ig + 4 * (ia & 1) + ib;
+  // Byte offsets of this lane's K operand: row 32 kb2 + krow, logical chunk
+  // 2 kk + lg.  swz only touches chunk bits 0..2, so kk bit 2 and kb2 are
+  // plain immediates: 4 base offsets for kk = 0..3.
+  int k_off[4];
+#pragma unroll
+  for (int kk = 0; kk < 4; ++kk) k_off[kk] = krow * 256 + (((2 * kk + lg) ^ swz(krow)) << 4);
+  // V^T operand through the transposing LDS read: within each 16-lane group
+  // (gq = lane / 16, li = lane % 16) lane li receives element li % 4 of the
+  // 4-element vectors addressed by lanes 4e + li / 4 (e = 0..3).  A lane
+  // addresses row k0 + li / 4, columns d0 + 4 (li % 4) .. +3, so it gets
+  // keys k0 .. k0+3 at column d0 + li.  For the A operand of O^T += V^T P^T
+  // (row d = 32 db + l32, keys 32 kb2 + 16 mm + 8 lg + s) two reads
+  // (s = 0..3, hh = 0, and s = 4..7, hh = 1) give the 8 slots.  Rows differ
+  // by 4 hh + 16 mm + 32 kb2 and columns by 64 B per db >= 2, none of which
+  // changes swz, so 2 base offsets (db & 1) cover every read.
+  const int gq = lane >> 4, li = lane & 15;
+  int v_base[2];
+#pragma unroll
+  for (int d0 = 0; d0 < 2; ++d0) {
+    const int r = 8 * (gq >> 1) + (li >> 2);
+    const int d = 32 * d0 + 16 * (gq & 1) + 4 * (li & 3);
+    v_base[d0] = r * 256 + (((d >> 3) ^ swz(r)) << 4) + (d & 7) * 2;
+  }
+  auto v_off = [&](int db, int kb2, int mm, int hh) -> int {
+    return v_base[db & 1] + (db >> 1) * 128 + (32 * kb2 + 16 * mm + 4 * hh) * 256;
+  };
 
-  // One pipeline step: keys key0 .. key0+63 from LDS stage `cur`, while the
-  // next step's tiles are in flight to registers.  kMasked is only used for
-  // the two steps of the diagonal block, which sorted lists put last.
-  auto do_step = [&](int step, auto masked_tag) {
-    constexpr bool kMasked = decltype(masked_tag)::value;
-    const int cur = step & 1;
-    const bool more = step + 1 < nsteps;
-    if (more) load_step(step + 1);
-
-    const int key0 = step_key0(step);
-    const __bf16* kbuf = ks[cur];
-    const __bf16* vbuf = vt[cur];
-
-    f32x16 s[2];
+  auto qk = [&](const __bf16* kbuf, f32x16 (&s)[2]) {
+    const char* kb8 = (const char*)kbuf;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) s[kb2][v] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 kf = as_bf16x8(*(const u32x4*)(kbuf + (32 * kb2 + krow) * kKsStride + 16 * kk + 8 * lg));
+        const bf16x8 kf = as_bf16x8(*(const u32x4*)(kb8 + k_off[kk & 3] + (kk >> 2) * 128 + kb2 * 8192));
         s[kb2] = mfma32(kf, qf[kk], s[kb2]);
       }
     }
+  };
+
+  // Iteration j of the software pipeline.  K and V have separate double
+  // buffers: K_t lives in ks[t & 1], V_t in vs[t & 1].  Iteration j
+  //   - starts the DMA of K_{j+2} over K_j (read in iteration j-1) and of
+  //     V_{j+1} over V_{j-1} (read in iteration j-1),
+  //   - computes S_{j+1} = K_{j+1} Q^T (MFMA) in the same basic block as the
+  //     softmax of S_j (VALU), so the two overlap,
+  //   - accumulates O += V_j P_j,
+  //   - waits for its DMA and meets the others at one barrier.
+  // kMasked marks the two steps of the diagonal block (sorted lists put it
+  // last); kNext is false on the final step.
+  auto iter = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2], auto masked_tag, auto next_tag) {
+    constexpr bool kMasked = decltype(masked_tag)::value;
+    constexpr bool kNext = decltype(next_tag)::value;
+    if (j + 2 < nsteps) dma(krs, ks[j & 1], j + 2);
+    if (j + 1 < nsteps) dma(vrs, vs[(j + 1) & 1], j + 1);
+    if (kNext) qk(ks[(j + 1) & 1], sn);
 
     if (kMasked) {
+      const int key0 = step_key0(j);
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int v = 0; v < 16; ++v)
-          if (key0 + 32 * kb2 + acc_key(v, lg) > qpos) s[kb2][v] = -INFINITY;
+          if (key0 + 32 * kb2 + acc_key(v, lg) > qpos) sc[kb2][v] = -INFINITY;
     }
 
     // Online softmax in base 2 on raw scores: t = s * scale_log2 (> 0 keeps
@@ -179,23 +202,18 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
     // is only raised when a score exceeds it by more than kHeadroom, so
     // rescaling the accumulator is rare; probabilities stay below
     // 2^kHeadroom, well inside bf16 and fp32 range.
-    float mx = fmaxf(s[0][0], s[0][1]);
+    float mx = fmaxf(sc[0][0], sc[0][1]);
 #pragma unroll
-    for (int v = 2; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[0][v], s[0][v + 1]));
+    for (int v = 2; v < 16; v += 2) mx = fmaxf(mx, fmaxf(sc[0][v], sc[0][v + 1]));
 #pragma unroll
-    for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[1][v], s[1][v + 1]));
+    for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(sc[1][v], sc[1][v + 1]));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float mxs = mx * p.scale_log2;
-    if (__any(mxs > m_run + kHeadroom)) {
-      const float m_new = fmaxf(m_run, mxs);
-      const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-      l_run *= alpha;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
-      m_run = m_new;
-    }
+    const bool raise = __any(mxs > m_run + kHeadroom);
+    const float m_new = raise ? fmaxf(m_run, mxs) : m_run;
+    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
+    m_run = m_new;
+    l_run *= alpha;
     const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
 
     bf16x8 pb[2][2];
@@ -204,36 +222,57 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
       float e[16];
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        e[v] = fast_exp2(fmaf(s[kb2][v], p.scale_log2, neg_m));
+        e[v] = fast_exp2(fmaf(sc[kb2][v], p.scale_log2, neg_m));
         l_run += e[v];
       }
       pb[kb2][0] = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
       pb[kb2][1] = pack_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
     }
 
+    if (raise) {
 #pragma unroll
-    for (int db = 0; db < 4; ++db) {
-      const __bf16* vrow = vbuf + (32 * db + l32) * kVtStride + 8 * lg;
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+    }
+
+    __attribute__((address_space(3))) char* vb8 = (__attribute__((address_space(3))) char*)vs[j & 1];
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int mm = 0; mm < 2; ++mm) {
-          const bf16x8 vf = as_bf16x8(*(const u32x4*)(vrow + 32 * kb2 + 16 * mm));
+          const bf16x4 lo = __builtin_bit_cast(
+              bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb8 + v_off(db, kb2, mm, 0))));
+          const bf16x4 hi = __builtin_bit_cast(
+              bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb8 + v_off(db, kb2, mm, 1))));
+          const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           o[db] = mfma32(vf, pb[kb2][mm], o[db]);
         }
-    }
 
-    if (more) store_step(cur ^ 1);
+    wait_dma();
     __syncthreads();
   };
 
-  load_step(0);
-  store_step(0);
+  f32x16 sa[2], sb[2];
+  dma(krs, ks[0], 0);
+  dma(vrs, vs[0], 0);
+  if (nsteps > 1) dma(krs, ks[1], 1);
+  wait_dma();
   __syncthreads();
-  // every block but the last (the diagonal) is fully visible to all rows
-  for (int step = 0; step < nsteps - 2; ++step) do_step(step, std::false_type{});
-  do_step(nsteps - 2, std::true_type{});
-  do_step(nsteps - 1, std::true_type{});
+  qk(ks[0], sa);
+  __syncthreads();  // every wave has read K_0 before iteration 0 overwrites it
+
+  // every block but the last (the diagonal) is fully visible to all rows;
+  // nsteps - 2 is even, so the loop alternates the two score buffers
+  int j = 0;
+  for (; j < nsteps - 2; j += 2) {
+    iter(j, sa, sb, std::false_type{}, std::true_type{});
+    iter(j + 1, sb, sa, std::false_type{}, std::true_type{});
+  }
+  iter(j, sa, sb, std::true_type{}, std::true_type{});
+  iter(j + 1, sb, sa, std::true_type{}, std::false_type{});
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / l_tot;
