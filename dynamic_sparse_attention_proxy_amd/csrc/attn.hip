@@ -114,13 +114,22 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
     dma_off[i] = r * 256 + (((lane & 15) ^ swz(r)) << 4);
   }
 
-  auto step_key0 = [&](int step) -> int {
-    const int kb = kDense ? (step >> 1) : min(max(list[step >> 1], 0), qb);
-    return kb * kBlock + (step & 1) * kStep;
+  // List entries are fetched with vector buffer loads two blocks ahead and
+  // moved to scalar registers when used: a scalar load here would be waited
+  // for by every LDS wait that follows it.  Entries past `cnt` read as 0, and
+  // every entry is clamped to [0, qb], so reads stay inside the head's rows.
+  const __amdgpu_buffer_rsrc_t lrs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)list, 0, kDense ? 0 : cnt * 4, kBufferFlags);
+  auto fetch_block = [&](int b) -> int {
+    return kDense ? b : __builtin_amdgcn_raw_buffer_load_b32(lrs, 0, b * 4, 0);
   };
+  auto use_block = [&](int fetched) -> int {
+    return kDense ? fetched : min(max(__builtin_amdgcn_readfirstlane(fetched), 0), qb);
+  };
+  auto key0_of = [&](int kb, int step) -> int { return kb * kBlock + (step & 1) * kStep; };
 
-  auto dma = [&](__amdgpu_buffer_rsrc_t rs, __bf16* stage, int step) {
-    const int soff = step_key0(step) * (kHeadDim * 2);
+  auto dma = [&](__amdgpu_buffer_rsrc_t rs, __bf16* stage, int kb, int step) {
+    const int soff = key0_of(kb, step) * (kHeadDim * 2);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + (16 * w + 4 * i) * kHeadDim),
@@ -181,15 +190,17 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   //   - waits for its DMA and meets the others at one barrier.
   // kMasked marks the two steps of the diagonal block (sorted lists put it
   // last); kNext is false on the final step.
-  auto iter = [&](int j, f32x16 (&sc)[2], f32x16 (&sn)[2], auto masked_tag, auto next_tag) {
+  // kb0, kb1, kb2: key blocks of steps j, j+1, j+2.
+  auto iter = [&](int j, int kb0, int kb1, int kb2s, f32x16 (&sc)[2], f32x16 (&sn)[2], auto masked_tag,
+                  auto next_tag) {
     constexpr bool kMasked = decltype(masked_tag)::value;
     constexpr bool kNext = decltype(next_tag)::value;
-    if (j + 2 < nsteps) dma(krs, ks[j & 1], j + 2);
-    if (j + 1 < nsteps) dma(vrs, vs[(j + 1) & 1], j + 1);
+    if (j + 2 < nsteps) dma(krs, ks[j & 1], kb2s, j + 2);
+    if (j + 1 < nsteps) dma(vrs, vs[(j + 1) & 1], kb1, j + 1);
     if (kNext) qk(ks[(j + 1) & 1], sn);
 
     if (kMasked) {
-      const int key0 = step_key0(j);
+      const int key0 = key0_of(kb0, j);
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -256,23 +267,31 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   };
 
   f32x16 sa[2], sb[2];
-  dma(krs, ks[0], 0);
-  dma(vrs, vs[0], 0);
-  if (nsteps > 1) dma(krs, ks[1], 1);
+  int f0 = fetch_block(0), f1 = fetch_block(1);
+  wait_dma();
+  int kb_cur = use_block(f0), kb_nxt = use_block(f1);
+  int pf = fetch_block(2);
+  dma(krs, ks[0], kb_cur, 0);
+  dma(vrs, vs[0], kb_cur, 0);
+  dma(krs, ks[1], kb_cur, 1);
   wait_dma();
   __syncthreads();
   qk(ks[0], sa);
   __syncthreads();  // every wave has read K_0 before iteration 0 overwrites it
 
-  // every block but the last (the diagonal) is fully visible to all rows;
-  // nsteps - 2 is even, so the loop alternates the two score buffers
+  // Every block but the last (the diagonal) is fully visible to all rows.
+  // Each pass handles the two steps of block j/2 (kb_cur); nsteps - 2 is
+  // even, so the loop alternates the two score buffers.
   int j = 0;
   for (; j < nsteps - 2; j += 2) {
-    iter(j, sa, sb, std::false_type{}, std::true_type{});
-    iter(j + 1, sb, sa, std::false_type{}, std::true_type{});
+    iter(j, kb_cur, kb_cur, kb_nxt, sa, sb, std::false_type{}, std::true_type{});
+    iter(j + 1, kb_cur, kb_nxt, kb_nxt, sb, sa, std::false_type{}, std::true_type{});
+    kb_cur = kb_nxt;
+    kb_nxt = use_block(pf);  // landed: every iteration ends with a full vmcnt wait
+    pf = fetch_block((j >> 1) + 3);
   }
-  iter(j, sa, sb, std::true_type{}, std::true_type{});
-  iter(j + 1, sb, sa, std::true_type{}, std::false_type{});
+  iter(j, kb_cur, kb_cur, kb_nxt, sa, sb, std::true_type{}, std::true_type{});
+  iter(j + 1, kb_cur, kb_nxt, kb_nxt, sb, sa, std::true_type{}, std::false_type{});
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / l_tot;

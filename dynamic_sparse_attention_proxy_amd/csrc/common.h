@@ -240,12 +240,13 @@ __device__ inline float block_max_f(float x, float* lds_tmp, int tid, int nthrea
   return r;
 }
 
-// Workgroup -> (head, query block) map shared by the attention kernels.
-// Work is dealt heaviest first (query block N-1 first, since causal rows
-// grow with qb) and so that all workgroups on one XCD - which share that
-// die's L2 - read the same KV group.
+// Workgroup -> (head, query block) map of the attention kernels.  Work is
+// ordered KV group by KV group, and within a group by query block from the
+// last (heaviest: causal rows grow with qb) to the first, heads of the group
+// adjacent.  Workgroup ids are dealt round-robin to the 8 XCDs, so at any
+// time every die works on the same KV group: each die's L2 and the shared
+// last-level cache hold one group's K/V instead of all of them.
 struct RowMap {
-  int mode;  // 1: Hkv % 8 == 0, 2: 8 % Hkv == 0, 0: plain order
   int hq, hkv, qpg, nblk;
 };
 
@@ -255,35 +256,14 @@ inline RowMap make_row_map(int hq, int hkv, int nblk) {
   m.hkv = hkv;
   m.qpg = hq / hkv;
   m.nblk = nblk;
-  const long long total = (long long)hq * nblk;
-  if (hkv % kNumXcd == 0 && hq % kNumXcd == 0)
-    m.mode = 1;
-  else if (kNumXcd % hkv == 0 && ((long long)m.qpg * nblk) % (kNumXcd / hkv) == 0 && total % kNumXcd == 0)
-    m.mode = 2;
-  else
-    m.mode = 0;
   return m;
 }
 
 __host__ __device__ inline void map_row(const RowMap& m, int id, int* h_out, int* qb_out) {
-  if (m.mode == 1) {
-    const int xcd = id % kNumXcd, s = id / kNumXcd;
-    const int hpx = m.hq / kNumXcd;
-    const int l = s % hpx;
-    const int grp = xcd + kNumXcd * (l / m.qpg);
-    *h_out = grp * m.qpg + l % m.qpg;
-    *qb_out = m.nblk - 1 - s / hpx;
-  } else if (m.mode == 2) {
-    const int xcd = id % kNumXcd, s = id / kNumXcd;
-    const int xpg = kNumXcd / m.hkv;
-    const int g = xcd % m.hkv, sub = xcd / m.hkv;
-    const int t = s * xpg + sub;
-    *h_out = g * m.qpg + t % m.qpg;
-    *qb_out = m.nblk - 1 - t / m.qpg;
-  } else {
-    *h_out = id % m.hq;
-    *qb_out = m.nblk - 1 - id / m.hq;
-  }
+  const int per_group = m.qpg * m.nblk;
+  const int g = id / per_group, rem = id - g * per_group;
+  *h_out = g * m.qpg + rem % m.qpg;
+  *qb_out = m.nblk - 1 - rem / m.qpg;
 }
 
 }  // namespace crisp

@@ -1,7 +1,6 @@
-// Host check of the workgroup -> (head, query block) map used by the
-// attention kernels: it must be a bijection onto Hq x N, deal each XCD one
-// KV group per die where the shape allows, and hand out heavier (larger qb)
-// rows no later than lighter ones on each XCD.
+// Host check of the workgroup -> (head, query block) map of the attention
+// kernels: a bijection onto Hq x N, ordered KV group by KV group, and within
+// a group from the heaviest query block (the last) to the lightest.
 #include <cstdio>
 #include <cstdlib>
 #include <vector>
@@ -9,16 +8,11 @@
 #include "../../dynamic_sparse_attention_proxy_amd/csrc/common.h"
 
 int main(int argc, char** argv) {
-  if (argc != 5) return 2;
-  const int hq = atoi(argv[1]), hkv = atoi(argv[2]), nblk = atoi(argv[3]), want_mode = atoi(argv[4]);
+  if (argc != 4) return 2;
+  const int hq = atoi(argv[1]), hkv = atoi(argv[2]), nblk = atoi(argv[3]);
   crisp::RowMap m = crisp::make_row_map(hq, hkv, nblk);
-  if (m.mode != want_mode) {
-    printf("mode %d, expected %d\n", m.mode, want_mode);
-    return 1;
-  }
   std::vector<int> seen((size_t)hq * nblk, 0);
-  std::vector<int> last_qb(crisp::kNumXcd, 1 << 30);
-  std::vector<int> xcd_group(crisp::kNumXcd, -1);
+  int prev_g = 0, prev_qb = nblk;
   for (int id = 0; id < hq * nblk; ++id) {
     int h = -1, qb = -1;
     crisp::map_row(m, id, &h, &qb);
@@ -30,23 +24,15 @@ int main(int argc, char** argv) {
       printf("id %d -> (%d, %d) duplicated\n", id, h, qb);
       return 1;
     }
-    const int x = id % crisp::kNumXcd;
-    if (m.mode != 0) {
-      if (qb > last_qb[x]) {
-        printf("xcd %d: qb %d after %d\n", x, qb, last_qb[x]);
-        return 1;
-      }
-      last_qb[x] = qb;
-      const int g = h / m.qpg;
-      if (hkv <= crisp::kNumXcd) {
-        if (xcd_group[x] >= 0 && xcd_group[x] != g) {
-          printf("xcd %d sees groups %d and %d\n", x, xcd_group[x], g);
-          return 1;
-        }
-        xcd_group[x] = g;
-      }
+    const int g = h / m.qpg;
+    if (g < prev_g || (g == prev_g && qb > prev_qb)) {
+      printf("id %d -> group %d qb %d after group %d qb %d\n", id, g, qb, prev_g, prev_qb);
+      return 1;
     }
+    if (g != prev_g) prev_qb = nblk;
+    prev_g = g;
+    prev_qb = qb;
   }
-  printf("ok mode %d\n", m.mode);
+  printf("ok\n");
   return 0;
 }
