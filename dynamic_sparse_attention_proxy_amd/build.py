@@ -28,6 +28,7 @@ FLAGS = [
     "-Wall",
     "-Wno-unused-command-line-argument",
     "-fno-honor-nans",  # inputs are finite; lets fmaxf map to v_max3 without canonicalisation
+    "-Wno-inline-asm",  # the LDS-DMA asm names m0, which it sets itself
     # packed fp32 ops stay off: ordinary float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-I", INCLUDE,

@@ -29,6 +29,7 @@ namespace {
 constexpr int kStep = 64;              // keys per pipeline step
 typedef __bf16 gcc_bf16x4 __attribute__((__vector_size__(8)));
 typedef __attribute__((address_space(3))) gcc_bf16x4 lds_bf16x4;
+constexpr int kKStages = 3;             // K tiles in flight: the next one is used, one more prefetched
 constexpr float kHeadroom = 8.f;        // log2 slack before the running max is raised
 constexpr int kBufferFlags = 0x00020000; // buffer resource word 3: raw 32-bit data, no swizzle
 
@@ -48,15 +49,24 @@ struct AttnArgs {
   RowMap map;
 };
 
-// LDS chunk swizzle of row r: bits (r3, r0, r1) into chunk bits (0, 1, 2).
-__device__ __forceinline__ int swz(int r) { return ((r >> 3) & 1) | ((r & 3) << 1); }
+// LDS chunk swizzles (chunk position = chunk ^ swz(row)), chosen from
+// measured bank-conflict counts on gfx950.  The K operand read has 16 lanes
+// reading one chunk of rows {0..3, 8..11, 4..7, 12..15} (+ multiples of 16):
+// any bijection of the row's low 4 bits keeps them apart; this one sends
+// (r0, r1) to chunk bits (2, 3) and (r2, r3) to (0, 1).  The transposing
+// V^T read has 32 lanes reading chunks c0 .. c0+3 of 4 consecutive rows: the
+// row's bits 0-1 must move the chunk's bits 2-3, which (r & 3) << 2 does
+// while leaving the other row bits free (so those offsets stay additive).
+__device__ __forceinline__ int swz_k(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 2; }
 
 // Key index (0..31) held by accumulator register v of lane group lg.
 __device__ __forceinline__ int acc_key(int v, int lg) { return (v < 8) ? (8 * lg + v) : (16 + 8 * lg + (v - 8)); }
 
 template <bool kDense>
 __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
-  __shared__ __attribute__((aligned(1024))) __bf16 ks[2][kStep * kHeadDim];
+  // 48 KiB of K stages + 32 KiB of V stages: two workgroups fill a CU's 160 KiB.
+  __shared__ __attribute__((aligned(1024))) __bf16 ks[kKStages][kStep * kHeadDim];
   __shared__ __attribute__((aligned(1024))) __bf16 vs[2][kStep * kHeadDim];
 
   int h, qb;
@@ -99,52 +109,66 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   // Global -> LDS by DMA (buffer_load ... lds): each wave instruction fills
   // 1 KiB of LDS, lane L at byte 16 L.  K and V tiles are stored row-major
   // (a 64-key step is 64 rows of 256 B) with the 16-byte chunk c of row r at
-  // chunk position c ^ swz(r).  swz spreads the two read patterns over the
-  // banks: the K operand (8 lanes read one chunk of rows {0..3, 8..11} + 4k)
-  // and the transposing V^T read (16 lanes read 2 chunks of 4 consecutive
-  // rows).  Wave w fills rows 16w .. 16w+15 with 4 instructions; lane L of
+  // chunk position c ^ swz(r), one swizzle per tile (see swz_k, swz_v).
+  // Wave w fills rows 16w .. 16w+15 with 4 instructions; lane L of
   // instruction i writes row r = 16w + 4i + L/16 at position L & 15, so it
   // loads global chunk (L & 15) ^ swz(r) of that row.
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kg, 0, (int)(nd * 2), kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vg, 0, (int)(nd * 2), kBufferFlags);
-  int dma_off[4];
+  int dma_k[4], dma_v[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 16 * w + 4 * i + (lane >> 4);
-    dma_off[i] = r * 256 + (((lane & 15) ^ swz(r)) << 4);
+    dma_k[i] = r * 256 + (((lane & 15) ^ swz_k(r)) << 4);
+    dma_v[i] = r * 256 + (((lane & 15) ^ swz_v(r)) << 4);
   }
 
-  // List entries are fetched with vector buffer loads two blocks ahead and
-  // moved to scalar registers when used: a scalar load here would be waited
-  // for by every LDS wait that follows it.  Entries past `cnt` read as 0, and
-  // every entry is clamped to [0, qb], so reads stay inside the head's rows.
+  // List entries: 64 at a time in one VGPR (lane i holds entry c0 + i),
+  // picked out with readlane; a chunk is reloaded only when a block past it
+  // is needed.  Entries past `cnt` read as 0, and every entry is clamped to
+  // [0, qb], so reads stay inside the head's rows.
   const __amdgpu_buffer_rsrc_t lrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)list, 0, kDense ? 0 : cnt * 4, kBufferFlags);
-  auto fetch_block = [&](int b) -> int {
-    return kDense ? b : __builtin_amdgcn_raw_buffer_load_b32(lrs, 0, b * 4, 0);
-  };
-  auto use_block = [&](int fetched) -> int {
-    return kDense ? fetched : min(max(__builtin_amdgcn_readfirstlane(fetched), 0), qb);
+  int chunk_base = 0;
+  int chunk = kDense ? 0 : __builtin_amdgcn_raw_buffer_load_b32(lrs, lane * 4, 0, 0);
+  auto block_at = [&](int b) -> int {
+    if (kDense) return b;
+    if (b - chunk_base >= 64) {
+      chunk_base = b;
+      chunk = __builtin_amdgcn_raw_buffer_load_b32(lrs, lane * 4, b * 4, 0);
+    }
+    return min(max(__builtin_amdgcn_readlane(chunk, b - chunk_base), 0), qb);
   };
   auto key0_of = [&](int kb, int step) -> int { return kb * kBlock + (step & 1) * kStep; };
 
-  auto dma = [&](__amdgpu_buffer_rsrc_t rs, __bf16* stage, int kb, int step) {
+  // The DMA is issued through inline asm so that the compiler does not
+  // track it: it would otherwise wait for every outstanding LDS DMA before
+  // the first LDS read of each step, whatever stage that read touches.
+  // Ordering is explicit instead: each step ends with a vmcnt wait covering
+  // the tiles the next step reads, then a barrier.
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  auto dma = [&](__amdgpu_buffer_rsrc_t rs, const int (&off)[4], __bf16* stage, int kb, int step) {
     const int soff = key0_of(kb, step) * (kHeadDim * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (__attribute__((address_space(3))) void*)(stage + (16 * w + 4 * i) * kHeadDim),
-                                               16, dma_off[i], soff, 0, 0);
+    for (int i = 0; i < 4; ++i) {
+      const unsigned lds_addr =
+          (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)(stage + (16 * wu + 4 * i) * kHeadDim);
+      // one wait state between writing M0 and the DMA that reads it
+      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                   :
+                   : "s"(lds_addr), "v"(off[i]), "s"(rs), "s"(soff)
+                   : "memory", "m0");
+    }
   };
 
   // Row of the K operand fed by this lane: a permutation of 0..31 (see top).
   const int ia = l32 >> 3, ig = (l32 >> 2) & 1, ib = l32 & 3;
   const int krow = 16 * (ia >> 1) + 8 * ig + 4 * (ia & 1) + ib;
   // Byte offsets of this lane's K operand: row 32 kb2 + krow, logical chunk
-  // 2 kk + lg.  swz only touches chunk bits 0..2, so kk bit 2 and kb2 are
-  // plain immediates: 4 base offsets for kk = 0..3.
-  int k_off[4];
+  // 2 kk + lg; kb2 leaves swz_k unchanged (+8 KiB).
+  int k_off[8];
 #pragma unroll
-  for (int kk = 0; kk < 4; ++kk) k_off[kk] = krow * 256 + (((2 * kk + lg) ^ swz(krow)) << 4);
+  for (int kk = 0; kk < 8; ++kk) k_off[kk] = krow * 256 + (((2 * kk + lg) ^ swz_k(krow)) << 4);
   // V^T operand through the transposing LDS read: within each 16-lane group
   // (gq = lane / 16, li = lane % 16) lane li receives element li % 4 of the
   // 4-element vectors addressed by lanes 4e + li / 4 (e = 0..3).  A lane
@@ -152,18 +176,18 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   // keys k0 .. k0+3 at column d0 + li.  For the A operand of O^T += V^T P^T
   // (row d = 32 db + l32, keys 32 kb2 + 16 mm + 8 lg + s) two reads
   // (s = 0..3, hh = 0, and s = 4..7, hh = 1) give the 8 slots.  Rows differ
-  // by 4 hh + 16 mm + 32 kb2 and columns by 64 B per db >= 2, none of which
-  // changes swz, so 2 base offsets (db & 1) cover every read.
+  // by 4 hh + 16 mm + 32 kb2, none of which changes swz_v, so one base
+  // offset per db covers every read.
   const int gq = lane >> 4, li = lane & 15;
-  int v_base[2];
+  int v_base[4];
 #pragma unroll
-  for (int d0 = 0; d0 < 2; ++d0) {
+  for (int db = 0; db < 4; ++db) {
     const int r = 8 * (gq >> 1) + (li >> 2);
-    const int d = 32 * d0 + 16 * (gq & 1) + 4 * (li & 3);
-    v_base[d0] = r * 256 + (((d >> 3) ^ swz(r)) << 4) + (d & 7) * 2;
+    const int d = 32 * db + 16 * (gq & 1) + 4 * (li & 3);
+    v_base[db] = r * 256 + (((d >> 3) ^ swz_v(r)) << 4) + (d & 7) * 2;
   }
   auto v_off = [&](int db, int kb2, int mm, int hh) -> int {
-    return v_base[db & 1] + (db >> 1) * 128 + (32 * kb2 + 16 * mm + 4 * hh) * 256;
+    return v_base[db] + (32 * kb2 + 16 * mm + 4 * hh) * 256;
   };
 
   auto qk = [&](const __bf16* kbuf, f32x16 (&s)[2]) {
@@ -174,33 +198,35 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
       for (int v = 0; v < 16; ++v) s[kb2][v] = 0.f;
 #pragma unroll
       for (int kk = 0; kk < 8; ++kk) {
-        const bf16x8 kf = as_bf16x8(*(const u32x4*)(kb8 + k_off[kk & 3] + (kk >> 2) * 128 + kb2 * 8192));
+        const bf16x8 kf = as_bf16x8(*(const u32x4*)(kb8 + k_off[kk] + kb2 * 8192));
         s[kb2] = mfma32(kf, qf[kk], s[kb2]);
       }
     }
   };
 
-  // Iteration j of the software pipeline.  K and V have separate double
-  // buffers: K_t lives in ks[t & 1], V_t in vs[t & 1].  Iteration j
-  //   - starts the DMA of K_{j+2} over K_j (read in iteration j-1) and of
-  //     V_{j+1} over V_{j-1} (read in iteration j-1),
+  // Iteration j of the software pipeline.  K_t lives in ks[t % 3] and V_t
+  // in vs[t & 1].  Iteration j
+  //   - starts the DMA of V_{j+1} over V_{j-1} and then of K_{j+3} over K_j
+  //     (both read in iteration j-1),
   //   - computes S_{j+1} = K_{j+1} Q^T (MFMA) in the same basic block as the
   //     softmax of S_j (VALU), so the two overlap,
   //   - accumulates O += V_j P_j,
-  //   - waits for its DMA and meets the others at one barrier.
+  //   - waits for all of its DMA but the K_{j+3} one, which has until the
+  //     end of iteration j+1, and meets the others at one barrier.
   // kMasked marks the two steps of the diagonal block (sorted lists put it
-  // last); kNext is false on the final step.
-  // kb0, kb1, kb2: key blocks of steps j, j+1, j+2.
-  auto iter = [&](int j, int kb0, int kb1, int kb2s, f32x16 (&sc)[2], f32x16 (&sn)[2], auto masked_tag,
-                  auto next_tag) {
+  // last); kNext is false on the final step.  kb_m, kb_v, kb_k: key blocks
+  // of steps j, j+1 and j+3; kst: stage of K_{j+1}.
+  auto iter = [&](int j, int kb_m, int kb_v, int kb_k, int kst, f32x16 (&sc)[2], f32x16 (&sn)[2],
+                  auto masked_tag, auto next_tag) {
     constexpr bool kMasked = decltype(masked_tag)::value;
     constexpr bool kNext = decltype(next_tag)::value;
-    if (j + 2 < nsteps) dma(krs, ks[j & 1], kb2s, j + 2);
-    if (j + 1 < nsteps) dma(vrs, vs[(j + 1) & 1], kb1, j + 1);
-    if (kNext) qk(ks[(j + 1) & 1], sn);
+    if (j + 1 < nsteps) dma(vrs, dma_v, vs[(j + 1) & 1], kb_v, j + 1);
+    const bool k_ahead = j + 3 < nsteps;
+    if (k_ahead) dma(krs, dma_k, ks[kst == 0 ? 2 : kst - 1], kb_k, j + 3);
+    if (kNext) qk(ks[kst], sn);
 
     if (kMasked) {
-      const int key0 = key0_of(kb0, j);
+      const int key0 = key0_of(kb_m, j);
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
@@ -262,18 +288,19 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
           o[db] = mfma32(vf, pb[kb2][mm], o[db]);
         }
 
-    wait_dma();
+    if (k_ahead)
+      wait_dma_but_4();
+    else
+      wait_dma();
     __syncthreads();
   };
 
   f32x16 sa[2], sb[2];
-  int f0 = fetch_block(0), f1 = fetch_block(1);
-  wait_dma();
-  int kb_cur = use_block(f0), kb_nxt = use_block(f1);
-  int pf = fetch_block(2);
-  dma(krs, ks[0], kb_cur, 0);
-  dma(vrs, vs[0], kb_cur, 0);
-  dma(krs, ks[1], kb_cur, 1);
+  int kb_cur = block_at(0), kb_nxt = block_at(1), kb_nn = block_at(2);
+  dma(krs, dma_k, ks[0], kb_cur, 0);
+  dma(vrs, dma_v, vs[0], kb_cur, 0);
+  dma(krs, dma_k, ks[1], kb_cur, 1);
+  if (nsteps > 2) dma(krs, dma_k, ks[2], kb_nxt, 2);
   wait_dma();
   __syncthreads();
   qk(ks[0], sa);
@@ -282,16 +309,19 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   // Every block but the last (the diagonal) is fully visible to all rows.
   // Each pass handles the two steps of block j/2 (kb_cur); nsteps - 2 is
   // even, so the loop alternates the two score buffers.
-  int j = 0;
+  int j = 0, kst = 1;
   for (; j < nsteps - 2; j += 2) {
-    iter(j, kb_cur, kb_cur, kb_nxt, sa, sb, std::false_type{}, std::true_type{});
-    iter(j + 1, kb_cur, kb_nxt, kb_nxt, sb, sa, std::false_type{}, std::true_type{});
+    iter(j, kb_cur, kb_cur, kb_nxt, kst, sa, sb, std::false_type{}, std::true_type{});
+    kst = kst == 2 ? 0 : kst + 1;
+    iter(j + 1, kb_cur, kb_nxt, kb_nn, kst, sb, sa, std::false_type{}, std::true_type{});
+    kst = kst == 2 ? 0 : kst + 1;
     kb_cur = kb_nxt;
-    kb_nxt = use_block(pf);  // landed: every iteration ends with a full vmcnt wait
-    pf = fetch_block((j >> 1) + 3);
+    kb_nxt = kb_nn;
+    kb_nn = block_at((j >> 1) + 3);
   }
-  iter(j, kb_cur, kb_cur, kb_nxt, sa, sb, std::true_type{}, std::true_type{});
-  iter(j + 1, kb_cur, kb_nxt, kb_nxt, sb, sa, std::true_type{}, std::false_type{});
+  iter(j, kb_cur, kb_cur, kb_nxt, kst, sa, sb, std::true_type{}, std::true_type{});
+  kst = kst == 2 ? 0 : kst + 1;
+  iter(j + 1, kb_cur, kb_nxt, kb_nn, kst, sb, sa, std::true_type{}, std::false_type{});
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / l_tot;

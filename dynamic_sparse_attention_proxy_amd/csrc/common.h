@@ -28,6 +28,8 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
 
 // Wait until this wave's buffer loads (including LDS DMA) have landed.
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// The same, except for the 4 most recently issued ones (loads complete in order).
+__device__ __forceinline__ void wait_dma_but_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
