@@ -9,8 +9,10 @@
 //   K goes straight from global memory into the B operand (lane = key), so
 //   each accumulator register holds one row and 32 consecutive keys across a
 //   half-wave.  Each lane keeps a running (max, sum of exp2) per row; the 32
-//   lanes of a row are merged with a butterfly at the end of the chunk.
-// Combine: per (head, row) merge the chunk partials into log2-sum-exp.
+//   lanes of a row are merged with a butterfly at the end of the chunk.  The
+//   next 32 keys are loaded while the current ones are used.
+// Combine: one wavefront per (head, row) merges the chunk partials into the
+//   row's log2-sum-exp.
 // Pass 2 (map): recompute S and store exp2(t - lse2) - a half-wave writes
 //   128 contiguous bytes of one row per store.
 // Route: C_struct = mean over rows of the mass on the first sink_width and
@@ -27,7 +29,7 @@ struct ProxyArgs {
   const __bf16* q;
   const __bf16* k;
   float* amap;
-  float* part;   // [Hq][chunks][128][2]
+  float* part;   // [Hq][128][chunks][2]
   float* lse2;   // [Hq][128]
   float* row_lse;
   int n;
@@ -52,15 +54,22 @@ __device__ __forceinline__ void load_q_rows(const ProxyArgs& p, int h, int w, in
   for (int kk = 0; kk < 8; ++kk) qf[kk] = as_bf16x8(*(const u32x4*)(qrow + 16 * kk));
 }
 
-__device__ __forceinline__ f32x16 qk_tile(const bf16x8 qf[8], const __bf16* krow) {
+__device__ __forceinline__ void load_k_tile(const __bf16* krow, bf16x8 kf[8]) {
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) kf[kk] = as_bf16x8(*(const u32x4*)(krow + 16 * kk));
+}
+
+__device__ __forceinline__ f32x16 qk_regs(const bf16x8 qf[8], const bf16x8 kf[8]) {
   f32x16 s;
 #pragma unroll
   for (int v = 0; v < 16; ++v) s[v] = 0.f;
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) s = mfma32(qf[kk], as_bf16x8(*(const u32x4*)(krow + 16 * kk)), s);
+  for (int kk = 0; kk < 8; ++kk) s = mfma32(qf[kk], kf[kk], s);
   return s;
 }
 
+// Partial statistics of proxy row r of head h over key chunk c live at
+// part[((h * 128 + r) * nchunks + c) * 2 + {0: max, 1: sum}] (base 2).
 __global__ __launch_bounds__(256) void proxy_stats_kernel(ProxyArgs p) {
   const int chunk = blockIdx.x, h = blockIdx.y, g = h / p.qpg;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, lg = lane >> 5;
@@ -74,14 +83,18 @@ __global__ __launch_bounds__(256) void proxy_stats_kernel(ProxyArgs p) {
   }
   const int kbeg = chunk * kProxyChunk;
   const int kend = min(p.n, kbeg + kProxyChunk);
-  const __bf16* kg = p.k + (size_t)g * p.n * kHeadDim;
+  const __bf16* kg = p.k + (size_t)g * p.n * kHeadDim + (size_t)l32 * kHeadDim + 8 * lg;
   const int pos0 = p.n - kBlock;
-  for (int key0 = kbeg; key0 < kend; key0 += 32) {
+  // K sub-blocks of 32 keys, the next one in flight while this one is used
+  bf16x8 ka[8], kb[8];
+  load_k_tile(kg + (size_t)kbeg * kHeadDim, ka);
+  auto consume = [&](const bf16x8 (&kf)[8], int key0) {
+    const f32x16 s = qk_regs(qf, kf);
     const int key = key0 + l32;
-    const f32x16 s = qk_tile(qf, kg + (size_t)key * kHeadDim + 8 * lg);
+    const bool masked_tile = key0 + 31 > pos0;  // only the last 128 keys can be masked
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
-      if (key <= pos0 + acc_row(w, v, lg)) {
+      if (!masked_tile || key <= pos0 + acc_row(w, v, lg)) {
         const float t = s[v] * p.scale_log2;
         const float dlt = t - m[v];
         const float e = fast_exp2(-fabsf(dlt));
@@ -90,6 +103,13 @@ __global__ __launch_bounds__(256) void proxy_stats_kernel(ProxyArgs p) {
         m[v] = up ? t : m[v];
       }
     }
+  };
+  for (int key0 = kbeg; key0 < kend; key0 += 64) {
+    if (key0 + 32 < kend) load_k_tile(kg + (size_t)(key0 + 32) * kHeadDim, kb);
+    consume(ka, key0);
+    if (key0 + 32 >= kend) break;
+    if (key0 + 64 < kend) load_k_tile(kg + (size_t)(key0 + 64) * kHeadDim, ka);
+    consume(kb, key0 + 32);
   }
 #pragma unroll
   for (int v = 0; v < 16; ++v) {
@@ -100,25 +120,37 @@ __global__ __launch_bounds__(256) void proxy_stats_kernel(ProxyArgs p) {
       merge_ml(m[v], l[v], mo, lo);
     }
   }
-  if (l32 == 0) {
-    float* dst = p.part + ((size_t)h * p.nchunks + chunk) * kBlock * 2;
+  // lane v of each half-wave writes row acc_row(w, v, lg)
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
+  for (int v = 0; v < 16; ++v) {
+    if (l32 == v) {
       const int r = acc_row(w, v, lg);
-      dst[2 * r] = m[v];
-      dst[2 * r + 1] = l[v];
+      float* dst = p.part + (((size_t)h * kBlock + r) * p.nchunks + chunk) * 2;
+      dst[0] = m[v];
+      dst[1] = l[v];
     }
   }
 }
 
-__global__ __launch_bounds__(128) void proxy_combine_kernel(ProxyArgs p) {
-  const int h = blockIdx.x, r = threadIdx.x;
+// One wavefront per proxy row: lanes stride over the chunk partials, then a
+// butterfly merge.
+__global__ __launch_bounds__(256) void proxy_combine_kernel(ProxyArgs p) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);  // h * 128 + r
   float m = -INFINITY, l = 0.f;
-  const float* src = p.part + (size_t)h * p.nchunks * kBlock * 2;
-  for (int c = 0; c < p.nchunks; ++c) merge_ml(m, l, src[(size_t)c * kBlock * 2 + 2 * r], src[(size_t)c * kBlock * 2 + 2 * r + 1]);
-  const float lse2 = m + fast_log2(l);
-  p.lse2[h * kBlock + r] = lse2;
-  if (p.row_lse != nullptr) p.row_lse[h * kBlock + r] = lse2 * kLn2;
+  const float* src = p.part + (size_t)row * p.nchunks * 2;
+  for (int c = lane; c < p.nchunks; c += 64) merge_ml(m, l, src[2 * c], src[2 * c + 1]);
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const float mo = __shfl_xor(m, o);
+    const float lo = __shfl_xor(l, o);
+    merge_ml(m, l, mo, lo);
+  }
+  if (lane == 0) {
+    const float lse2 = m + fast_log2(l);
+    p.lse2[row] = lse2;
+    if (p.row_lse != nullptr) p.row_lse[row] = lse2 * kLn2;
+  }
 }
 
 __global__ __launch_bounds__(256) void proxy_map_kernel(ProxyArgs p) {
@@ -131,18 +163,29 @@ __global__ __launch_bounds__(256) void proxy_map_kernel(ProxyArgs p) {
   for (int v = 0; v < 16; ++v) lse2[v] = p.lse2[h * kBlock + acc_row(w, v, lg)];
   const int kbeg = chunk * kProxyChunk;
   const int kend = min(p.n, kbeg + kProxyChunk);
-  const __bf16* kg = p.k + (size_t)g * p.n * kHeadDim;
+  const __bf16* kg = p.k + (size_t)g * p.n * kHeadDim + (size_t)l32 * kHeadDim + 8 * lg;
   float* arow = p.amap + (size_t)h * kBlock * p.n;
   const int pos0 = p.n - kBlock;
-  for (int key0 = kbeg; key0 < kend; key0 += 32) {
+  bf16x8 ka[8], kb[8];
+  load_k_tile(kg + (size_t)kbeg * kHeadDim, ka);
+  auto consume = [&](const bf16x8 (&kf)[8], int key0) {
+    const f32x16 s = qk_regs(qf, kf);
     const int key = key0 + l32;
-    const f32x16 s = qk_tile(qf, kg + (size_t)key * kHeadDim + 8 * lg);
+    const bool masked_tile = key0 + 31 > pos0;
 #pragma unroll
     for (int v = 0; v < 16; ++v) {
       const int r = acc_row(w, v, lg);
-      const float a = (key <= pos0 + r) ? fast_exp2(s[v] * p.scale_log2 - lse2[v]) : 0.f;
+      float a = fast_exp2(s[v] * p.scale_log2 - lse2[v]);
+      if (masked_tile && key > pos0 + r) a = 0.f;
       arow[(size_t)r * p.n + key] = a;
     }
+  };
+  for (int key0 = kbeg; key0 < kend; key0 += 64) {
+    if (key0 + 32 < kend) load_k_tile(kg + (size_t)(key0 + 32) * kHeadDim, kb);
+    consume(ka, key0);
+    if (key0 + 32 >= kend) break;
+    if (key0 + 64 < kend) load_k_tile(kg + (size_t)(key0 + 64) * kHeadDim, ka);
+    consume(kb, key0 + 32);
   }
 }
 
@@ -191,7 +234,7 @@ hipError_t launch_proxy(const __bf16* q, const __bf16* k, float* amap, float* ro
   hipLaunchKernelGGL(proxy_stats_kernel, dim3(a.nchunks, hq), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(proxy_combine_kernel, dim3(hq), dim3(128), 0, stream, a);
+  hipLaunchKernelGGL(proxy_combine_kernel, dim3(hq * kBlock / 4), dim3(256), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(proxy_map_kernel, dim3(a.nchunks, hq), dim3(256), 0, stream, a);

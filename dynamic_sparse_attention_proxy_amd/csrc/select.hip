@@ -331,27 +331,39 @@ __global__ __launch_bounds__(kPeThreads) void pe_select_kernel(PeArgs p) {
   if (tid == 0) p.count[(size_t)h * N + qb] = total;
 }
 
+// One workgroup per (head, 64 query blocks): the head's two masks are staged
+// in LDS as bytes once, then each wavefront builds whole rows, deciding 64
+// key blocks per ballot and writing the kept ones in ascending order.
+constexpr int kExpandRows = 64;
+constexpr int kMaxBlocks = 4096;  // n <= 524288
+
 __global__ __launch_bounds__(256) void vs_expand_kernel(const int32_t* route, const int32_t* vmask,
-                                                        const int32_t* smask, int32_t* count, int32_t* idx, int hq,
-                                                        int nblk) {
-  __shared__ int redi[8];
-  const int N = nblk, id = blockIdx.x;
-  const int h = id % hq, qb = N - 1 - id / hq;
+                                                        const int32_t* smask, int32_t* count, int32_t* idx, int nblk) {
+  __shared__ uint8_t vm[kMaxBlocks], sm[kMaxBlocks];
+  const int N = nblk, h = blockIdx.y, qb0 = blockIdx.x * kExpandRows;
   if (route[h] != 1) return;
-  const int tid = threadIdx.x;
-  const int L = qb + 1;
-  const int32_t* vm = vmask + (size_t)h * N;
-  const int32_t* sm = smask + (size_t)h * N;
-  const int per = (L + 255) / 256;
-  const int beg = min(L, tid * per), end = min(L, beg + per);
-  int c = 0;
-  for (int kb = beg; kb < end; ++kb) c += (vm[kb] | sm[qb - kb] | (kb < qb ? sm[qb - kb - 1] : 0)) ? 1 : 0;
-  int total;
-  int pos = block_exclusive_scan(c, redi, tid, 256, &total);
-  int32_t* out = idx + (size_t)h * ((size_t)N * (N + 1) / 2) + (size_t)qb * (qb + 1) / 2;
-  for (int kb = beg; kb < end; ++kb)
-    if (vm[kb] | sm[qb - kb] | (kb < qb ? sm[qb - kb - 1] : 0)) out[pos++] = kb;
-  if (tid == 0) count[(size_t)h * N + qb] = total;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  for (int i = tid; i < N; i += 256) {
+    vm[i] = vmask[(size_t)h * N + i] != 0;
+    sm[i] = smask[(size_t)h * N + i] != 0;
+  }
+  __syncthreads();
+  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int r = wv; r < kExpandRows; r += 4) {
+    const int qb = qb0 + r;
+    if (qb >= N) break;
+    int32_t* out = idx + (size_t)h * ((size_t)N * (N + 1) / 2) + (size_t)qb * (qb + 1) / 2;
+    int total = 0;
+    for (int kb0 = 0; kb0 <= qb; kb0 += 64) {
+      const int kb = kb0 + lane;
+      bool f = false;
+      if (kb <= qb) f = vm[kb] | sm[qb - kb] | (kb < qb ? sm[qb - kb - 1] : 0);
+      const uint64_t bal = __ballot(f);
+      if (f) out[total + __popcll(bal & below)] = kb;
+      total += __popcll(bal);
+    }
+    if (lane == 0) count[(size_t)h * N + qb] = total;
+  }
 }
 
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -450,8 +462,8 @@ hipError_t launch_select(const __bf16* q, const __bf16* k, const float* amap, co
   hipLaunchKernelGGL(pe_select_kernel, dim3(hq * N), dim3(kPeThreads), pe_lds, stream, pa);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  hipLaunchKernelGGL(vs_expand_kernel, dim3(hq * N), dim3(256), 0, stream, route, b.vmask, b.smask, count, idx, hq,
-                     N);
+  hipLaunchKernelGGL(vs_expand_kernel, dim3((N + kExpandRows - 1) / kExpandRows, hq), dim3(256), 0, stream, route,
+                     b.vmask, b.smask, count, idx, N);
   return hipGetLastError();
 }
 
