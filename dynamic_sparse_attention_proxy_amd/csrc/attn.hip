@@ -205,54 +205,63 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   };
 
   // Iteration j of the software pipeline.  K_t lives in ks[t % 3] and V_t
-  // in vs[t & 1].  Iteration j
+  // in vs[t & 1]; S_j arrives in `sc` already masked, with the running max
+  // m_run valid for it.  Iteration j
   //   - starts the DMA of V_{j+1} over V_{j-1} and then of K_{j+3} over K_j
   //     (both read in iteration j-1),
-  //   - computes S_{j+1} = K_{j+1} Q^T (MFMA) in the same basic block as the
-  //     softmax of S_j (VALU), so the two overlap,
-  //   - accumulates O += V_j P_j,
+  //   - block 1: S_{j+1} = K_{j+1} Q^T (MFMA) beside exp / row sum / bf16
+  //     packing of S_j (VALU),
+  //   - block 2: O += V_j P_j (MFMA) beside masking and row max of S_{j+1},
+  //   - raises the running max for S_{j+1} when needed (rare branch),
   //   - waits for all of its DMA but the K_{j+3} one, which has until the
-  //     end of iteration j+1, and meets the others at one barrier.
-  // kMasked marks the two steps of the diagonal block (sorted lists put it
-  // last); kNext is false on the final step.  kb_m, kb_v, kb_k: key blocks
-  // of steps j, j+1 and j+3; kst: stage of K_{j+1}.
-  auto iter = [&](int j, int kb_m, int kb_v, int kb_k, int kst, f32x16 (&sc)[2], f32x16 (&sn)[2],
-                  auto masked_tag, auto next_tag) {
-    constexpr bool kMasked = decltype(masked_tag)::value;
+  //     end of iteration j+1, and meets the other waves at one barrier.
+  // No branch separates the MFMA and VALU halves of a block, so the
+  // scheduler can interleave them.  kNextMasked: step j+1 is one of the two
+  // steps of the diagonal block (sorted lists put it last); kNext: j+1 is a
+  // step.  kb_v, kb_k, kb_n: key blocks of steps j+1, j+3, j+1; kst: stage
+  // of K_{j+1}.
+  float neg_m = 0.f;
+  auto raise_max = [&](const f32x16 (&s)[2]) {
+    float mx = fmaxf(s[0][0], s[0][1]);
+#pragma unroll
+    for (int v = 2; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[0][v], s[0][v + 1]));
+#pragma unroll
+    for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[1][v], s[1][v + 1]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    // t = s * scale_log2 (> 0 keeps the order, so the max is taken before
+    // scaling).  The running max is raised only when a score exceeds it by
+    // more than kHeadroom; probabilities then stay below 2^kHeadroom.
+    const float mxs = mx * p.scale_log2;
+    if (__any(mxs > m_run + kHeadroom)) {
+      const float m_new = fmaxf(m_run, mxs);
+      const float alpha = fast_exp2(m_run - m_new);  // 0 while m_run is -inf
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+      l_run *= alpha;
+      m_run = m_new;
+      neg_m = -m_new;
+    }
+  };
+  auto mask_scores = [&](f32x16 (&s)[2], int key0) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int v = 0; v < 16; ++v)
+        if (key0 + 32 * kb2 + acc_key(v, lg) > qpos) s[kb2][v] = -INFINITY;
+  };
+
+  auto iter = [&](int j, int kb_v, int kb_k, int kb_n, int kst, f32x16 (&sc)[2], f32x16 (&sn)[2],
+                  auto next_masked_tag, auto next_tag) {
+    constexpr bool kNextMasked = decltype(next_masked_tag)::value;
     constexpr bool kNext = decltype(next_tag)::value;
-    if (j + 1 < nsteps) dma(vrs, dma_v, vs[(j + 1) & 1], kb_v, j + 1);
+    if (kNext) dma(vrs, dma_v, vs[(j + 1) & 1], kb_v, j + 1);
     const bool k_ahead = j + 3 < nsteps;
     if (k_ahead) dma(krs, dma_k, ks[kst == 0 ? 2 : kst - 1], kb_k, j + 3);
+
+    // block 1
     if (kNext) qk(ks[kst], sn);
-
-    if (kMasked) {
-      const int key0 = key0_of(kb_m, j);
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int v = 0; v < 16; ++v)
-          if (key0 + 32 * kb2 + acc_key(v, lg) > qpos) sc[kb2][v] = -INFINITY;
-    }
-
-    // Online softmax in base 2 on raw scores: t = s * scale_log2 (> 0 keeps
-    // the order, so the row max is taken before scaling).  The running max
-    // is only raised when a score exceeds it by more than kHeadroom, so
-    // rescaling the accumulator is rare; probabilities stay below
-    // 2^kHeadroom, well inside bf16 and fp32 range.
-    float mx = fmaxf(sc[0][0], sc[0][1]);
-#pragma unroll
-    for (int v = 2; v < 16; v += 2) mx = fmaxf(mx, fmaxf(sc[0][v], sc[0][v + 1]));
-#pragma unroll
-    for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(sc[1][v], sc[1][v + 1]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float mxs = mx * p.scale_log2;
-    const bool raise = __any(mxs > m_run + kHeadroom);
-    const float m_new = raise ? fmaxf(m_run, mxs) : m_run;
-    const float alpha = (m_new == -INFINITY) ? 1.f : fast_exp2(m_run - m_new);
-    m_run = m_new;
-    l_run *= alpha;
-    const float neg_m = (m_run == -INFINITY) ? 0.f : -m_run;
-
     bf16x8 pb[2][2];
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
@@ -266,13 +275,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
       pb[kb2][1] = pack_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
     }
 
-    if (raise) {
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
-    }
-
+    // block 2
     __attribute__((address_space(3))) char* vb8 = (__attribute__((address_space(3))) char*)vs[j & 1];
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -287,6 +290,10 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
           const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
           o[db] = mfma32(vf, pb[kb2][mm], o[db]);
         }
+    if (kNext) {
+      if (kNextMasked) mask_scores(sn, key0_of(kb_n, j + 1));
+      raise_max(sn);
+    }
 
     if (k_ahead)
       wait_dma_but_4();
@@ -304,24 +311,38 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   wait_dma();
   __syncthreads();
   qk(ks[0], sa);
+  if (nsteps == 2) mask_scores(sa, key0_of(kb_cur, 0));
+  raise_max(sa);
   __syncthreads();  // every wave has read K_0 before iteration 0 overwrites it
 
-  // Every block but the last (the diagonal) is fully visible to all rows.
-  // Each pass handles the two steps of block j/2 (kb_cur); nsteps - 2 is
-  // even, so the loop alternates the two score buffers.
+  // Steps 0 .. nsteps-3 cover the fully visible blocks, the last two the
+  // diagonal block.  The pair loop runs the iterations whose next step is
+  // fully visible two at a time (alternating the score buffers); the tail
+  // runs the last four (two when the list holds only the diagonal block).
+  using F = std::false_type;
+  using T = std::true_type;
   int j = 0, kst = 1;
-  for (; j < nsteps - 2; j += 2) {
-    iter(j, kb_cur, kb_cur, kb_nxt, kst, sa, sb, std::false_type{}, std::true_type{});
+  if (nsteps >= 4) {
+    for (; j < nsteps - 4; j += 2) {
+      iter(j, kb_cur, kb_nxt, kb_cur, kst, sa, sb, F{}, T{});
+      kst = kst == 2 ? 0 : kst + 1;
+      iter(j + 1, kb_nxt, kb_nn, kb_nxt, kst, sb, sa, F{}, T{});
+      kst = kst == 2 ? 0 : kst + 1;
+      kb_cur = kb_nxt;
+      kb_nxt = kb_nn;
+      kb_nn = block_at((j >> 1) + 3);
+    }
+    // j = nsteps - 4: kb_cur is the last fully visible block, kb_nxt the diagonal one
+    iter(j, kb_cur, kb_nxt, kb_cur, kst, sa, sb, F{}, T{});
     kst = kst == 2 ? 0 : kst + 1;
-    iter(j + 1, kb_cur, kb_nxt, kb_nn, kst, sb, sa, std::false_type{}, std::true_type{});
+    iter(j + 1, kb_nxt, kb_nxt, kb_nxt, kst, sb, sa, T{}, T{});
     kst = kst == 2 ? 0 : kst + 1;
+    j += 2;
     kb_cur = kb_nxt;
-    kb_nxt = kb_nn;
-    kb_nn = block_at((j >> 1) + 3);
   }
-  iter(j, kb_cur, kb_cur, kb_nxt, kst, sa, sb, std::true_type{}, std::true_type{});
+  iter(j, kb_cur, kb_cur, kb_cur, kst, sa, sb, T{}, T{});
   kst = kst == 2 ? 0 : kst + 1;
-  iter(j + 1, kb_cur, kb_nxt, kb_nn, kst, sb, sa, std::true_type{}, std::false_type{});
+  iter(j + 1, kb_cur, kb_cur, kb_cur, kst, sb, sa, F{}, F{});
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / l_tot;
