@@ -221,17 +221,26 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   // step.  kb_v, kb_k, kb_n: key blocks of steps j+1, j+3, j+1; kst: stage
   // of K_{j+1}.
   float neg_m = 0.f;
-  auto raise_max = [&](const f32x16 (&s)[2]) {
+  // Row max across the two half-waves holding a query's keys: with both
+  // operands equal, permlane32_swap returns lane l's value and that of lane
+  // l ^ 32 in its two results.
+  auto pair_max = [](float x) -> float {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+  };
+  // Row max of a step's scores, scaled: t = s * scale_log2 (> 0 keeps the
+  // order, so the max is taken before scaling).
+  auto row_max = [&](const f32x16 (&s)[2]) -> float {
     float mx = fmaxf(s[0][0], s[0][1]);
 #pragma unroll
     for (int v = 2; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[0][v], s[0][v + 1]));
 #pragma unroll
     for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[1][v], s[1][v + 1]));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    // t = s * scale_log2 (> 0 keeps the order, so the max is taken before
-    // scaling).  The running max is raised only when a score exceeds it by
-    // more than kHeadroom; probabilities then stay below 2^kHeadroom.
-    const float mxs = mx * p.scale_log2;
+    return pair_max(mx) * p.scale_log2;
+  };
+  // The running max is raised only when a score exceeds it by more than
+  // kHeadroom; probabilities then stay below 2^kHeadroom.
+  auto raise_to = [&](float mxs) {
     if (__any(mxs > m_run + kHeadroom)) {
       const float m_new = fmaxf(m_run, mxs);
       const float alpha = fast_exp2(m_run - m_new);  // 0 while m_run is -inf
@@ -260,40 +269,78 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
     const bool k_ahead = j + 3 < nsteps;
     if (k_ahead) dma(krs, dma_k, ks[kst == 0 ? 2 : kst - 1], kb_k, j + 3);
 
-    // block 1
-    if (kNext) qk(ks[kst], sn);
-    bf16x8 pb[2][2];
+    // The two blocks are written out in issue order, one unit per MFMA, with
+    // operand reads three MFMAs ahead through 4-entry register rings;
+    // sched_barrier(0) keeps the units as written.
+    // Block 1: MFMA t of S_{j+1} (key half t & 1, d slice t / 2) beside the
+    // exp, row sum and bf16 packing of scores 2t, 2t+1 of S_j.
+    const char* kb8 = (const char*)ks[kst];
+    auto kread = [&](int t) -> bf16x8 {
+      return as_bf16x8(*(const u32x4*)(kb8 + k_off[t >> 1] + (t & 1) * 8192));
+    };
+    bf16x8 kr[4];
+    if (kNext) {
+      kr[0] = kread(0);
+      kr[1] = kread(1);
+      kr[2] = kread(2);
+    }
+    float e[32];
+    bf16x8 pb[4];  // P_j operand f = 2 * key half + 16-key group: keys 16 f + 8 lg .. +7
+    const f32x16 zero = {};
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2) {
-      float e[16];
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        e[v] = fast_exp2(fmaf(sc[kb2][v], p.scale_log2, neg_m));
-        l_run += e[v];
+    for (int t = 0; t < 16; ++t) {
+      if (kNext) {
+        sn[t & 1] = mfma32(kr[t & 3], qf[t >> 1], t < 2 ? zero : sn[t & 1]);
+        if (t + 3 < 16) kr[(t + 3) & 3] = kread(t + 3);
       }
-      pb[kb2][0] = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
-      pb[kb2][1] = pack_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
+#pragma unroll
+      for (int u = 2 * t; u < 2 * t + 2; ++u) {
+        e[u] = fast_exp2(fmaf(sc[u >> 4][u & 15], p.scale_log2, neg_m));
+        l_run += e[u];
+      }
+      if ((t & 3) == 3) {
+        const int f = t >> 2;
+        pb[f] = pack_bf16x8(e[8 * f], e[8 * f + 1], e[8 * f + 2], e[8 * f + 3], e[8 * f + 4], e[8 * f + 5],
+                            e[8 * f + 6], e[8 * f + 7]);
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
 
-    // block 2
+    // Block 2: MFMA u of O += V_j P_j (d slice u & 3, P operand u / 4) beside
+    // masking and row max of scores 2u, 2u+1 of S_{j+1}.
     __attribute__((address_space(3))) char* vb8 = (__attribute__((address_space(3))) char*)vs[j & 1];
+    auto vread = [&](int u) -> bf16x8 {
+      const int db = u & 3, f = u >> 2;
+      const bf16x4 lo = __builtin_bit_cast(
+          bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb8 + v_off(db, f >> 1, f & 1, 0))));
+      const bf16x4 hi = __builtin_bit_cast(
+          bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb8 + v_off(db, f >> 1, f & 1, 1))));
+      return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    };
+    bf16x8 vr[4];
+    vr[0] = vread(0);
+    vr[1] = vread(1);
+    vr[2] = vread(2);
+    float mx = -INFINITY;
+    const int key0n = kNextMasked ? key0_of(kb_n, j + 1) : 0;
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-        for (int mm = 0; mm < 2; ++mm) {
-          const bf16x4 lo = __builtin_bit_cast(
-              bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb8 + v_off(db, kb2, mm, 0))));
-          const bf16x4 hi = __builtin_bit_cast(
-              bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4*)(vb8 + v_off(db, kb2, mm, 1))));
-          const bf16x8 vf = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-          o[db] = mfma32(vf, pb[kb2][mm], o[db]);
+    for (int u = 0; u < 16; ++u) {
+      o[u & 3] = mfma32(vr[u & 3], pb[u >> 2], o[u & 3]);
+      if (u + 3 < 16) vr[(u + 3) & 3] = vread(u + 3);
+      if (kNext) {
+        float a = sn[u >> 3][(2 * u) & 15], b = sn[u >> 3][(2 * u + 1) & 15];
+        if (kNextMasked) {
+          const int kbase = key0n + 32 * (u >> 3);
+          if (kbase + acc_key((2 * u) & 15, lg) > qpos) a = -INFINITY;
+          if (kbase + acc_key((2 * u + 1) & 15, lg) > qpos) b = -INFINITY;
+          sn[u >> 3][(2 * u) & 15] = a;
+          sn[u >> 3][(2 * u + 1) & 15] = b;
         }
-    if (kNext) {
-      if (kNextMasked) mask_scores(sn, key0_of(kb_n, j + 1));
-      raise_max(sn);
+        mx = fmaxf(mx, fmaxf(a, b));
+      }
+      __builtin_amdgcn_sched_barrier(0);
     }
+    if (kNext) raise_to(pair_max(mx) * p.scale_log2);
 
     if (k_ahead)
       wait_dma_but_4();
@@ -312,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   __syncthreads();
   qk(ks[0], sa);
   if (nsteps == 2) mask_scores(sa, key0_of(kb_cur, 0));
-  raise_max(sa);
+  raise_to(row_max(sa));
   __syncthreads();  // every wave has read K_0 before iteration 0 overwrites it
 
   // Steps 0 .. nsteps-3 cover the fully visible blocks, the last two the
