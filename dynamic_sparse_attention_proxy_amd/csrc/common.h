@@ -243,13 +243,12 @@ __device__ inline float block_max_f(float x, float* lds_tmp, int tid, int nthrea
 }
 
 // Workgroup -> (head, query block) map of the attention kernels.  Work is
-// ordered KV group by KV group, and within a group by query block from the
-// last (heaviest: causal rows grow with qb) to the first, heads of the group
-// adjacent.  Workgroup ids are dealt round-robin to the 8 XCDs, so at any
-// time every die works on the same KV group: each die's L2 and the shared
-// last-level cache hold one group's K/V instead of all of them.
+// ordered KV group by KV group (at any time every die works on the same
+// group, so the shared last-level cache holds one group's K/V), and within a
+// group from the last query block (heaviest: causal rows grow with qb) to
+// the first.
 struct RowMap {
-  int hq, hkv, qpg, nblk;
+  int hq, hkv, qpg, nblk, xcd;
 };
 
 inline RowMap make_row_map(int hq, int hkv, int nblk) {
@@ -258,14 +257,31 @@ inline RowMap make_row_map(int hq, int hkv, int nblk) {
   m.hkv = hkv;
   m.qpg = hq / hkv;
   m.nblk = nblk;
+  m.xcd = (nblk % 8 == 0) ? 1 : 0;
   return m;
 }
 
+// Workgroup id -> (head, query block).  Ids run KV group by KV group.  The
+// dispatcher deals workgroups to the 8 XCDs round-robin (id % 8), each XCD
+// with its own L2; when the block count is a multiple of 8, XCD x takes the
+// query blocks x, x+8, x+16, ... counted from the last (heaviest) one and
+// runs the qpg heads of each on consecutive slots, so heads that read the
+// same K/V blocks at the same time share an L2.  Otherwise the heads of a
+// query block take adjacent ids, heaviest block first.
 __host__ __device__ inline void map_row(const RowMap& m, int id, int* h_out, int* qb_out) {
   const int per_group = m.qpg * m.nblk;
   const int g = id / per_group, rem = id - g * per_group;
-  *h_out = g * m.qpg + rem % m.qpg;
-  *qb_out = m.nblk - 1 - rem / m.qpg;
+  int hh, qi;
+  if (m.xcd) {
+    const int x = rem & 7, s = rem >> 3;
+    hh = s % m.qpg;
+    qi = 8 * (s / m.qpg) + x;
+  } else {
+    hh = rem % m.qpg;
+    qi = rem / m.qpg;
+  }
+  *h_out = g * m.qpg + hh;
+  *qb_out = m.nblk - 1 - qi;
 }
 
 }  // namespace crisp
