@@ -30,7 +30,7 @@ constexpr int kStep = 64;              // keys per pipeline step
 typedef __bf16 gcc_bf16x4 __attribute__((__vector_size__(8)));
 typedef __attribute__((address_space(3))) gcc_bf16x4 lds_bf16x4;
 constexpr int kKStages = 3;             // K tiles in flight: the next one is used, one more prefetched
-constexpr float kHeadroom = 8.f;        // log2 slack before the running max is raised
+constexpr float kSumLimit = 65536.f;     // a lane's step sum above this raises the running max
 constexpr int kBufferFlags = 0x00020000; // buffer resource word 3: raw 32-bit data, no swizzle
 
 struct AttnArgs {
@@ -205,21 +205,20 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   };
 
   // Iteration j of the software pipeline.  K_t lives in ks[t % 3] and V_t
-  // in vs[t & 1]; S_j arrives in `sc` already masked, with the running max
-  // m_run valid for it.  Iteration j
+  // in vs[t & 1]; S_j arrives in `sc` already masked.  Iteration j
   //   - starts the DMA of V_{j+1} over V_{j-1} and then of K_{j+3} over K_j
   //     (both read in iteration j-1),
   //   - block 1: S_{j+1} = K_{j+1} Q^T (MFMA) beside exp / row sum / bf16
-  //     packing of S_j (VALU),
-  //   - block 2: O += V_j P_j (MFMA) beside masking and row max of S_{j+1},
-  //   - raises the running max for S_{j+1} when needed (rare branch),
+  //     packing of S_j (VALU) against the current running max,
+  //   - raises the running max and redoes the exps when they grew too large
+  //     (rare branch; the running max only needs to keep probabilities in
+  //     range, any value works for exactness),
+  //   - block 2: O += V_j P_j (MFMA) beside masking of S_{j+1},
   //   - waits for all of its DMA but the K_{j+3} one, which has until the
   //     end of iteration j+1, and meets the other waves at one barrier.
-  // No branch separates the MFMA and VALU halves of a block, so the
-  // scheduler can interleave them.  kNextMasked: step j+1 is one of the two
-  // steps of the diagonal block (sorted lists put it last); kNext: j+1 is a
-  // step.  kb_v, kb_k, kb_n: key blocks of steps j+1, j+3, j+1; kst: stage
-  // of K_{j+1}.
+  // kNextMasked: step j+1 is one of the two steps of the diagonal block
+  // (sorted lists put it last); kNext: j+1 is a step.  kb_v, kb_k, kb_n: key
+  // blocks of steps j+1, j+3, j+1; kst: stage of K_{j+1}.
   float neg_m = 0.f;
   // Row max across the two half-waves holding a query's keys: with both
   // operands equal, permlane32_swap returns lane l's value and that of lane
@@ -238,20 +237,20 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
     for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[1][v], s[1][v + 1]));
     return pair_max(mx) * p.scale_log2;
   };
-  // The running max is raised only when a score exceeds it by more than
-  // kHeadroom; probabilities then stay below 2^kHeadroom.
-  auto raise_to = [&](float mxs) {
-    if (__any(mxs > m_run + kHeadroom)) {
-      const float m_new = fmaxf(m_run, mxs);
-      const float alpha = fast_exp2(m_run - m_new);  // 0 while m_run is -inf
+  // Raises the running max to cover scores `s` (rescaling O and the row
+  // sum); used on the first step and whenever a step's probabilities grow
+  // past kSumLimit.
+  auto raise_for = [&](const f32x16 (&s)[2]) {
+    const float mxs = row_max(s);
+    const float m_new = fmaxf(m_run, mxs);
+    const float alpha = fast_exp2(m_run - m_new);  // 0 while m_run is -inf
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
-      l_run *= alpha;
-      m_run = m_new;
-      neg_m = -m_new;
-    }
+      for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
+    l_run *= alpha;
+    m_run = m_new;
+    neg_m = -m_new;
   };
   auto mask_scores = [&](f32x16 (&s)[2], int key0) {
 #pragma unroll
@@ -286,6 +285,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
     }
     float e[32];
     bf16x8 pb[4];  // P_j operand f = 2 * key half + 16-key group: keys 16 f + 8 lg .. +7
+    float ls = 0.f;
     const f32x16 zero = {};
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
@@ -296,7 +296,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
 #pragma unroll
       for (int u = 2 * t; u < 2 * t + 2; ++u) {
         e[u] = fast_exp2(fmaf(sc[u >> 4][u & 15], p.scale_log2, neg_m));
-        l_run += e[u];
+        ls += e[u];
       }
       if ((t & 3) == 3) {
         const int f = t >> 2;
@@ -305,9 +305,26 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    // The running max is only raised when it was too low for this step:
+    // some lane's probabilities sum past kSumLimit (+inf included).  Every
+    // probability then stays at most kSumLimit, far inside bf16 / fp32 range.
+    if (__any(!(ls <= kSumLimit))) {
+      raise_for(sc);
+      ls = 0.f;
+#pragma unroll
+      for (int u = 0; u < 32; ++u) {
+        e[u] = fast_exp2(fmaf(sc[u >> 4][u & 15], p.scale_log2, neg_m));
+        ls += e[u];
+      }
+#pragma unroll
+      for (int f = 0; f < 4; ++f)
+        pb[f] = pack_bf16x8(e[8 * f], e[8 * f + 1], e[8 * f + 2], e[8 * f + 3], e[8 * f + 4], e[8 * f + 5],
+                            e[8 * f + 6], e[8 * f + 7]);
+    }
+    l_run += ls;
 
     // Block 2: MFMA u of O += V_j P_j (d slice u & 3, P operand u / 4) beside
-    // masking and row max of scores 2u, 2u+1 of S_{j+1}.
+    // masking of scores 2u, 2u+1 of S_{j+1}.
     __attribute__((address_space(3))) char* vb8 = (__attribute__((address_space(3))) char*)vs[j & 1];
     auto vread = [&](int u) -> bf16x8 {
       const int db = u & 3, f = u >> 2;
@@ -321,26 +338,18 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
     vr[0] = vread(0);
     vr[1] = vread(1);
     vr[2] = vread(2);
-    float mx = -INFINITY;
     const int key0n = kNextMasked ? key0_of(kb_n, j + 1) : 0;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       o[u & 3] = mfma32(vr[u & 3], pb[u >> 2], o[u & 3]);
       if (u + 3 < 16) vr[(u + 3) & 3] = vread(u + 3);
-      if (kNext) {
-        float a = sn[u >> 3][(2 * u) & 15], b = sn[u >> 3][(2 * u + 1) & 15];
-        if (kNextMasked) {
-          const int kbase = key0n + 32 * (u >> 3);
-          if (kbase + acc_key((2 * u) & 15, lg) > qpos) a = -INFINITY;
-          if (kbase + acc_key((2 * u + 1) & 15, lg) > qpos) b = -INFINITY;
-          sn[u >> 3][(2 * u) & 15] = a;
-          sn[u >> 3][(2 * u + 1) & 15] = b;
-        }
-        mx = fmaxf(mx, fmaxf(a, b));
+      if (kNextMasked) {
+        const int kbase = key0n + 32 * (u >> 3);
+        if (kbase + acc_key((2 * u) & 15, lg) > qpos) sn[u >> 3][(2 * u) & 15] = -INFINITY;
+        if (kbase + acc_key((2 * u + 1) & 15, lg) > qpos) sn[u >> 3][(2 * u + 1) & 15] = -INFINITY;
       }
       __builtin_amdgcn_sched_barrier(0);
     }
-    if (kNext) raise_to(pair_max(mx) * p.scale_log2);
 
     if (k_ahead)
       wait_dma_but_4();
@@ -359,7 +368,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   __syncthreads();
   qk(ks[0], sa);
   if (nsteps == 2) mask_scores(sa, key0_of(kb_cur, 0));
-  raise_to(row_max(sa));
+  raise_for(sa);
   __syncthreads();  // every wave has read K_0 before iteration 0 overwrites it
 
   // Steps 0 .. nsteps-3 cover the fully visible blocks, the last two the
