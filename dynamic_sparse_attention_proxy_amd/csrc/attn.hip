@@ -147,18 +147,20 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   // Ordering is explicit instead: each step ends with a vmcnt wait covering
   // the tiles the next step reads, then a barrier.
   const int wu = __builtin_amdgcn_readfirstlane(w);
-  auto dma = [&](__amdgpu_buffer_rsrc_t rs, const int (&off)[4], __bf16* stage, int kb, int step) {
+  // One DMA instruction: rows 16 wu + 4 i .. +3 of the tile of step `step`.
+  auto dma1 = [&](__amdgpu_buffer_rsrc_t rs, int off, __bf16* stage, int kb, int step, int i) {
     const int soff = key0_of(kb, step) * (kHeadDim * 2);
+    const unsigned lds_addr =
+        (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)(stage + (16 * wu + 4 * i) * kHeadDim);
+    // one wait state between writing M0 and the DMA that reads it
+    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+                 :
+                 : "s"(lds_addr), "v"(off), "s"(rs), "s"(soff)
+                 : "memory", "m0");
+  };
+  auto dma = [&](__amdgpu_buffer_rsrc_t rs, const int (&off)[4], __bf16* stage, int kb, int step) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const unsigned lds_addr =
-          (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)(stage + (16 * wu + 4 * i) * kHeadDim);
-      // one wait state between writing M0 and the DMA that reads it
-      asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                   :
-                   : "s"(lds_addr), "v"(off[i]), "s"(rs), "s"(soff)
-                   : "memory", "m0");
-    }
+    for (int i = 0; i < 4; ++i) dma1(rs, off[i], stage, kb, step, i);
   };
 
   // Row of the K operand fed by this lane: a permutation of 0..31 (see top).
@@ -206,19 +208,23 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
 
   // Iteration j of the software pipeline.  K_t lives in ks[t % 3] and V_t
   // in vs[t & 1]; S_j arrives in `sc` already masked.  Iteration j
-  //   - starts the DMA of V_{j+1} over V_{j-1} and then of K_{j+3} over K_j
-  //     (both read in iteration j-1),
   //   - block 1: S_{j+1} = K_{j+1} Q^T (MFMA) beside exp / row sum / bf16
-  //     packing of S_j (VALU) against the current running max,
+  //     packing of S_j (VALU) against the current running max, and the DMA
+  //     of V_{j+1} over V_{j-1} (read in iteration j-1),
   //   - raises the running max and redoes the exps when they grew too large
   //     (rare branch; the running max only needs to keep probabilities in
   //     range, any value works for exactness),
-  //   - block 2: O += V_j P_j (MFMA) beside masking of S_{j+1},
+  //   - block 2: O += V_j P_j (MFMA) beside masking of S_{j+1}, and the DMA
+  //     of K_{j+3} over K_j (read in iteration j-1),
   //   - waits for all of its DMA but the K_{j+3} one, which has until the
   //     end of iteration j+1, and meets the other waves at one barrier.
-  // kNextMasked: step j+1 is one of the two steps of the diagonal block
-  // (sorted lists put it last); kNext: j+1 is a step.  kb_v, kb_k, kb_n: key
-  // blocks of steps j+1, j+3, j+1; kst: stage of K_{j+1}.
+  // The 8 DMA instructions of a wave are spread one per four MFMAs: issued
+  // together right after the barrier, the 32 of a workgroup queue up in the
+  // CU's address unit and stall the waves' in-order issue.
+  // kKAhead: there is a step j+3; kNextMasked: step j+1 is one of the two
+  // steps of the diagonal block (sorted lists put it last); kNext: j+1 is a
+  // step.  kb_v, kb_k, kb_n: key blocks of steps j+1, j+3, j+1; kst: stage
+  // of K_{j+1}.
   float neg_m = 0.f;
   // Row max across the two half-waves holding a query's keys: with both
   // operands equal, permlane32_swap returns lane l's value and that of lane
@@ -261,12 +267,12 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   };
 
   auto iter = [&](int j, int kb_v, int kb_k, int kb_n, int kst, f32x16 (&sc)[2], f32x16 (&sn)[2],
-                  auto next_masked_tag, auto next_tag) {
+                  auto k_ahead_tag, auto next_masked_tag, auto next_tag) {
+    constexpr bool kKAhead = decltype(k_ahead_tag)::value;
     constexpr bool kNextMasked = decltype(next_masked_tag)::value;
     constexpr bool kNext = decltype(next_tag)::value;
-    if (kNext) dma(vrs, dma_v, vs[(j + 1) & 1], kb_v, j + 1);
-    const bool k_ahead = j + 3 < nsteps;
-    if (k_ahead) dma(krs, dma_k, ks[kst == 0 ? 2 : kst - 1], kb_k, j + 3);
+    __bf16* vdst = vs[(j + 1) & 1];
+    __bf16* kdst = ks[kst == 0 ? 2 : kst - 1];
 
     // The two blocks are written out in issue order, one unit per MFMA, with
     // operand reads three MFMAs ahead through 4-entry register rings;
@@ -292,6 +298,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
       if (kNext) {
         sn[t & 1] = mfma32(kr[t & 3], qf[t >> 1], t < 2 ? zero : sn[t & 1]);
         if (t + 3 < 16) kr[(t + 3) & 3] = kread(t + 3);
+        if ((t & 3) == 0) dma1(vrs, dma_v[t >> 2], vdst, kb_v, j + 1, t >> 2);
       }
 #pragma unroll
       for (int u = 2 * t; u < 2 * t + 2; ++u) {
@@ -343,6 +350,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
     for (int u = 0; u < 16; ++u) {
       o[u & 3] = mfma32(vr[u & 3], pb[u >> 2], o[u & 3]);
       if (u + 3 < 16) vr[(u + 3) & 3] = vread(u + 3);
+      if (kKAhead && (u & 3) == 0) dma1(krs, dma_k[u >> 2], kdst, kb_k, j + 3, u >> 2);
       if (kNextMasked) {
         const int kbase = key0n + 32 * (u >> 3);
         if (kbase + acc_key((2 * u) & 15, lg) > qpos) sn[u >> 3][(2 * u) & 15] = -INFINITY;
@@ -351,7 +359,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
       __builtin_amdgcn_sched_barrier(0);
     }
 
-    if (k_ahead)
+    if (kKAhead)
       wait_dma_but_4();
     else
       wait_dma();
@@ -380,25 +388,25 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   int j = 0, kst = 1;
   if (nsteps >= 4) {
     for (; j < nsteps - 4; j += 2) {
-      iter(j, kb_cur, kb_nxt, kb_cur, kst, sa, sb, F{}, T{});
+      iter(j, kb_cur, kb_nxt, kb_cur, kst, sa, sb, T{}, F{}, T{});
       kst = kst == 2 ? 0 : kst + 1;
-      iter(j + 1, kb_nxt, kb_nn, kb_nxt, kst, sb, sa, F{}, T{});
+      iter(j + 1, kb_nxt, kb_nn, kb_nxt, kst, sb, sa, T{}, F{}, T{});
       kst = kst == 2 ? 0 : kst + 1;
       kb_cur = kb_nxt;
       kb_nxt = kb_nn;
       kb_nn = block_at((j >> 1) + 3);
     }
     // j = nsteps - 4: kb_cur is the last fully visible block, kb_nxt the diagonal one
-    iter(j, kb_cur, kb_nxt, kb_cur, kst, sa, sb, F{}, T{});
+    iter(j, kb_cur, kb_nxt, kb_cur, kst, sa, sb, T{}, F{}, T{});
     kst = kst == 2 ? 0 : kst + 1;
-    iter(j + 1, kb_nxt, kb_nxt, kb_nxt, kst, sb, sa, T{}, T{});
+    iter(j + 1, kb_nxt, kb_nxt, kb_nxt, kst, sb, sa, F{}, T{}, T{});
     kst = kst == 2 ? 0 : kst + 1;
     j += 2;
     kb_cur = kb_nxt;
   }
-  iter(j, kb_cur, kb_cur, kb_cur, kst, sa, sb, T{}, T{});
+  iter(j, kb_cur, kb_cur, kb_cur, kst, sa, sb, F{}, T{}, T{});
   kst = kst == 2 ? 0 : kst + 1;
-  iter(j + 1, kb_cur, kb_cur, kb_cur, kst, sb, sa, F{}, F{});
+  iter(j + 1, kb_cur, kb_cur, kb_cur, kst, sb, sa, F{}, F{}, F{});
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / l_tot;
