@@ -115,13 +115,16 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   // loads global chunk (L & 15) ^ swz(r) of that row.
   const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc((void*)kg, 0, (int)(nd * 2), kBufferFlags);
   const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc((void*)vg, 0, (int)(nd * 2), kBufferFlags);
-  int dma_k[4], dma_v[4];
+  // swz_v depends only on the row's bits 0-1 (lane / 16 here), so the V
+  // offsets of the 4 instructions differ by exactly 1024 bytes; swz_k also
+  // takes bits 2-3 (= i) and needs one offset per instruction.
+  int dma_k[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 16 * w + 4 * i + (lane >> 4);
     dma_k[i] = r * 256 + (((lane & 15) ^ swz_k(r)) << 4);
-    dma_v[i] = r * 256 + (((lane & 15) ^ swz_v(r)) << 4);
   }
+  const int dma_v = (16 * w + (lane >> 4)) * 256 + (((lane & 15) ^ swz_v(lane >> 4)) << 4);
 
   // List entries: 64 at a time in one VGPR (lane i holds entry c0 + i),
   // picked out with readlane; a chunk is reloaded only when a block past it
@@ -148,19 +151,40 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   // the tiles the next step reads, then a barrier.
   const int wu = __builtin_amdgcn_readfirstlane(w);
   // One DMA instruction: rows 16 wu + 4 i .. +3 of the tile of step `step`.
-  auto dma1 = [&](__amdgpu_buffer_rsrc_t rs, int off, __bf16* stage, int kb, int step, int i) {
+  // `off` is the lane's byte offset for i = 0 when `imm` is set: the
+  // instruction's immediate offset (1024 i) then moves both the global read
+  // and the LDS destination.  Otherwise `off` is the lane's offset for i.
+  auto dma1 = [&](__amdgpu_buffer_rsrc_t rs, int off, __bf16* stage, int kb, int step, int i, bool imm) {
     const int soff = key0_of(kb, step) * (kHeadDim * 2);
-    const unsigned lds_addr =
-        (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)(stage + (16 * wu + 4 * i) * kHeadDim);
     // one wait state between writing M0 and the DMA that reads it
-    asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
-                 :
-                 : "s"(lds_addr), "v"(off), "s"(rs), "s"(soff)
-                 : "memory", "m0");
+#define CRISP_DMA(OFF)                                                                        \
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen offset:" #OFF " lds" \
+               :                                                                              \
+               : "s"(lds_addr), "v"(off), "s"(rs), "s"(soff)                                  \
+               : "memory", "m0")
+    if (imm) {
+      const unsigned lds_addr =
+          (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)(stage + 16 * wu * kHeadDim);
+      switch (i) {
+        case 0: CRISP_DMA(0); break;
+        case 1: CRISP_DMA(1024); break;
+        case 2: CRISP_DMA(2048); break;
+        default: CRISP_DMA(3072); break;
+      }
+    } else {
+      const unsigned lds_addr =
+          (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)(stage + (16 * wu + 4 * i) * kHeadDim);
+      CRISP_DMA(0);
+    }
+#undef CRISP_DMA
   };
-  auto dma = [&](__amdgpu_buffer_rsrc_t rs, const int (&off)[4], __bf16* stage, int kb, int step) {
+  auto dma_k_tile = [&](__bf16* stage, int kb, int step) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) dma1(rs, off[i], stage, kb, step, i);
+    for (int i = 0; i < 4; ++i) dma1(krs, dma_k[i], stage, kb, step, i, false);
+  };
+  auto dma_v_tile = [&](__bf16* stage, int kb, int step) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) dma1(vrs, dma_v, stage, kb, step, i, true);
   };
 
   // Row of the K operand fed by this lane: a permutation of 0..31 (see top).
@@ -204,28 +228,42 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
         s[kb2] = mfma32(kf, qf[kk], s[kb2]);
       }
     }
+  };  // One key half (keys key0 + 32 kb2 .. +31) of a step's scores, with the
+  // K operand read from global memory in the layout the LDS path gives.
+  auto qk_half_global = [&](int key0, int kb2) -> f32x16 {
+    const __bf16* krow_g = kg + (size_t)(key0 + 32 * kb2 + krow) * kHeadDim + 8 * lg;
+    f32x16 s = {};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) s = mfma32(as_bf16x8(*(const u32x4*)(krow_g + 16 * kk)), qf[kk], s);
+    return s;
   };
 
   // Iteration j of the software pipeline.  K_t lives in ks[t % 3] and V_t
   // in vs[t & 1]; S_j arrives in `sc` already masked.  Iteration j
   //   - block 1: S_{j+1} = K_{j+1} Q^T (MFMA) beside exp / row sum / bf16
-  //     packing of S_j (VALU) against the current running max, and the DMA
-  //     of V_{j+1} over V_{j-1} (read in iteration j-1),
+  //     packing of the second key half of S_j (VALU) against the current
+  //     running max, and the DMA of V_{j+1} over V_{j-1} (read in iteration
+  //     j-1),
   //   - raises the running max and redoes the exps when they grew too large
   //     (rare branch; the running max only needs to keep probabilities in
   //     range, any value works for exactness),
-  //   - block 2: O += V_j P_j (MFMA) beside masking of S_{j+1}, and the DMA
-  //     of K_{j+3} over K_j (read in iteration j-1),
+  //   - block 2: O += V_j P_j (MFMA) beside masking of S_{j+1} and the exps
+  //     of its first key half, and the DMA of K_{j+3} over K_j (read in
+  //     iteration j-1),
   //   - waits for all of its DMA but the K_{j+3} one, which has until the
   //     end of iteration j+1, and meets the other waves at one barrier.
   // The 8 DMA instructions of a wave are spread one per four MFMAs: issued
   // together right after the barrier, the 32 of a workgroup queue up in the
   // CU's address unit and stall the waves' in-order issue.
-  // kKAhead: there is a step j+3; kNextMasked: step j+1 is one of the two
-  // steps of the diagonal block (sorted lists put it last); kNext: j+1 is a
-  // step.  kb_v, kb_k, kb_n: key blocks of steps j+1, j+3, j+1; kst: stage
-  // of K_{j+1}.
+  // kCurMasked / kNextMasked: step j / j+1 is one of the two steps of the
+  // diagonal block (sorted lists put it last); kKAhead: there is a step j+3;
+  // kNext: j+1 is a step.  kb_c, kb_v, kb_k, kb_n: key blocks of steps j,
+  // j+1, j+3, j+1; kst: stage of K_{j+1}.
   float neg_m = 0.f;
+  // First-key-half probabilities of the next step (bf16 operands) and their
+  // row sum, computed one iteration ahead.
+  bf16x8 p_lo[2];
+  float ls_lo = 0.f;
   // Row max across the two half-waves holding a query's keys: with both
   // operands equal, permlane32_swap returns lane l's value and that of lane
   // l ^ 32 in its two results.
@@ -243,11 +281,10 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
     for (int v = 0; v < 16; v += 2) mx = fmaxf(mx, fmaxf(s[1][v], s[1][v + 1]));
     return pair_max(mx) * p.scale_log2;
   };
-  // Raises the running max to cover scores `s` (rescaling O and the row
-  // sum); used on the first step and whenever a step's probabilities grow
-  // past kSumLimit.
-  auto raise_for = [&](const f32x16 (&s)[2]) {
-    const float mxs = row_max(s);
+  // Raises the running max to at least `mxs` (a scaled row max), rescaling
+  // O and the row sum; used on the first step and whenever a step's
+  // probabilities grow past kSumLimit.
+  auto raise_to = [&](float mxs) {
     const float m_new = fmaxf(m_run, mxs);
     const float alpha = fast_exp2(m_run - m_new);  // 0 while m_run is -inf
 #pragma unroll
@@ -266,8 +303,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
         if (key0 + 32 * kb2 + acc_key(v, lg) > qpos) s[kb2][v] = -INFINITY;
   };
 
-  auto iter = [&](int j, int kb_v, int kb_k, int kb_n, int kst, f32x16 (&sc)[2], f32x16 (&sn)[2],
-                  auto k_ahead_tag, auto next_masked_tag, auto next_tag) {
+  auto iter = [&](int j, int kb_c, int kb_v, int kb_k, int kb_n, int kst, f32x16 (&sc)[2], f32x16 (&sn)[2],
+                  auto cur_masked_tag, auto k_ahead_tag, auto next_masked_tag, auto next_tag) {
+    constexpr bool kCurMasked = decltype(cur_masked_tag)::value;
     constexpr bool kKAhead = decltype(k_ahead_tag)::value;
     constexpr bool kNextMasked = decltype(next_masked_tag)::value;
     constexpr bool kNext = decltype(next_tag)::value;
@@ -276,9 +314,12 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
 
     // The two blocks are written out in issue order, one unit per MFMA, with
     // operand reads three MFMAs ahead through 4-entry register rings;
-    // sched_barrier(0) keeps the units as written.
+    // sched_barrier(0) keeps the units as written.  The exps of a step are
+    // split over both blocks so that every MFMA has about the same VALU work
+    // beside it: scores 0..15 of S_{j+1} (its first key half) in block 2 of
+    // iteration j, scores 16..31 in block 1 of iteration j+1.
     // Block 1: MFMA t of S_{j+1} (key half t & 1, d slice t / 2) beside the
-    // exp, row sum and bf16 packing of scores 2t, 2t+1 of S_j.
+    // exp, row sum and bf16 packing of score 16 + t of S_j.
     const char* kb8 = (const char*)ks[kst];
     auto kread = [&](int t) -> bf16x8 {
       return as_bf16x8(*(const u32x4*)(kb8 + k_off[t >> 1] + (t & 1) * 8192));
@@ -289,49 +330,66 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
       kr[1] = kread(1);
       kr[2] = kread(2);
     }
-    float e[32];
-    bf16x8 pb[4];  // P_j operand f = 2 * key half + 16-key group: keys 16 f + 8 lg .. +7
-    float ls = 0.f;
+    float e[16];
+    // P_j operand f = 2 * key half + 16-key group (keys 16 f + 8 lg .. +7);
+    // pb[0], pb[1] come from the previous iteration.
+    bf16x8 pb[4] = {p_lo[0], p_lo[1], {}, {}};
+    float ls = ls_lo;
     const f32x16 zero = {};
 #pragma unroll
     for (int t = 0; t < 16; ++t) {
       if (kNext) {
         sn[t & 1] = mfma32(kr[t & 3], qf[t >> 1], t < 2 ? zero : sn[t & 1]);
         if (t + 3 < 16) kr[(t + 3) & 3] = kread(t + 3);
-        if ((t & 3) == 0) dma1(vrs, dma_v[t >> 2], vdst, kb_v, j + 1, t >> 2);
+        if ((t & 3) == 0) dma1(vrs, dma_v, vdst, kb_v, j + 1, t >> 2, true);
       }
-#pragma unroll
-      for (int u = 2 * t; u < 2 * t + 2; ++u) {
-        e[u] = fast_exp2(fmaf(sc[u >> 4][u & 15], p.scale_log2, neg_m));
-        ls += e[u];
-      }
-      if ((t & 3) == 3) {
-        const int f = t >> 2;
-        pb[f] = pack_bf16x8(e[8 * f], e[8 * f + 1], e[8 * f + 2], e[8 * f + 3], e[8 * f + 4], e[8 * f + 5],
-                            e[8 * f + 6], e[8 * f + 7]);
+      e[t] = fast_exp2(fmaf(sc[1][t], p.scale_log2, neg_m));
+      ls += e[t];
+      if (t & 1) {  // pack each pair as soon as it is complete
+        pb[2 + (t >> 3)][(t & 7) - 1] = (__bf16)e[t - 1];
+        pb[2 + (t >> 3)][t & 7] = (__bf16)e[t];
       }
       __builtin_amdgcn_sched_barrier(0);
     }
     // The running max is only raised when it was too low for this step:
     // some lane's probabilities sum past kSumLimit (+inf included).  Every
     // probability then stays at most kSumLimit, far inside bf16 / fp32 range.
+    // On the fully visible steps S_j is recomputed from K_j in global memory
+    // (its LDS stage may already be refilled by waves in block 2), one key
+    // half at a time, once for the max and once for the exps, so that its
+    // first key half need not stay live; the two diagonal steps keep their
+    // masked scores instead.
     if (__any(!(ls <= kSumLimit))) {
-      raise_for(sc);
+      const int key0c = key0_of(kb_c, j);
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const f32x16 sr = kCurMasked ? sc[kb2] : qk_half_global(key0c, kb2);
+#pragma unroll
+        for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sr[v]);
+      }
+      raise_to(pair_max(mx) * p.scale_log2);
       ls = 0.f;
 #pragma unroll
-      for (int u = 0; u < 32; ++u) {
-        e[u] = fast_exp2(fmaf(sc[u >> 4][u & 15], p.scale_log2, neg_m));
-        ls += e[u];
-      }
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const f32x16 sr = kCurMasked ? sc[kb2] : qk_half_global(key0c, kb2);
 #pragma unroll
-      for (int f = 0; f < 4; ++f)
-        pb[f] = pack_bf16x8(e[8 * f], e[8 * f + 1], e[8 * f + 2], e[8 * f + 3], e[8 * f + 4], e[8 * f + 5],
-                            e[8 * f + 6], e[8 * f + 7]);
+        for (int f = 0; f < 2; ++f) {
+          float x[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            x[i] = fast_exp2(fmaf(sr[8 * f + i], p.scale_log2, neg_m));
+            ls += x[i];
+          }
+          pb[2 * kb2 + f] = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+        }
+      }
     }
     l_run += ls;
 
     // Block 2: MFMA u of O += V_j P_j (d slice u & 3, P operand u / 4) beside
-    // masking of scores 2u, 2u+1 of S_{j+1}.
+    // masking of scores 2u, 2u+1 of S_{j+1} and the exp, row sum and packing
+    // of its score u.
     __attribute__((address_space(3))) char* vb8 = (__attribute__((address_space(3))) char*)vs[j & 1];
     auto vread = [&](int u) -> bf16x8 {
       const int db = u & 3, f = u >> 2;
@@ -346,18 +404,28 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
     vr[1] = vread(1);
     vr[2] = vread(2);
     const int key0n = kNextMasked ? key0_of(kb_n, j + 1) : 0;
+    float lsn = 0.f;
 #pragma unroll
     for (int u = 0; u < 16; ++u) {
       o[u & 3] = mfma32(vr[u & 3], pb[u >> 2], o[u & 3]);
       if (u + 3 < 16) vr[(u + 3) & 3] = vread(u + 3);
-      if (kKAhead && (u & 3) == 0) dma1(krs, dma_k[u >> 2], kdst, kb_k, j + 3, u >> 2);
-      if (kNextMasked) {
-        const int kbase = key0n + 32 * (u >> 3);
-        if (kbase + acc_key((2 * u) & 15, lg) > qpos) sn[u >> 3][(2 * u) & 15] = -INFINITY;
-        if (kbase + acc_key((2 * u + 1) & 15, lg) > qpos) sn[u >> 3][(2 * u + 1) & 15] = -INFINITY;
+      if (kKAhead && (u & 3) == 0) dma1(krs, dma_k[u >> 2], kdst, kb_k, j + 3, u >> 2, false);
+      if (kNext) {
+        if (kNextMasked) {
+          const int kbase = key0n + 32 * (u >> 3);
+          if (kbase + acc_key((2 * u) & 15, lg) > qpos) sn[u >> 3][(2 * u) & 15] = -INFINITY;
+          if (kbase + acc_key((2 * u + 1) & 15, lg) > qpos) sn[u >> 3][(2 * u + 1) & 15] = -INFINITY;
+        }
+        e[u] = fast_exp2(fmaf(sn[0][u], p.scale_log2, neg_m));
+        lsn += e[u];
+        if (u & 1) {
+          p_lo[u >> 3][(u & 7) - 1] = (__bf16)e[u - 1];
+          p_lo[u >> 3][u & 7] = (__bf16)e[u];
+        }
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    ls_lo = lsn;
 
     if (kKAhead)
       wait_dma_but_4();
@@ -368,15 +436,25 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
 
   f32x16 sa[2], sb[2];
   int kb_cur = block_at(0), kb_nxt = block_at(1), kb_nn = block_at(2);
-  dma(krs, dma_k, ks[0], kb_cur, 0);
-  dma(vrs, dma_v, vs[0], kb_cur, 0);
-  dma(krs, dma_k, ks[1], kb_cur, 1);
-  if (nsteps > 2) dma(krs, dma_k, ks[2], kb_nxt, 2);
+  dma_k_tile(ks[0], kb_cur, 0);
+  dma_v_tile(vs[0], kb_cur, 0);
+  dma_k_tile(ks[1], kb_cur, 1);
+  if (nsteps > 2) dma_k_tile(ks[2], kb_nxt, 2);
   wait_dma();
   __syncthreads();
   qk(ks[0], sa);
   if (nsteps == 2) mask_scores(sa, key0_of(kb_cur, 0));
-  raise_for(sa);
+  raise_to(row_max(sa));
+#pragma unroll
+  for (int f = 0; f < 2; ++f) {
+    float x[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      x[i] = fast_exp2(fmaf(sa[0][8 * f + i], p.scale_log2, neg_m));
+      ls_lo += x[i];
+    }
+    p_lo[f] = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+  }
   __syncthreads();  // every wave has read K_0 before iteration 0 overwrites it
 
   // Steps 0 .. nsteps-3 cover the fully visible blocks, the last two the
@@ -388,25 +466,25 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   int j = 0, kst = 1;
   if (nsteps >= 4) {
     for (; j < nsteps - 4; j += 2) {
-      iter(j, kb_cur, kb_nxt, kb_cur, kst, sa, sb, T{}, F{}, T{});
+      iter(j, kb_cur, kb_cur, kb_nxt, kb_cur, kst, sa, sb, F{}, T{}, F{}, T{});
       kst = kst == 2 ? 0 : kst + 1;
-      iter(j + 1, kb_nxt, kb_nn, kb_nxt, kst, sb, sa, T{}, F{}, T{});
+      iter(j + 1, kb_cur, kb_nxt, kb_nn, kb_nxt, kst, sb, sa, F{}, T{}, F{}, T{});
       kst = kst == 2 ? 0 : kst + 1;
       kb_cur = kb_nxt;
       kb_nxt = kb_nn;
       kb_nn = block_at((j >> 1) + 3);
     }
     // j = nsteps - 4: kb_cur is the last fully visible block, kb_nxt the diagonal one
-    iter(j, kb_cur, kb_nxt, kb_cur, kst, sa, sb, T{}, F{}, T{});
+    iter(j, kb_cur, kb_cur, kb_nxt, kb_cur, kst, sa, sb, F{}, T{}, F{}, T{});
     kst = kst == 2 ? 0 : kst + 1;
-    iter(j + 1, kb_nxt, kb_nxt, kb_nxt, kst, sb, sa, F{}, T{}, T{});
+    iter(j + 1, kb_cur, kb_nxt, kb_nxt, kb_nxt, kst, sb, sa, F{}, F{}, T{}, T{});
     kst = kst == 2 ? 0 : kst + 1;
     j += 2;
     kb_cur = kb_nxt;
   }
-  iter(j, kb_cur, kb_cur, kb_cur, kst, sa, sb, F{}, T{}, T{});
+  iter(j, kb_cur, kb_cur, kb_cur, kb_cur, kst, sa, sb, T{}, F{}, T{}, T{});
   kst = kst == 2 ? 0 : kst + 1;
-  iter(j + 1, kb_cur, kb_cur, kb_cur, kst, sb, sa, F{}, F{}, F{});
+  iter(j + 1, kb_cur, kb_cur, kb_cur, kb_cur, kst, sb, sa, T{}, F{}, F{}, F{});
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / l_tot;

@@ -105,10 +105,60 @@ def _pack_lists(all_lists, hq, N):
     return torch.from_numpy(count).cuda(), torch.from_numpy(idx).cuda()
 
 
+@pytest.mark.parametrize("where", ["visible", "diagonal", "first"])
+def test_attention_raises_running_max_mid_row(where):
+    """Planted keys score about 23 (natural-log units) above everything the
+    first step of a row sees, so the kernels' running max must be raised in
+    the middle of a row: on a fully visible step ("visible", scores redone
+    from K in global memory), on the masked diagonal steps ("diagonal", both
+    halves of the block), or never after the first step ("first")."""
+    n, N = 2048, 16
+    w = synth.custom(2, 1, n, seed=77, needles=0)
+    x = synth.make_inputs(w, device="cuda")
+    g = torch.Generator().manual_seed(5)
+    u = torch.randn(128, generator=g, dtype=torch.float64)
+    u = (u / u.norm()).to("cuda")
+    planted = {"visible": [5 * BLK + 17, 9 * BLK + 100], "diagonal": [12 * BLK + 3, 15 * BLK + 70],
+               "first": [1]}[where]
+    q = (x.q.double() + 5.0 * u).to(torch.bfloat16)
+    k = x.k.double()
+    for pos in planted:
+        k[0, pos] += 60.0 * u
+    k = k.to(torch.bfloat16)
+    v = x.v
+    print(f"[raise] where={where} planted={planted}", flush=True)
+    dims = B.make_dims(2, 1, n)
+    rng = np.random.default_rng(11)
+    lists = [_random_lists(rng, N, "full"), _random_lists(rng, N, "random")]
+    count, idx = _pack_lists(lists, 2, N)
+    out = torch.empty((2, n, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((2, n), dtype=torch.float32, device="cuda")
+    dense = torch.empty_like(out)
+    dlse = torch.empty_like(lse)
+    B.crisp_sparse_attn(dims, q, k, v, count, idx, out, lse)
+    B.crisp_dense_attn(dims, q, k, v, dense, dlse)
+    torch.cuda.synchronize()
+    k64, v64 = to64(k[0]), to64(v[0])
+    for h in range(2):
+        q64 = to64(q[h])
+        ref = O.attention_rows(q64, k64, v64, lists[h], dims.scale, range(N))
+        dref = O.attention_rows(q64, k64, v64, O.dense_lists(N), dims.scale, range(N))
+        og, lg = out[h].cpu().numpy(), lse[h].cpu().numpy()
+        dg, dl = dense[h].cpu().numpy(), dlse[h].cpu().numpy()
+        for qb in range(N):
+            rows = slice(qb * BLK, (qb + 1) * BLK)
+            check_attention(og[rows], ref[qb][0], f"{where} sparse h {h} qb {qb}")
+            np.testing.assert_allclose(lg[rows], ref[qb][1], rtol=2e-5, atol=2e-5)
+            check_attention(dg[rows], dref[qb][0], f"{where} dense h {h} qb {qb}")
+            np.testing.assert_allclose(dl[rows], dref[qb][1], rtol=2e-5, atol=2e-5)
+    # the planted keys dominate the rows that see them
+    assert float(lse[0, planted[-1] + 1]) > 20.0
+
+
 @pytest.mark.parametrize("hq,hkv,n,kind", [
-    (1, 1, 256, "random"),     # smallest length, mode-2 map
-    (3, 1, 640, "random"),     # plain map (3 * 5 blocks)
-    (4, 2, 1024, "diag"),      # local window only
+    (1, 1, 256, "random"),     # smallest length (N = 2: heads of a block on adjacent ids)
+    (3, 1, 640, "random"),     # N = 5, not a multiple of 8
+    (4, 2, 1024, "diag"),      # local window only (N = 8: blocks dealt across XCDs)
     (7, 1, 384, "full"),       # 7:1 GQA, full lists = dense
     (8, 8, 1024, "random"),    # one KV head per query head
 ])
