@@ -65,9 +65,12 @@ __device__ __forceinline__ int acc_key(int v, int lg) { return (v < 8) ? (8 * lg
 
 template <bool kDense>
 __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
-  // 48 KiB of K stages + 32 KiB of V stages: two workgroups fill a CU's 160 KiB.
-  __shared__ __attribute__((aligned(1024))) __bf16 ks[kKStages][kStep * kHeadDim];
-  __shared__ __attribute__((aligned(1024))) __bf16 vs[2][kStep * kHeadDim];
+  // 32 KiB of V stages (tiles 0-1) then 48 KiB of K stages (tiles 2-4): two
+  // workgroups fill a CU's 160 KiB.  With V first, every stage offset of a
+  // statically known stage fits the 16-bit immediate of an LDS read.
+  __shared__ __attribute__((aligned(1024))) __bf16 lds[2 + kKStages][kStep * kHeadDim];
+  auto kstage = [&](int i) -> __bf16* { return lds[2 + i]; };
+  auto vstage = [&](int i) -> __bf16* { return lds[i]; };
 
   int h, qb;
   map_row(p.map, blockIdx.x, &h, &qb);
@@ -190,11 +193,13 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   // Row of the K operand fed by this lane: a permutation of 0..31 (see top).
   const int ia = l32 >> 3, ig = (l32 >> 2) & 1, ib = l32 & 3;
   const int krow = 16 * (ia >> 1) + 8 * ig + 4 * (ia & 1) + ib;
-  // Byte offsets of this lane's K operand: row 32 kb2 + krow, logical chunk
-  // 2 kk + lg; kb2 leaves swz_k unchanged (+8 KiB).
+  // Byte offsets, from the start of the K stages, of this lane's K operand:
+  // row 32 kb2 + krow, logical chunk 2 kk + lg; kb2 leaves swz_k unchanged
+  // (+8 KiB).
+  constexpr int kKBase = 2 * kStep * kHeadDim * 2;  // bytes of the two V stages
   int k_off[8];
 #pragma unroll
-  for (int kk = 0; kk < 8; ++kk) k_off[kk] = krow * 256 + (((2 * kk + lg) ^ swz_k(krow)) << 4);
+  for (int kk = 0; kk < 8; ++kk) k_off[kk] = kKBase + krow * 256 + (((2 * kk + lg) ^ swz_k(krow)) << 4);
   // V^T operand through the transposing LDS read: within each 16-lane group
   // (gq = lane / 16, li = lane % 16) lane li receives element li % 4 of the
   // 4-element vectors addressed by lanes 4e + li / 4 (e = 0..3).  A lane
@@ -216,8 +221,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
     return v_base[db] + (32 * kb2 + 16 * mm + 4 * hh) * 256;
   };
 
-  auto qk = [&](const __bf16* kbuf, f32x16 (&s)[2]) {
-    const char* kb8 = (const char*)kbuf;
+  // Scores of the step whose K tile is in stage kst.
+  auto qk = [&](int kst, f32x16 (&s)[2]) {
+    const char* kb8 = (const char*)lds + kst * (kStep * kHeadDim * 2);
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; ++kb2) {
 #pragma unroll
@@ -228,7 +234,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
         s[kb2] = mfma32(kf, qf[kk], s[kb2]);
       }
     }
-  };  // One key half (keys key0 + 32 kb2 .. +31) of a step's scores, with the
+  };
+
+  // One key half (keys key0 + 32 kb2 .. +31) of a step's scores, with the
   // K operand read from global memory in the layout the LDS path gives.
   auto qk_half_global = [&](int key0, int kb2) -> f32x16 {
     const __bf16* krow_g = kg + (size_t)(key0 + 32 * kb2 + krow) * kHeadDim + 8 * lg;
@@ -238,8 +246,10 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
     return s;
   };
 
-  // Iteration j of the software pipeline.  K_t lives in ks[t % 3] and V_t
-  // in vs[t & 1]; S_j arrives in `sc` already masked.  Iteration j
+  // Iteration j of the software pipeline.  K_t lives in K stage t % 3 and
+  // V_t in V stage t & 1 (`kst_in` = (j + 1) % 3 and `vpar_in` = j & 1,
+  // compile-time constants in the main loop so that LDS read offsets become
+  // instruction immediates); S_j arrives in `sc` already masked.  Iteration j
   //   - block 1: S_{j+1} = K_{j+1} Q^T (MFMA) beside exp / row sum / bf16
   //     packing of the second key half of S_j (VALU) against the current
   //     running max, and the DMA of V_{j+1} over V_{j-1} (read in iteration
@@ -303,14 +313,15 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
         if (key0 + 32 * kb2 + acc_key(v, lg) > qpos) s[kb2][v] = -INFINITY;
   };
 
-  auto iter = [&](int j, int kb_c, int kb_v, int kb_k, int kb_n, int kst, f32x16 (&sc)[2], f32x16 (&sn)[2],
-                  auto cur_masked_tag, auto k_ahead_tag, auto next_masked_tag, auto next_tag) {
+  auto iter = [&](int j, int kb_c, int kb_v, int kb_k, int kb_n, auto kst_in, auto vpar_in, f32x16 (&sc)[2],
+                  f32x16 (&sn)[2], auto cur_masked_tag, auto k_ahead_tag, auto next_masked_tag, auto next_tag) {
+    const int kst = kst_in, vpar = vpar_in;
     constexpr bool kCurMasked = decltype(cur_masked_tag)::value;
     constexpr bool kKAhead = decltype(k_ahead_tag)::value;
     constexpr bool kNextMasked = decltype(next_masked_tag)::value;
     constexpr bool kNext = decltype(next_tag)::value;
-    __bf16* vdst = vs[(j + 1) & 1];
-    __bf16* kdst = ks[kst == 0 ? 2 : kst - 1];
+    __bf16* vdst = vstage(vpar ^ 1);
+    __bf16* kdst = kstage(kst == 0 ? 2 : kst - 1);
 
     // The two blocks are written out in issue order, one unit per MFMA, with
     // operand reads three MFMAs ahead through 4-entry register rings;
@@ -320,7 +331,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
     // iteration j, scores 16..31 in block 1 of iteration j+1.
     // Block 1: MFMA t of S_{j+1} (key half t & 1, d slice t / 2) beside the
     // exp, row sum and bf16 packing of score 16 + t of S_j.
-    const char* kb8 = (const char*)ks[kst];
+    const char* kb8 = (const char*)lds + kst * (kStep * kHeadDim * 2);
     auto kread = [&](int t) -> bf16x8 {
       return as_bf16x8(*(const u32x4*)(kb8 + k_off[t >> 1] + (t & 1) * 8192));
     };
@@ -390,7 +401,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
     // Block 2: MFMA u of O += V_j P_j (d slice u & 3, P operand u / 4) beside
     // masking of scores 2u, 2u+1 of S_{j+1} and the exp, row sum and packing
     // of its score u.
-    __attribute__((address_space(3))) char* vb8 = (__attribute__((address_space(3))) char*)vs[j & 1];
+    __attribute__((address_space(3))) char* vb8 = (__attribute__((address_space(3))) char*)vstage(vpar);
     auto vread = [&](int u) -> bf16x8 {
       const int db = u & 3, f = u >> 2;
       const bf16x4 lo = __builtin_bit_cast(
@@ -436,13 +447,13 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
 
   f32x16 sa[2], sb[2];
   int kb_cur = block_at(0), kb_nxt = block_at(1), kb_nn = block_at(2);
-  dma_k_tile(ks[0], kb_cur, 0);
-  dma_v_tile(vs[0], kb_cur, 0);
-  dma_k_tile(ks[1], kb_cur, 1);
-  if (nsteps > 2) dma_k_tile(ks[2], kb_nxt, 2);
+  dma_k_tile(kstage(0), kb_cur, 0);
+  dma_v_tile(vstage(0), kb_cur, 0);
+  dma_k_tile(kstage(1), kb_cur, 1);
+  if (nsteps > 2) dma_k_tile(kstage(2), kb_nxt, 2);
   wait_dma();
   __syncthreads();
-  qk(ks[0], sa);
+  qk(0, sa);
   if (nsteps == 2) mask_scores(sa, key0_of(kb_cur, 0));
   raise_to(row_max(sa));
 #pragma unroll
@@ -458,33 +469,51 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   __syncthreads();  // every wave has read K_0 before iteration 0 overwrites it
 
   // Steps 0 .. nsteps-3 cover the fully visible blocks, the last two the
-  // diagonal block.  The pair loop runs the iterations whose next step is
-  // fully visible two at a time (alternating the score buffers); the tail
-  // runs the last four (two when the list holds only the diagonal block).
+  // diagonal block.  The main loop runs the iterations whose next step is
+  // fully visible six at a time (3 K stages x 2 V stages / score buffers,
+  // so every stage is known at compile time), a pair loop runs the 0-2
+  // remaining pairs, and the tail runs the last four iterations (two when
+  // the list holds only the diagonal block).
   using F = std::false_type;
   using T = std::true_type;
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
   int j = 0, kst = 1;
   if (nsteps >= 4) {
+    for (; j + 6 <= nsteps - 4; j += 6) {
+      // blocks of steps j .. j+8: kb_cur (j, j+1), kb_nxt (j+2, j+3), kb_nn (j+4, j+5), then two more
+      const int kb3 = block_at((j >> 1) + 3), kb4 = block_at((j >> 1) + 4);
+      iter(j, kb_cur, kb_cur, kb_nxt, kb_cur, S1{}, S0{}, sa, sb, F{}, T{}, F{}, T{});
+      iter(j + 1, kb_cur, kb_nxt, kb_nn, kb_nxt, S2{}, S1{}, sb, sa, F{}, T{}, F{}, T{});
+      iter(j + 2, kb_nxt, kb_nxt, kb_nn, kb_nxt, S0{}, S0{}, sa, sb, F{}, T{}, F{}, T{});
+      iter(j + 3, kb_nxt, kb_nn, kb3, kb_nn, S1{}, S1{}, sb, sa, F{}, T{}, F{}, T{});
+      iter(j + 4, kb_nn, kb_nn, kb3, kb_nn, S2{}, S0{}, sa, sb, F{}, T{}, F{}, T{});
+      iter(j + 5, kb_nn, kb3, kb4, kb3, S0{}, S1{}, sb, sa, F{}, T{}, F{}, T{});
+      kb_cur = kb3;
+      kb_nxt = kb4;
+      kb_nn = block_at((j >> 1) + 5);
+    }
     for (; j < nsteps - 4; j += 2) {
-      iter(j, kb_cur, kb_cur, kb_nxt, kb_cur, kst, sa, sb, F{}, T{}, F{}, T{});
+      iter(j, kb_cur, kb_cur, kb_nxt, kb_cur, kst, 0, sa, sb, F{}, T{}, F{}, T{});
       kst = kst == 2 ? 0 : kst + 1;
-      iter(j + 1, kb_cur, kb_nxt, kb_nn, kb_nxt, kst, sb, sa, F{}, T{}, F{}, T{});
+      iter(j + 1, kb_cur, kb_nxt, kb_nn, kb_nxt, kst, 1, sb, sa, F{}, T{}, F{}, T{});
       kst = kst == 2 ? 0 : kst + 1;
       kb_cur = kb_nxt;
       kb_nxt = kb_nn;
       kb_nn = block_at((j >> 1) + 3);
     }
     // j = nsteps - 4: kb_cur is the last fully visible block, kb_nxt the diagonal one
-    iter(j, kb_cur, kb_cur, kb_nxt, kb_cur, kst, sa, sb, F{}, T{}, F{}, T{});
+    iter(j, kb_cur, kb_cur, kb_nxt, kb_cur, kst, 0, sa, sb, F{}, T{}, F{}, T{});
     kst = kst == 2 ? 0 : kst + 1;
-    iter(j + 1, kb_cur, kb_nxt, kb_nxt, kb_nxt, kst, sb, sa, F{}, F{}, T{}, T{});
+    iter(j + 1, kb_cur, kb_nxt, kb_nxt, kb_nxt, kst, 1, sb, sa, F{}, F{}, T{}, T{});
     kst = kst == 2 ? 0 : kst + 1;
     j += 2;
     kb_cur = kb_nxt;
   }
-  iter(j, kb_cur, kb_cur, kb_cur, kb_cur, kst, sa, sb, T{}, F{}, T{}, T{});
+  iter(j, kb_cur, kb_cur, kb_cur, kb_cur, kst, 0, sa, sb, T{}, F{}, T{}, T{});
   kst = kst == 2 ? 0 : kst + 1;
-  iter(j + 1, kb_cur, kb_cur, kb_cur, kb_cur, kst, sb, sa, T{}, F{}, F{}, F{});
+  iter(j + 1, kb_cur, kb_cur, kb_cur, kb_cur, kst, 1, sb, sa, T{}, F{}, F{}, F{});
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / l_tot;
