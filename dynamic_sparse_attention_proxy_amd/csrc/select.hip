@@ -18,7 +18,8 @@
 // Pooled-Estimation heads ("Key Contributions" item 2; gamma = 0.95 on PE):
 //   pe_pool    - mean of each 128-row block of q (PE heads) and k.
 //   pe_select  - per (head, query block): pooled logits against kb <= qb,
-//                softmax, LDS sort, shortest prefix reaching gamma, plus qb.
+//                softmax, radix select of the shortest prefix reaching
+//                gamma, plus qb.
 
 #include "common.h"
 #include "internal.h"
@@ -28,8 +29,6 @@ namespace crisp {
 namespace {
 
 constexpr int kAlign = 256;
-
-__device__ __forceinline__ int pow2_ceil(int x) { return x <= 1 ? 1 : 1 << (32 - __clz(x - 1)); }
 
 __global__ __launch_bounds__(256) void tile_sums_kernel(const float* amap, float* lo_out, float* up_out, int n,
                                                         int nblk) {
@@ -243,20 +242,71 @@ struct PeArgs {
 };
 
 constexpr int kPeThreads = 256;
+constexpr float kFixOne = 2147483648.0f;  // 2^31: probabilities as 32-bit fixed point (a row sums to <= 2^31)
 
+// Wave 0 of a workgroup: the smallest digit d with
+// below + sum(hist[0..d]) >= target, and the mass below it; d = 256 if none.
+__device__ inline void find_digit(const uint32_t* hist, uint32_t below, uint32_t target, int lane, int* d_out,
+                                  uint32_t* below_out) {
+  uint32_t s[4], tot = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    s[b] = hist[4 * lane + b];
+    tot += s[b];
+  }
+  uint32_t incl = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  uint32_t run = below + incl - tot;
+  int cand = 256;
+  uint32_t cand_below = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    if (cand == 256 && run + s[b] >= target) {
+      cand = 4 * lane + b;
+      cand_below = run;
+    }
+    run += s[b];
+  }
+  int best = cand;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) best = min(best, __shfl_xor(best, o));
+  if (cand == best && cand < 256) {
+    *d_out = cand;
+    *below_out = cand_below;
+  }
+  if (lane == 0 && best == 256) *d_out = 256;
+}
+
+// One workgroup per (head, query block) of a Pooled-Estimation head.
+// The kept set is the shortest prefix, in (descending probability, ascending
+// block) order, whose mass reaches gamma.  That order is the ascending order
+// of desc_key(p, kb), so the cut is the smallest key K whose cumulative mass
+// over keys <= K reaches gamma.  K is found digit by digit from the top
+// (radix select): per 8-bit digit a 256-bin histogram of the mass of the
+// keys that match the digits fixed so far, then the digit where the running
+// mass crosses gamma.  Keys hold the probability's bits above the block index
+// (< 4096, so key bits 16..31 are zero): 6 passes cover them.  Masses are
+// 2^-31 fixed point (truncated; at most 4096 x 2^-31 below the real sum), so
+// sums are exact integers and the result deterministic.
 __global__ __launch_bounds__(kPeThreads) void pe_select_kernel(PeArgs p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ float redf[8];
   __shared__ int redi[8];
+  __shared__ uint32_t hist[256];
+  __shared__ int sel_digit;
+  __shared__ uint32_t sel_below;
   const int N = p.nblk;
   const int id = blockIdx.x;
   const int h = id % p.hq, qb = N - 1 - id / p.hq;
   if (p.route[h] != 0) return;
-  const int L = qb + 1, P = pow2_ceil(L);
-  uint64_t* keys = (uint64_t*)smem;
-  float* pr = (float*)(keys + pow2_ceil(N));
+  const int L = qb + 1;
+  float* pr = (float*)smem;
   uint8_t* flags = (uint8_t*)(pr + N);
-  const int tid = threadIdx.x, l16 = tid & 15, grp = tid >> 4;
+  const int tid = threadIdx.x, l16 = tid & 15, grp = tid >> 4, lane = tid & 63;
   const int g = h / p.qpg;
 
   // pooled logits (base 2): 16 lanes per key block, 8 dims each
@@ -289,40 +339,46 @@ __global__ __launch_bounds__(kPeThreads) void pe_select_kernel(PeArgs p) {
     loc += e;
   }
   const float sum = block_sum_f(loc, redf, tid, kPeThreads);
-  for (int i = tid; i < P; i += kPeThreads) {
-    if (i < L) {
-      const float pv = pr[i] / sum;
-      keys[i] = desc_key(pv, i);
-      flags[i] = 0;
-    } else {
-      keys[i] = ~0ull;
-    }
-  }
+  for (int i = tid; i < L; i += kPeThreads) pr[i] = pr[i] / sum;
   __syncthreads();
-  bitonic_sort_lds(keys, P, tid, kPeThreads);
 
-  const int per = (L + kPeThreads - 1) / kPeThreads;
-  const int beg = min(L, tid * per), end = min(L, beg + per);
-  float local = 0.f;
-  for (int i = beg; i < end; ++i) local += key_value(keys[i]);
-  float run = block_exclusive_scan_f(local, redf, tid, kPeThreads);
-  int cut = 0x7fffffff;
-  for (int i = beg; i < end; ++i) {
-    run += key_value(keys[i]);
-    if (run >= p.gamma) {
-      cut = i;
+  const uint32_t target = (uint32_t)(p.gamma * kFixOne);
+  constexpr int kShift[6] = {56, 48, 40, 32, 8, 0};
+  uint64_t decided = 0;
+  uint32_t below = 0;
+  bool keep_all = false;
+#pragma unroll 1
+  for (int pass = 0; pass < 6; ++pass) {
+    const int sh = kShift[pass];
+    const uint64_t hi_mask = pass == 0 ? 0ull : ~((uint64_t(1) << (sh + 8)) - 1);
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    for (int i = tid; i < L; i += kPeThreads) {
+      const uint64_t key = desc_key(pr[i], (uint32_t)i);
+      if ((key & hi_mask) == decided)
+        atomicAdd(&hist[(key >> sh) & 255], (uint32_t)(pr[i] * kFixOne));
+    }
+    __syncthreads();
+    if (tid < 64) find_digit(hist, below, target, lane, &sel_digit, &sel_below);
+    __syncthreads();
+    const int d = sel_digit;
+    if (d == 256) {  // the whole row never reaches gamma (rounding): keep everything
+      keep_all = true;
       break;
     }
+    below = sel_below;
+    decided |= (uint64_t)d << sh;
   }
-  cut = block_min_i(cut, redi, tid, kPeThreads);
-  if (cut == 0x7fffffff) cut = L - 1;
-  for (int i = tid; i <= cut; i += kPeThreads) flags[key_index(keys[i])] = 1;
-  if (tid == 0) flags[qb] = 1;
-  __syncthreads();
 
-  // ascending compaction
+  // ascending compaction of the kept blocks plus the diagonal one
+  const int per = (L + kPeThreads - 1) / kPeThreads;
+  const int beg = min(L, tid * per), end = min(L, beg + per);
   int c = 0;
-  for (int kb = beg; kb < end; ++kb) c += flags[kb];
+  for (int kb = beg; kb < end; ++kb) {
+    const bool f = keep_all || kb == qb || desc_key(pr[kb], (uint32_t)kb) <= decided;
+    flags[kb] = f;
+    c += f;
+  }
   int total;
   int pos = block_exclusive_scan(c, redi, tid, kPeThreads, &total);
   int32_t* out = p.idx + (size_t)h * ((size_t)N * (N + 1) / 2) + (size_t)qb * (qb + 1) / 2;
@@ -458,7 +514,7 @@ hipError_t launch_select(const __bf16* q, const __bf16* k, const float* amap, co
   pa.nblk = N;
   pa.scale_log2 = scale * kLog2e;
   pa.gamma = use_gamma ? gamma : gamma_pe;
-  const size_t pe_lds = (size_t)host_pow2_ceil(N) * 8 + (size_t)N * 4 + (size_t)N;
+  const size_t pe_lds = (size_t)N * 4 + (size_t)N;
   hipLaunchKernelGGL(pe_select_kernel, dim3(hq * N), dim3(kPeThreads), pe_lds, stream, pa);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
