@@ -2,6 +2,8 @@
 
 One step = one layer's whole path (proxy -> route -> select -> block-sparse
 attention) on one batch of seeded synthetic inputs already resident in HBM.
+The proxy emits per-block masses instead of the full proxy map; routing and
+selection read those.
 The headline workload is the Llama-3.1-8B-shaped 512k-token layer (32 query
 heads, 8 KV heads, head dim 128); the Qwen2.5-7B-shaped 128k layer is
 reported beside it.  The dense causal kernel, the forced Vertical-Slash
@@ -91,13 +93,18 @@ def run_workload(torch, B, synth, wname, args, cfg_kw, compare):
     cfg = B.make_cfg(**dict(cfg_kw, route_override=override))
     res = {"workload": w.name}
 
+    # The proxy emits the block masses only (no 4 * 128 * n * Hq-byte map);
+    # routing and selection read them.
+    mass = bufs.block_mass
+
     def chain(c, gamma, attn_timer=None):
-        B.crisp_proxy(dims, x.q, x.k, bufs.attn_map, bufs.row_lse, bufs.partials)
-        B.crisp_route(dims, c, bufs.attn_map, bufs.c_struct, bufs.route)
+        B.crisp_proxy(dims, x.q, x.k, None, bufs.row_lse, bufs.partials, block_mass=mass)
+        B.crisp_route(dims, c, None, bufs.c_struct, bufs.route, block_mass=mass)
         if gamma is None:
-            B.crisp_select(dims, c, x.q, x.k, bufs.attn_map, bufs.route, bufs.blocks, bufs.workspace)
+            B.crisp_select(dims, c, x.q, x.k, None, bufs.route, bufs.blocks, bufs.workspace, block_mass=mass)
         else:
-            B.crisp_select_gamma(dims, c, gamma, x.q, x.k, bufs.attn_map, bufs.route, bufs.blocks, bufs.workspace)
+            B.crisp_select_gamma(dims, c, gamma, x.q, x.k, None, bufs.route, bufs.blocks, bufs.workspace,
+                                 block_mass=mass)
         if attn_timer is None:
             B.crisp_sparse_attn(dims, x.q, x.k, x.v, bufs.blocks["count"], bufs.blocks["idx"], bufs.out, bufs.lse)
         else:
@@ -280,7 +287,7 @@ def main():
         "data": "synthetic (seeded Gaussians with planted sink and needles, RoPE; shapes of the named model)",
         "config": {"workload": main_res["workload"], "num_q_heads": dims.num_q_heads,
                    "num_kv_heads": dims.num_kv_heads, "seq_len": dims.seq_len, "head_dim": 128, "block": 128,
-                   "route": args.route, **cfg_kw},
+                   "route": args.route, "proxy_output": "block_mass", **cfg_kw},
         "speedup_vs_dense": round(speed / value, 4) if speed else None,
         "dense_ms": round(speed, 3) if speed else None,
         "roofline": roofline,

@@ -58,13 +58,13 @@ _lib = None
 
 _P = ctypes.c_void_p
 _SIGS = {
-    "crisp_proxy": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "crisp_proxy": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "crisp_proxy_scratch_bytes": (ctypes.c_size_t, [ctypes.POINTER(crisp_dims)]),
-    "crisp_route": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), _P, _P, _P, _P]),
-    "crisp_select": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), _P, _P, _P, _P,
+    "crisp_route": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), _P, _P, _P, _P, _P]),
+    "crisp_select": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), _P, _P, _P, _P, _P,
                                     ctypes.POINTER(crisp_blocks), _P, ctypes.c_size_t, _P]),
     "crisp_select_gamma": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), ctypes.c_float, _P,
-                                          _P, _P, _P, ctypes.POINTER(crisp_blocks), _P, ctypes.c_size_t, _P]),
+                                          _P, _P, _P, _P, ctypes.POINTER(crisp_blocks), _P, ctypes.c_size_t, _P]),
     "crisp_select_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(crisp_dims)]),
     "crisp_list_capacity": (ctypes.c_size_t, [ctypes.POINTER(crisp_dims)]),
     "crisp_sparse_attn": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P,
@@ -139,15 +139,15 @@ def crisp_abi_version() -> int:
     return int(lib().crisp_abi_version())
 
 
-def crisp_proxy(dims: crisp_dims, q, k, attn_map, row_lse=None, partials=None, stream=None):
+def crisp_proxy(dims: crisp_dims, q, k, attn_map, row_lse=None, partials=None, stream=None, block_mass=None):
     nbytes = partials.numel() * partials.element_size() if partials is not None else 0
-    _check("crisp_proxy", lib().crisp_proxy(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(attn_map), _ptr(row_lse),
-                                            _ptr(partials), nbytes, _stream(stream)))
+    _check("crisp_proxy", lib().crisp_proxy(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(attn_map), _ptr(block_mass),
+                                            _ptr(row_lse), _ptr(partials), nbytes, _stream(stream)))
 
 
-def crisp_route(dims: crisp_dims, cfg: crisp_cfg, attn_map, c_struct, route, stream=None):
-    _check("crisp_route", lib().crisp_route(ctypes.byref(dims), ctypes.byref(cfg), _ptr(attn_map), _ptr(c_struct),
-                                            _ptr(route), _stream(stream)))
+def crisp_route(dims: crisp_dims, cfg: crisp_cfg, attn_map, c_struct, route, stream=None, block_mass=None):
+    _check("crisp_route", lib().crisp_route(ctypes.byref(dims), ctypes.byref(cfg), _ptr(attn_map), _ptr(block_mass),
+                                            _ptr(c_struct), _ptr(route), _stream(stream)))
 
 
 def _blocks(out: dict) -> crisp_blocks:
@@ -158,19 +158,21 @@ def _blocks(out: dict) -> crisp_blocks:
     return b
 
 
-def crisp_select(dims: crisp_dims, cfg: crisp_cfg, q, k, attn_map, route, out: dict, workspace, stream=None):
+def crisp_select(dims: crisp_dims, cfg: crisp_cfg, q, k, attn_map, route, out: dict, workspace, stream=None,
+                 block_mass=None):
     b = _blocks(out)
     _check("crisp_select", lib().crisp_select(ctypes.byref(dims), ctypes.byref(cfg), _ptr(q), _ptr(k),
-                                              _ptr(attn_map), _ptr(route), ctypes.byref(b), _ptr(workspace),
-                                              workspace.numel() * workspace.element_size(), _stream(stream)))
+                                              _ptr(attn_map), _ptr(block_mass), _ptr(route), ctypes.byref(b),
+                                              _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                              _stream(stream)))
 
 
 def crisp_select_gamma(dims: crisp_dims, cfg: crisp_cfg, gamma: float, q, k, attn_map, route, out: dict,
-                       workspace, stream=None):
+                       workspace, stream=None, block_mass=None):
     b = _blocks(out)
     _check("crisp_select_gamma", lib().crisp_select_gamma(ctypes.byref(dims), ctypes.byref(cfg), gamma, _ptr(q),
-                                                          _ptr(k), _ptr(attn_map), _ptr(route), ctypes.byref(b),
-                                                          _ptr(workspace),
+                                                          _ptr(k), _ptr(attn_map), _ptr(block_mass), _ptr(route),
+                                                          ctypes.byref(b), _ptr(workspace),
                                                           workspace.numel() * workspace.element_size(),
                                                           _stream(stream)))
 
@@ -193,15 +195,20 @@ def crisp_dense_attn(dims: crisp_dims, q, k, v, out, lse=None, stream=None):
 
 
 class CrispBuffers:
-    """Device buffers of one layer's CRISP chain, allocated once and reused."""
+    """Device buffers of one layer's CRISP chain, allocated once and reused.
 
-    def __init__(self, dims: crisp_dims, device=None, out_dtype=torch.bfloat16, diagnostics: bool = True):
+    The proxy map itself (4 * 128 * n * Hq bytes) is only allocated with
+    `with_map=True`; the chain otherwise runs on the block masses."""
+
+    def __init__(self, dims: crisp_dims, device=None, out_dtype=torch.bfloat16, diagnostics: bool = True,
+                 with_map: bool = False):
         dev = torch.device("cuda") if device is None else torch.device(device)
         hq, n = dims.num_q_heads, dims.seq_len
         N = n // dims.block
         f32, i32 = torch.float32, torch.int32
         self.dims = dims
-        self.attn_map = torch.empty((hq, dims.block, n), dtype=f32, device=dev)
+        self.attn_map = torch.empty((hq, dims.block, n), dtype=f32, device=dev) if with_map else None
+        self.block_mass = torch.empty((2, hq, N), dtype=f32, device=dev)
         self.row_lse = torch.empty((hq, dims.block), dtype=f32, device=dev)
         self.partials = torch.empty(crisp_proxy_scratch_bytes(dims), dtype=torch.uint8, device=dev)
         self.c_struct = torch.empty((hq,), dtype=f32, device=dev)
@@ -225,14 +232,23 @@ class CrispBuffers:
 
 
 def crisp_prefill(dims: crisp_dims, cfg: crisp_cfg, q, k, v, bufs: CrispBuffers, gamma: Optional[float] = None,
-                  stream=None):
+                  stream=None, use_map: bool = False):
     """One layer's path: proxy -> route -> select (or the gamma comparison
-    chain when `gamma` is given) -> block-sparse attention, all on `stream`."""
-    crisp_proxy(dims, q, k, bufs.attn_map, bufs.row_lse, bufs.partials, stream)
-    crisp_route(dims, cfg, bufs.attn_map, bufs.c_struct, bufs.route, stream)
+    chain when `gamma` is given) -> block-sparse attention, all on `stream`.
+
+    Routing and selection read the block masses, unless `use_map` asks for
+    the materialised map (bufs must then hold one); with a map in bufs the
+    proxy fills both."""
+    if use_map and bufs.attn_map is None:
+        raise ValueError("use_map needs CrispBuffers(with_map=True)")
+    mass = None if use_map else bufs.block_mass
+    amap = bufs.attn_map if use_map else None
+    crisp_proxy(dims, q, k, bufs.attn_map, bufs.row_lse, bufs.partials, stream, block_mass=bufs.block_mass)
+    crisp_route(dims, cfg, amap, bufs.c_struct, bufs.route, stream, block_mass=mass)
     if gamma is None:
-        crisp_select(dims, cfg, q, k, bufs.attn_map, bufs.route, bufs.blocks, bufs.workspace, stream)
+        crisp_select(dims, cfg, q, k, amap, bufs.route, bufs.blocks, bufs.workspace, stream, block_mass=mass)
     else:
-        crisp_select_gamma(dims, cfg, gamma, q, k, bufs.attn_map, bufs.route, bufs.blocks, bufs.workspace, stream)
+        crisp_select_gamma(dims, cfg, gamma, q, k, amap, bufs.route, bufs.blocks, bufs.workspace, stream,
+                           block_mass=mass)
     crisp_sparse_attn(dims, q, k, v, bufs.blocks["count"], bufs.blocks["idx"], bufs.out, bufs.lse, stream)
     return bufs.out

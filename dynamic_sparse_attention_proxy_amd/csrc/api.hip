@@ -75,16 +75,23 @@ crisp_status check_device() {
 
 crisp_status launched(hipError_t e) { return e == hipSuccess ? CRISP_OK : CRISP_ERR_LAUNCH; }
 
+// The proxy's output: the map, the block masses, or both; at least one.
+crisp_status check_map_or_mass(const void* attn_map, const void* block_mass) {
+  if (attn_map == nullptr && block_mass == nullptr) return CRISP_ERR_NULL;
+  CRISP_TRY(check_opt(attn_map));
+  return check_opt(block_mass);
+}
+
 crisp_status select_common(const crisp_dims* dims, const crisp_cfg* cfg, bool use_gamma, float gamma, const void* q,
-                           const void* k, const float* attn_map, const int32_t* route, const crisp_blocks* out,
-                           void* workspace, size_t workspace_bytes, void* stream) {
+                           const void* k, const float* attn_map, const float* block_mass, const int32_t* route,
+                           const crisp_blocks* out, void* workspace, size_t workspace_bytes, void* stream) {
   CRISP_TRY(check_dims(dims));
   CRISP_TRY(check_cfg(dims, cfg));
   if (use_gamma && !(gamma > 0.f && gamma <= 1.f)) return CRISP_ERR_PARAM;
   if (out == nullptr) return CRISP_ERR_NULL;
   CRISP_TRY(check_ptr(q));
   CRISP_TRY(check_ptr(k));
-  CRISP_TRY(check_ptr(attn_map));
+  CRISP_TRY(check_map_or_mass(attn_map, block_mass));
   CRISP_TRY(check_ptr(route));
   CRISP_TRY(check_ptr(out->count));
   CRISP_TRY(check_ptr(out->idx));
@@ -109,7 +116,8 @@ crisp_status select_common(const crisp_dims* dims, const crisp_cfg* cfg, bool us
   if (out->s_mask) b.smask = out->s_mask;
   if (out->n_v) b.n_v = out->n_v;
   if (out->n_s) b.n_s = out->n_s;
-  return launched(crisp::launch_select((const __bf16*)q, (const __bf16*)k, attn_map, route, b, out->count, out->idx,
+  return launched(crisp::launch_select((const __bf16*)q, (const __bf16*)k, attn_map, block_mass, route, b, out->count,
+                                       out->idx,
                                        hq, hkv, n, dims->scale, cfg->alpha, cfg->gamma_pe, cfg->kmin_blocks,
                                        cfg->nf_stat, use_gamma, gamma, (hipStream_t)stream));
 }
@@ -142,43 +150,49 @@ size_t crisp_proxy_scratch_bytes(const crisp_dims* dims) {
   return crisp::proxy_scratch_bytes(dims->num_q_heads, dims->seq_len);
 }
 
-crisp_status crisp_proxy(const crisp_dims* dims, const void* q, const void* k, float* attn_map, float* row_lse,
-                         void* partials, size_t partials_bytes, void* stream) {
+crisp_status crisp_proxy(const crisp_dims* dims, const void* q, const void* k, float* attn_map, float* block_mass,
+                         float* row_lse, void* partials, size_t partials_bytes, void* stream) {
   CRISP_TRY(check_dims(dims));
   CRISP_TRY(check_ptr(q));
   CRISP_TRY(check_ptr(k));
-  CRISP_TRY(check_ptr(attn_map));
+  CRISP_TRY(check_map_or_mass(attn_map, block_mass));
   CRISP_TRY(check_opt(row_lse));
   CRISP_TRY(check_ptr(partials));
   if (partials_bytes < crisp::proxy_scratch_bytes(dims->num_q_heads, dims->seq_len)) return CRISP_ERR_WORKSPACE;
   CRISP_TRY(check_device());
-  return launched(crisp::launch_proxy((const __bf16*)q, (const __bf16*)k, attn_map, row_lse, partials,
+  return launched(crisp::launch_proxy((const __bf16*)q, (const __bf16*)k, attn_map, block_mass, row_lse, partials,
                                       dims->num_q_heads, dims->num_kv_heads, dims->seq_len, dims->scale,
                                       (hipStream_t)stream));
 }
 
-crisp_status crisp_route(const crisp_dims* dims, const crisp_cfg* cfg, const float* attn_map, float* c_struct,
-                         int32_t* route, void* stream) {
+crisp_status crisp_route(const crisp_dims* dims, const crisp_cfg* cfg, const float* attn_map, const float* block_mass,
+                         float* c_struct, int32_t* route, void* stream) {
   CRISP_TRY(check_dims(dims));
   CRISP_TRY(check_cfg(dims, cfg));
-  CRISP_TRY(check_ptr(attn_map));
+  CRISP_TRY(check_map_or_mass(attn_map, block_mass));
+  // block masses resolve whole key blocks only
+  if (block_mass != nullptr && (cfg->sink_width != dims->block || cfg->recency_width != dims->block))
+    return CRISP_ERR_PARAM;
   CRISP_TRY(check_ptr(c_struct));
   CRISP_TRY(check_ptr(route));
   CRISP_TRY(check_device());
-  return launched(crisp::launch_route(attn_map, c_struct, route, dims->num_q_heads, dims->seq_len, cfg->sink_width,
-                                      cfg->recency_width, cfg->tau, cfg->route_override, (hipStream_t)stream));
+  return launched(crisp::launch_route(attn_map, block_mass, c_struct, route, dims->num_q_heads, dims->seq_len,
+                                      cfg->sink_width, cfg->recency_width, cfg->tau, cfg->route_override,
+                                      (hipStream_t)stream));
 }
 
 crisp_status crisp_select(const crisp_dims* dims, const crisp_cfg* cfg, const void* q, const void* k,
-                          const float* attn_map, const int32_t* route, const crisp_blocks* out, void* workspace,
-                          size_t workspace_bytes, void* stream) {
-  return select_common(dims, cfg, false, 0.f, q, k, attn_map, route, out, workspace, workspace_bytes, stream);
+                          const float* attn_map, const float* block_mass, const int32_t* route,
+                          const crisp_blocks* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return select_common(dims, cfg, false, 0.f, q, k, attn_map, block_mass, route, out, workspace, workspace_bytes,
+                       stream);
 }
 
 crisp_status crisp_select_gamma(const crisp_dims* dims, const crisp_cfg* cfg, float gamma, const void* q,
-                                const void* k, const float* attn_map, const int32_t* route, const crisp_blocks* out,
-                                void* workspace, size_t workspace_bytes, void* stream) {
-  return select_common(dims, cfg, true, gamma, q, k, attn_map, route, out, workspace, workspace_bytes, stream);
+                                const void* k, const float* attn_map, const float* block_mass, const int32_t* route,
+                                const crisp_blocks* out, void* workspace, size_t workspace_bytes, void* stream) {
+  return select_common(dims, cfg, true, gamma, q, k, attn_map, block_mass, route, out, workspace, workspace_bytes,
+                       stream);
 }
 
 size_t crisp_select_workspace_bytes(const crisp_dims* dims) {
@@ -217,6 +231,6 @@ const char* crisp_status_string(crisp_status status) {
   return "unknown status";
 }
 
-int32_t crisp_abi_version(void) { return (1 << 16) | 0; }
+int32_t crisp_abi_version(void) { return (2 << 16) | 0; }
 
 }  // extern "C"

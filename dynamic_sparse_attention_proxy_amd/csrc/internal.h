@@ -16,11 +16,15 @@ inline size_t proxy_scratch_bytes(int hq, int n) {
   return (size_t)hq * proxy_chunks(n) * 128 * 2 * sizeof(float) + (size_t)hq * 128 * sizeof(float);
 }
 
-hipError_t launch_proxy(const __bf16* q, const __bf16* k, float* amap, float* row_lse, void* scratch, int hq,
-                        int hkv, int n, float scale, hipStream_t stream);
+// amap and/or mass (at least one non-null): the proxy map and the block
+// masses [2][Hq][N] (on/below, above each tile's diagonal).
+hipError_t launch_proxy(const __bf16* q, const __bf16* k, float* amap, float* mass, float* row_lse, void* scratch,
+                        int hq, int hkv, int n, float scale, hipStream_t stream);
 
-hipError_t launch_route(const float* amap, float* c_struct, int32_t* route, int hq, int n, int sink_width,
-                        int recency_width, float tau, int route_override, hipStream_t stream);
+// From the block masses when mass != nullptr (widths of one block), else
+// from the map.
+hipError_t launch_route(const float* amap, const float* mass, float* c_struct, int32_t* route, int hq, int n,
+                        int sink_width, int recency_width, float tau, int route_override, hipStream_t stream);
 
 struct SelectBuffers {
   float* lo;      // [Hq][N] lower-triangle tile sums of the proxy map
@@ -42,7 +46,9 @@ SelectBuffers carve_select_workspace(void* ws, int hq, int hkv, int n);
 
 // use_gamma = false: noise floor on VS heads, gamma_pe on PE heads.
 // use_gamma = true: gamma-cumulative on VS heads and `gamma` on PE heads.
-hipError_t launch_select(const __bf16* q, const __bf16* k, const float* amap, const int32_t* route,
+// VS scores come from the block masses when mass != nullptr, else from a
+// pass over the map.
+hipError_t launch_select(const __bf16* q, const __bf16* k, const float* amap, const float* mass, const int32_t* route,
                          const SelectBuffers& b, int32_t* count, int32_t* idx, int hq, int hkv, int n, float scale,
                          float alpha, float gamma_pe, int kmin, int nf_stat, bool use_gamma, float gamma,
                          hipStream_t stream);

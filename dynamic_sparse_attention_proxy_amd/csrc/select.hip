@@ -4,7 +4,8 @@
 // ai-feeds summary, method module 2):
 //   tile_sums  - one streaming pass over the proxy map: per (head, key block)
 //                the mass on and below the tile diagonal (row >= column) and
-//                above it.  Proxy row r sits at position 128(N-1)+r, so key
+//                above it (skipped when the proxy pass already produced
+//                these block masses).  Proxy row r sits at position 128(N-1)+r, so key
 //                128kb+c is at offset 128(N-1-kb)+(r-c): the lower triangle
 //                falls in slash block N-1-kb, the upper one in N-2-kb.  The
 //                vertical score of kb is the tile total.
@@ -468,18 +469,24 @@ SelectBuffers carve_select_workspace(void* ws, int hq, int hkv, int n) {
   return b;
 }
 
-hipError_t launch_select(const __bf16* q, const __bf16* k, const float* amap, const int32_t* route,
+hipError_t launch_select(const __bf16* q, const __bf16* k, const float* amap, const float* mass, const int32_t* route,
                          const SelectBuffers& b, int32_t* count, int32_t* idx, int hq, int hkv, int n, float scale,
                          float alpha, float gamma_pe, int kmin, int nf_stat, bool use_gamma, float gamma,
                          hipStream_t stream) {
   const int N = n / kBlock;
   hipError_t e;
-  hipLaunchKernelGGL(tile_sums_kernel, dim3(N, hq), dim3(256), 0, stream, amap, b.lo, b.up, n, N);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const float* lo = mass;
+  const float* up = mass + (size_t)hq * N;
+  if (mass == nullptr) {
+    hipLaunchKernelGGL(tile_sums_kernel, dim3(N, hq), dim3(256), 0, stream, amap, b.lo, b.up, n, N);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    lo = b.lo;
+    up = b.up;
+  }
 
   VsArgs va;
-  va.lo = b.lo;
-  va.up = b.up;
+  va.lo = lo;
+  va.up = up;
   va.route = route;
   va.vscore = b.vscore;
   va.sscore = b.sscore;

@@ -116,11 +116,24 @@ typedef struct crisp_blocks {
  * causally to all keys:
  *   attn_map[h][r][j] = softmax_j(scale * q[h][n-128+r] . k[g(h)][j]), j <= n-128+r,
  *   and 0 for j > n-128+r.                                 [Hq][128][n] fp32
+ * block_mass: the map summed per 128x128 tile (key block kb, all 128 rows),
+ * split at the tile's diagonal:                               [2][Hq][N] fp32
+ *   block_mass[0][h][kb] = sum_{r >= c} attn_map[h][r][128 kb + c]
+ *   block_mass[1][h][kb] = sum_{r <  c} attn_map[h][r][128 kb + c]
+ * Every quantity routing and selection read from the map follows from
+ * these (ai.info summary, "Methodology in Plain English": vertical mass per
+ * key block, slash mass per offset band): the vertical score of kb is the
+ * tile total over 128, and since proxy row r sits at offset
+ * 128(N-1-kb) + r - c from key 128 kb + c, the lower part falls in slash
+ * band N-1-kb and the upper part in band N-2-kb.  C_struct with one-block
+ * sink and recency widths is (total of block 0 + total of block N-1) / 128.
+ * Either output may be NULL, not both; computing only block_mass skips the
+ * 4 * 128 * n * Hq bytes of the map.
  * row_lse (optional, [Hq][128] fp32): natural log of each row's sum of
  * exp(scale * q.k).  `partials` is scratch of crisp_proxy_scratch_bytes
  * bytes (caller-owned device memory). */
 CRISP_API crisp_status crisp_proxy(const crisp_dims* dims, const void* q, const void* k, float* attn_map,
-                         float* row_lse, void* partials, size_t partials_bytes, void* stream);
+                         float* block_mass, float* row_lse, void* partials, size_t partials_bytes, void* stream);
 
 CRISP_API size_t crisp_proxy_scratch_bytes(const crisp_dims* dims);
 
@@ -130,9 +143,11 @@ CRISP_API size_t crisp_proxy_scratch_bytes(const crisp_dims* dims);
  * sink_width and the last recency_width key columns, averaged over the 128
  * proxy rows, so it lies in [0, 1]; route[h] = VS when C_struct >= tau, PE
  * otherwise, unless cfg->route_override forces one path.
+ * Reads block_mass when it is non-NULL (then both widths must be 128,
+ * CRISP_ERR_PARAM otherwise), else attn_map.
  * c_struct [Hq] fp32, route [Hq] int32. */
 CRISP_API crisp_status crisp_route(const crisp_dims* dims, const crisp_cfg* cfg, const float* attn_map,
-                         float* c_struct, int32_t* route, void* stream);
+                         const float* block_mass, float* c_struct, int32_t* route, void* stream);
 
 /* Step 3 - block selection (ai.info summary, "Methodology in Plain English";
  * ai-feeds summary, method module 2).
@@ -147,11 +162,13 @@ CRISP_API crisp_status crisp_route(const crisp_dims* dims, const crisp_cfg* cfg,
  *   PE heads: mean-pool q and k over 128-token blocks, softmax of
  *   scale * qbar[qb] . kbar[kb] over kb <= qb, keep the shortest prefix of the
  *   descending order whose mass reaches gamma_pe, plus qb.
- * q, k, attn_map: as above; route: [Hq] from crisp_route.  `workspace` must
- * hold crisp_select_workspace_bytes(dims) bytes of device memory. */
+ * q, k, attn_map, block_mass: as above (the VS scores come from block_mass
+ * when it is non-NULL, else from a pass over attn_map; at least one is
+ * needed); route: [Hq] from crisp_route.  `workspace` must hold
+ * crisp_select_workspace_bytes(dims) bytes of device memory. */
 CRISP_API crisp_status crisp_select(const crisp_dims* dims, const crisp_cfg* cfg, const void* q, const void* k,
-                          const float* attn_map, const int32_t* route, const crisp_blocks* out,
-                          void* workspace, size_t workspace_bytes, void* stream);
+                          const float* attn_map, const float* block_mass, const int32_t* route,
+                          const crisp_blocks* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Comparison chain - gamma-cumulative coverage on both paths (ai.info
  * summary, "Main Findings": the budget rule CRISP replaces on VS heads,
@@ -161,9 +178,9 @@ CRISP_API crisp_status crisp_select(const crisp_dims* dims, const crisp_cfg* cfg
  * kmin top-up; PE heads use `gamma` instead of cfg->gamma_pe.
  * gamma in (0, 1]. */
 CRISP_API crisp_status crisp_select_gamma(const crisp_dims* dims, const crisp_cfg* cfg, float gamma, const void* q,
-                                const void* k, const float* attn_map, const int32_t* route,
-                                const crisp_blocks* out, void* workspace, size_t workspace_bytes,
-                                void* stream);
+                                const void* k, const float* attn_map, const float* block_mass,
+                                const int32_t* route, const crisp_blocks* out, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 CRISP_API size_t crisp_select_workspace_bytes(const crisp_dims* dims);
 

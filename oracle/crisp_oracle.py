@@ -162,6 +162,25 @@ def pooled_scores(c: np.ndarray, dg: np.ndarray, block: int = 128):
     return v, sl
 
 
+def block_masses(A: np.ndarray, block: int = 128):
+    """Per key block kb, the proxy map's mass on and below the diagonal of
+    its tile (proxy row r, key 128 kb + c, r >= c) and above it (r < c).
+    Reading R5 pools offsets in bands of 128: row r against key 128 kb + c
+    lies at offset 128 (N-1-kb) + r - c, so these two parts are what the
+    tile gives to slash bands N-1-kb and N-2-kb, and their sum is the tile's
+    vertical mass."""
+    B, n = A.shape
+    N = n // block
+    lo = np.zeros(N, dtype=np.float64)
+    up = np.zeros(N, dtype=np.float64)
+    for kb in range(N):
+        for r in range(B):
+            row = A[r, kb * block:(kb + 1) * block]
+            lo[kb] += row[: r + 1].sum()
+            up[kb] += row[r + 1:].sum()
+    return lo, up
+
+
 # ---------------------------------------------------------------------------
 # Step 4a: sink-aware noise-floor selection on Vertical-Slash heads
 # (ai.info "Methodology in Plain English": expected background mass over the

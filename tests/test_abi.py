@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert B.crisp_abi_version() >> 16 == 1
+    assert B.crisp_abi_version() >> 16 == 2
     lib = B.lib()
     for s in range(8):
         assert lib.crisp_status_string(s)
@@ -85,8 +85,8 @@ def test_pointer_and_param_errors():
     lib = B.lib()
     assert lib.crisp_sparse_attn(ctypes.byref(dims), P16, P16, P16, None, P16, P16, 0, None, None) == 1
     # proxy scratch too small
-    assert lib.crisp_proxy(ctypes.byref(dims), P16, P16, P16, None, P16, 16, None) == 5
-    assert lib.crisp_proxy(None, P16, P16, P16, None, P16, 1 << 30, None) == 1
+    assert lib.crisp_proxy(ctypes.byref(dims), P16, P16, P16, None, None, P16, 16, None) == 5
+    assert lib.crisp_proxy(None, P16, P16, P16, None, None, P16, 1 << 30, None) == 1
 
 
 @pytest.mark.parametrize("field,value", [
@@ -98,11 +98,11 @@ def test_cfg_errors(field, value):
     cfg = B.make_cfg()
     setattr(cfg, field, value)
     lib = B.lib()
-    assert lib.crisp_route(ctypes.byref(dims), ctypes.byref(cfg), P16, P16, P16, None) == 3
+    assert lib.crisp_route(ctypes.byref(dims), ctypes.byref(cfg), P16, None, P16, P16, None) == 3
     blocks = B.crisp_blocks()
     blocks.count = P16
     blocks.idx = P16
-    assert lib.crisp_select(ctypes.byref(dims), ctypes.byref(cfg), P16, P16, P16, P16, ctypes.byref(blocks), P16,
+    assert lib.crisp_select(ctypes.byref(dims), ctypes.byref(cfg), P16, P16, P16, None, P16, ctypes.byref(blocks), P16,
                             1 << 40, None) == 3
 
 
@@ -113,19 +113,50 @@ def test_select_errors():
     blocks = B.crisp_blocks()
     blocks.count = P16
     blocks.idx = None
-    assert lib.crisp_select(ctypes.byref(dims), ctypes.byref(cfg), P16, P16, P16, P16, ctypes.byref(blocks), P16,
+    assert lib.crisp_select(ctypes.byref(dims), ctypes.byref(cfg), P16, P16, P16, None, P16, ctypes.byref(blocks), P16,
                             1 << 40, None) == 1
     blocks.idx = P16
     blocks.v_score = P8
-    assert lib.crisp_select(ctypes.byref(dims), ctypes.byref(cfg), P16, P16, P16, P16, ctypes.byref(blocks), P16,
+    assert lib.crisp_select(ctypes.byref(dims), ctypes.byref(cfg), P16, P16, P16, None, P16, ctypes.byref(blocks), P16,
                             1 << 40, None) == 4
     blocks.v_score = None
-    assert lib.crisp_select(ctypes.byref(dims), ctypes.byref(cfg), P16, P16, P16, P16, ctypes.byref(blocks), P16,
+    assert lib.crisp_select(ctypes.byref(dims), ctypes.byref(cfg), P16, P16, P16, None, P16, ctypes.byref(blocks), P16,
                             64, None) == 5
-    assert lib.crisp_select_gamma(ctypes.byref(dims), ctypes.byref(cfg), 0.0, P16, P16, P16, P16,
+    assert lib.crisp_select_gamma(ctypes.byref(dims), ctypes.byref(cfg), 0.0, P16, P16, P16, None, P16,
                                   ctypes.byref(blocks), P16, 1 << 40, None) == 3
-    assert lib.crisp_select_gamma(ctypes.byref(dims), ctypes.byref(cfg), 1.2, P16, P16, P16, P16,
+    assert lib.crisp_select_gamma(ctypes.byref(dims), ctypes.byref(cfg), 1.2, P16, P16, P16, None, P16,
                                   ctypes.byref(blocks), P16, 1 << 40, None) == 3
+
+
+def test_map_or_block_mass_rules():
+    """The proxy output is the map, the block masses or both: at least one,
+    each aligned; routing from block masses needs one-block widths.  A call
+    that passes validation reaches the device check (no GPU here: 6)."""
+    dims = B.make_dims(4, 2, 1024)
+    lib = B.lib()
+    sb = 1 << 30
+    assert lib.crisp_proxy(ctypes.byref(dims), P16, P16, None, None, None, P16, sb, None) == 1
+    assert lib.crisp_proxy(ctypes.byref(dims), P16, P16, None, P8, None, P16, sb, None) == 4
+    assert lib.crisp_proxy(ctypes.byref(dims), P16, P16, P8, P16, None, P16, sb, None) == 4
+    assert lib.crisp_proxy(ctypes.byref(dims), P16, P16, None, P16, None, P16, sb, None) == 6
+    assert lib.crisp_proxy(ctypes.byref(dims), P16, P16, P16, P16, P16, P16, sb, None) == 6
+    cfg = B.make_cfg()
+    assert lib.crisp_route(ctypes.byref(dims), ctypes.byref(cfg), None, None, P16, P16, None) == 1
+    assert lib.crisp_route(ctypes.byref(dims), ctypes.byref(cfg), None, P16, P16, P16, None) == 6
+    for field in ("sink_width", "recency_width"):
+        c2 = B.make_cfg()
+        setattr(c2, field, 64)
+        assert lib.crisp_route(ctypes.byref(dims), ctypes.byref(c2), None, P16, P16, P16, None) == 3
+        assert lib.crisp_route(ctypes.byref(dims), ctypes.byref(c2), P16, None, P16, P16, None) == 6
+    blocks = B.crisp_blocks()
+    blocks.count = P16
+    blocks.idx = P16
+    assert lib.crisp_select(ctypes.byref(dims), ctypes.byref(cfg), P16, P16, None, None, P16, ctypes.byref(blocks),
+                            P16, 1 << 40, None) == 1
+    assert lib.crisp_select(ctypes.byref(dims), ctypes.byref(cfg), P16, P16, None, P16, P16, ctypes.byref(blocks),
+                            P16, 1 << 40, None) == 6
+    assert lib.crisp_select_gamma(ctypes.byref(dims), ctypes.byref(cfg), 0.95, P16, P16, None, P8, P16,
+                                  ctypes.byref(blocks), P16, 1 << 40, None) == 4
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

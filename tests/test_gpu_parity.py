@@ -46,11 +46,13 @@ def inputs(widx, seq_len=None):
     return _INPUTS[key]
 
 
-def run_chain(x, cfg, gamma=None, out_dtype=torch.float32):
+def run_chain(x, cfg, gamma=None, out_dtype=torch.float32, use_map=False):
+    """The chain with the proxy map materialised beside the block masses;
+    routing and selection read the masses unless use_map."""
     hq, hkv, n = x.q.shape[0], x.k.shape[0], x.q.shape[1]
     dims = B.make_dims(hq, hkv, n)
-    bufs = B.CrispBuffers(dims, out_dtype=out_dtype)
-    B.crisp_prefill(dims, cfg, x.q, x.k, x.v, bufs, gamma=gamma)
+    bufs = B.CrispBuffers(dims, out_dtype=out_dtype, with_map=True)
+    B.crisp_prefill(dims, cfg, x.q, x.k, x.v, bufs, gamma=gamma, use_map=use_map)
     torch.cuda.synchronize()
     return dims, bufs
 
@@ -206,6 +208,11 @@ def test_proxy_and_route_single_head_4k():
     for r in range(BLK):
         assert np.all(A_g[r, 4096 - BLK + r + 1:] == 0.0)
     np.testing.assert_allclose(bufs.row_lse[0].cpu().numpy(), lse_o, rtol=1e-5, atol=1e-5)
+    lo_o, up_o = O.block_masses(A_o)
+    bm = bufs.block_mass[:, 0].cpu().numpy().astype(np.float64)
+    np.testing.assert_allclose(bm[0], lo_o, rtol=1e-4, atol=1e-9)
+    np.testing.assert_allclose(bm[1], up_o, rtol=1e-4, atol=1e-9)
+    assert bm[1, -1] == 0.0  # the masked half of the diagonal tile
     c_o = O.c_struct(A_o)
     c_g = float(bufs.c_struct[0])
     assert abs(c_g - c_o) <= REL_CSTRUCT * c_o
@@ -310,12 +317,40 @@ def test_llama_32k_layer(override):
                 check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"h {h} qb {qb}")
 
 
+@pytest.mark.parametrize("override", [B.ROUTE_AUTO, B.ROUTE_FORCE_VS])
+def test_map_and_block_mass_paths_agree(override):
+    """Routing and selection from the block masses (the default chain) and
+    from a pass over the materialised map: the same C_struct up to fp32
+    summation order, and the same kept blocks except within the parity
+    tolerance of a threshold."""
+    x = inputs(1)
+    cfg = B.make_cfg(route_override=override)
+    _, bm = run_chain(x, cfg)
+    _, bp = run_chain(x, cfg, use_map=True)
+    c1, c2 = bm.c_struct.cpu().numpy(), bp.c_struct.cpu().numpy()
+    np.testing.assert_allclose(c1, c2, rtol=1e-5)
+    assert torch.equal(bm.route, bp.route)
+    for key in ("v_score", "s_score"):
+        np.testing.assert_allclose(bm.blocks[key].cpu().numpy(), bp.blocks[key].cpu().numpy(), rtol=1e-5,
+                                   atol=1e-9)
+    if override == B.ROUTE_FORCE_VS:
+        for key, skey, fkey in (("v_mask", "v_score", "floor_v"), ("s_mask", "s_score", "floor_s")):
+            m1, m2 = bm.blocks[key].cpu().numpy(), bp.blocks[key].cpu().numpy()
+            xs = bp.blocks[skey].cpu().numpy()
+            fl = bp.blocks[fkey].cpu().numpy()
+            for h, b in zip(*np.nonzero(m1 != m2)):
+                assert abs(xs[h, b] - fl[h]) <= 1e-3 * fl[h], (key, h, b)
+    else:
+        assert torch.equal(bm.blocks["count"], bp.blocks["count"])
+
+
 def test_chain_is_deterministic():
     x = inputs(1)
     cfg = B.make_cfg(route_override=B.ROUTE_FORCE_VS)
     _, b1 = run_chain(x, cfg)
     _, b2 = run_chain(x, cfg)
     assert torch.equal(b1.attn_map, b2.attn_map)
+    assert torch.equal(b1.block_mass, b2.block_mass)
     for key in ("count", "v_score", "s_score", "v_mask", "s_mask", "floor_v", "floor_s"):
         assert torch.equal(b1.blocks[key], b2.blocks[key]), key
     c, i1, i2 = b1.blocks["count"].cpu().numpy(), b1.blocks["idx"].cpu().numpy(), b2.blocks["idx"].cpu().numpy()

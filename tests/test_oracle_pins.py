@@ -183,6 +183,42 @@ def test_scores_sum_to_one_and_tile_triangle_identity():
     np.testing.assert_allclose(sl, sl_t, rtol=1e-12, atol=1e-18)
 
 
+def test_block_masses_give_vertical_slash_and_c_struct():
+    # block_masses is pinned by quantities computed along other routes: the
+    # column sums (v), the diagonal loop (sl) and the slice sums (C_struct).
+    rng = _rng(16)
+    n, d = 1536, 64
+    A, _ = O.proxy_map(rng.standard_normal((B, d)), rng.standard_normal((n, d)), 0.3)
+    lo, up = O.block_masses(A)
+    v, sl = O.pooled_scores(*O.token_scores(A))
+    N = n // B
+    np.testing.assert_allclose((lo + up) / B, v, rtol=1e-12)
+    sl_b = np.zeros(N)
+    for s in range(N):
+        sl_b[s] = lo[N - 1 - s] + (up[N - 2 - s] if s <= N - 2 else 0.0)
+    np.testing.assert_allclose(sl_b / B, sl, rtol=1e-12, atol=1e-18)
+    assert up[N - 1] == 0.0  # the masked half of the diagonal tile
+    c = (lo[0] + up[0] + lo[N - 1] + up[N - 1]) / B
+    assert c == pytest.approx(O.c_struct(A), rel=1e-12)
+
+
+def test_block_masses_closed_form_at_zero_query():
+    # Q = 0: row r (position i_r = n - 128 + r) is uniform, 1/(i_r + 1), on
+    # keys 0..i_r.  A fully visible tile gives r + 1 columns on/below the
+    # diagonal and 127 - r above; the diagonal tile only the r + 1.
+    n = 768
+    N = n // B
+    A, _ = O.proxy_map(np.zeros((B, 16)), _rng(17).standard_normal((n, 16)), 1.0)
+    lo, up = O.block_masses(A)
+    inv = np.array([1.0 / (n - B + r + 1) for r in range(B)])
+    r = np.arange(B)
+    for kb in range(N - 1):
+        assert lo[kb] == pytest.approx(float(((r + 1) * inv).sum()), rel=1e-12)
+        assert up[kb] == pytest.approx(float(((B - 1 - r) * inv).sum()), rel=1e-12)
+    assert lo[N - 1] == pytest.approx(float(((r + 1) * inv).sum()), rel=1e-12)
+    assert up[N - 1] == 0.0
+
+
 def test_periodic_slash_closed_form():
     # One-hot Q_i = a e_{i mod 128}, K_j = a e_{(j + o*) mod 128}:
     # logit x only where (i - j) = o* (mod 128).  Closed forms for c[j], dg[o].
