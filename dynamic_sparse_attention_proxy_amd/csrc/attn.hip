@@ -31,7 +31,6 @@ typedef __bf16 gcc_bf16x4 __attribute__((__vector_size__(8)));
 typedef __attribute__((address_space(3))) gcc_bf16x4 lds_bf16x4;
 constexpr int kKStages = 3;             // K tiles in flight: the next one is used, one more prefetched
 constexpr float kSumLimit = 65536.f;     // a lane's step sum above this raises the running max
-constexpr int kBufferFlags = 0x00020000; // buffer resource word 3: raw 32-bit data, no swizzle
 
 struct AttnArgs {
   const __bf16* q;
@@ -48,17 +47,6 @@ struct AttnArgs {
   int out_fp32;
   RowMap map;
 };
-
-// LDS chunk swizzles (chunk position = chunk ^ swz(row)), chosen from
-// measured bank-conflict counts on gfx950.  The K operand read has 16 lanes
-// reading one chunk of rows {0..3, 8..11, 4..7, 12..15} (+ multiples of 16):
-// any bijection of the row's low 4 bits keeps them apart; this one sends
-// (r0, r1) to chunk bits (2, 3) and (r2, r3) to (0, 1).  The transposing
-// V^T read has 32 lanes reading chunks c0 .. c0+3 of 4 consecutive rows: the
-// row's bits 0-1 must move the chunk's bits 2-3, which (r & 3) << 2 does
-// while leaving the other row bits free (so those offsets stay additive).
-__device__ __forceinline__ int swz_k(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
-__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 2; }
 
 // Key index (0..31) held by accumulator register v of lane group lg.
 __device__ __forceinline__ int acc_key(int v, int lg) { return (v < 8) ? (8 * lg + v) : (16 + 8 * lg + (v - 8)); }

@@ -26,6 +26,32 @@ __device__ __forceinline__ f32x16 mfma32(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// LDS chunk swizzles of [row][128 bf16] tiles (chunk position =
+// chunk ^ swz(row)), chosen from measured bank-conflict counts on gfx950.  The K operand read has 16 lanes
+// reading one chunk of rows {0..3, 8..11, 4..7, 12..15} (+ multiples of 16):
+// any bijection of the row's low 4 bits keeps them apart; this one sends
+// (r0, r1) to chunk bits (2, 3) and (r2, r3) to (0, 1).  The transposing
+// V^T read has 32 lanes reading chunks c0 .. c0+3 of 4 consecutive rows: the
+// row's bits 0-1 must move the chunk's bits 2-3, which (r & 3) << 2 does
+// while leaving the other row bits free (so those offsets stay additive).
+__device__ __forceinline__ int swz_k(int r) { return ((r & 3) << 2) | ((r >> 2) & 3); }
+__device__ __forceinline__ int swz_v(int r) { return (r & 3) << 2; }
+
+// Buffer resource word 3: raw 32-bit data, no swizzle.
+constexpr int kBufferFlags = 0x00020000;
+
+// One LDS-DMA instruction: lane L copies the 16 bytes at byte offset
+// voff + soff of buffer `rs` to LDS address lds_addr + 16 L.  Inline asm, so
+// the compiler does not insert a vmcnt(0) before unrelated LDS reads; the
+// caller waits (wait_dma*) and synchronises before reading.  One wait state
+// separates the M0 write from the DMA that reads it.
+__device__ __forceinline__ void lds_dma_16B(__amdgpu_buffer_rsrc_t rs, int voff, int soff, unsigned lds_addr) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen lds"
+               :
+               : "s"(lds_addr), "v"(voff), "s"(rs), "s"(soff)
+               : "memory", "m0");
+}
+
 // Wait until this wave's buffer loads (including LDS DMA) have landed.
 __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // The same, except for the 4 most recently issued ones (loads complete in order).

@@ -9,7 +9,7 @@
 namespace crisp {
 
 // Proxy: keys per workgroup of the two proxy passes.
-constexpr int kProxyChunk = 512;
+constexpr int kProxyChunk = 1024;
 inline int proxy_chunks(int n) { return (n + kProxyChunk - 1) / kProxyChunk; }
 inline size_t proxy_scratch_bytes(int hq, int n) {
   // per (head, chunk, row): running max and sum; per (head, row): log2-sum-exp

@@ -4,20 +4,21 @@
 // causally to all n keys (CRISP, ai.info summary, "Key Contributions" item 2:
 // C_struct reads a proxy attention map the method computes anyway).
 //
-// Pass 1 (stats): a workgroup takes one head and a chunk of 512 keys; wave w
-//   owns proxy rows 32w..32w+31 with Q held as the A operand of S = Q.K^T.
-//   K goes straight from global memory into the B operand (lane = key), so
-//   each accumulator register holds one row and 32 consecutive keys across a
-//   half-wave.  Each lane keeps a running (max, sum of exp2) per row; the 32
-//   lanes of a row are merged with a butterfly at the end of the chunk.  The
-//   next 32 keys are loaded while the current ones are used.
+// Both passes run one workgroup per (head, chunk of kProxyChunk keys): its 4
+// wavefronts own proxy rows 32w..32w+31 and compute S^T = K.Q^T with Q in
+// VGPRs, so each lane owns one row (keys split between lanes l and l ^ 32).
+// K streams through three LDS stages, 64 keys per step, by LDS DMA shared by
+// the 4 waves (one barrier per step).
+// Pass 1 (stats): per lane a running (max, sum of exp2) of its row over its
+//   keys of the chunk; the running max only has to keep the exps in range,
+//   so it is taken from the first step and raised only when a step's sum
+//   exceeds kSumLimit.  Lanes l and l ^ 32 merge at the end.
 // Combine: one wavefront per (head, row) merges the chunk partials into the
 //   row's log2-sum-exp.
-// Pass 2 (map): recompute S and form exp2(t - lse2).  It stores the map (a
-//   half-wave writes 128 contiguous bytes of one row per store) and/or the
-//   block masses: per (head, key block) the map's mass on and below the
-//   tile diagonal (row >= column) and above it.  A workgroup's 512 keys are
-//   4 whole key blocks and its 4 waves all 128 rows, so each block's masses
+// Pass 2 (map): recompute S and form exp2(t - lse2).  It stores the map
+//   and/or the block masses: per (head, key block) the map's mass on and
+//   below the tile diagonal (row >= column) and above it.  A chunk is whole
+//   key blocks and its 4 waves cover all 128 rows, so each block's masses
 //   are complete inside one workgroup.
 // Route: C_struct = mean over rows of the mass on the first sink_width and
 //   the last recency_width columns (from the map, or from the block masses
@@ -30,6 +31,10 @@
 namespace crisp {
 
 namespace {
+
+constexpr int kPStep = 64;          // keys per pipeline step
+constexpr int kPStages = 3;         // K tiles in LDS: the current one and two in flight
+constexpr float kSumLimit = 65536.f; // a step's sum above this raises the running max
 
 struct ProxyArgs {
   const __bf16* q;
@@ -45,9 +50,6 @@ struct ProxyArgs {
   float scale_log2;
 };
 
-// Proxy row held by accumulator register v of lane group lg in wave w.
-__device__ __forceinline__ int acc_row(int w, int v, int lg) { return 32 * w + 8 * (v >> 2) + 4 * lg + (v & 3); }
-
 __device__ __forceinline__ void merge_ml(float& m, float& l, float mo, float lo) {
   const float M = fmaxf(m, mo);
   if (M == -INFINITY) return;
@@ -55,88 +57,187 @@ __device__ __forceinline__ void merge_ml(float& m, float& l, float mo, float lo)
   m = M;
 }
 
-__device__ __forceinline__ void load_q_rows(const ProxyArgs& p, int h, int w, int l32, int lg, bf16x8 qf[8]) {
-  const __bf16* qrow = p.q + ((size_t)h * p.n + (size_t)(p.n - kBlock + 32 * w + l32)) * kHeadDim + 8 * lg;
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) qf[kk] = as_bf16x8(*(const u32x4*)(qrow + 16 * kk));
-}
+// Key offset (0..31 within a 32-key half) of accumulator register v in
+// lane group lg: rows 8 (v / 4) + 4 lg + v % 4 of the K operand.
+__device__ __forceinline__ int acc_key(int v, int lg) { return 8 * (v >> 2) + 4 * lg + (v & 3); }
 
-__device__ __forceinline__ void load_k_tile(const __bf16* krow, bf16x8 kf[8]) {
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) kf[kk] = as_bf16x8(*(const u32x4*)(krow + 16 * kk));
-}
-
-__device__ __forceinline__ f32x16 qk_regs(const bf16x8 qf[8], const bf16x8 kf[8]) {
-  f32x16 s;
-#pragma unroll
-  for (int v = 0; v < 16; ++v) s[v] = 0.f;
-#pragma unroll
-  for (int kk = 0; kk < 8; ++kk) s = mfma32(qf[kk], kf[kk], s);
-  return s;
-}
-
-// Partial statistics of proxy row r of head h over key chunk c live at
-// part[((h * 128 + r) * nchunks + c) * 2 + {0: max, 1: sum}] (base 2).
-__global__ __launch_bounds__(256) void proxy_stats_kernel(ProxyArgs p) {
+// kPass 0: row statistics.  kPass 1: map (kMap) and/or block masses (kMass).
+template <int kPass, bool kMap, bool kMass>
+__global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
+  __shared__ __attribute__((aligned(1024))) __bf16 ks[kPStages][kPStep * kHeadDim];
+  __shared__ float part[4][kProxyChunk / kBlock][2];  // masses per wave and key block of the chunk
   const int chunk = blockIdx.x, h = blockIdx.y, g = h / p.qpg;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, lg = lane >> 5;
-  bf16x8 qf[8];
-  load_q_rows(p, h, w, l32, lg, qf);
-  float m[16], l[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    m[v] = -INFINITY;
-    l[v] = 0.f;
-  }
-  const int kbeg = chunk * kProxyChunk;
-  const int kend = min(p.n, kbeg + kProxyChunk);
-  const __bf16* kg = p.k + (size_t)g * p.n * kHeadDim + (size_t)l32 * kHeadDim + 8 * lg;
+  const int kbeg = chunk * kProxyChunk, kend = min(p.n, kbeg + kProxyChunk);
+  const int nsteps = (kend - kbeg) / kPStep;  // whole key blocks: even, >= 2
   const int pos0 = p.n - kBlock;
-  // K sub-blocks of 32 keys, the next one in flight while this one is used
-  bf16x8 ka[8], kb[8];
-  load_k_tile(kg + (size_t)kbeg * kHeadDim, ka);
-  auto consume = [&](const bf16x8 (&kf)[8], int key0) {
-    const f32x16 s = qk_regs(qf, kf);
-    const int key = key0 + l32;
-    const bool masked_tile = key0 + 31 > pos0;  // only the last 128 keys can be masked
+  const int row = 32 * w + l32;
+
+  // Q row as the B operand: d = 16 kk + 8 lg + [0, 8)
+  bf16x8 qf[8];
+  const __bf16* qrow = p.q + ((size_t)h * p.n + pos0 + row) * kHeadDim + 8 * lg;
 #pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      if (!masked_tile || key <= pos0 + acc_row(w, v, lg)) {
-        const float t = s[v] * p.scale_log2;
-        const float dlt = t - m[v];
-        const float e = fast_exp2(-fabsf(dlt));
-        const bool up = dlt > 0.f;
-        l[v] = up ? l[v] * e + 1.f : l[v] + e;
-        m[v] = up ? t : m[v];
-      }
+  for (int kk = 0; kk < 8; ++kk) qf[kk] = as_bf16x8(*(const u32x4*)(qrow + 16 * kk));
+
+  // LDS DMA of a 64-key tile: wave w fills rows 16w .. 16w+15, lane L of
+  // instruction i row 16w + 4i + L/16 at chunk position L & 15.
+  const size_t nd = (size_t)p.n * kHeadDim;
+  const __amdgpu_buffer_rsrc_t krs =
+      __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + (size_t)g * nd), 0, (int)(nd * 2), kBufferFlags);
+  int dma_k[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 16 * w + 4 * i + (lane >> 4);
+    dma_k[i] = r * 256 + (((lane & 15) ^ swz_k(r)) << 4);
+  }
+  const int wu = __builtin_amdgcn_readfirstlane(w);
+  auto dma_tile = [&](int stage, int step) {
+    const int soff = (kbeg + step * kPStep) * (kHeadDim * 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      lds_dma_16B(krs, dma_k[i], soff,
+                  (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)(ks[stage] + (16 * wu + 4 * i) *
+                                                                                              kHeadDim));
+  };
+  // K operand of this lane: row l32 of each 32-key half, logical chunk 2 kk + lg.
+  int k_off[8];
+#pragma unroll
+  for (int kk = 0; kk < 8; ++kk) k_off[kk] = l32 * 256 + (((2 * kk + lg) ^ swz_k(l32)) << 4);
+  auto qk = [&](int stage, f32x16 (&s)[2]) {
+    const char* kb8 = (const char*)ks[stage];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) acc = mfma32(as_bf16x8(*(const u32x4*)(kb8 + k_off[kk] + kb2 * 8192)), qf[kk], acc);
+      s[kb2] = acc;
     }
   };
-  // A chunk is whole key blocks, so key0 + 32 < kend always; the second
-  // prefetch is clamped into the chunk on the last trip (its data unused),
-  // which keeps both loads unconditional.
-  for (int key0 = kbeg; key0 < kend; key0 += 64) {
-    load_k_tile(kg + (size_t)(key0 + 32) * kHeadDim, kb);
-    consume(ka, key0);
-    load_k_tile(kg + (size_t)min(key0 + 64, kend - 32) * kHeadDim, ka);
-    consume(kb, key0 + 32);
-  }
+
+  float m = -INFINITY, l = 0.f;  // pass 1: this lane's running max (scaled) and sum
+  float neg_lse = 0.f;           // pass 2
+  if (kPass == 1) neg_lse = -p.lse2[h * kBlock + row];
+  float lo = 0.f, up = 0.f;      // pass 2: this lane's masses of the current key block
+
+  dma_tile(0, 0);
+  dma_tile(1, 1);
+  wait_dma();
+  __syncthreads();
+  for (int j = 0; j < nsteps; ++j) {
+    const bool ahead = j + 2 < nsteps;
+    if (ahead) dma_tile((j + 2) % kPStages, j + 2);
+    f32x16 s[2];
+    qk(j % kPStages, s);
+    const int key0 = kbeg + j * kPStep;
+    if (key0 + kPStep - 1 > pos0) {  // keys past the first proxy row: causal mask
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
-      const float mo = __shfl_xor(m[v], o);
-      const float lo = __shfl_xor(l[v], o);
-      merge_ml(m[v], l[v], mo, lo);
+        for (int v = 0; v < 16; ++v)
+          if (key0 + 32 * kb2 + acc_key(v, lg) > pos0 + row) s[kb2][v] = -INFINITY;
     }
-  }
-  // lane v of each half-wave writes row acc_row(w, v, lg)
+    if (kPass == 0) {
+      if (j == 0) {  // key kbeg <= pos0 is visible to every row
+        float mx = -INFINITY;
 #pragma unroll
-  for (int v = 0; v < 16; ++v) {
-    if (l32 == v) {
-      const int r = acc_row(w, v, lg);
-      float* dst = p.part + (((size_t)h * kBlock + r) * p.nchunks + chunk) * 2;
-      dst[0] = m[v];
-      dst[1] = l[v];
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb2][v]);
+        m = mx * p.scale_log2;
+      }
+      const float neg_m = (m == -INFINITY) ? 0.f : -m;
+      float ls = 0.f;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) ls += fast_exp2(fmaf(s[kb2][v], p.scale_log2, neg_m));
+      if (__any(!(ls <= kSumLimit))) {  // rare: raise this lane's max to its step max, redo the sum
+        float mx = -INFINITY;
+#pragma unroll
+        for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb2][v]);
+        const float m_new = fmaxf(m, mx * p.scale_log2);
+        if (m_new != -INFINITY) {
+          l *= fast_exp2(m - m_new);
+          m = m_new;
+          ls = 0.f;
+#pragma unroll
+          for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+            for (int v = 0; v < 16; ++v) ls += fast_exp2(fmaf(s[kb2][v], p.scale_log2, -m));
+        }
+      }
+      l += ls;
+    } else {
+      // sub-tile t (32 keys) of the key block against row group w: all
+      // below the diagonal when t < w, all above when t > w, split when equal
+      const int half = (key0 >> 6) & 1;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const int t = 2 * half + kb2;
+        float a[16];
+#pragma unroll
+        for (int v = 0; v < 16; ++v) {
+          a[v] = fast_exp2(fmaf(s[kb2][v], p.scale_log2, neg_lse));
+          if (kMass) {
+            if (t < w || (t == w && l32 >= acc_key(v, lg)))
+              lo += a[v];
+            else
+              up += a[v];
+          }
+        }
+        if (kMap) {
+          float* dst = p.amap + ((size_t)h * kBlock + row) * p.n + key0 + 32 * kb2 + 4 * lg;
+#pragma unroll
+          for (int q4 = 0; q4 < 4; ++q4) {
+            f32x4 o;
+            o[0] = a[4 * q4];
+            o[1] = a[4 * q4 + 1];
+            o[2] = a[4 * q4 + 2];
+            o[3] = a[4 * q4 + 3];
+            *(f32x4*)(dst + 8 * q4) = o;
+          }
+        }
+      }
+      if (kMass && half == 1) {  // end of a key block: reduce and park the wave's sums
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+          lo += __shfl_xor(lo, o);
+          up += __shfl_xor(up, o);
+        }
+        if (lane == 0) {
+          part[w][(key0 - kbeg) >> 7][0] = lo;
+          part[w][(key0 - kbeg) >> 7][1] = up;
+        }
+        lo = 0.f;
+        up = 0.f;
+      }
+    }
+    if (ahead)
+      wait_dma_but_4();
+    else
+      wait_dma();
+    __syncthreads();
+  }
+
+  if (kPass == 0) {
+    // lanes l and l ^ 32 hold the same row: merge, then one lane writes it
+    const float mo = __shfl_xor(m, 32), lo2 = __shfl_xor(l, 32);
+    merge_ml(m, l, mo, lo2);
+    if (lg == 0) {
+      float* dst = p.part + (((size_t)h * kBlock + row) * p.nchunks + chunk) * 2;
+      dst[0] = m;
+      dst[1] = l;
+    }
+  } else if (kMass) {
+    // the loop's last barrier orders every wave's parked sums before this
+    const int nkb = (kend - kbeg) >> 7;
+    if (tid < 2 * nkb) {
+      const int jb = tid >> 1, which = tid & 1;
+      const float v = part[0][jb][which] + part[1][jb][which] + part[2][jb][which] + part[3][jb][which];
+      const int N = p.n / kBlock, hq = gridDim.y;
+      p.mass[((size_t)which * hq + h) * N + (kbeg >> 7) + jb] = v;
     }
   }
 }
@@ -159,81 +260,6 @@ __global__ __launch_bounds__(256) void proxy_combine_kernel(ProxyArgs p) {
     const float lse2 = m + fast_log2(l);
     p.lse2[row] = lse2;
     if (p.row_lse != nullptr) p.row_lse[row] = lse2 * kLn2;
-  }
-}
-
-template <bool kMap, bool kMass>
-__global__ __launch_bounds__(256) void proxy_map_kernel(ProxyArgs p) {
-  __shared__ float part[4][4][2];  // [wave][key block of the chunk][lower, upper]
-  const int chunk = blockIdx.x, h = blockIdx.y, g = h / p.qpg;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, lg = lane >> 5;
-  bf16x8 qf[8];
-  load_q_rows(p, h, w, l32, lg, qf);
-  float lse2[16];
-#pragma unroll
-  for (int v = 0; v < 16; ++v) lse2[v] = p.lse2[h * kBlock + acc_row(w, v, lg)];
-  const int kbeg = chunk * kProxyChunk;
-  const int kend = min(p.n, kbeg + kProxyChunk);
-  const __bf16* kg = p.k + (size_t)g * p.n * kHeadDim + (size_t)l32 * kHeadDim + 8 * lg;
-  float* arow = p.amap + (size_t)h * kBlock * p.n;
-  const int pos0 = p.n - kBlock;
-  float lo = 0.f, up = 0.f;  // this lane's mass of the current key block
-  bf16x8 ka[8], kb[8];
-  load_k_tile(kg + (size_t)kbeg * kHeadDim, ka);
-  auto consume = [&](const bf16x8 (&kf)[8], int key0) {
-    const f32x16 s = qk_regs(qf, kf);
-    const int key = key0 + l32;
-    const bool masked_tile = key0 + 31 > pos0;
-    // Sub-block `sub` of the key block holds columns 32 sub .. 32 sub + 31;
-    // wave w holds rows 32 w .. 32 w + 31: below the diagonal when sub < w,
-    // above when sub > w, split per element when sub == w.
-    const int sub = (key0 >> 5) & 3;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) {
-      const int r = acc_row(w, v, lg);
-      float a = fast_exp2(s[v] * p.scale_log2 - lse2[v]);
-      if (masked_tile && key > pos0 + r) a = 0.f;
-      if (kMap) arow[(size_t)r * p.n + key] = a;
-      if (kMass) {
-        if (sub < w || (sub == w && r - 32 * w >= l32))
-          lo += a;
-        else
-          up += a;
-      }
-    }
-    if (kMass && sub == 3) {  // last sub-block of a key block: reduce and park the wave's sums
-#pragma unroll
-      for (int o = 1; o < 64; o <<= 1) {
-        lo += __shfl_xor(lo, o);
-        up += __shfl_xor(up, o);
-      }
-      if (lane == 0) {
-        part[w][(key0 - kbeg) >> 7][0] = lo;
-        part[w][(key0 - kbeg) >> 7][1] = up;
-      }
-      lo = 0.f;
-      up = 0.f;
-    }
-  };
-  // A chunk is whole key blocks, so key0 + 32 < kend always; the second
-  // prefetch is clamped into the chunk on the last trip (its data unused),
-  // which keeps both loads unconditional.
-  for (int key0 = kbeg; key0 < kend; key0 += 64) {
-    load_k_tile(kg + (size_t)(key0 + 32) * kHeadDim, kb);
-    consume(ka, key0);
-    load_k_tile(kg + (size_t)min(key0 + 64, kend - 32) * kHeadDim, ka);
-    consume(kb, key0 + 32);
-  }
-  if (kMass) {
-    __syncthreads();
-    // the chunk's key blocks (n is a multiple of 128): sum the 4 waves in order
-    const int nkb = (kend - kbeg) >> 7;
-    if (tid < 2 * nkb) {
-      const int j = tid >> 1, which = tid & 1;
-      const float m = part[0][j][which] + part[1][j][which] + part[2][j][which] + part[3][j][which];
-      const int N = p.n / kBlock, hq = gridDim.y;
-      p.mass[((size_t)which * hq + h) * N + (kbeg >> 7) + j] = m;
-    }
   }
 }
 
@@ -293,7 +319,7 @@ hipError_t launch_proxy(const __bf16* q, const __bf16* k, float* amap, float* ma
   a.n = n;
   a.qpg = hq / hkv;
   a.scale_log2 = scale * kLog2e;
-  hipLaunchKernelGGL(proxy_stats_kernel, dim3(a.nchunks, hq), dim3(256), 0, stream, a);
+  hipLaunchKernelGGL((proxy_pass_kernel<0, false, false>), dim3(a.nchunks, hq), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(proxy_combine_kernel, dim3(hq * kBlock / 4), dim3(256), 0, stream, a);
@@ -301,11 +327,11 @@ hipError_t launch_proxy(const __bf16* q, const __bf16* k, float* amap, float* ma
   if (e != hipSuccess) return e;
   const dim3 grid(a.nchunks, hq);
   if (amap != nullptr && mass != nullptr)
-    hipLaunchKernelGGL((proxy_map_kernel<true, true>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((proxy_pass_kernel<1, true, true>), grid, dim3(256), 0, stream, a);
   else if (amap != nullptr)
-    hipLaunchKernelGGL((proxy_map_kernel<true, false>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((proxy_pass_kernel<1, true, false>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((proxy_map_kernel<false, true>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((proxy_pass_kernel<1, false, true>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
