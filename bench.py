@@ -35,8 +35,10 @@ def log(msg):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=3)
-    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10, help="timed steps of the CRISP chain and of the dense kernel")
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--compare-steps", type=int, default=3,
+                    help="timed steps of each supplementary chain (forced-VS, gamma)")
     ap.add_argument("--workload", default="llama3.1-8b-512k")
     ap.add_argument("--secondary", default="qwen2.5-7b-128k", help="extra workload reported beside ('' for none)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -46,6 +48,7 @@ def parse():
                     help="run one 1 GiB device-to-device copy first (HBM counter calibration)")
     ap.add_argument("--route", choices=["auto", "vs", "pe"], default="auto",
                     help="route override of the timed CRISP chain (the reported value uses auto)")
+    ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA ceiling probe")
     return ap.parse_args()
 
 
@@ -97,41 +100,58 @@ def run_workload(torch, B, synth, wname, args, cfg_kw, compare):
     # routing and selection read them.
     mass = bufs.block_mass
 
-    def chain(c, gamma, attn_timer=None):
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record()
+        return e
+
+    def chain(c, gamma, marks=None):
+        """One layer; `marks` collects an event after each stage."""
+        t = [ev()] if marks is not None else None
         B.crisp_proxy(dims, x.q, x.k, None, bufs.row_lse, bufs.partials, block_mass=mass)
+        if t is not None:
+            t.append(ev())
         B.crisp_route(dims, c, None, bufs.c_struct, bufs.route, block_mass=mass)
+        if t is not None:
+            t.append(ev())
         if gamma is None:
             B.crisp_select(dims, c, x.q, x.k, None, bufs.route, bufs.blocks, bufs.workspace, block_mass=mass)
         else:
             B.crisp_select_gamma(dims, c, gamma, x.q, x.k, None, bufs.route, bufs.blocks, bufs.workspace,
                                  block_mass=mass)
-        if attn_timer is None:
-            B.crisp_sparse_attn(dims, x.q, x.k, x.v, bufs.blocks["count"], bufs.blocks["idx"], bufs.out, bufs.lse)
-        else:
-            with attn_timer:
-                B.crisp_sparse_attn(dims, x.q, x.k, x.v, bufs.blocks["count"], bufs.blocks["idx"], bufs.out,
-                                    bufs.lse)
+        if t is not None:
+            t.append(ev())
+        B.crisp_sparse_attn(dims, x.q, x.k, x.v, bufs.blocks["count"], bufs.blocks["idx"], bufs.out, bufs.lse)
+        if t is not None:
+            t.append(ev())
+            marks.append(t)
+
+    def stats(xs):
+        ys = sorted(xs)
+        return {"median": ys[len(ys) // 2], "min": ys[0], "mean": sum(ys) / len(ys)}
 
     def timed_chain(c, gamma, steps, warmup):
         for _ in range(warmup):
             chain(c, gamma)
         torch.cuda.synchronize()
-        at = Timer(torch)
+        marks = []
         t0 = time.perf_counter()
-        ev0 = torch.cuda.Event(enable_timing=True)
-        ev1 = torch.cuda.Event(enable_timing=True)
-        ev0.record()
+        ev0 = ev()
         for _ in range(steps):
-            chain(c, gamma, at)
-        ev1.record()
+            chain(c, gamma, marks)
+        ev1 = ev()
         torch.cuda.synchronize()
         wall = (time.perf_counter() - t0) * 1e3 / steps
         step_ms = ev0.elapsed_time(ev1) / steps
+        stage = {name: [m[i].elapsed_time(m[i + 1]) for m in marks]
+                 for i, name in enumerate(("proxy", "route", "select", "attn"))}
         tiles = int(bufs.blocks["count"].sum().item())
         routes = bufs.route.cpu().tolist()
-        attn = at.ms()
+        attn = stage["attn"]
         return {"ms_per_layer": step_ms, "wall_ms_per_layer": wall, "attn_ms": sum(attn) / len(attn),
-                "attn_ms_all": attn, "tiles": tiles, "tile_frac": tiles / (w.num_q_heads * N * (N + 1) / 2),
+                "attn_ms_all": attn, "stage_ms": {k: {kk: round(vv, 4) for kk, vv in stats(v).items()}
+                                                  for k, v in stage.items()},
+                "tiles": tiles, "tile_frac": tiles / (w.num_q_heads * N * (N + 1) / 2),
                 "heads_vs": int(sum(routes)), "heads_pe": len(routes) - int(sum(routes))}
 
     log(f"{w.name}: CRISP chain (route {args.route}), warmup {args.warmup}, steps {args.steps}")
@@ -151,12 +171,13 @@ def run_workload(torch, B, synth, wname, args, cfg_kw, compare):
     torch.cuda.synchronize()
     d_ms = dt.ms()
     res["dense"] = {"ms_per_layer": sum(d_ms) / len(d_ms), "ms_all": d_ms,
+                    "ms": {kk: round(vv, 4) for kk, vv in stats(d_ms).items()},
                     "tiles": w.num_q_heads * N * (N + 1) // 2}
     log(f"{w.name}: dense {res['dense']['ms_per_layer']:.2f} ms")
     # forced Vertical-Slash: the noise-floor selection on every head
     for alpha in (1.25, 1.0):
         c = B.make_cfg(**dict(cfg_kw, route_override=B.ROUTE_FORCE_VS, alpha=alpha))
-        r = timed_chain(c, None, args.steps, 1)
+        r = timed_chain(c, None, args.compare_steps, 1)
         r["n_v_mean"] = float(bufs.blocks["n_v"].float().mean())
         r["n_s_mean"] = float(bufs.blocks["n_s"].float().mean())
         res[f"forced_vs_alpha{alpha}"] = r
@@ -164,7 +185,7 @@ def run_workload(torch, B, synth, wname, args, cfg_kw, compare):
     if compare:
         for gamma in (0.95, 0.97):
             c = B.make_cfg(**dict(cfg_kw, route_override=B.ROUTE_FORCE_VS))
-            r = timed_chain(c, gamma, max(1, args.steps - 1), 0)
+            r = timed_chain(c, gamma, args.compare_steps, 1)
             r["n_v_mean"] = float(bufs.blocks["n_v"].float().mean())
             r["n_s_mean"] = float(bufs.blocks["n_s"].float().mean())
             res[f"gamma{gamma}_forced_vs"] = r
@@ -174,6 +195,48 @@ def run_workload(torch, B, synth, wname, args, cfg_kw, compare):
         if isinstance(res[key], dict) and "ms_per_layer" in res[key] and key != "dense":
             res[key]["speedup_vs_dense"] = dense_ms / res[key]["ms_per_layer"]
     return res, x, dims
+
+
+def mfma_ceiling(torch):
+    """Sustained bf16 MFMA rate of this GPU on N(0,1) operands (the data the
+    attention kernels see; the clock under load depends on it), measured by
+    the probe library: median of 5 launches of ~20 ms."""
+    import ctypes
+
+    path = os.path.join(ROOT, "dynamic_sparse_attention_proxy_amd", "libcrisp_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} not found: build it with `python -m dynamic_sparse_attention_proxy_amd.build`")
+    probe = ctypes.CDLL(path)
+    probe.crisp_probe_mfma_bf16.restype = ctypes.c_int
+    probe.crisp_probe_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int, ctypes.c_int,
+                                            ctypes.c_void_p]
+    probe.crisp_probe_mfma_bf16_flops.restype = ctypes.c_double
+    probe.crisp_probe_mfma_bf16_flops.argtypes = [ctypes.c_int, ctypes.c_int]
+    gen = torch.Generator(device="cuda").manual_seed(11)
+    ops = torch.randn(16 * 64 * 8, generator=gen, device="cuda").to(torch.bfloat16)
+    nblocks, iters = 256 * 2 * 8, 4096
+    sink = torch.empty(nblocks * 256, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+    def launch():
+        st = probe.crisp_probe_mfma_bf16(ctypes.c_void_p(ops.data_ptr()), ctypes.c_void_p(sink.data_ptr()), nblocks,
+                                         iters, stream)
+        if st != 0:
+            raise RuntimeError(f"MFMA probe failed ({st})")
+
+    launch()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(5):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        launch()
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    ms.sort()
+    return probe.crisp_probe_mfma_bf16_flops(nblocks, iters) / (ms[2] * 1e-3) / 1e12
 
 
 def cpu_baseline(q, k, v, dims, res, cfg_kw):
@@ -256,6 +319,13 @@ def main():
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4), "traffic": traffic,
                 "kernel": "fa_fwd_kernel<false> (crisp_sparse_attn)", "kernel_ms": round(crisp["attn_ms"], 3),
                 "flop_per_launch": TILE_FLOP * crisp["tiles"]}
+    if not args.no_ceiling:
+        log("measuring the MFMA ceiling on N(0,1) bf16 operands")
+        ceil = mfma_ceiling(torch)
+        roofline["ceiling_measured"] = {
+            "value": round(ceil, 1), "unit": "TFLOP/s", "frac": round(achieved / ceil, 4),
+            "probe": "independent v_mfma_f32_32x32x16_bf16 chains on N(0,1) bf16 operands, 2 workgroups of "
+                     "4 waves per CU (libcrisp_probe.so)"}
     cpu_inputs = None
     if not args.no_cpu_baseline and not args.only_crisp:
         g0 = 0

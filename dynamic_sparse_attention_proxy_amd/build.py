@@ -17,6 +17,9 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcrisp.so")
 SOURCES = ["api.hip", "proxy.hip", "select.hip", "attn.hip"]
+# Measurement probe, a library of its own so it stays out of the CRISP ABI.
+PROBE_LIB = os.path.join(PKG, "libcrisp_probe.so")
+PROBE_SOURCES = ["probe.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -44,24 +47,29 @@ def _compile(src):
     return src, obj, r.returncode, out
 
 
+def _link(objs, out):
+    tmp = out + ".tmp"
+    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
+    r = subprocess.run(cmd, capture_output=True, text=True)
+    if r.returncode != 0:
+        print(r.stdout + r.stderr, file=sys.stderr)
+        raise RuntimeError(f"link of {os.path.basename(out)} failed")
+    os.replace(tmp, out)
+
+
 def build(jobs: int = 4, verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
     with ThreadPoolExecutor(max_workers=max(1, jobs)) as ex:
-        results = list(ex.map(_compile, SOURCES))
-    objs = []
+        results = list(ex.map(_compile, SOURCES + PROBE_SOURCES))
+    objs = {}
     for src, obj, rc, out in results:
         if out.strip() and (verbose or rc != 0):
             print(f"[{src}]\n{out}", file=sys.stderr)
         if rc != 0:
             raise RuntimeError(f"hipcc failed on {src}")
-        objs.append(obj)
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp] + objs
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        print(r.stdout + r.stderr, file=sys.stderr)
-        raise RuntimeError("link of libcrisp.so failed")
-    os.replace(tmp, LIB)
+        objs[src] = obj
+    _link([objs[s] for s in SOURCES], LIB)
+    _link([objs[s] for s in PROBE_SOURCES], PROBE_LIB)
     return LIB
 
 
