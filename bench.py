@@ -160,6 +160,8 @@ def run_workload(torch, B, synth, wname, args, cfg_kw, compare):
     log(f"{w.name}: crisp {res['crisp']['ms_per_layer']:.2f} ms")
     if args.only_crisp:
         return res, x, dims
+    res["map_path"] = time_map_path(torch, B, x, dims, cfg, args.compare_steps)
+    log(f"{w.name}: map path proxy {res['map_path']['proxy_ms']:.3f} ms, select {res['map_path']['select_ms']:.3f} ms")
     # dense baseline
     for _ in range(args.warmup):
         B.crisp_dense_attn(dims, x.q, x.k, x.v, bufs.out)
@@ -195,6 +197,32 @@ def run_workload(torch, B, synth, wname, args, cfg_kw, compare):
         if isinstance(res[key], dict) and "ms_per_layer" in res[key] and key != "dense":
             res[key]["speedup_vs_dense"] = dense_ms / res[key]["ms_per_layer"]
     return res, x, dims
+
+
+def time_map_path(torch, B, x, dims, cfg, steps):
+    """The proxy writing the full map and selection reading it (the ABI's map
+    path, off the default chain): stage times and the map store's HBM rate."""
+    bufs = B.CrispBuffers(dims, out_dtype=torch.bfloat16, diagnostics=False, with_map=True)
+    ts = {"proxy": [], "route": [], "select": []}
+    for it in range(steps + 1):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+        e[0].record()
+        B.crisp_proxy(dims, x.q, x.k, bufs.attn_map, bufs.row_lse, bufs.partials)
+        e[1].record()
+        B.crisp_route(dims, cfg, bufs.attn_map, bufs.c_struct, bufs.route)
+        e[2].record()
+        B.crisp_select(dims, cfg, x.q, x.k, bufs.attn_map, bufs.route, bufs.blocks, bufs.workspace)
+        e[3].record()
+        torch.cuda.synchronize()
+        if it > 0:
+            for i, k in enumerate(ts):
+                ts[k].append(e[i].elapsed_time(e[i + 1]))
+    med = {k: sorted(v)[len(v) // 2] for k, v in ts.items()}
+    map_bytes = 4 * dims.block * dims.seq_len * dims.num_q_heads
+    del bufs
+    torch.cuda.empty_cache()
+    return {"proxy_ms": round(med["proxy"], 4), "route_ms": round(med["route"], 4),
+            "select_ms": round(med["select"], 4), "map_bytes": map_bytes}
 
 
 def mfma_ceiling(torch):

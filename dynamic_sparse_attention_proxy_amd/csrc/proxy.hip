@@ -66,6 +66,11 @@ template <int kPass, bool kMap, bool kMass>
 __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
   __shared__ __attribute__((aligned(1024))) __bf16 ks[kPStages][kPStep * kHeadDim];
   __shared__ float part[4][kProxyChunk / kBlock][2];  // masses per wave and key block of the chunk
+  // map path: each wave's 32 x 32 tile of the map (one key half of a step),
+  // row stride 36 floats so that the per-lane 16-byte writes of 16 rows hit
+  // distinct banks
+  constexpr int kTStride = 36;
+  __shared__ __attribute__((aligned(16))) float tbuf[kMap ? 4 * 32 * kTStride : 1];
   const int chunk = blockIdx.x, h = blockIdx.y, g = h / p.qpg;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, lg = lane >> 5;
   const int kbeg = chunk * kProxyChunk, kend = min(p.n, kbeg + kProxyChunk);
@@ -188,7 +193,12 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
           }
         }
         if (kMap) {
-          float* dst = p.amap + ((size_t)h * kBlock + row) * p.n + key0 + 32 * kb2 + 4 * lg;
+          // Through the wave's LDS tile (row l32, keys 8 q4 + 4 lg + [0, 4)),
+          // then row-major out: instruction i writes rows 8i .. 8i+7 of the
+          // wave, 128 contiguous bytes each, with non-temporal stores (the
+          // map is written once).  The wave reads back only its own writes,
+          // and LDS operations of a wave complete in order.
+          float* t = tbuf + (32 * w + l32) * kTStride + 4 * lg;
 #pragma unroll
           for (int q4 = 0; q4 < 4; ++q4) {
             f32x4 o;
@@ -196,7 +206,15 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
             o[1] = a[4 * q4 + 1];
             o[2] = a[4 * q4 + 2];
             o[3] = a[4 * q4 + 3];
-            *(f32x4*)(dst + 8 * q4) = o;
+            *(f32x4*)(t + 8 * q4) = o;
+          }
+          const int rr = lane >> 3, cc = 4 * (lane & 7);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = 8 * i + rr;
+            const f32x4 o = *(const f32x4*)(tbuf + (32 * w + r) * kTStride + cc);
+            __builtin_nontemporal_store(
+                o, (f32x4*)(p.amap + ((size_t)h * kBlock + 32 * w + r) * p.n + key0 + 32 * kb2 + cc));
           }
         }
       }
