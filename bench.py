@@ -49,6 +49,10 @@ def parse():
     ap.add_argument("--route", choices=["auto", "vs", "pe"], default="auto",
                     help="route override of the timed CRISP chain (the reported value uses auto)")
     ap.add_argument("--no-ceiling", action="store_true", help="skip the MFMA ceiling probe")
+    ap.add_argument("--sweep", action="store_true",
+                    help="length sweep instead of the benchmark line: CRISP (route auto, and forced-VS at several "
+                         "alpha) against dense from 8k to 512k on the Llama-3.1-8B shape; prints a markdown table")
+    ap.add_argument("--sweep-out", default="", help="also write the sweep as JSON to this path")
     return ap.parse_args()
 
 
@@ -310,6 +314,62 @@ def cpu_baseline(q, k, v, dims, res, cfg_kw):
             "measured_s": round(t_head + t_rows + t_att, 2)}
 
 
+SWEEP_LENGTHS = (8192, 16384, 32768, 65536, 131072, 262144, 524288)
+SWEEP_ALPHAS = (1.0, 1.25, 1.5)
+
+
+def sweep(torch, B, synth, args):
+    """CRISP vs dense across context lengths (Llama-3.1-8B shape, the 512k
+    workload's generator at each length): median of `--compare-steps` runs."""
+    base = synth.workload("llama3.1-8b-512k")
+    rows = []
+
+    def med(fn, steps):
+        for _ in range(2):
+            fn()
+        torch.cuda.synchronize()
+        ms = []
+        for _ in range(steps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record()
+            fn()
+            b.record()
+            torch.cuda.synchronize()
+            ms.append(a.elapsed_time(b))
+        return sorted(ms)[len(ms) // 2]
+
+    for n in SWEEP_LENGTHS:
+        x = synth.make_inputs(base, device="cuda", seq_len=n)
+        dims = B.make_dims(base.num_q_heads, base.num_kv_heads, n)
+        bufs = B.CrispBuffers(dims, out_dtype=torch.bfloat16)
+        N = n // 128
+        dense_tiles = base.num_q_heads * N * (N + 1) // 2
+        row = {"seq_len": n, "dense_ms": med(lambda: B.crisp_dense_attn(dims, x.q, x.k, x.v, bufs.out),
+                                             args.compare_steps)}
+        chains = [("auto", B.make_cfg())] + [(f"vs_alpha{a}", B.make_cfg(route_override=B.ROUTE_FORCE_VS, alpha=a))
+                                             for a in SWEEP_ALPHAS]
+        for name, cfg in chains:
+            t = med(lambda: B.crisp_prefill(dims, cfg, x.q, x.k, x.v, bufs, dense_below=0), args.compare_steps)
+            tiles = int(bufs.blocks["count"].sum().item())
+            row[name] = {"ms": t, "tiles": tiles, "tile_frac": tiles / dense_tiles, "speedup": row["dense_ms"] / t}
+        log(f"sweep n={n}: dense {row['dense_ms']:.3f} ms, " +
+            ", ".join(f"{nm} {row[nm]['ms']:.3f} ms" for nm, _ in chains))
+        rows.append(row)
+        del x, bufs
+        torch.cuda.empty_cache()
+    names = ["auto"] + [f"vs_alpha{a}" for a in SWEEP_ALPHAS]
+    print("| n | dense ms | " + " | ".join(f"{nm} ms (speedup, tiles)" for nm in names) + " |")
+    print("|---|---|" + "---|" * len(names))
+    for r in rows:
+        cells = [f"{r[nm]['ms']:.3f} ({r[nm]['speedup']:.2f}x, {100 * r[nm]['tile_frac']:.1f}%)" for nm in names]
+        print(f"| {r['seq_len']} | {r['dense_ms']:.3f} | " + " | ".join(cells) + " |")
+    if args.sweep_out:
+        with open(args.sweep_out, "w") as f:
+            json.dump(rows, f, indent=1)
+    return rows
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -323,6 +383,9 @@ def main():
 
     B.lib()
     torch.cuda.set_device(0)
+    if args.sweep:
+        sweep(torch, B, synth, args)
+        return
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
         dst = torch.empty_like(src)

@@ -177,3 +177,30 @@ def test_row_map_is_a_bijection(tmp_path_factory, hq, hkv, nblk):
                         "-o", str(exe)], check=True, capture_output=True)
     r = subprocess.run([str(exe), str(hq), str(hkv), str(nblk)], capture_output=True, text=True)
     assert r.returncode == 0, r.stdout
+
+
+def test_prefill_context_length_gate(monkeypatch):
+    """crisp_prefill runs the dense kernel alone below DENSE_BELOW tokens and
+    the four-call chain from there on; dense_below=0 always runs the chain
+    and the gamma comparison chain is never gated."""
+    import types
+
+    calls = []
+    for name in ("crisp_proxy", "crisp_route", "crisp_select", "crisp_select_gamma", "crisp_sparse_attn",
+                 "crisp_dense_attn"):
+        monkeypatch.setattr(B, name, lambda *a, _n=name, **kw: calls.append(_n))
+    bufs = types.SimpleNamespace(out=None, lse=None, attn_map=None, block_mass=None, row_lse=None, partials=None,
+                                 c_struct=None, route=None, blocks={"count": None, "idx": None}, workspace=None)
+    cfg = B.make_cfg()
+    chain = ["crisp_proxy", "crisp_route", "crisp_select", "crisp_sparse_attn"]
+    for n, expect in ((B.DENSE_BELOW // 2, ["crisp_dense_attn"]), (B.DENSE_BELOW - 128, ["crisp_dense_attn"]),
+                      (B.DENSE_BELOW, chain), (4 * B.DENSE_BELOW, chain)):
+        calls.clear()
+        B.crisp_prefill(B.make_dims(32, 8, n), cfg, None, None, None, bufs)
+        assert calls == expect, (n, calls)
+    calls.clear()
+    B.crisp_prefill(B.make_dims(32, 8, 1024), cfg, None, None, None, bufs, dense_below=0)
+    assert calls == chain
+    calls.clear()
+    B.crisp_prefill(B.make_dims(32, 8, 1024), cfg, None, None, None, bufs, gamma=0.95)
+    assert calls == ["crisp_proxy", "crisp_route", "crisp_select_gamma", "crisp_sparse_attn"]

@@ -31,7 +31,7 @@ def _run(x, cfg, gamma=None):
     hq, hkv, n = x.q.shape[0], x.k.shape[0], x.q.shape[1]
     dims = B.make_dims(hq, hkv, n)
     bufs = B.CrispBuffers(dims, out_dtype=torch.float32)
-    B.crisp_prefill(dims, cfg, x.q, x.k, x.v, bufs, gamma=gamma)
+    B.crisp_prefill(dims, cfg, x.q, x.k, x.v, bufs, gamma=gamma, dense_below=0)
     torch.cuda.synchronize()
     return dims, bufs
 

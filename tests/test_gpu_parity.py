@@ -52,7 +52,7 @@ def run_chain(x, cfg, gamma=None, out_dtype=torch.float32, use_map=False):
     hq, hkv, n = x.q.shape[0], x.k.shape[0], x.q.shape[1]
     dims = B.make_dims(hq, hkv, n)
     bufs = B.CrispBuffers(dims, out_dtype=out_dtype, with_map=True)
-    B.crisp_prefill(dims, cfg, x.q, x.k, x.v, bufs, gamma=gamma, use_map=use_map)
+    B.crisp_prefill(dims, cfg, x.q, x.k, x.v, bufs, gamma=gamma, use_map=use_map, dense_below=0)
     torch.cuda.synchronize()
     return dims, bufs
 
@@ -342,6 +342,20 @@ def test_map_and_block_mass_paths_agree(override):
                 assert abs(xs[h, b] - fl[h]) <= 1e-3 * fl[h], (key, h, b)
     else:
         assert torch.equal(bm.blocks["count"], bp.blocks["count"])
+
+
+def test_gated_short_layer_is_the_dense_kernel():
+    """Below the context-length gate crisp_prefill runs the dense kernel."""
+    n = B.DENSE_BELOW // 2
+    w = synth.custom(4, 2, n, seed=21, needles=2)
+    x = synth.make_inputs(w, device="cuda")
+    dims = B.make_dims(4, 2, n)
+    bufs = B.CrispBuffers(dims, out_dtype=torch.float32)
+    B.crisp_prefill(dims, B.make_cfg(), x.q, x.k, x.v, bufs)
+    dense = torch.empty_like(bufs.out)
+    B.crisp_dense_attn(dims, x.q, x.k, x.v, dense)
+    torch.cuda.synchronize()
+    assert torch.equal(bufs.out, dense)
 
 
 def test_chain_is_deterministic():
