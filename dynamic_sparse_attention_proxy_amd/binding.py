@@ -231,10 +231,13 @@ class CrispBuffers:
         self.lse = torch.empty((hq, n), dtype=f32, device=dev)
 
 
-# Context-length gate: below this many tokens the route-auto chain does not
-# recover the cost of proxy, routing and selection on MI355X (measured
-# Llama-3.1-8B-shaped layers: 0.90x of dense at 8k, 1.02x at 16k, 1.00-1.04x
-# from 32k to 512k), so a layer this short runs the dense kernel instead.
+# Context-length gate (ai.info summary: "Main Findings" puts the crossover
+# where sparse prefill starts to pay between 8K and 64K, and "Why This
+# Matters" suggests gating sparse prefill on a context-length threshold).
+# Below this many tokens the route-auto chain does not recover the cost of
+# proxy, routing and selection on MI355X (measured Llama-3.1-8B-shaped
+# layers: 0.90x of dense at 8k, 1.02x at 16k, 1.00-1.04x from 32k to 512k),
+# so a layer this short runs the dense kernel instead.
 DENSE_BELOW = 16384
 
 
