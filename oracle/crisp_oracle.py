@@ -21,7 +21,7 @@ exact values of the bf16 tensors the GPU sees.  Array conventions:
   B  : block size (128); N = n / B blocks.
 
 Where the pages leave a step open, the reading used here is named in the
-function's docstring with its tag (R1..R22); the same tags are listed with
+function's docstring with its tag (R1..R25); the same tags are listed with
 their justification in the repository's design notes.
 
 Parity pins: every function below is pinned by tests that do not reuse its
@@ -440,3 +440,54 @@ def run_layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, cfg: OracleConfig,
             hr.attn = attention_rows(q[h], k[g], v[g], hr.lists, scale, qbs, cfg.block)
         res[h] = hr
     return res
+
+
+# ---------------------------------------------------------------------------
+# Comparison: FlexPrefill's routing signal, the one C_struct replaces
+# (ai.info "Key Contributions" items 1 and 2: C_struct drops the pooled
+# matmul and the KL divergence that JSD routing needs, and reproduces its
+# decisions; "Methodology in Plain English": an extra pooled attention
+# estimate is compared by Jensen-Shannon divergence with the per-query
+# attention to decide whether a head is concentrated).  Readings R23-R25.
+# ---------------------------------------------------------------------------
+
+
+def jsd_estimate(q_last: np.ndarray, k: np.ndarray, scale: float, block: int = 128) -> np.ndarray:
+    """Pooled attention estimate of the last query block over the N key
+    blocks (reading R23): softmax over kb of scale * <qbar, kbar[kb]>, with
+    qbar the mean of the B proxy query rows and kbar[kb] the mean of the
+    keys of block kb.  Every key block is visible to the last query block,
+    so no block is masked."""
+    qbar = q_last.mean(axis=0)
+    kbar = pe_pool(k, block)
+    e = scale * (kbar @ qbar)
+    p = np.exp(e - e.max())
+    return p / p.sum()
+
+
+def jsd_actual(A: np.ndarray, block: int = 128) -> np.ndarray:
+    """The per-query attention of the proxy rows, summed over each key block
+    and averaged over the rows: a distribution over the N key blocks."""
+    B, n = A.shape
+    return A.reshape(B, n // block, block).sum(axis=(0, 2)) / B
+
+
+def js_divergence(p: np.ndarray, q: np.ndarray) -> float:
+    """Jensen-Shannon divergence in nats: the mean of KL(p || m) and
+    KL(q || m), m the midpoint of p and q, with 0 log 0 = 0."""
+    m = 0.5 * (p + q)
+
+    def kl(a):
+        nz = a > 0
+        return float(np.sum(a[nz] * np.log(a[nz] / m[nz])))
+
+    return 0.5 * kl(p) + 0.5 * kl(q)
+
+
+def jsd_route(p_est: np.ndarray, a_bar: np.ndarray, tau_jsd: float):
+    """Jensen-Shannon distance sqrt(JSD) between the block-summed proxy and
+    the pooled estimate, and the route it implies (reading R24): a head whose
+    attention the pooled estimate misses by at least tau_jsd is concentrated
+    and goes Vertical-Slash; otherwise Pooled-Estimation.  Ties go to VS."""
+    d = math.sqrt(max(js_divergence(a_bar, p_est), 0.0))
+    return d, (ROUTE_VS if d >= tau_jsd else ROUTE_PE)

@@ -567,3 +567,122 @@ def test_structured_inputs_gamma_grows_noise_floor_flat():
     assert all(s == [0, 5, 10] for s in nf_v)
     assert g_v[0] < g_v[1] < g_v[2]
     assert g_v[2] / g_v[0] > 3.0  # roughly proportional to n
+
+
+# --------------------------------------------------------------------------
+# JSD routing signal (the comparison C_struct replaces)
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_js_divergence_matches_scipy_distance(seed):
+    from scipy.spatial.distance import jensenshannon
+
+    r = _rng(seed)
+    for n in (2, 7, 300):
+        p = r.random(n)
+        q = r.random(n) ** 4
+        q[r.random(n) < 0.2] = 0.0  # zero entries exercise 0 log 0
+        q[0] = 0.5
+        p /= p.sum()
+        q /= q.sum()
+        d = jensenshannon(p, q)  # natural log by default
+        assert math.isclose(O.js_divergence(p, q), d * d, rel_tol=1e-12, abs_tol=1e-15)
+
+
+def test_js_divergence_two_point_entropy_form():
+    # JSD = H(midpoint) - (H(p) + H(q)) / 2 with the binary entropy H
+    def h(a):
+        return -sum(x * math.log(x) for x in (a, 1 - a) if x > 0)
+
+    for a, b in [(0.1, 0.9), (0.5, 0.5), (0.0, 1.0), (0.3, 0.31), (1.0, 0.25)]:
+        p = np.array([a, 1 - a])
+        q = np.array([b, 1 - b])
+        want = h((a + b) / 2) - (h(a) + h(b)) / 2
+        assert math.isclose(O.js_divergence(p, q), want, rel_tol=1e-12, abs_tol=1e-15)
+
+
+def test_js_divergence_limits():
+    r = _rng(5)
+    p = r.random(50)
+    p /= p.sum()
+    q = r.random(50)
+    q /= q.sum()
+    assert O.js_divergence(p, p) == 0.0
+    assert O.js_divergence(p, q) == pytest.approx(O.js_divergence(q, p), rel=1e-14)
+    # disjoint supports reach the bound ln 2
+    a = np.array([0.2, 0.8, 0.0, 0.0])
+    b = np.array([0.0, 0.0, 0.6, 0.4])
+    assert O.js_divergence(a, b) == pytest.approx(math.log(2.0), rel=1e-15)
+    assert 0.0 < O.js_divergence(p, q) < math.log(2.0)
+
+
+def test_jsd_actual_is_row_mean_of_block_sums():
+    r = _rng(7)
+    n, Bq = 4 * B, B
+    A = r.random((Bq, n))
+    A /= A.sum(axis=1, keepdims=True)
+    got = O.jsd_actual(A, B)
+    assert got.sum() == pytest.approx(1.0, abs=1e-12)
+    for kb in range(n // B):
+        hand = 0.0
+        for row in range(Bq):
+            for j in range(kb * B, (kb + 1) * B):
+                hand += A[row, j]
+        assert got[kb] == pytest.approx(hand / Bq, rel=1e-12)
+
+
+def test_jsd_estimate_brute_force():
+    r = _rng(8)
+    n, d = 3 * B, 16
+    ql = r.standard_normal((B, d))
+    k = r.standard_normal((n, d))
+    scale = 0.3
+    qbar = [sum(ql[i, c] for i in range(B)) / B for c in range(d)]
+    logits = []
+    for kb in range(n // B):
+        kbar = [sum(k[j, c] for j in range(kb * B, (kb + 1) * B)) / B for c in range(d)]
+        logits.append(scale * sum(qbar[c] * kbar[c] for c in range(d)))
+    z = sum(math.exp(x) for x in logits)
+    want = [math.exp(x) / z for x in logits]
+    np.testing.assert_allclose(O.jsd_estimate(ql, k, scale, B), want, rtol=1e-12)
+
+
+def test_pooled_estimate_exact_for_block_constant_keys():
+    # With one query vector for every proxy row and keys constant within each
+    # block, unmasked per-row attention summed per block equals the pooled
+    # softmax: the divergence vanishes.  A wrong pooling axis, a dropped
+    # scale or a per-row normalisation error breaks the equality.
+    r = _rng(9)
+    N, d = 5, 8
+    kb_vecs = r.standard_normal((N, d))
+    k = np.repeat(kb_vecs, B, axis=0)
+    q1 = r.standard_normal(d)
+    ql = np.tile(q1, (B, 1))
+    scale = 0.7
+    s = scale * (ql @ k.T)
+    A = np.exp(s - s.max(axis=1, keepdims=True))
+    A /= A.sum(axis=1, keepdims=True)
+    p_est = O.jsd_estimate(ql, k, scale, B)
+    a_bar = O.jsd_actual(A, B)
+    np.testing.assert_allclose(p_est, a_bar, rtol=1e-12)
+    assert O.js_divergence(a_bar, p_est) == pytest.approx(0.0, abs=1e-15)
+    # scaling the query changes the estimate unless the scale goes with it
+    assert not np.allclose(O.jsd_estimate(ql, k, 2 * scale, B), a_bar, rtol=1e-6)
+
+
+def test_jsd_route_direction_and_tie():
+    u = np.full(8, 1.0 / 8)
+    one_hot = np.zeros(8)
+    one_hot[0] = 1.0
+    # a head whose mass sits on one block, against a flat estimate: VS
+    d, rt = O.jsd_route(u, one_hot, 0.1)
+    # midpoint: 9/16 on block 0, 1/16 elsewhere
+    want = math.sqrt(0.5 * math.log(16 / 9) + 0.5 * (1 / 8) * math.log(2 / 9) + 0.5 * (7 / 8) * math.log(2.0))
+    assert d == pytest.approx(want, rel=1e-12)
+    assert rt == O.ROUTE_VS
+    # the estimate matches the attention: PE
+    d0, rt0 = O.jsd_route(u, u, 0.1)
+    assert d0 == 0.0 and rt0 == O.ROUTE_PE
+    # a distance equal to the threshold goes VS
+    assert O.jsd_route(u, one_hot, d)[1] == O.ROUTE_VS
