@@ -53,6 +53,10 @@ def parse():
                     help="length sweep instead of the benchmark line: CRISP (route auto, and forced-VS at several "
                          "alpha) against dense from 8k to 512k on the Llama-3.1-8B shape; prints a markdown table")
     ap.add_argument("--sweep-out", default="", help="also write the sweep as JSON to this path")
+    ap.add_argument("--agreement", action="store_true",
+                    help="C_struct vs JSD routing agreement and routing cost on the five synthetic layers")
+    ap.add_argument("--agreement-out", default="", help="also write the agreement report as JSON to this path")
+    ap.add_argument("--tau-jsd", type=float, default=0.1, help="JSD distance threshold of the agreement report")
     return ap.parse_args()
 
 
@@ -370,6 +374,140 @@ def sweep(torch, B, synth, args):
     return rows
 
 
+AGREEMENT_WORKLOADS = (0, 1, 2, 3, 4, "family-32k", "family-512k")
+AGREEMENT_TAUS = (0.2, 0.5)
+AGREEMENT_TAU_JSDS = (0.1, 0.2, 0.3, 0.4, 0.5)
+
+
+def _med_ms(torch, fn, steps):
+    for _ in range(2):
+        fn()
+    torch.cuda.synchronize()
+    ms = []
+    for _ in range(steps):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record()
+        fn()
+        b.record()
+        torch.cuda.synchronize()
+        ms.append(a.elapsed_time(b))
+    return sorted(ms)[len(ms) // 2]
+
+
+def _ranks(xs):
+    order = sorted(range(len(xs)), key=lambda i: xs[i])
+    r = [0.0] * len(xs)
+    i = 0
+    while i < len(order):
+        j = i
+        while j + 1 < len(order) and xs[order[j + 1]] == xs[order[i]]:
+            j += 1
+        for t in range(i, j + 1):
+            r[order[t]] = (i + j) / 2.0
+        i = j + 1
+    return r
+
+
+def _spearman(a, b):
+    if len(a) < 3:
+        return None
+    ra, rb = _ranks(a), _ranks(b)
+    ma, mb = sum(ra) / len(ra), sum(rb) / len(rb)
+    num = sum((x - ma) * (y - mb) for x, y in zip(ra, rb))
+    den = math.sqrt(sum((x - ma) ** 2 for x in ra) * sum((y - mb) ** 2 for y in rb))
+    return num / den if den > 0 else None
+
+
+def agreement_stats(c, d, tau, tau_jsds):
+    """Share of heads on which 'C_struct >= tau' and 'JSD distance >= t'
+    agree, for each t in tau_jsds and for the best t over all thresholds."""
+    vs_c = [x >= tau for x in c]
+    h = len(c)
+    at = {t: sum(int((dd >= t) == v) for dd, v in zip(d, vs_c)) / h for t in tau_jsds}
+    best, best_t = -1.0, None
+    for t in sorted(set(d)) + [float("inf")]:
+        acc = sum(int((dd >= t) == v) for dd, v in zip(d, vs_c)) / h
+        if acc > best:
+            best, best_t = acc, t
+    return {"tau": tau, "vs_heads_cstruct": int(sum(vs_c)), "agreement_at": at, "best_agreement": best,
+            "best_tau_jsd": None if best_t == float("inf") else best_t}
+
+
+def agreement(torch, B, synth, args):
+    """Routing agreement between C_struct and the JSD signal on every head of
+    the five synthetic layers and of the graded-structure family, and the
+    cost of each routing step on top of the proxy (median of --steps runs)."""
+    rows = []
+    for wid in AGREEMENT_WORKLOADS:
+        if isinstance(wid, int):
+            x = synth.make_inputs(synth.workload(wid), device="cuda")
+        else:
+            x = synth.make_routing_family(seq_len=32768 if wid == "family-32k" else 524288, device="cuda")
+        w = x.workload
+        hq, hkv, n = w.num_q_heads, w.num_kv_heads, w.seq_len
+        dims = B.make_dims(hq, hkv, n)
+        cfg = B.make_cfg()
+        N = n // 128
+        mass = torch.empty((2, hq, N), dtype=torch.float32, device="cuda")
+        partials = torch.empty(B.crisp_proxy_scratch_bytes(dims), dtype=torch.uint8, device="cuda")
+        cs = torch.empty(hq, dtype=torch.float32, device="cuda")
+        rt = torch.empty(hq, dtype=torch.int32, device="cuda")
+        ws = torch.empty(B.crisp_route_jsd_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+        jd = torch.empty(hq, dtype=torch.float32, device="cuda")
+        jr = torch.empty(hq, dtype=torch.int32, device="cuda")
+
+        def proxy():
+            B.crisp_proxy(dims, x.q, x.k, None, partials=partials, block_mass=mass)
+
+        def route_c():
+            B.crisp_route(dims, cfg, None, cs, rt, block_mass=mass)
+
+        def route_j():
+            B.crisp_route_jsd(dims, args.tau_jsd, x.q, x.k, mass, jd, jr, ws)
+
+        t_proxy = _med_ms(torch, proxy, args.steps)
+        t_c = _med_ms(torch, route_c, args.steps)
+        t_j = _med_ms(torch, route_j, args.steps)
+        torch.cuda.synchronize()
+        c, d = cs.cpu().tolist(), jd.cpu().tolist()
+        k_bytes = hkv * n * 128 * 2
+        row = {"workload": w.name, "heads": hq, "seq_len": n,
+               "stats": [agreement_stats(c, d, tau, AGREEMENT_TAU_JSDS) for tau in AGREEMENT_TAUS],
+               "spearman": _spearman(c, d),
+               "proxy_ms": t_proxy, "route_cstruct_ms": t_c, "route_jsd_ms": t_j,
+               "route_jsd_k_bytes": k_bytes, "route_jsd_gbs": k_bytes / (t_j * 1e-3) / 1e9,
+               "c_struct": c, "js_dist": d}
+        log(f"agreement {w.name}: C_struct in [{min(c):.3f}, {max(c):.3f}], JSD distance in "
+            f"[{min(d):.3f}, {max(d):.3f}]; proxy {t_proxy:.3f} ms, route C {t_c * 1e3:.1f} us, "
+            f"route JSD {t_j * 1e3:.1f} us")
+        rows.append(row)
+        del x
+        torch.cuda.empty_cache()
+    for si, tau in enumerate(AGREEMENT_TAUS):
+        print(f"\nC_struct tau = {tau}: share of heads routed alike, by JSD-distance threshold\n")
+        print("| workload | heads | VS by C_struct | " + " | ".join(f"tau_jsd {t}" for t in AGREEMENT_TAU_JSDS) +
+              " | best (at tau_jsd) | Spearman(C, JSD) |")
+        print("|---|---|---|" + "---|" * len(AGREEMENT_TAU_JSDS) + "---|---|")
+        for r in rows:
+            st = r["stats"][si]
+            bt = "-" if st["best_tau_jsd"] is None else f"{st['best_tau_jsd']:.3f}"
+            sp = "-" if r["spearman"] is None else f"{r['spearman']:.3f}"
+            print(f"| {r['workload']} | {r['heads']} | {st['vs_heads_cstruct']} | " +
+                  " | ".join(f"{100 * st['agreement_at'][t]:.1f}%" for t in AGREEMENT_TAU_JSDS) +
+                  f" | {100 * st['best_agreement']:.1f}% ({bt}) | {sp} |")
+    print("\nRouting cost on top of the proxy (median, ms)\n")
+    print("| workload | proxy (block masses) | route from C_struct | route from JSD | JSD K read GB/s |")
+    print("|---|---|---|---|---|")
+    for r in rows:
+        print(f"| {r['workload']} | {r['proxy_ms']:.3f} | {r['route_cstruct_ms']:.4f} | {r['route_jsd_ms']:.4f} | "
+              f"{r['route_jsd_gbs']:.0f} |")
+    if args.agreement_out:
+        with open(args.agreement_out, "w") as f:
+            json.dump({"taus": AGREEMENT_TAUS, "tau_jsds": AGREEMENT_TAU_JSDS, "rows": rows}, f, indent=1)
+    return rows
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -385,6 +523,9 @@ def main():
     torch.cuda.set_device(0)
     if args.sweep:
         sweep(torch, B, synth, args)
+        return
+    if args.agreement:
+        agreement(torch, B, synth, args)
         return
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")

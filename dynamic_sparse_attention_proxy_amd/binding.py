@@ -61,6 +61,9 @@ _SIGS = {
     "crisp_proxy": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "crisp_proxy_scratch_bytes": (ctypes.c_size_t, [ctypes.POINTER(crisp_dims)]),
     "crisp_route": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), _P, _P, _P, _P, _P]),
+    "crisp_route_jsd": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.c_float, _P, _P, _P, _P, _P, _P, _P,
+                                       ctypes.c_size_t, _P]),
+    "crisp_route_jsd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(crisp_dims)]),
     "crisp_select": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), _P, _P, _P, _P, _P,
                                     ctypes.POINTER(crisp_blocks), _P, ctypes.c_size_t, _P]),
     "crisp_select_gamma": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), ctypes.c_float, _P,
@@ -148,6 +151,18 @@ def crisp_proxy(dims: crisp_dims, q, k, attn_map, row_lse=None, partials=None, s
 def crisp_route(dims: crisp_dims, cfg: crisp_cfg, attn_map, c_struct, route, stream=None, block_mass=None):
     _check("crisp_route", lib().crisp_route(ctypes.byref(dims), ctypes.byref(cfg), _ptr(attn_map), _ptr(block_mass),
                                             _ptr(c_struct), _ptr(route), _stream(stream)))
+
+
+def crisp_route_jsd_workspace_bytes(dims: crisp_dims) -> int:
+    return int(lib().crisp_route_jsd_workspace_bytes(ctypes.byref(dims)))
+
+
+def crisp_route_jsd(dims: crisp_dims, tau_jsd: float, q, k, block_mass, js_dist, route, workspace, estimate=None,
+                    stream=None):
+    nbytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check("crisp_route_jsd", lib().crisp_route_jsd(ctypes.byref(dims), ctypes.c_float(tau_jsd), _ptr(q), _ptr(k),
+                                                    _ptr(block_mass), _ptr(js_dist), _ptr(route), _ptr(estimate),
+                                                    _ptr(workspace), nbytes, _stream(stream)))
 
 
 def _blocks(out: dict) -> crisp_blocks:

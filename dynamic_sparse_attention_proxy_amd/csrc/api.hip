@@ -181,6 +181,30 @@ crisp_status crisp_route(const crisp_dims* dims, const crisp_cfg* cfg, const flo
                                       (hipStream_t)stream));
 }
 
+size_t crisp_route_jsd_workspace_bytes(const crisp_dims* dims) {
+  if (check_dims(dims) != CRISP_OK) return 0;
+  return crisp::jsd_workspace_bytes(dims->num_q_heads, dims->seq_len);
+}
+
+crisp_status crisp_route_jsd(const crisp_dims* dims, float tau_jsd, const void* q, const void* k,
+                             const float* block_mass, float* js_dist, int32_t* route, float* estimate,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  CRISP_TRY(check_dims(dims));
+  if (!(tau_jsd >= 0.f) || !isfinite(tau_jsd)) return CRISP_ERR_PARAM;
+  CRISP_TRY(check_ptr(q));
+  CRISP_TRY(check_ptr(k));
+  CRISP_TRY(check_ptr(block_mass));
+  CRISP_TRY(check_ptr(js_dist));
+  CRISP_TRY(check_ptr(route));
+  CRISP_TRY(check_opt(estimate));
+  CRISP_TRY(check_ptr(workspace));
+  if (workspace_bytes < crisp::jsd_workspace_bytes(dims->num_q_heads, dims->seq_len)) return CRISP_ERR_WORKSPACE;
+  CRISP_TRY(check_device());
+  return launched(crisp::launch_route_jsd((const __bf16*)q, (const __bf16*)k, block_mass, js_dist, route, estimate,
+                                          workspace, dims->num_q_heads, dims->num_kv_heads, dims->seq_len,
+                                          dims->scale, tau_jsd, (hipStream_t)stream));
+}
+
 crisp_status crisp_select(const crisp_dims* dims, const crisp_cfg* cfg, const void* q, const void* k,
                           const float* attn_map, const float* block_mass, const int32_t* route,
                           const crisp_blocks* out, void* workspace, size_t workspace_bytes, void* stream) {
@@ -231,6 +255,6 @@ const char* crisp_status_string(crisp_status status) {
   return "unknown status";
 }
 
-int32_t crisp_abi_version(void) { return (2 << 16) | 0; }
+int32_t crisp_abi_version(void) { return (2 << 16) | 1; }
 
 }  // extern "C"

@@ -53,6 +53,12 @@ hipError_t launch_select(const __bf16* q, const __bf16* k, const float* amap, co
                          float alpha, float gamma_pe, int kmin, int nf_stat, bool use_gamma, float gamma,
                          hipStream_t stream);
 
+// JSD routing signal: workspace holds qbar [Hq][128] and the logits [Hq][N].
+size_t jsd_workspace_bytes(int hq, int n);
+hipError_t launch_route_jsd(const __bf16* q, const __bf16* k, const float* mass, float* js_dist, int32_t* route,
+                            float* estimate, void* workspace, int hq, int hkv, int n, float scale, float tau_jsd,
+                            hipStream_t stream);
+
 hipError_t launch_attention(const __bf16* q, const __bf16* k, const __bf16* v, const int32_t* count,
                             const int32_t* idx, void* out, int out_fp32, float* lse, int hq, int hkv, int n,
                             float scale, bool dense, hipStream_t stream);

@@ -160,3 +160,75 @@ def make_inputs(w: Workload, device="cpu", seq_len: Optional[int] = None) -> Inp
         k[g] = _rope(kg.double(), cos, sin).to(torch.bfloat16)
         kraw[g] = None
     return Inputs(q, k, v, w, sink_heads, needle_pos)
+
+
+# ---------------------------------------------------------------------------
+# Graded-structure family for the routing-agreement measurement.
+# ---------------------------------------------------------------------------
+
+ROUTING_FAMILY_SINK_STEP = 2.5   # query coupling to the sink direction, per grid step
+ROUTING_FAMILY_LOCAL_STEP = 0.35 # query coupling to the local direction, per grid step
+
+
+def make_routing_family(seq_len: int = 32768, num_q_heads: int = 32, num_kv_heads: int = 8, seed: int = 5,
+                        rope_theta: float = 5e5, sink_k_boost: float = 8.0, local_norm: float = 12.0,
+                        device="cpu") -> Inputs:
+    """Heads whose sink and recency structure is graded, so that routing
+    signals cross their thresholds (Llama-3.1-8B attention shape).
+
+    Q, K, V are iid N(0,1) from one generator seeded with `seed` (Q per query
+    head, K per KV head, V per KV head, then per KV group: the sink direction
+    u and the local direction c).  Per KV group g:
+      * u is a random unit vector on the four lowest-frequency rotary pairs,
+        which barely rotate over the sequence, so a sink coupling keeps its
+        strength at every distance; keys 0..3 get + sink_k_boost * u;
+      * c is a random vector of norm local_norm on the sixteen
+        highest-frequency rotary pairs; every key gets + c, and after RoPE a
+        query carrying c scores keys at small offsets highest (a recency
+        window), the product decaying within about a hundred positions.
+    Query head h = g * qpg + t gets + beta_h * u + lambda_h * c on every row,
+    beta_h = 2.5 * (h mod 8) and lambda_h = 0.35 * (h div 8 mod 4): 32 heads
+    span an 8 x 4 grid from structureless to sink- and recency-dominated.
+    RoPE is applied after the additions, as in make_inputs.
+    """
+    n, d = seq_len, 128
+    Hq, Hkv = num_q_heads, num_kv_heads
+    qpg = Hq // Hkv
+    half = d // 2
+    dev = torch.device(device)
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(seed)
+    q = torch.empty((Hq, n, d), dtype=torch.bfloat16, device=dev)
+    k = torch.empty((Hkv, n, d), dtype=torch.bfloat16, device=dev)
+    v = torch.empty((Hkv, n, d), dtype=torch.bfloat16, device=dev)
+    qraw = [torch.randn((n, d), generator=gen, device=dev, dtype=torch.float32) for _ in range(Hq)]
+    kraw = [torch.randn((n, d), generator=gen, device=dev, dtype=torch.float32) for _ in range(Hkv)]
+    for g in range(Hkv):
+        v[g] = torch.randn((n, d), generator=gen, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    low = torch.tensor([p for p in range(half - 4, half)] + [p + half for p in range(half - 4, half)], device=dev)
+    high = torch.tensor(list(range(16)) + [p + half for p in range(16)], device=dev)
+    cos, sin = _rope_tables(n, d, rope_theta, dev)
+    sink_heads = []
+    for g in range(Hkv):
+        u = torch.zeros(d, device=dev, dtype=torch.float32)
+        u[low] = torch.randn((low.numel(),), generator=gen, device=dev, dtype=torch.float32)
+        u = _unit(u)
+        c = torch.zeros(d, device=dev, dtype=torch.float32)
+        c[high] = torch.randn((high.numel(),), generator=gen, device=dev, dtype=torch.float32)
+        c = local_norm * _unit(c)
+        kg = kraw[g]
+        kg[0:4] += sink_k_boost * u
+        kg += c
+        for t in range(qpg):
+            h = g * qpg + t
+            beta = ROUTING_FAMILY_SINK_STEP * (h % 8)
+            lam = ROUTING_FAMILY_LOCAL_STEP * ((h // 8) % 4)
+            if beta > 0:
+                sink_heads.append(h)
+            qraw[h] += beta * u + lam * c
+            q[h] = _rope(qraw[h].double(), cos, sin).to(torch.bfloat16)
+            qraw[h] = None
+        k[g] = _rope(kg.double(), cos, sin).to(torch.bfloat16)
+        kraw[g] = None
+    w = Workload(f"routing-family-{Hq}x{Hkv}-{n}", Hq, Hkv, n, d, seed, rope_theta, 0.0, 0)
+    return Inputs(q, k, v, w, sink_heads, {})

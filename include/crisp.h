@@ -205,6 +205,31 @@ CRISP_API crisp_status crisp_sparse_attn(const crisp_dims* dims, const void* q, 
 CRISP_API crisp_status crisp_dense_attn(const crisp_dims* dims, const void* q, const void* k, const void* v, void* out,
                               int32_t out_is_fp32, float* lse, void* stream);
 
+/* Comparison routing signal - FlexPrefill's Jensen-Shannon routing, the one
+ * C_struct replaces (ai.info summary, "Key Contributions" items 1 and 2:
+ * C_struct drops its pooled matmul and KL divergence and reproduces its
+ * decisions; "Methodology in Plain English": a pooled attention estimate is
+ * compared with the per-query attention to decide whether a head is
+ * concentrated).  The pages give no formula; this computes, per query head h
+ * of KV group g:
+ *   qbar       = mean of q[h] rows n-128 .. n-1 (the proxy rows)
+ *   kbar[kb]   = mean of k[g] rows 128kb .. 128kb+127
+ *   est[kb]    = softmax over all N key blocks of scale * qbar . kbar[kb]
+ *   a[kb]      = (block_mass[0][h][kb] + block_mass[1][h][kb]) / 128, the
+ *                proxy map summed per key block and averaged over its rows
+ *   js_dist[h] = sqrt(JSD(a, est)), natural log (0 .. sqrt(ln 2))
+ *   route[h]   = CRISP_ROUTE_VS when js_dist >= tau_jsd, else CRISP_ROUTE_PE.
+ * block_mass: [2][Hq][N] from crisp_proxy.  js_dist [Hq] fp32, route [Hq]
+ * int32; estimate (optional, [Hq][N] fp32) receives est.  tau_jsd >= 0,
+ * finite (CRISP_ERR_PARAM otherwise).  `workspace` must hold
+ * crisp_route_jsd_workspace_bytes(dims) bytes of device memory.  Reads all
+ * of K once: this is the extra pass C_struct does without. */
+CRISP_API crisp_status crisp_route_jsd(const crisp_dims* dims, float tau_jsd, const void* q, const void* k,
+                             const float* block_mass, float* js_dist, int32_t* route, float* estimate,
+                             void* workspace, size_t workspace_bytes, void* stream);
+
+CRISP_API size_t crisp_route_jsd_workspace_bytes(const crisp_dims* dims);
+
 /* Static description of a status code. */
 CRISP_API const char* crisp_status_string(crisp_status status);
 

@@ -8,6 +8,12 @@ Tolerances (applied element by element):
     gamma cut); a gamma prefix may differ in length by one when the oracle's
     running sum crosses gamma within 1e-3 relative;
   * attention: max-abs 1e-2 and mean-abs 1e-3 against fp64, on identical lists.
+  * JSD routing signal: the pooled estimate 1e-4 relative per key block
+    (fp32 logits, errors of order 1e-6 in the exponent); the divergence
+    JSD = dist^2 within 2e-6 absolute plus 1e-4 relative (the kernel reads
+    the block masses, each within about 1e-5 relative of the oracle's, and
+    JSD moves by at most ln(2)/2 per unit of mass moved); the route as
+    above, with the distance in place of C_struct.
 """
 from __future__ import annotations
 
@@ -23,6 +29,9 @@ REL_SEL = 1e-3
 REL_CSTRUCT = 1e-4
 ATTN_MAXABS = 1e-2
 ATTN_MEANABS = 1e-3
+REL_JSD_EST = 1e-4
+JSD_ABS = 2e-6
+JSD_REL = 1e-4
 
 
 def to64(t: torch.Tensor) -> np.ndarray:

@@ -26,7 +26,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 11
+    assert len(names) == 13
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -204,3 +204,31 @@ def test_prefill_context_length_gate(monkeypatch):
     calls.clear()
     B.crisp_prefill(B.make_dims(32, 8, 1024), cfg, None, None, None, bufs, gamma=0.95)
     assert calls == ["crisp_proxy", "crisp_route", "crisp_select_gamma", "crisp_sparse_attn"]
+
+
+def test_route_jsd_errors():
+    """The JSD routing signal validates like the other calls: a finite,
+    non-negative threshold, every required pointer, an aligned optional
+    estimate and a large enough workspace; then the device check (6)."""
+    dims = B.make_dims(4, 2, 1024)
+    lib = B.lib()
+    ws = B.crisp_route_jsd_workspace_bytes(dims)
+    assert ws >= 4 * 128 * 4 + 4 * 8 * 4
+    assert B.crisp_route_jsd_workspace_bytes(B.make_dims(4, 2, 1000)) == 0
+
+    def call(tau=0.1, q=P16, k=P16, mass=P16, dist=P16, route=P16, est=None, w=P16, wb=ws):
+        return lib.crisp_route_jsd(ctypes.byref(dims), tau, q, k, mass, dist, route, est, w, wb, None)
+
+    assert call() == 6
+    assert call(est=P16) == 6
+    assert call(tau=-0.01) == 3
+    assert call(tau=float("nan")) == 3
+    assert call(tau=float("inf")) == 3
+    assert call(mass=None) == 1
+    assert call(k=None) == 1
+    assert call(route=None) == 1
+    assert call(dist=P8) == 4
+    assert call(est=P8) == 4
+    assert call(wb=ws - 4) == 5
+    bad = B.crisp_dims(4, 2, 1000, 128, 128, 0.088)
+    assert lib.crisp_route_jsd(ctypes.byref(bad), 0.1, P16, P16, P16, P16, P16, None, P16, ws, None) == 2

@@ -10,7 +10,7 @@ import torch
 from dynamic_sparse_attention_proxy_amd import binding as B
 from dynamic_sparse_attention_proxy_amd import synth
 from oracle import crisp_oracle as O
-from parity import (REL_CSTRUCT, check_attention, check_gamma_set, check_noise_floor_mask, check_pe_lists,
+from parity import (JSD_ABS, JSD_REL, REL_CSTRUCT, check_attention, check_gamma_set, check_noise_floor_mask, check_pe_lists,
                     check_route, gpu_lists, to64)
 
 pytestmark = pytest.mark.gpu
@@ -55,7 +55,15 @@ def test_layer_route_auto(widx):
     rt = bufs.route.cpu().numpy()
     count = bufs.blocks["count"].cpu().numpy()
     idx = bufs.blocks["idx"].cpu().numpy()
-    # C_struct and route of every head; block masses of the sampled heads
+    # the comparison JSD signal on the same block masses
+    tau_jsd = 0.1
+    ws = torch.empty(B.crisp_route_jsd_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    jd = torch.empty(hq, dtype=torch.float32, device="cuda")
+    jr = torch.empty(hq, dtype=torch.int32, device="cuda")
+    B.crisp_route_jsd(dims, tau_jsd, x.q, x.k, bufs.block_mass, jd, jr, ws)
+    torch.cuda.synchronize()
+    jd, jr = jd.cpu().numpy(), jr.cpu().numpy()
+    # C_struct, route and JSD signal of every head; block masses of the sampled heads
     sampled = [0, hq - 1]
     kcache = {}
     for h in range(hq):
@@ -63,10 +71,14 @@ def test_layer_route_auto(widx):
         if g not in kcache:
             kcache.clear()
             kcache[g] = to64(x.k[g])
-        A, _ = O.proxy_map(to64(x.q[h, n - BLK:]), kcache[g], dims.scale)
+        q_last = to64(x.q[h, n - BLK:])
+        A, _ = O.proxy_map(q_last, kcache[g], dims.scale)
         c_o = O.c_struct(A)
         assert abs(cs[h] - c_o) <= REL_CSTRUCT * c_o, (h, cs[h], c_o)
         check_route(c_o, cfg.tau, int(rt[h]), O.route(c_o, cfg.tau))
+        d_o, r_o = O.jsd_route(O.jsd_estimate(q_last, kcache[g], dims.scale), O.jsd_actual(A), tau_jsd)
+        assert abs(float(jd[h]) ** 2 - d_o * d_o) <= JSD_ABS + JSD_REL * d_o * d_o, (h, jd[h], d_o)
+        check_route(d_o, tau_jsd, int(jr[h]), r_o)
         if h in sampled:
             lo_o, up_o = O.block_masses(A)
             bm = bufs.block_mass[:, h].cpu().numpy().astype(np.float64)

@@ -12,7 +12,7 @@ import torch
 from dynamic_sparse_attention_proxy_amd import binding as B
 from dynamic_sparse_attention_proxy_amd import synth
 from oracle import crisp_oracle as O
-from parity import (REL_CSTRUCT, check_attention, check_gamma_set, check_noise_floor_mask, check_pe_lists,
+from parity import (JSD_ABS, JSD_REL, REL_CSTRUCT, REL_JSD_EST, check_attention, check_gamma_set, check_noise_floor_mask, check_pe_lists,
                     check_route, gpu_lists, near, to64)
 
 pytestmark = pytest.mark.gpu
@@ -217,6 +217,64 @@ def test_proxy_and_route_single_head_4k():
     c_g = float(bufs.c_struct[0])
     assert abs(c_g - c_o) <= REL_CSTRUCT * c_o
     check_route(c_o, cfg.tau, int(bufs.route[0]), O.route(c_o, cfg.tau))
+
+
+TAU_JSD = 0.1
+
+
+@pytest.mark.parametrize("hq,hkv,n,family", [(1, 1, 4096, False), (8, 2, 4480, False), (14, 2, 2048, False),
+                                             (32, 8, 8192, True)])
+def test_jsd_routing_signal_matches_oracle(hq, hkv, n, family):
+    """The comparison routing signal, and C_struct beside it, on the
+    single-head 4k workload, a GQA layer whose 35 key blocks leave a partial
+    workgroup, a 7:1 group (more heads per group than row groups per wave),
+    and the graded-structure family, whose heads range from structureless to
+    sink- or recency-dominated (C_struct from about 0.02 to 0.9)."""
+    if family:
+        x = synth.make_routing_family(seq_len=n, device="cuda")
+    elif hq == 1:
+        x = inputs(0)
+    else:
+        x = synth.make_inputs(synth.custom(hq, hkv, n, seed=hq * 31 + n, needles=4), device="cuda")
+    dims = B.make_dims(hq, hkv, n)
+    cfg = B.make_cfg(tau=0.2)
+    N = n // BLK
+    mass = torch.empty((2, hq, N), dtype=torch.float32, device="cuda")
+    partials = torch.empty(B.crisp_proxy_scratch_bytes(dims), dtype=torch.uint8, device="cuda")
+    B.crisp_proxy(dims, x.q, x.k, None, partials=partials, block_mass=mass)
+    cs = torch.empty(hq, dtype=torch.float32, device="cuda")
+    rt = torch.empty(hq, dtype=torch.int32, device="cuda")
+    B.crisp_route(dims, cfg, None, cs, rt, block_mass=mass)
+    ws = torch.empty(B.crisp_route_jsd_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    dist = torch.empty(hq, dtype=torch.float32, device="cuda")
+    route = torch.empty(hq, dtype=torch.int32, device="cuda")
+    est = torch.empty((hq, N), dtype=torch.float32, device="cuda")
+    B.crisp_route_jsd(dims, TAU_JSD, x.q, x.k, mass, dist, route, ws, estimate=est)
+    torch.cuda.synchronize()
+    est_g, dist_g, route_g = est.cpu().numpy(), dist.cpu().numpy(), route.cpu().numpy()
+    cs_g, rt_g = cs.cpu().numpy(), rt.cpu().numpy()
+    c_all = []
+    for h in range(hq):
+        g = h * hkv // hq
+        q, k = to64(x.q[h]), to64(x.k[g])
+        A, _ = O.proxy_map(q[n - BLK:], k, dims.scale)
+        c_o = O.c_struct(A)
+        c_all.append(c_o)
+        assert abs(float(cs_g[h]) - c_o) <= REL_CSTRUCT * c_o, (h, cs_g[h], c_o)
+        check_route(c_o, cfg.tau, int(rt_g[h]), O.route(c_o, cfg.tau))
+        a_bar = O.jsd_actual(A)
+        p_est = O.jsd_estimate(q[n - BLK:], k, dims.scale)
+        np.testing.assert_allclose(est_g[h], p_est, rtol=REL_JSD_EST, atol=1e-9, err_msg=f"head {h}")
+        d_o, r_o = O.jsd_route(p_est, a_bar, TAU_JSD)
+        d_g = float(dist_g[h])
+        assert abs(d_g * d_g - d_o * d_o) <= JSD_ABS + JSD_REL * d_o * d_o, f"head {h}: {d_g} vs {d_o}"
+        check_route(d_o, TAU_JSD, int(route_g[h]), r_o)
+        # the kernel's decision, taken on its own distance
+        assert int(route_g[h]) == (B.ROUTE_VS if d_g >= TAU_JSD else B.ROUTE_PE)
+    if family:
+        # both routes occur, so the agreement measurement is not degenerate
+        assert min(c_all) < 0.05 and max(c_all) > 0.8
+        assert 0 < int(rt_g.sum()) < hq and 0 < int(route_g.sum()) < hq
 
 
 @pytest.mark.parametrize("alpha,stat", [(1.25, B.NF_MEDIAN), (1.0, B.NF_MEDIAN), (1.25, B.NF_MEAN)])
