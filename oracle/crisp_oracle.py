@@ -491,3 +491,103 @@ def jsd_route(p_est: np.ndarray, a_bar: np.ndarray, tau_jsd: float):
     and goes Vertical-Slash; otherwise Pooled-Estimation.  Ties go to VS."""
     d = math.sqrt(max(js_divergence(a_bar, p_est), 0.0))
     return d, (ROUTE_VS if d >= tau_jsd else ROUTE_PE)
+
+
+# ---------------------------------------------------------------------------
+# Token-granular Vertical-Slash selection (ai-feeds "方法", module 2: keep the
+# tokens whose mass stands clearly above the noise floor; ai.info
+# "Methodology in Plain English": k_min = 1024 tokens per direction).
+# Readings R26-R28.
+# ---------------------------------------------------------------------------
+
+
+def token_noise_floor_select(x: np.ndarray, alpha: float, kmin_tokens: int, retained: int = 128,
+                             stat: int = NF_MEDIAN):
+    """Noise floor over one direction's token scores (reading R26).
+
+    Entries 0 .. retained-1 (the sink columns for vertical, the local
+    offsets for slash) are always kept and excluded from the floor estimate.
+    The floor is the lower median (or the mean) of the other entries; every
+    other entry above alpha times the floor is kept.  If fewer than
+    min(kmin_tokens, n) entries are kept in all, the best unkept entries
+    (descending score, ties to the lower index) are added until there are.
+    Returns (mask [n] bool, T)."""
+    n = x.shape[0]
+    cand = list(range(retained, n))
+    if stat == NF_MEDIAN:
+        mu = lower_median([x[j] for j in cand])
+    else:
+        mu = float(np.mean([x[j] for j in cand]))
+    T = alpha * mu
+    sel = set(range(retained))
+    for j in cand:
+        if x[j] > T:
+            sel.add(j)
+    want = min(kmin_tokens, n)
+    if len(sel) < want:
+        for j in _order_desc(x, [j for j in cand if j not in sel]):
+            if len(sel) >= want:
+                break
+            sel.add(j)
+    mask = np.zeros(n, dtype=bool)
+    mask[sorted(sel)] = True
+    return mask, T
+
+
+@dataclass
+class TokenPlan:
+    vmask: np.ndarray       # [n] kept vertical columns
+    smask: np.ndarray       # [n] kept slash offsets
+    floor_v: float
+    floor_s: float
+    bands: np.ndarray       # [N] slash bands holding a kept offset
+    cols: List[int]         # kept columns outside key block 0, ascending
+    lists: List[List[int]]  # per query block: listed key blocks (tiles)
+
+
+def token_vs_plan(c: np.ndarray, dg: np.ndarray, alpha: float, kmin_tokens: int, block: int = 128,
+                  stat: int = NF_MEDIAN) -> TokenPlan:
+    """What a Vertical-Slash head computes under token-granular selection.
+
+    Reading R27: kept slash offsets are computed by whole tiles: offset o
+    falls in band floor(o / 128), and a band is expanded as in R5 (query
+    block qb reads key blocks qb - b and qb - b - 1).  Key block 0 holds the
+    retained sink columns and is always listed.  Reading R28: every kept
+    column outside key block 0 is read one by one, by every query block
+    past it, on top of the tiles."""
+    n = c.shape[0]
+    N = n // block
+    vmask, Tv = token_noise_floor_select(c, alpha, kmin_tokens, block, stat)
+    smask, Ts = token_noise_floor_select(dg, alpha, kmin_tokens, block, stat)
+    bands = np.zeros(N, dtype=bool)
+    for o in np.nonzero(smask)[0]:
+        bands[o // block] = True
+    vblocks = np.zeros(N, dtype=bool)
+    vblocks[0] = True
+    cols = [int(j) for j in np.nonzero(vmask)[0] if j >= block]
+    return TokenPlan(vmask, smask, Tv, Ts, bands, cols, vs_lists(vblocks, bands))
+
+
+def attention_rows_mixed(q: np.ndarray, k: np.ndarray, v: np.ndarray, lists: Sequence[Sequence[int]],
+                         cols: Sequence[int], scale: float, qbs: Sequence[int], block: int = 128):
+    """Causal attention of one head over listed tiles plus single key
+    columns: for query i in block qb the key set is every key j <= i that
+    lies in a listed key block of qb or is one of `cols`.  Each key counts
+    once.  Returns {qb: (O [block][d], lse [block])}."""
+    out = {}
+    col_set = set(int(j) for j in cols)
+    for qb in qbs:
+        keys = set()
+        for kb in lists[qb]:
+            keys.update(range(int(kb) * block, (int(kb) + 1) * block))
+        keys.update(j for j in col_set if j < (qb + 1) * block)
+        keys = np.array(sorted(keys), dtype=np.int64)
+        rows = np.arange(qb * block, (qb + 1) * block)
+        s = scale * (q[rows] @ k[keys].T)
+        s[keys[None, :] > rows[:, None]] = -np.inf
+        m = s.max(axis=1)
+        e = np.exp(s - m[:, None])
+        l = e.sum(axis=1)
+        O = (e @ v[keys]) / l[:, None]
+        out[qb] = (O, m + np.log(l))
+    return out

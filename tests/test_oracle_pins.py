@@ -686,3 +686,92 @@ def test_jsd_route_direction_and_tie():
     assert d0 == 0.0 and rt0 == O.ROUTE_PE
     # a distance equal to the threshold goes VS
     assert O.jsd_route(u, one_hot, d)[1] == O.ROUTE_VS
+
+
+# --------------------------------------------------------------------------
+# token-granular Vertical-Slash selection
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("seed", [0, 1])
+def test_token_floor_with_one_retained_is_the_block_rule(seed):
+    # one retained entry is exactly the block-level rule with block 0 kept
+    r = _rng(seed)
+    x = r.random(40) ** 3
+    for alpha, kmin, stat in [(1.25, 8, O.NF_MEDIAN), (1.0, 3, O.NF_MEDIAN), (2.0, 12, O.NF_MEAN)]:
+        got, T1 = O.token_noise_floor_select(x, alpha, kmin, retained=1, stat=stat)
+        want, T2 = O.noise_floor_select(x, alpha, kmin, stat)
+        np.testing.assert_array_equal(got, want)
+        assert T1 == T2
+
+
+def test_token_floor_planted_spikes():
+    # background 1.0 everywhere, spikes of 5 at three columns, first 4 retained:
+    # median 1, floor alpha = 1.25 -> exactly the spikes; k_min 10 adds the
+    # lowest-index background columns (ties to the lower index)
+    n = 64
+    x = np.ones(n)
+    spikes = [9, 30, 61]
+    x[spikes] = 5.0
+    x[:4] = 0.0  # retained entries do not enter the median
+    m, T = O.token_noise_floor_select(x, 1.25, 7, retained=4)
+    assert T == 1.25
+    assert sorted(np.nonzero(m)[0].tolist()) == [0, 1, 2, 3] + spikes
+    m2, _ = O.token_noise_floor_select(x, 1.25, 10, retained=4)
+    assert sorted(np.nonzero(m2)[0].tolist()) == [0, 1, 2, 3, 4, 5, 6, 9, 30, 61]
+    # the mean statistic: (3 * 5 + 57) / 60 = 1.2 -> floor 1.5
+    _, Tm = O.token_noise_floor_select(x, 1.25, 7, retained=4, stat=O.NF_MEAN)
+    assert Tm == pytest.approx(1.25 * 72 / 60, rel=1e-15)
+
+
+def test_token_plan_bands_columns_and_lists():
+    n, blk = 8 * 16, 16  # N = 8 blocks of 16 tokens
+    c = np.ones(n)
+    dg = np.ones(n)
+    c[[5, 40, 41, 100]] = 9.0    # 5 is a sink column (block 0): not gathered
+    dg[[16, 47, 100]] = 9.0      # bands 1, 2 and 6
+    p = O.token_vs_plan(c, dg, 1.25, 1, blk)
+    assert p.cols == [40, 41, 100]
+    assert np.nonzero(p.bands)[0].tolist() == [0, 1, 2, 6]
+    # query block 7 reads block 0, bands 0,1,2 -> 7,6,5,4; band 6 -> 1,0
+    assert p.lists[7] == [0, 1, 4, 5, 6, 7]
+    assert p.lists[0] == [0]
+    assert p.lists[3] == [0, 1, 2, 3]
+
+
+def _mixed_brute(q, k, v, lists, cols, scale, qb, block):
+    outs = []
+    for i in range(qb * block, (qb + 1) * block):
+        keys = [j for j in range(i + 1) if (j // block) in set(lists[qb]) or j in set(cols)]
+        s = [scale * float(np.dot(q[i], k[j])) for j in keys]
+        mx = max(s)
+        w = [math.exp(t - mx) for t in s]
+        z = sum(w)
+        outs.append(sum(wi * v[j] for wi, j in zip(w, keys)) / z)
+    return np.array(outs)
+
+
+def test_mixed_attention_brute_force_and_reductions():
+    r = _rng(11)
+    blk, N, d = 8, 6, 4
+    n = blk * N
+    q = r.standard_normal((n, d))
+    k = r.standard_normal((n, d))
+    v = r.standard_normal((n, d))
+    lists = [[0], [0, 1], [1, 2], [0, 3], [2, 4], [0, 4, 5]]
+    cols = [3, 9, 17, 18, 33, 46]  # some inside listed tiles, one in a later block
+    res = O.attention_rows_mixed(q, k, v, lists, cols, 0.5, range(N), blk)
+    for qb in range(N):
+        np.testing.assert_allclose(res[qb][0], _mixed_brute(q, k, v, lists, cols, 0.5, qb, blk), rtol=1e-12,
+                                   atol=1e-12)
+    # no columns: the tile-only attention
+    tiles = O.attention_rows(q, k, v, lists, 0.5, range(N), blk)
+    none = O.attention_rows_mixed(q, k, v, lists, [], 0.5, range(N), blk)
+    for qb in range(N):
+        np.testing.assert_array_equal(none[qb][0], tiles[qb][0])
+    # every column plus the diagonal tile: dense causal attention
+    dense = O.attention_rows(q, k, v, O.dense_lists(N), 0.5, range(N), blk)
+    allc = O.attention_rows_mixed(q, k, v, [[qb] for qb in range(N)], list(range(n)), 0.5, range(N), blk)
+    for qb in range(N):
+        np.testing.assert_allclose(allc[qb][0], dense[qb][0], rtol=1e-12, atol=1e-12)
+        np.testing.assert_allclose(allc[qb][1], dense[qb][1], rtol=1e-12, atol=1e-12)
