@@ -537,35 +537,33 @@ def token_noise_floor_select(x: np.ndarray, alpha: float, kmin_tokens: int, reta
 @dataclass
 class TokenPlan:
     vmask: np.ndarray       # [n] kept vertical columns
-    smask: np.ndarray       # [n] kept slash offsets
-    floor_v: float
+    floor_v: float          # token floor of the vertical direction
+    smask: np.ndarray       # [N] kept slash bands (block-level rule)
     floor_s: float
-    bands: np.ndarray       # [N] slash bands holding a kept offset
     cols: List[int]         # kept columns outside key block 0, ascending
     lists: List[List[int]]  # per query block: listed key blocks (tiles)
 
 
-def token_vs_plan(c: np.ndarray, dg: np.ndarray, alpha: float, kmin_tokens: int, block: int = 128,
-                  stat: int = NF_MEDIAN) -> TokenPlan:
-    """What a Vertical-Slash head computes under token-granular selection.
+def token_vs_plan(c: np.ndarray, sl: np.ndarray, alpha: float, kmin_tokens: int, kmin_blocks: int,
+                  block: int = 128, stat: int = NF_MEDIAN) -> TokenPlan:
+    """What a Vertical-Slash head computes under token-granular vertical
+    selection.
 
-    Reading R27: kept slash offsets are computed by whole tiles: offset o
-    falls in band floor(o / 128), and a band is expanded as in R5 (query
-    block qb reads key blocks qb - b and qb - b - 1).  Key block 0 holds the
-    retained sink columns and is always listed.  Reading R28: every kept
-    column outside key block 0 is read one by one, by every query block
-    past it, on top of the tiles."""
-    n = c.shape[0]
-    N = n // block
+    Reading R26: the vertical direction keeps columns by the token floor
+    over the column masses c.  Reading R27: the slash direction keeps its
+    block rule on the band scores sl (offsets far from the diagonal carry
+    background mass only, so kept single offsets would scatter over nearly
+    every band and a tile cover of them would be almost dense).  Key block 0
+    holds the retained sink columns and is always a tile.  Reading R28:
+    every kept column outside key block 0 is read one by one, by every query
+    block past it, on top of the tiles."""
+    N = c.shape[0] // block
     vmask, Tv = token_noise_floor_select(c, alpha, kmin_tokens, block, stat)
-    smask, Ts = token_noise_floor_select(dg, alpha, kmin_tokens, block, stat)
-    bands = np.zeros(N, dtype=bool)
-    for o in np.nonzero(smask)[0]:
-        bands[o // block] = True
+    smask, Ts = noise_floor_select(sl, alpha, kmin_blocks, stat)
     vblocks = np.zeros(N, dtype=bool)
     vblocks[0] = True
     cols = [int(j) for j in np.nonzero(vmask)[0] if j >= block]
-    return TokenPlan(vmask, smask, Tv, Ts, bands, cols, vs_lists(vblocks, bands))
+    return TokenPlan(vmask, Tv, smask, Ts, cols, vs_lists(vblocks, smask))
 
 
 def attention_rows_mixed(q: np.ndarray, k: np.ndarray, v: np.ndarray, lists: Sequence[Sequence[int]],

@@ -724,19 +724,22 @@ def test_token_floor_planted_spikes():
     assert Tm == pytest.approx(1.25 * 72 / 60, rel=1e-15)
 
 
-def test_token_plan_bands_columns_and_lists():
+def test_token_plan_columns_and_lists():
     n, blk = 8 * 16, 16  # N = 8 blocks of 16 tokens
     c = np.ones(n)
-    dg = np.ones(n)
-    c[[5, 40, 41, 100]] = 9.0    # 5 is a sink column (block 0): not gathered
-    dg[[16, 47, 100]] = 9.0      # bands 1, 2 and 6
-    p = O.token_vs_plan(c, dg, 1.25, 1, blk)
+    c[[5, 40, 41, 100]] = 9.0    # 5 is a sink column (block 0): a tile, not gathered
+    sl = np.ones(8)
+    sl[[2, 6]] = 9.0             # slash bands 2 and 6 (band 0 always)
+    p = O.token_vs_plan(c, sl, 1.25, 1, 1, blk)
     assert p.cols == [40, 41, 100]
-    assert np.nonzero(p.bands)[0].tolist() == [0, 1, 2, 6]
-    # query block 7 reads block 0, bands 0,1,2 -> 7,6,5,4; band 6 -> 1,0
+    assert np.nonzero(p.smask)[0].tolist() == [0, 2, 6]
+    # query block 7 reads block 0, bands 0, 2 -> 7, 6, 5, 4; band 6 -> 1, 0
     assert p.lists[7] == [0, 1, 4, 5, 6, 7]
     assert p.lists[0] == [0]
     assert p.lists[3] == [0, 1, 2, 3]
+    # only block 0 and the bands make tiles: query block 5 lists 0, then
+    # bands 0 and 2 -> 5, 4, 3, 2
+    assert p.lists[5] == [0, 2, 3, 4, 5]
 
 
 def _mixed_brute(q, k, v, lists, cols, scale, qb, block):
