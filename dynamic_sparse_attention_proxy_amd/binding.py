@@ -61,6 +61,10 @@ _SIGS = {
     "crisp_proxy": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "crisp_proxy_scratch_bytes": (ctypes.c_size_t, [ctypes.POINTER(crisp_dims)]),
     "crisp_route": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), _P, _P, _P, _P, _P]),
+    "crisp_proxy_cols": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "crisp_select_tokens": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), _P, _P, _P, _P,
+                                           _P, ctypes.POINTER(crisp_blocks), _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "crisp_sparse_attn_cols": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
     "crisp_route_jsd": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.c_float, _P, _P, _P, _P, _P, _P, _P,
                                        ctypes.c_size_t, _P]),
     "crisp_route_jsd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(crisp_dims)]),
@@ -153,6 +157,13 @@ def crisp_route(dims: crisp_dims, cfg: crisp_cfg, attn_map, c_struct, route, str
                                             _ptr(c_struct), _ptr(route), _stream(stream)))
 
 
+def crisp_proxy_cols(dims: crisp_dims, q, k, block_mass, col_mass, row_lse=None, partials=None, stream=None):
+    nbytes = partials.numel() * partials.element_size() if partials is not None else 0
+    _check("crisp_proxy_cols", lib().crisp_proxy_cols(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(block_mass),
+                                                      _ptr(col_mass), _ptr(row_lse), _ptr(partials), nbytes,
+                                                      _stream(stream)))
+
+
 def crisp_route_jsd_workspace_bytes(dims: crisp_dims) -> int:
     return int(lib().crisp_route_jsd_workspace_bytes(ctypes.byref(dims)))
 
@@ -192,6 +203,26 @@ def crisp_select_gamma(dims: crisp_dims, cfg: crisp_cfg, gamma: float, q, k, att
                                                           _stream(stream)))
 
 
+def crisp_select_tokens(dims: crisp_dims, cfg: crisp_cfg, q, k, block_mass, col_mass, route, out: dict, cols,
+                        ncols, col_below, workspace, stream=None):
+    b = _blocks(out)
+    _check("crisp_select_tokens", lib().crisp_select_tokens(ctypes.byref(dims), ctypes.byref(cfg), _ptr(q), _ptr(k),
+                                                            _ptr(block_mass), _ptr(col_mass), _ptr(route),
+                                                            ctypes.byref(b), _ptr(cols), _ptr(ncols),
+                                                            _ptr(col_below), _ptr(workspace),
+                                                            workspace.numel() * workspace.element_size(),
+                                                            _stream(stream)))
+
+
+def crisp_sparse_attn_cols(dims: crisp_dims, q, k, v, count, idx, cols, col_below, out, lse, stream=None):
+    if out.dtype != torch.float32:
+        raise TypeError("crisp_sparse_attn_cols updates an fp32 output in place")
+    _check("crisp_sparse_attn_cols", lib().crisp_sparse_attn_cols(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
+                                                                  _ptr(count), _ptr(idx), _ptr(cols),
+                                                                  _ptr(col_below), _ptr(out), _ptr(lse),
+                                                                  _stream(stream)))
+
+
 def crisp_sparse_attn(dims: crisp_dims, q, k, v, count, idx, out, lse=None, stream=None):
     out_fp32 = 1 if out.dtype == torch.float32 else 0
     _check("crisp_sparse_attn", lib().crisp_sparse_attn(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(count),
@@ -216,7 +247,7 @@ class CrispBuffers:
     `with_map=True`; the chain otherwise runs on the block masses."""
 
     def __init__(self, dims: crisp_dims, device=None, out_dtype=torch.bfloat16, diagnostics: bool = True,
-                 with_map: bool = False):
+                 with_map: bool = False, tokens: bool = False):
         dev = torch.device("cuda") if device is None else torch.device(device)
         hq, n = dims.num_q_heads, dims.seq_len
         N = n // dims.block
@@ -242,6 +273,12 @@ class CrispBuffers:
                 "n_v": torch.empty((hq,), dtype=i32, device=dev),
                 "n_s": torch.empty((hq,), dtype=i32, device=dev),
             })
+        if tokens:  # token-granular vertical selection; its attention output is fp32
+            self.col_mass = torch.empty((hq, n), dtype=f32, device=dev)
+            self.cols = torch.empty((hq, n), dtype=i32, device=dev)
+            self.ncols = torch.empty((hq,), dtype=i32, device=dev)
+            self.col_below = torch.empty((hq, N), dtype=i32, device=dev)
+            out_dtype = f32
         self.out = torch.empty((hq, n, dims.head_dim), dtype=out_dtype, device=dev)
         self.lse = torch.empty((hq, n), dtype=f32, device=dev)
 
@@ -281,4 +318,21 @@ def crisp_prefill(dims: crisp_dims, cfg: crisp_cfg, q, k, v, bufs: CrispBuffers,
         crisp_select_gamma(dims, cfg, gamma, q, k, amap, bufs.route, bufs.blocks, bufs.workspace, stream,
                            block_mass=mass)
     crisp_sparse_attn(dims, q, k, v, bufs.blocks["count"], bufs.blocks["idx"], bufs.out, bufs.lse, stream)
+    return bufs.out
+
+
+def crisp_prefill_tokens(dims: crisp_dims, cfg: crisp_cfg, q, k, v, bufs: CrispBuffers, stream=None):
+    """One layer with token-granular vertical selection: proxy with column
+    masses -> route -> select (kept columns; slash bands as in the block
+    rule) -> tile attention -> the kept columns merged in.  bufs must come
+    from CrispBuffers(tokens=True); the output is fp32."""
+    if not hasattr(bufs, "cols"):
+        raise ValueError("crisp_prefill_tokens needs CrispBuffers(tokens=True)")
+    crisp_proxy_cols(dims, q, k, bufs.block_mass, bufs.col_mass, bufs.row_lse, bufs.partials, stream)
+    crisp_route(dims, cfg, None, bufs.c_struct, bufs.route, stream, block_mass=bufs.block_mass)
+    crisp_select_tokens(dims, cfg, q, k, bufs.block_mass, bufs.col_mass, bufs.route, bufs.blocks, bufs.cols,
+                        bufs.ncols, bufs.col_below, bufs.workspace, stream)
+    crisp_sparse_attn(dims, q, k, v, bufs.blocks["count"], bufs.blocks["idx"], bufs.out, bufs.lse, stream)
+    crisp_sparse_attn_cols(dims, q, k, v, bufs.blocks["count"], bufs.blocks["idx"], bufs.cols, bufs.col_below,
+                           bufs.out, bufs.lse, stream)
     return bufs.out

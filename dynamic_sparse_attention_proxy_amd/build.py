@@ -16,7 +16,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libcrisp.so")
-SOURCES = ["api.hip", "proxy.hip", "select.hip", "attn.hip", "jsd.hip"]
+SOURCES = ["api.hip", "proxy.hip", "select.hip", "attn.hip", "jsd.hip", "cols.hip"]
 # Measurement probe, a library of its own so it stays out of the CRISP ABI.
 PROBE_LIB = os.path.join(PKG, "libcrisp_probe.so")
 PROBE_SOURCES = ["probe.hip"]

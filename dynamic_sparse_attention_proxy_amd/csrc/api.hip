@@ -84,7 +84,8 @@ crisp_status check_map_or_mass(const void* attn_map, const void* block_mass) {
 
 crisp_status select_common(const crisp_dims* dims, const crisp_cfg* cfg, bool use_gamma, float gamma, const void* q,
                            const void* k, const float* attn_map, const float* block_mass, const int32_t* route,
-                           const crisp_blocks* out, void* workspace, size_t workspace_bytes, void* stream) {
+                           const crisp_blocks* out, void* workspace, size_t workspace_bytes,
+                           const crisp::TokenCols* tok, void* stream) {
   CRISP_TRY(check_dims(dims));
   CRISP_TRY(check_cfg(dims, cfg));
   if (use_gamma && !(gamma > 0.f && gamma <= 1.f)) return CRISP_ERR_PARAM;
@@ -119,7 +120,7 @@ crisp_status select_common(const crisp_dims* dims, const crisp_cfg* cfg, bool us
   return launched(crisp::launch_select((const __bf16*)q, (const __bf16*)k, attn_map, block_mass, route, b, out->count,
                                        out->idx,
                                        hq, hkv, n, dims->scale, cfg->alpha, cfg->gamma_pe, cfg->kmin_blocks,
-                                       cfg->nf_stat, use_gamma, gamma, (hipStream_t)stream));
+                                       cfg->nf_stat, use_gamma, gamma, tok, (hipStream_t)stream));
 }
 
 crisp_status attn_common(const crisp_dims* dims, const void* q, const void* k, const void* v, const int32_t* count,
@@ -160,8 +161,24 @@ crisp_status crisp_proxy(const crisp_dims* dims, const void* q, const void* k, f
   CRISP_TRY(check_ptr(partials));
   if (partials_bytes < crisp::proxy_scratch_bytes(dims->num_q_heads, dims->seq_len)) return CRISP_ERR_WORKSPACE;
   CRISP_TRY(check_device());
-  return launched(crisp::launch_proxy((const __bf16*)q, (const __bf16*)k, attn_map, block_mass, row_lse, partials,
-                                      dims->num_q_heads, dims->num_kv_heads, dims->seq_len, dims->scale,
+  return launched(crisp::launch_proxy((const __bf16*)q, (const __bf16*)k, attn_map, block_mass, nullptr, row_lse,
+                                      partials, dims->num_q_heads, dims->num_kv_heads, dims->seq_len, dims->scale,
+                                      (hipStream_t)stream));
+}
+
+crisp_status crisp_proxy_cols(const crisp_dims* dims, const void* q, const void* k, float* block_mass,
+                              float* col_mass, float* row_lse, void* partials, size_t partials_bytes, void* stream) {
+  CRISP_TRY(check_dims(dims));
+  CRISP_TRY(check_ptr(q));
+  CRISP_TRY(check_ptr(k));
+  CRISP_TRY(check_ptr(block_mass));
+  CRISP_TRY(check_ptr(col_mass));
+  CRISP_TRY(check_opt(row_lse));
+  CRISP_TRY(check_ptr(partials));
+  if (partials_bytes < crisp::proxy_scratch_bytes(dims->num_q_heads, dims->seq_len)) return CRISP_ERR_WORKSPACE;
+  CRISP_TRY(check_device());
+  return launched(crisp::launch_proxy((const __bf16*)q, (const __bf16*)k, nullptr, block_mass, col_mass, row_lse,
+                                      partials, dims->num_q_heads, dims->num_kv_heads, dims->seq_len, dims->scale,
                                       (hipStream_t)stream));
 }
 
@@ -209,6 +226,24 @@ crisp_status crisp_select(const crisp_dims* dims, const crisp_cfg* cfg, const vo
                           const float* attn_map, const float* block_mass, const int32_t* route,
                           const crisp_blocks* out, void* workspace, size_t workspace_bytes, void* stream) {
   return select_common(dims, cfg, false, 0.f, q, k, attn_map, block_mass, route, out, workspace, workspace_bytes,
+                       nullptr, stream);
+}
+
+crisp_status crisp_select_tokens(const crisp_dims* dims, const crisp_cfg* cfg, const void* q, const void* k,
+                                 const float* block_mass, const float* col_mass, const int32_t* route,
+                                 const crisp_blocks* out, int32_t* cols, int32_t* ncols, int32_t* col_below,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+  CRISP_TRY(check_ptr(block_mass));
+  CRISP_TRY(check_ptr(col_mass));
+  CRISP_TRY(check_ptr(cols));
+  CRISP_TRY(check_ptr(ncols));
+  CRISP_TRY(check_ptr(col_below));
+  crisp::TokenCols tc;
+  tc.colmass = col_mass;
+  tc.cols = cols;
+  tc.ncols = ncols;
+  tc.col_below = col_below;
+  return select_common(dims, cfg, false, 0.f, q, k, nullptr, block_mass, route, out, workspace, workspace_bytes, &tc,
                        stream);
 }
 
@@ -216,7 +251,7 @@ crisp_status crisp_select_gamma(const crisp_dims* dims, const crisp_cfg* cfg, fl
                                 const void* k, const float* attn_map, const float* block_mass, const int32_t* route,
                                 const crisp_blocks* out, void* workspace, size_t workspace_bytes, void* stream) {
   return select_common(dims, cfg, true, gamma, q, k, attn_map, block_mass, route, out, workspace, workspace_bytes,
-                       stream);
+                       nullptr, stream);
 }
 
 size_t crisp_select_workspace_bytes(const crisp_dims* dims) {
@@ -234,6 +269,25 @@ crisp_status crisp_sparse_attn(const crisp_dims* dims, const void* q, const void
                                const int32_t* count, const int32_t* idx, void* out, int32_t out_is_fp32, float* lse,
                                void* stream) {
   return attn_common(dims, q, k, v, count, idx, out, out_is_fp32, lse, false, stream);
+}
+
+crisp_status crisp_sparse_attn_cols(const crisp_dims* dims, const void* q, const void* k, const void* v,
+                                    const int32_t* count, const int32_t* idx, const int32_t* cols,
+                                    const int32_t* col_below, float* out, float* lse, void* stream) {
+  CRISP_TRY(check_dims(dims));
+  CRISP_TRY(check_ptr(q));
+  CRISP_TRY(check_ptr(k));
+  CRISP_TRY(check_ptr(v));
+  CRISP_TRY(check_ptr(count));
+  CRISP_TRY(check_ptr(idx));
+  CRISP_TRY(check_ptr(cols));
+  CRISP_TRY(check_ptr(col_below));
+  CRISP_TRY(check_ptr(out));
+  CRISP_TRY(check_ptr(lse));
+  CRISP_TRY(check_device());
+  return launched(crisp::launch_col_attention((const __bf16*)q, (const __bf16*)k, (const __bf16*)v, count, idx, cols,
+                                              col_below, out, lse, dims->num_q_heads, dims->num_kv_heads,
+                                              dims->seq_len, dims->scale, (hipStream_t)stream));
 }
 
 crisp_status crisp_dense_attn(const crisp_dims* dims, const void* q, const void* k, const void* v, void* out,
@@ -255,6 +309,6 @@ const char* crisp_status_string(crisp_status status) {
   return "unknown status";
 }
 
-int32_t crisp_abi_version(void) { return (2 << 16) | 1; }
+int32_t crisp_abi_version(void) { return (2 << 16) | 2; }
 
 }  // extern "C"

@@ -17,9 +17,10 @@ inline size_t proxy_scratch_bytes(int hq, int n) {
 }
 
 // amap and/or mass (at least one non-null): the proxy map and the block
-// masses [2][Hq][N] (on/below, above each tile's diagonal).
-hipError_t launch_proxy(const __bf16* q, const __bf16* k, float* amap, float* mass, float* row_lse, void* scratch,
-                        int hq, int hkv, int n, float scale, hipStream_t stream);
+// masses [2][Hq][N] (on/below, above each tile's diagonal).  colmass
+// [Hq][n] (the column masses) may only be given with mass and without amap.
+hipError_t launch_proxy(const __bf16* q, const __bf16* k, float* amap, float* mass, float* colmass, float* row_lse,
+                        void* scratch, int hq, int hkv, int n, float scale, hipStream_t stream);
 
 // From the block masses when mass != nullptr (widths of one block), else
 // from the map.
@@ -44,6 +45,14 @@ struct SelectBuffers {
 size_t select_workspace_bytes(int hq, int hkv, int n);
 SelectBuffers carve_select_workspace(void* ws, int hq, int hkv, int n);
 
+// Token-granular vertical selection: column masses in, kept columns out.
+struct TokenCols {
+  const float* colmass;  // [Hq][n]
+  int32_t* cols;         // [Hq][n]: kept columns past key block 0, ascending
+  int32_t* ncols;        // [Hq]
+  int32_t* col_below;    // [Hq][N]: kept columns below 128 qb
+};
+
 // use_gamma = false: noise floor on VS heads, gamma_pe on PE heads.
 // use_gamma = true: gamma-cumulative on VS heads and `gamma` on PE heads.
 // VS scores come from the block masses when mass != nullptr, else from a
@@ -51,13 +60,19 @@ SelectBuffers carve_select_workspace(void* ws, int hq, int hkv, int n);
 hipError_t launch_select(const __bf16* q, const __bf16* k, const float* amap, const float* mass, const int32_t* route,
                          const SelectBuffers& b, int32_t* count, int32_t* idx, int hq, int hkv, int n, float scale,
                          float alpha, float gamma_pe, int kmin, int nf_stat, bool use_gamma, float gamma,
-                         hipStream_t stream);
+                         const TokenCols* tok, hipStream_t stream);
 
 // JSD routing signal: workspace holds qbar [Hq][128] and the logits [Hq][N].
 size_t jsd_workspace_bytes(int hq, int n);
 hipError_t launch_route_jsd(const __bf16* q, const __bf16* k, const float* mass, float* js_dist, int32_t* route,
                             float* estimate, void* workspace, int hq, int hkv, int n, float scale, float tau_jsd,
                             hipStream_t stream);
+
+// Kept single columns merged into the tile attention (out fp32 and lse are
+// read and updated in place).
+hipError_t launch_col_attention(const __bf16* q, const __bf16* k, const __bf16* v, const int32_t* count,
+                                const int32_t* idx, const int32_t* cols, const int32_t* col_below, float* out,
+                                float* lse, int hq, int hkv, int n, float scale, hipStream_t stream);
 
 hipError_t launch_attention(const __bf16* q, const __bf16* k, const __bf16* v, const int32_t* count,
                             const int32_t* idx, void* out, int out_fp32, float* lse, int hq, int hkv, int n,

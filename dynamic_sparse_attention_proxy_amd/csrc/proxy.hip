@@ -41,6 +41,7 @@ struct ProxyArgs {
   const __bf16* k;
   float* amap;
   float* mass;   // [2][Hq][N]: on/below, above the tile diagonal
+  float* colmass;  // [Hq][n]: column mass, the map's column sums over the rows / 128
   float* part;   // [Hq][128][chunks][2]
   float* lse2;   // [Hq][128]
   float* row_lse;
@@ -61,11 +62,32 @@ __device__ __forceinline__ void merge_ml(float& m, float& l, float mo, float lo)
 // lane group lg: rows 8 (v / 4) + 4 lg + v % 4 of the K operand.
 __device__ __forceinline__ int acc_key(int v, int lg) { return 8 * (v >> 2) + 4 * lg + (v & 3); }
 
-// kPass 0: row statistics.  kPass 1: map (kMap) and/or block masses (kMass).
-template <int kPass, bool kMap, bool kMass>
+// Sum over the 32 rows of a wave of each of a lane's 16 key values (one
+// 32-key half of a step): reduce-scatter by halving over lane bits 4..1 of
+// l32 (8 + 4 + 2 + 1 exchanges), then one exchange with lane ^ 1.  Lane l32
+// returns the total of register v = l32 >> 1 (both lanes of a pair hold it).
+__device__ __forceinline__ float rows_sum_scatter(const float (&a)[16], int l32) {
+  float r8[8], r4[4], r2[2];
+  const bool b4 = l32 & 16, b3 = l32 & 8, b2 = l32 & 4, b1 = l32 & 2;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) r8[e] = (b4 ? a[e + 8] : a[e]) + __shfl_xor(b4 ? a[e] : a[e + 8], 16);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) r4[e] = (b3 ? r8[e + 4] : r8[e]) + __shfl_xor(b3 ? r8[e] : r8[e + 4], 8);
+#pragma unroll
+  for (int e = 0; e < 2; ++e) r2[e] = (b2 ? r4[e + 2] : r4[e]) + __shfl_xor(b2 ? r4[e] : r4[e + 2], 4);
+  const float r1 = (b1 ? r2[1] : r2[0]) + __shfl_xor(b1 ? r2[0] : r2[1], 2);
+  return r1 + __shfl_xor(r1, 1);
+}
+
+// kPass 0: row statistics.  kPass 1: map (kMap) and/or block masses (kMass),
+// and the column masses (kCols).
+template <int kPass, bool kMap, bool kMass, bool kCols = false>
 __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
   __shared__ __attribute__((aligned(1024))) __bf16 ks[kPStages][kPStep * kHeadDim];
   __shared__ float part[4][kProxyChunk / kBlock][2];  // masses per wave and key block of the chunk
+  // column masses of a step per wave, by step parity: summed over the waves
+  // by the first 64 threads in the next step (after its barrier)
+  __shared__ float colpart[kCols ? 2 : 1][4][kPStep];
   // map path: each wave's 32 x 32 tile of the map (one key half of a step),
   // row stride 36 floats so that the per-lane 16-byte writes of 16 rows hit
   // distinct banks
@@ -192,6 +214,10 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
               up += a[v];
           }
         }
+        if (kCols) {
+          const float cs = rows_sum_scatter(a, l32);
+          if ((l32 & 1) == 0) colpart[j & 1][w][32 * kb2 + acc_key(l32 >> 1, lg)] = cs;
+        }
         if (kMap) {
           // Through the wave's LDS tile (row l32, keys 8 q4 + 4 lg + [0, 4)),
           // then row-major out: instruction i writes rows 8i .. 8i+7 of the
@@ -217,6 +243,11 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
                 o, (f32x4*)(p.amap + ((size_t)h * kBlock + 32 * w + r) * p.n + key0 + 32 * kb2 + cc));
           }
         }
+      }
+      if (kCols && j > 0 && tid < kPStep) {  // the previous step's column masses
+        const float* cp = &colpart[(j - 1) & 1][0][tid];
+        p.colmass[(size_t)h * p.n + key0 - kPStep + tid] =
+            (cp[0] + cp[kPStep] + cp[2 * kPStep] + cp[3 * kPStep]) * (1.f / kBlock);
       }
       if (kMass && half == 1) {  // end of a key block: reduce and park the wave's sums
 #pragma unroll
@@ -248,7 +279,14 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
       dst[0] = m;
       dst[1] = l;
     }
-  } else if (kMass) {
+  } else {
+    if (kCols && tid < kPStep) {  // the last step's column masses
+      const float* cp = &colpart[(nsteps - 1) & 1][0][tid];
+      p.colmass[(size_t)h * p.n + kend - kPStep + tid] =
+          (cp[0] + cp[kPStep] + cp[2 * kPStep] + cp[3 * kPStep]) * (1.f / kBlock);
+    }
+  }
+  if (kPass == 1 && kMass) {
     // the loop's last barrier orders every wave's parked sums before this
     const int nkb = (kend - kbeg) >> 7;
     if (tid < 2 * nkb) {
@@ -323,13 +361,14 @@ __global__ void route_mass_kernel(const float* mass, float* c_struct, int32_t* r
 
 }  // namespace
 
-hipError_t launch_proxy(const __bf16* q, const __bf16* k, float* amap, float* mass, float* row_lse, void* scratch,
-                        int hq, int hkv, int n, float scale, hipStream_t stream) {
+hipError_t launch_proxy(const __bf16* q, const __bf16* k, float* amap, float* mass, float* colmass, float* row_lse,
+                        void* scratch, int hq, int hkv, int n, float scale, hipStream_t stream) {
   ProxyArgs a;
   a.q = q;
   a.k = k;
   a.amap = amap;
   a.mass = mass;
+  a.colmass = colmass;
   a.nchunks = proxy_chunks(n);
   a.part = (float*)scratch;
   a.lse2 = a.part + (size_t)hq * a.nchunks * kBlock * 2;
@@ -344,7 +383,9 @@ hipError_t launch_proxy(const __bf16* q, const __bf16* k, float* amap, float* ma
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const dim3 grid(a.nchunks, hq);
-  if (amap != nullptr && mass != nullptr)
+  if (colmass != nullptr)  // with the block masses, without the map
+    hipLaunchKernelGGL((proxy_pass_kernel<1, false, true, true>), grid, dim3(256), 0, stream, a);
+  else if (amap != nullptr && mass != nullptr)
     hipLaunchKernelGGL((proxy_pass_kernel<1, true, true>), grid, dim3(256), 0, stream, a);
   else if (amap != nullptr)
     hipLaunchKernelGGL((proxy_pass_kernel<1, true, false>), grid, dim3(256), 0, stream, a);

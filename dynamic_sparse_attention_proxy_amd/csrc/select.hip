@@ -423,6 +423,188 @@ __global__ __launch_bounds__(256) void vs_expand_kernel(const int32_t* route, co
   }
 }
 
+// ---------------------------------------------------------------------------
+// Token-granular vertical selection (ai-feeds summary, method module 2: keep
+// the tokens clearly above the noise floor).  One workgroup per VS head over
+// its column masses c[j]: columns 0..127 are always kept (the sink tile);
+// the floor is alpha x the lower median (or the mean) of columns 128..n-1;
+// columns above it are kept, topped up to k_min tokens in all by the best
+// remaining ones (descending mass, ties to the lower index).  The median and
+// the top-up cut are exact radix selects over the masses' bit patterns
+// (non-negative floats order like their bits).  Output: the kept columns past
+// the sink tile in ascending order, their count, and per query block qb the
+// number of them below 128 qb; v_mask becomes block 0 only (the sink tile).
+// ---------------------------------------------------------------------------
+
+constexpr int kTokThreads = 1024;
+constexpr int kTokPer = 8;  // consecutive columns per thread in the in-order passes
+
+struct TokArgs {
+  const float* colmass;
+  const int32_t* route;
+  int32_t* cols;       // [Hq][n]
+  int32_t* ncols;      // [Hq]
+  int32_t* col_below;  // [Hq][N]
+  int32_t* vmask;      // [Hq][N]
+  float* floor_v;      // [Hq]
+  int32_t* n_v;        // [Hq]
+  int n;
+  int nblk;
+  float alpha;
+  int kmin_tokens;
+  int nf_stat;
+};
+
+// Histogram of 8-bit digits with one LDS atomic per run of equal digits led
+// by the wave's first active lane (column masses share their high bits).
+__device__ __forceinline__ void hist_add(uint32_t* hist, bool valid, uint32_t digit, int lane) {
+  const uint32_t mine = valid ? digit : 0xffffffffu;
+  const uint32_t lead = __builtin_amdgcn_readfirstlane(mine);
+  const bool same = mine == lead;
+  const uint64_t bal = __ballot(same);
+  if (same) {
+    if (lead != 0xffffffffu && lane == (int)__builtin_ctzll(bal)) atomicAdd(&hist[lead], (uint32_t)__popcll(bal));
+  } else if (valid) {
+    atomicAdd(&hist[digit], 1u);
+  }
+}
+
+// The bit pattern of rank k (0-based, ascending) among the candidate columns
+// j in [kBlock, n) with (only_le ? bits <= le_bits : true).
+__device__ uint32_t tok_radix_kth(const float* x, int n, bool only_le, uint32_t le_bits, uint32_t k, uint32_t* hist,
+                                  int* sel_digit, uint32_t* sel_below, int tid) {
+  const int lane = tid & 63;
+  uint32_t prefix = 0, pmask = 0, below = 0;
+  for (int shift = 24; shift >= 0; shift -= 8) {
+    for (int i = tid; i < 256; i += kTokThreads) hist[i] = 0;
+    __syncthreads();
+    for (int j0 = kBlock; j0 < n; j0 += kTokThreads * kTokPer) {
+      uint32_t u[kTokPer];
+#pragma unroll
+      for (int e = 0; e < kTokPer; ++e) {  // all loads first: kTokPer in flight
+        const int j = j0 + e * kTokThreads + tid;
+        u[e] = j < n ? __float_as_uint(x[j]) : 0xffffffffu;
+      }
+#pragma unroll
+      for (int e = 0; e < kTokPer; ++e) {
+        const bool v = u[e] != 0xffffffffu && (u[e] & pmask) == prefix && (!only_le || u[e] <= le_bits);
+        hist_add(hist, v, (u[e] >> shift) & 255u, lane);
+      }
+    }
+    __syncthreads();
+    if (tid < 64) find_digit(hist, below, k + 1, lane, sel_digit, sel_below);
+    __syncthreads();
+    const int d = *sel_digit;
+    below = *sel_below;
+    prefix |= (uint32_t)min(d, 255) << shift;
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  return prefix;
+}
+
+__global__ __launch_bounds__(kTokThreads) void tok_select_kernel(TokArgs p) {
+  __shared__ uint32_t hist[256];
+  __shared__ int sel_digit;
+  __shared__ uint32_t sel_below;
+  __shared__ float redf[20];
+  __shared__ int redi[20];
+  const int h = blockIdx.x, tid = threadIdx.x, N = p.nblk, n = p.n;
+  int32_t* below_out = p.col_below + (size_t)h * N;
+  if (p.route[h] != 1) {
+    for (int b = tid; b < N; b += kTokThreads) below_out[b] = 0;
+    if (tid == 0) p.ncols[h] = 0;
+    return;
+  }
+  const float* x = p.colmass + (size_t)h * n;
+  const int m = n - kBlock;  // candidates
+  float mu;
+  if (p.nf_stat == 0) {
+    mu = __uint_as_float(tok_radix_kth(x, n, false, 0u, (uint32_t)((m - 1) / 2), hist, &sel_digit, &sel_below, tid));
+  } else {
+    float sacc = 0.f;
+    for (int j = kBlock + tid; j < n; j += kTokThreads) sacc += x[j];
+    mu = block_sum_f(sacc, redf, tid, kTokThreads) / (float)m;
+  }
+  const float T = p.alpha * mu;
+  int above = 0;
+  for (int j = kBlock + tid; j < n; j += kTokThreads) above += x[j] > T ? 1 : 0;
+  above = block_sum_i(above, redi, tid, kTokThreads);
+  const int need = max(0, min(p.kmin_tokens, n) - kBlock - above);
+  // top-up cut: the need-th largest among the columns at or below the floor
+  uint32_t cut = 0xffffffffu;
+  int ties = 0;
+  if (need > 0) {
+    const uint32_t tbits = __float_as_uint(T);
+    const int le = m - above;
+    cut = tok_radix_kth(x, n, true, tbits, (uint32_t)(le - need), hist, &sel_digit, &sel_below, tid);
+    int gt = 0;
+    for (int j = kBlock + tid; j < n; j += kTokThreads) {
+      const float xv = x[j];
+      gt += (!(xv > T) && __float_as_uint(xv) > cut) ? 1 : 0;
+    }
+    gt = block_sum_i(gt, redi, tid, kTokThreads);
+    ties = need - gt;  // columns equal to the cut value taken, lowest index first
+  }
+  // in-order compaction, kTokPer consecutive columns per thread
+  int kept_before = 0, ties_before = 0;
+  for (int c0 = kBlock; c0 < n; c0 += kTokThreads * kTokPer) {
+    const int jb = c0 + kTokPer * tid;
+    uint32_t tie_bits = 0;
+    int nt = 0;
+#pragma unroll
+    for (int e = 0; e < kTokPer; ++e) {
+      const int j = jb + e;
+      if (j < n) {
+        const float xv = x[j];
+        if (need > 0 && !(xv > T) && __float_as_uint(xv) == cut) {
+          tie_bits |= 1u << e;
+          ++nt;
+        }
+      }
+    }
+    int tie_tot;
+    const int tie_excl = ties_before + block_exclusive_scan(nt, redi, tid, kTokThreads, &tie_tot);
+    ties_before += tie_tot;
+    uint32_t keep_bits = 0;
+    int nk = 0, tr = tie_excl;
+#pragma unroll
+    for (int e = 0; e < kTokPer; ++e) {
+      const int j = jb + e;
+      if (j < n) {
+        const float xv = x[j];
+        bool keep = xv > T;
+        if (!keep && need > 0) {
+          const uint32_t u = __float_as_uint(xv);
+          if (u > cut) keep = true;
+          if (tie_bits & (1u << e)) keep = tr++ < ties;
+        }
+        if (keep) {
+          keep_bits |= 1u << e;
+          ++nk;
+        }
+      }
+    }
+    int kept_tot;
+    int pos = kept_before + block_exclusive_scan(nk, redi, tid, kTokThreads, &kept_tot);
+    int32_t* out = p.cols + (size_t)h * n;
+#pragma unroll
+    for (int e = 0; e < kTokPer; ++e) {
+      const int j = jb + e;
+      if (j < n && (j & (kBlock - 1)) == 0) below_out[j >> 7] = pos;  // kept columns below 128 qb
+      if (keep_bits & (1u << e)) out[pos++] = j;
+    }
+    kept_before += kept_tot;
+  }
+  for (int b = tid; b < N; b += kTokThreads) p.vmask[(size_t)h * N + b] = b == 0 ? 1 : 0;
+  if (tid == 0) {
+    below_out[0] = 0;
+    p.ncols[h] = kept_before;
+    p.floor_v[h] = T;
+    p.n_v[h] = kBlock + kept_before;
+  }
+}
+
 inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 inline int host_pow2_ceil(int x) {
@@ -472,7 +654,7 @@ SelectBuffers carve_select_workspace(void* ws, int hq, int hkv, int n) {
 hipError_t launch_select(const __bf16* q, const __bf16* k, const float* amap, const float* mass, const int32_t* route,
                          const SelectBuffers& b, int32_t* count, int32_t* idx, int hq, int hkv, int n, float scale,
                          float alpha, float gamma_pe, int kmin, int nf_stat, bool use_gamma, float gamma,
-                         hipStream_t stream) {
+                         const TokenCols* tok, hipStream_t stream) {
   const int N = n / kBlock;
   hipError_t e;
   const float* lo = mass;
@@ -506,6 +688,24 @@ hipError_t launch_select(const __bf16* q, const __bf16* k, const float* amap, co
   const size_t vs_lds = (size_t)va.pw2 * 8 + (size_t)N * 4 + (size_t)N;
   hipLaunchKernelGGL(vs_select_kernel, dim3(hq, 2), dim3(kVsThreads), vs_lds, stream, va);
   if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (tok != nullptr) {  // token-granular vertical: replaces the vertical block selection
+    TokArgs ta;
+    ta.colmass = tok->colmass;
+    ta.route = route;
+    ta.cols = tok->cols;
+    ta.ncols = tok->ncols;
+    ta.col_below = tok->col_below;
+    ta.vmask = b.vmask;
+    ta.floor_v = b.floor_v;
+    ta.n_v = b.n_v;
+    ta.n = n;
+    ta.nblk = N;
+    ta.alpha = alpha;
+    ta.kmin_tokens = kmin * kBlock;
+    ta.nf_stat = nf_stat;
+    hipLaunchKernelGGL(tok_select_kernel, dim3(hq), dim3(kTokThreads), 0, stream, ta);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
 
   hipLaunchKernelGGL(pe_pool_kernel, dim3(N, hq + hkv), dim3(256), 0, stream, q, k, route, b.qbar, b.kbar, hq, n);
   if ((e = hipGetLastError()) != hipSuccess) return e;

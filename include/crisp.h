@@ -205,6 +205,52 @@ CRISP_API crisp_status crisp_sparse_attn(const crisp_dims* dims, const void* q, 
 CRISP_API crisp_status crisp_dense_attn(const crisp_dims* dims, const void* q, const void* k, const void* v, void* out,
                               int32_t out_is_fp32, float* lse, void* stream);
 
+/* Token-granular Vertical-Slash (ai-feeds summary, method module 2: keep
+ * the tokens whose mass stands clearly above the noise floor; ai.info
+ * summary, "Methodology in Plain English": k_min = 1024 tokens).  Vertical
+ * columns are selected one by one; slash bands keep the block rule (kept
+ * single offsets far from the diagonal scatter over nearly every band).
+ * The chain is crisp_proxy_cols -> crisp_route -> crisp_select_tokens ->
+ * crisp_sparse_attn (fp32 out, with lse) -> crisp_sparse_attn_cols. */
+
+/* Proxy with the block masses (as crisp_proxy) and the column masses:
+ *   col_mass[h][j] = (1/128) sum_r attn_map[h][r][j]          [Hq][n] fp32
+ * without writing the map.  Arguments otherwise as crisp_proxy. */
+CRISP_API crisp_status crisp_proxy_cols(const crisp_dims* dims, const void* q, const void* k, float* block_mass,
+                              float* col_mass, float* row_lse, void* partials, size_t partials_bytes,
+                              void* stream);
+
+/* Selection as crisp_select (block_mass required), except the vertical
+ * direction of VS heads: columns 0..127 (the sink tile) are always kept and
+ * excluded from the floor; the floor is alpha times the lower median (or
+ * mean) of col_mass over columns 128..n-1; every column above it is kept,
+ * topped up to kmin_blocks * 128 columns in all by the best remaining ones
+ * (descending mass, ties to the lower index).  The tile lists then hold key
+ * block 0, the slash bands' tiles and the diagonal; out->v_mask is block 0
+ * only, out->floor_v the column floor and out->n_v the kept columns in all.
+ *   cols      [Hq][n] int32: kept columns >= 128 of head h, ascending, in
+ *             cols[h][0 .. ncols[h]) (0 for PE heads)
+ *   ncols     [Hq] int32
+ *   col_below [Hq][N] int32: how many of them lie below 128 qb
+ * The column floor, the top-up cut and the compaction are exact and
+ * deterministic (radix selects and in-order scans). */
+CRISP_API crisp_status crisp_select_tokens(const crisp_dims* dims, const crisp_cfg* cfg, const void* q, const void* k,
+                                 const float* block_mass, const float* col_mass, const int32_t* route,
+                                 const crisp_blocks* out, int32_t* cols, int32_t* ncols, int32_t* col_below,
+                                 void* workspace, size_t workspace_bytes, void* stream);
+
+/* Adds the kept columns to a tile attention already in `out` (fp32,
+ * [Hq][n][d]) and `lse` ([Hq][n], natural log), as written by
+ * crisp_sparse_attn on the same count/idx.  For query i in block qb the
+ * key set becomes the listed tiles (keys j <= i) plus the columns
+ * cols[h][0 .. col_below[h][qb]) that lie outside the listed tiles; the two
+ * softmaxes are merged exactly and out/lse updated in place.  Column
+ * entries are clamped to [0, 128 qb - 1] and counts to [0, n]; entries must
+ * be distinct for the result to mean anything. */
+CRISP_API crisp_status crisp_sparse_attn_cols(const crisp_dims* dims, const void* q, const void* k, const void* v,
+                                    const int32_t* count, const int32_t* idx, const int32_t* cols,
+                                    const int32_t* col_below, float* out, float* lse, void* stream);
+
 /* Comparison routing signal - FlexPrefill's Jensen-Shannon routing, the one
  * C_struct replaces (ai.info summary, "Key Contributions" items 1 and 2:
  * C_struct drops its pooled matmul and KL divergence and reproduces its

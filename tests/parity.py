@@ -75,6 +75,31 @@ def check_noise_floor_mask(x: np.ndarray, alpha: float, kmin: int, stat: int, ma
     return mask_o
 
 
+def check_token_cols(c: np.ndarray, alpha: float, kmin_tokens: int, stat: int, cols_gpu: Sequence[int],
+                     floor_gpu: float, retained: int = 128):
+    """Kept columns past the retained ones: exact, except columns whose
+    oracle mass lies within REL_SEL of the floor or of the k_min cut."""
+    mask_o, T = O.token_noise_floor_select(c, alpha, kmin_tokens, retained, stat)
+    assert near(floor_gpu, T), f"column floor {floor_gpu} vs oracle {T}"
+    n = c.shape[0]
+    got = np.zeros(n, dtype=bool)
+    got[:retained] = True
+    cols = np.asarray(cols_gpu, dtype=np.int64)
+    assert np.all(np.diff(cols) > 0), "kept columns must be ascending without repeats"
+    assert cols.size == 0 or cols[0] >= retained
+    got[cols] = True
+    bounds = [T]
+    want = min(kmin_tokens, n)
+    if want - retained >= 1:
+        order = O._order_desc(c, list(range(retained, n)))
+        bounds.append(float(c[order[want - retained - 1]]))
+    diff = np.nonzero(mask_o != got)[0]
+    for j in diff:
+        assert any(near(float(c[j]), t) for t in bounds), (
+            f"column {j} (mass {c[j]}) differs away from the boundaries {bounds}")
+    return mask_o
+
+
 def gamma_candidates(x: np.ndarray, items: Sequence[int], gamma: float):
     """Prefix lengths the GPU may legitimately take, with the cut score of each."""
     order = O._order_desc(x, list(items))

@@ -1,0 +1,183 @@
+"""GPU parity of token-granular Vertical-Slash selection and of the mixed
+tile-plus-column attention against the fp64 oracle (needs an MI355X).
+
+Every call goes through the C ABI; the oracle sees the same bf16 bits."""
+import numpy as np
+import pytest
+import torch
+
+from dynamic_sparse_attention_proxy_amd import binding as B
+from dynamic_sparse_attention_proxy_amd import synth
+from oracle import crisp_oracle as O
+from parity import check_attention, check_noise_floor_mask, check_token_cols, gpu_lists, to64
+
+pytestmark = pytest.mark.gpu
+
+BLK = 128
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    B.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def _inputs(hq, hkv, n, seed):
+    print(f"[gen] tokens {hq}x{hkv} n={n} seed={seed}", flush=True)
+    if hq == 1:
+        return synth.make_inputs(synth.workload(0), device="cuda")
+    return synth.make_inputs(synth.custom(hq, hkv, n, seed=seed, needles=8), device="cuda")
+
+
+def _token_chain(x, cfg):
+    hq, hkv, n = x.q.shape[0], x.k.shape[0], x.q.shape[1]
+    dims = B.make_dims(hq, hkv, n)
+    bufs = B.CrispBuffers(dims, tokens=True)
+    B.crisp_prefill_tokens(dims, cfg, x.q, x.k, x.v, bufs)
+    torch.cuda.synchronize()
+    return dims, bufs
+
+
+def test_column_masses_match_oracle_and_block_masses_unchanged():
+    for hq, hkv, n in [(1, 1, 4096), (8, 2, 4480)]:
+        x = _inputs(hq, hkv, n, 41)
+        dims = B.make_dims(hq, hkv, n)
+        N = n // BLK
+        mass = torch.empty((2, hq, N), dtype=torch.float32, device="cuda")
+        mass_ref = torch.empty_like(mass)
+        cm = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+        part = torch.empty(B.crisp_proxy_scratch_bytes(dims), dtype=torch.uint8, device="cuda")
+        B.crisp_proxy_cols(dims, x.q, x.k, mass, cm, None, part)
+        B.crisp_proxy(dims, x.q, x.k, None, partials=part, block_mass=mass_ref)
+        torch.cuda.synchronize()
+        assert torch.equal(mass, mass_ref), "column variant changed the block masses"
+        cg = cm.cpu().numpy().astype(np.float64)
+        for h in range(hq):
+            g = h * hkv // hq
+            A, _ = O.proxy_map(to64(x.q[h, n - BLK:]), to64(x.k[g]), dims.scale)
+            c, _ = O.token_scores(A)
+            np.testing.assert_allclose(cg[h], c, rtol=1e-4, atol=1e-10, err_msg=f"head {h}")
+
+
+@pytest.mark.parametrize("alpha,stat,kmin", [(1.25, B.NF_MEDIAN, 8), (1.0, B.NF_MEDIAN, 8), (1.25, B.NF_MEAN, 8),
+                                             (3.0, B.NF_MEDIAN, 20)])
+def test_token_selection_matches_oracle(alpha, stat, kmin):
+    """Forced VS on a GQA layer with needles: the kept columns, the column
+    floor and the slash bands, and the tile lists from them.  alpha = 3 with
+    k_min = 20 blocks makes the top-up decide most columns."""
+    hq, hkv, n = 4, 2, 8192
+    x = _inputs(hq, hkv, n, 43)
+    cfg = B.make_cfg(alpha=alpha, nf_stat=stat, kmin_blocks=kmin, route_override=B.ROUTE_FORCE_VS)
+    dims, bufs = _token_chain(x, cfg)
+    N = n // BLK
+    cols = bufs.cols.cpu().numpy()
+    ncols = bufs.ncols.cpu().numpy()
+    below = bufs.col_below.cpu().numpy()
+    count = bufs.blocks["count"].cpu().numpy()
+    idx = bufs.blocks["idx"].cpu().numpy()
+    smask = bufs.blocks["s_mask"].cpu().numpy()
+    vmask = bufs.blocks["v_mask"].cpu().numpy()
+    floor_v = bufs.blocks["floor_v"].cpu().numpy()
+    floor_s = bufs.blocks["floor_s"].cpu().numpy()
+    n_v = bufs.blocks["n_v"].cpu().numpy()
+    for h in range(hq):
+        g = h * hkv // hq
+        A, _ = O.proxy_map(to64(x.q[h, n - BLK:]), to64(x.k[g]), dims.scale)
+        c, dg = O.token_scores(A)
+        _, sl = O.pooled_scores(c, dg)
+        kept = cols[h, :ncols[h]]
+        check_token_cols(c, alpha, kmin * BLK, stat, kept, float(floor_v[h]))
+        assert n_v[h] == BLK + ncols[h]
+        check_noise_floor_mask(sl, alpha, kmin, stat, smask[h], float(floor_s[h]))
+        assert vmask[h].tolist() == [1] + [0] * (N - 1)
+        # per query block: kept columns below it, and the tile lists
+        for qb in range(N):
+            assert below[h, qb] == int(np.sum(kept < qb * BLK)), (h, qb)
+        lists = gpu_lists(count, idx, h, N)
+        vb = np.zeros(N, dtype=bool)
+        vb[0] = True
+        assert lists == O.vs_lists(vb, smask[h].astype(bool)), f"head {h} tile lists"
+
+
+def test_token_chain_attention_matches_oracle():
+    hq, hkv, n = 4, 2, 8192
+    x = _inputs(hq, hkv, n, 47)
+    cfg = B.make_cfg(route_override=B.ROUTE_FORCE_VS)
+    dims, bufs = _token_chain(x, cfg)
+    N = n // BLK
+    cols = bufs.cols.cpu().numpy()
+    ncols = bufs.ncols.cpu().numpy()
+    count = bufs.blocks["count"].cpu().numpy()
+    idx = bufs.blocks["idx"].cpu().numpy()
+    out = bufs.out.cpu().numpy()
+    lse = bufs.lse.cpu().numpy()
+    qbs = [0, 1, 2, 17, 40, N - 2, N - 1]
+    for h in (0, hq - 1):
+        g = h * hkv // hq
+        q, k, v = to64(x.q[h]), to64(x.k[g]), to64(x.v[g])
+        lists = gpu_lists(count, idx, h, N)
+        ref = O.attention_rows_mixed(q, k, v, lists, cols[h, :ncols[h]].tolist(), dims.scale, qbs)
+        for qb in qbs:
+            rows = slice(qb * BLK, (qb + 1) * BLK)
+            check_attention(out[h, rows], ref[qb][0], f"head {h} qb {qb}")
+            np.testing.assert_allclose(lse[h, rows], ref[qb][1], rtol=2e-5, atol=2e-5)
+
+
+@pytest.mark.parametrize("ncol", [1, 64, 200])
+def test_column_kernel_on_given_lists_and_columns(ncol):
+    """crisp_sparse_attn_cols on random tile lists and random columns (some
+    inside listed tiles, counts that leave partial 64-column steps)."""
+    hq, hkv, n = 4, 2, 2048
+    N = n // BLK
+    x = _inputs(hq, hkv, n, 53 + ncol)
+    dims = B.make_dims(hq, hkv, n)
+    rng = np.random.default_rng(ncol)
+    lists_all, cols_all = [], []
+    for h in range(hq):
+        lists = [sorted(set(rng.choice(qb + 1, size=int(rng.integers(1, qb + 2)), replace=False).tolist()) | {qb})
+                 for qb in range(N)]
+        lists_all.append(lists)
+        cols_all.append(np.sort(rng.choice(np.arange(BLK, n), size=ncol, replace=False)).astype(np.int32))
+    count = np.zeros((hq, N), np.int32)
+    idx = np.zeros(hq * N * (N + 1) // 2, np.int32)
+    cols = np.zeros((hq, n), np.int32)
+    below = np.zeros((hq, N), np.int32)
+    for h in range(hq):
+        base = h * N * (N + 1) // 2
+        for qb, l in enumerate(lists_all[h]):
+            count[h, qb] = len(l)
+            s = base + qb * (qb + 1) // 2
+            idx[s:s + len(l)] = l
+            below[h, qb] = int(np.sum(cols_all[h] < qb * BLK))
+        cols[h, :ncol] = cols_all[h]
+    cd, idd, cold, bd = (torch.from_numpy(a).cuda() for a in (count, idx, cols, below))
+    out = torch.empty((hq, n, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    B.crisp_sparse_attn(dims, x.q, x.k, x.v, cd, idd, out, lse)
+    B.crisp_sparse_attn_cols(dims, x.q, x.k, x.v, cd, idd, cold, bd, out, lse)
+    torch.cuda.synchronize()
+    og, lg = out.cpu().numpy(), lse.cpu().numpy()
+    for h in range(hq):
+        g = h * hkv // hq
+        q, k, v = to64(x.q[h]), to64(x.k[g]), to64(x.v[g])
+        ref = O.attention_rows_mixed(q, k, v, lists_all[h], cols_all[h].tolist(), dims.scale, range(N))
+        for qb in range(N):
+            rows = slice(qb * BLK, (qb + 1) * BLK)
+            check_attention(og[h, rows], ref[qb][0], f"head {h} qb {qb}")
+            np.testing.assert_allclose(lg[h, rows], ref[qb][1], rtol=2e-5, atol=2e-5)
+
+
+def test_token_chain_is_deterministic():
+    hq, hkv, n = 4, 2, 8192
+    x = _inputs(hq, hkv, n, 59)
+    cfg = B.make_cfg(route_override=B.ROUTE_FORCE_VS)
+    _, b1 = _token_chain(x, cfg)
+    _, b2 = _token_chain(x, cfg)
+    for name in ("col_mass", "ncols", "col_below", "out", "lse"):
+        assert torch.equal(getattr(b1, name), getattr(b2, name)), name
+    for h in range(hq):
+        k = int(b1.ncols[h])
+        assert torch.equal(b1.cols[h, :k], b2.cols[h, :k])
