@@ -192,6 +192,25 @@ def run_workload(torch, B, synth, wname, args, cfg_kw, compare):
         r["n_s_mean"] = float(bufs.blocks["n_s"].float().mean())
         res[f"forced_vs_alpha{alpha}"] = r
         log(f"{w.name}: forced-VS alpha {alpha}: {r['ms_per_layer']:.2f} ms, {r['tiles']} tiles")
+    # token-granular vertical selection, forced VS
+    tb = B.CrispBuffers(dims, tokens=True)
+    for alpha in (1.25,):
+        c = B.make_cfg(**dict(cfg_kw, route_override=B.ROUTE_FORCE_VS, alpha=alpha))
+        r = timed_token_chain(torch, B, x, dims, tb, c, args.compare_steps, 1)
+        r["tiles"] = int(tb.blocks["count"].sum().item())
+        r["tile_frac"] = r["tiles"] / (w.num_q_heads * N * (N + 1) / 2)
+        r["kept_columns_mean"] = float(tb.ncols.float().mean())
+        r["gathered_columns"] = int(tb.col_below.sum().item())
+        r["needle_recall_last_block"] = needle_recall(x, tb, N, tokens=True)
+        res[f"forced_vs_tokens_alpha{alpha}"] = r
+        log(f"{w.name}: forced-VS tokens alpha {alpha}: {r['ms_per_layer']:.2f} ms, {r['tiles']} tiles + "
+            f"{r['gathered_columns']} gathered columns, needle recall {r['needle_recall_last_block']:.3f}")
+    del tb
+    torch.cuda.empty_cache()
+    c = B.make_cfg(**dict(cfg_kw, route_override=B.ROUTE_FORCE_VS, alpha=1.25))
+    chain(c, None)
+    torch.cuda.synchronize()
+    res["forced_vs_alpha1.25"]["needle_recall_last_block"] = needle_recall(x, bufs, N, tokens=False)
     if compare:
         for gamma in (0.95, 0.97):
             c = B.make_cfg(**dict(cfg_kw, route_override=B.ROUTE_FORCE_VS))
@@ -205,6 +224,72 @@ def run_workload(torch, B, synth, wname, args, cfg_kw, compare):
         if isinstance(res[key], dict) and "ms_per_layer" in res[key] and key != "dense":
             res[key]["speedup_vs_dense"] = dense_ms / res[key]["ms_per_layer"]
     return res, x, dims
+
+
+def timed_token_chain(torch, B, x, dims, tb, cfg, steps, warmup):
+    """The token-granular chain (forced route in cfg): per-stage event times."""
+    names = ("proxy_cols", "route", "select_tokens", "attn_tiles", "attn_cols")
+
+    def one(marks=None):
+        t = []
+
+        def mark():
+            if marks is not None:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record()
+                t.append(e)
+
+        mark()
+        B.crisp_proxy_cols(dims, x.q, x.k, tb.block_mass, tb.col_mass, tb.row_lse, tb.partials)
+        mark()
+        B.crisp_route(dims, cfg, None, tb.c_struct, tb.route, block_mass=tb.block_mass)
+        mark()
+        B.crisp_select_tokens(dims, cfg, x.q, x.k, tb.block_mass, tb.col_mass, tb.route, tb.blocks, tb.cols,
+                              tb.ncols, tb.col_below, tb.workspace)
+        mark()
+        B.crisp_sparse_attn(dims, x.q, x.k, x.v, tb.blocks["count"], tb.blocks["idx"], tb.out, tb.lse)
+        mark()
+        B.crisp_sparse_attn_cols(dims, x.q, x.k, x.v, tb.blocks["count"], tb.blocks["idx"], tb.cols, tb.col_below,
+                                 tb.out, tb.lse)
+        mark()
+        if marks is not None:
+            marks.append(t)
+
+    for _ in range(warmup):
+        one()
+    torch.cuda.synchronize()
+    marks = []
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        one(marks)
+    e1.record()
+    torch.cuda.synchronize()
+    stage = {nm: sorted(m[i].elapsed_time(m[i + 1]) for m in marks)[len(marks) // 2] for i, nm in enumerate(names)}
+    return {"ms_per_layer": e0.elapsed_time(e1) / steps, "stage_ms_median": {k: round(v, 4) for k, v in stage.items()}}
+
+
+def needle_recall(x, bufs, N, tokens):
+    """Share of (sink head, needle) pairs whose key the last query block
+    attends: its key block is listed, or (token chain) it is a kept column."""
+    qpg = x.q.shape[0] // x.k.shape[0]
+    count = bufs.blocks["count"].cpu().numpy()
+    idx = bufs.blocks["idx"].cpu().numpy()
+    if tokens:
+        cols = bufs.cols.cpu().numpy()
+        ncols = bufs.ncols.cpu().numpy()
+    hit = tot = 0
+    base_last = (N - 1) * N // 2
+    for h in x.sink_heads:
+        g = h // qpg
+        s = h * (N * (N + 1) // 2) + base_last
+        listed = set(idx[s:s + int(count[h, N - 1])].tolist())
+        kept = set(cols[h, :int(ncols[h])].tolist()) if tokens else set()
+        for p in x.needle_pos.get(g, []):
+            tot += 1
+            hit += int((p // 128) in listed or p in kept)
+    return hit / tot if tot else None
 
 
 def time_map_path(torch, B, x, dims, cfg, steps):

@@ -10,7 +10,7 @@ import torch
 from dynamic_sparse_attention_proxy_amd import binding as B
 from dynamic_sparse_attention_proxy_amd import synth
 from oracle import crisp_oracle as O
-from parity import (JSD_ABS, JSD_REL, REL_CSTRUCT, check_attention, check_gamma_set, check_noise_floor_mask, check_pe_lists,
+from parity import (JSD_ABS, JSD_REL, REL_CSTRUCT, check_attention, check_token_cols, check_gamma_set, check_noise_floor_mask, check_pe_lists,
                     check_route, gpu_lists, to64)
 
 pytestmark = pytest.mark.gpu
@@ -105,6 +105,51 @@ def test_layer_route_auto(widx):
     torch.cuda.synchronize()
     for h in sampled:
         assert torch.equal(outb[h], bufs.out[h].to(torch.bfloat16))
+
+
+def test_token_chain_512k():
+    """Token-granular vertical selection at the 512k layer, forced VS, in
+    the benchmark's launch configuration: column masses, kept columns, slash
+    bands and tile lists of two sampled heads, and the mixed attention of
+    sampled query blocks."""
+    w = synth.workload(4)
+    print(f"[fullsize] {w.name} token chain", flush=True)
+    x = synth.make_inputs(w, device="cuda")
+    hq, hkv, n = w.num_q_heads, w.num_kv_heads, w.seq_len
+    N = n // BLK
+    qpg = hq // hkv
+    dims = B.make_dims(hq, hkv, n)
+    cfg = B.make_cfg(route_override=B.ROUTE_FORCE_VS)
+    bufs = B.CrispBuffers(dims, tokens=True)
+    B.crisp_prefill_tokens(dims, cfg, x.q, x.k, x.v, bufs)
+    torch.cuda.synchronize()
+    count = bufs.blocks["count"].cpu().numpy()
+    idx = bufs.blocks["idx"].cpu().numpy()
+    for h in (0, hq - 1):
+        g = h // qpg
+        q, k, v = to64(x.q[h]), to64(x.k[g]), to64(x.v[g])
+        A, _ = O.proxy_map(q[n - BLK:], k, dims.scale)
+        ct, dg = O.token_scores(A)
+        del A
+        _, ss = O.pooled_scores(ct, dg)
+        np.testing.assert_allclose(bufs.col_mass[h].cpu().numpy(), ct, rtol=1e-3, atol=1e-12)
+        kept = bufs.cols[h, :int(bufs.ncols[h])].cpu().numpy()
+        check_token_cols(ct, cfg.alpha, 8 * BLK, 0, kept, float(bufs.blocks["floor_v"][h]))
+        below = bufs.col_below[h].cpu().numpy()
+        assert below.tolist() == [int(np.sum(kept < qb * BLK)) for qb in range(N)]
+        sm = bufs.blocks["s_mask"][h].cpu().numpy()
+        check_noise_floor_mask(ss, cfg.alpha, 8, 0, sm, float(bufs.blocks["floor_s"][h]))
+        lists = gpu_lists(count, idx, h, N)
+        vb = np.zeros(N, dtype=bool)
+        vb[0] = True
+        assert lists == O.vs_lists(vb, sm.astype(bool))
+        qbs = _sample_qbs(N, 70 + h)
+        ref = O.attention_rows_mixed(q, k, v, lists, kept.tolist(), dims.scale, qbs)
+        og = bufs.out[h].cpu().numpy()
+        lg = bufs.lse[h].cpu().numpy()
+        for qb in qbs:
+            check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"tokens h {h} qb {qb}")
+            np.testing.assert_allclose(lg[qb * BLK:(qb + 1) * BLK], ref[qb][1], rtol=2e-5, atol=2e-5)
 
 
 @pytest.mark.parametrize("widx", [2, 4])
