@@ -181,85 +181,164 @@ __global__ __launch_bounds__(kColThreads, 1) void col_attn_kernel(ColArgs p) {
   const int nchunks = (cnt + kIdxChunk - 1) / kIdxChunk;
   // a step issues the gather three steps ahead
   auto issues = [&](int s) { return s + kCStages - 1 < nsteps; };
+
+  // Slot mask of step s for this wave's query block.
+  auto mask_of = [&](int s) -> uint64_t {
+    const int slot = s * kCStep + lane;
+    const int c = cidx[(s >> 5) & 1][(s & 31) * kCStep + lane];
+    const bool ok = slot < cnt_mine && ((tbits[blk][c >> 12] >> ((c >> 7) & 31)) & 1u) == 0;
+    return __ballot(ok);
+  };
+  auto kread = [&](int s, int t) -> bf16x8 {  // K operand of MFMA t (key half t & 1, d slice t / 2)
+    const char* kb8 = (const char*)kst[s & (kCStages - 1)];
+    return as_bf16x8(*(const u32x4*)(kb8 + k_off[t >> 1] + (t & 1) * 8192));
+  };
+  auto vread = [&](int s, int u) -> bf16x8 {  // V^T operand of PV MFMA u (d slice u & 3, P operand u / 4)
+    __attribute__((address_space(3))) char* vb8 =
+        (__attribute__((address_space(3))) char*)vst[s & (kCStages - 1)];
+    const int db = u & 3, f = u >> 2;
+    const int off = v_base[db] + (32 * (f >> 1) + 16 * (f & 1)) * 256;
+    const bf16x4 lo = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4c*)(vb8 + off)));
+    const bf16x4 hi =
+        __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4c*)(vb8 + off + 4 * 256)));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+  };
+  // register v < 8 of lane group lg holds slot 8lg + v, v >= 8 slot 16 + 8lg + (v - 8)
+  auto lane_bits = [&](uint64_t m, int kb2) -> uint32_t {
+    const uint32_t mh = (uint32_t)(m >> (32 * kb2));
+    return ((mh >> (8 * lg)) & 0xffu) | (((mh >> (16 + 8 * lg)) & 0xffu) << 8);
+  };
+  auto row_max = [&](const f32x16 (&sc)[2]) -> float {
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kb2][v]);
+    return fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
+  };
+  // Probabilities of a step against m_run, packed as the PV B operands.
+  auto exps = [&](const f32x16 (&sc)[2], bf16x8 (&pb)[4]) -> float {
+    float ls = 0.f;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+      for (int f = 0; f < 2; ++f) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          x[i] = fast_exp2(fmaf(sc[kb2][8 * f + i], p.scale_log2, -m_run));
+          ls += x[i];
+        }
+        pb[2 * kb2 + f] = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+      }
+    return ls;
+  };
+
   for (int s = 0; s < kCStages - 1 && s < nsteps; ++s) gather(s);
-  // step 0's rows must have landed: at most the gathers of steps 1 and 2 (4 each) outstanding
+  // steps 0 and 1 must have landed: at most the gather of step 2 (4 per wave) outstanding
   if (nsteps >= 3)
-    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-  else if (nsteps == 2)
     asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
   else
     wait_dma();
   __syncthreads();
 
-  for (int s = 0; s < nsteps; ++s) {
-    const int st = s & (kCStages - 1);
+  // Iteration s: block 1 computes S_{s+1} = K_{s+1} Q^T (MFMA) beside the
+  // exps of the second key half of S_s (VALU); block 2 computes O += V_s P_s
+  // (MFMA) beside the masking of S_{s+1} and the exps of its first key half,
+  // carried to the next iteration in p_lo / ls_lo.  S_s arrives masked in
+  // `sc`.  Lazy running max: set from the first counted step and raised
+  // (rare) when a step's probabilities sum past kColSumLimit, the step's
+  // exps then redone from `sc`; any value keeps the result exact.
+  f32x16 sa[2], sb[2];
+  uint64_t m_cur = 0;
+  bf16x8 p_lo[2];
+  float ls_lo = 0.f;
+  bool lo_ready = false;  // p_lo / ls_lo hold the first key half of S_s against m_run
+  if (active) {
+    m_cur = mask_of(0);
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; ++kb2) {
+      f32x16 acc = {};
+#pragma unroll
+      for (int kk = 0; kk < 8; ++kk) acc = mfma32(kread(0, 2 * kk + kb2), qf[kk], acc);
+      sa[kb2] = acc;
+    }
+    if (m_cur != ~0ull) {
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+        const uint32_t bits = lane_bits(m_cur, kb2);
+#pragma unroll
+        for (int v = 0; v < 16; ++v)
+          if (!((bits >> v) & 1u)) sa[kb2][v] = -INFINITY;
+      }
+    }
+  }
+  // exps of one key half, packed as two PV B operands
+  auto half_exps = [&](const f32x16& x, bf16x8& pa, bf16x8& pbb) -> float {
+    float e[16], sum = 0.f;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      e[i] = fast_exp2(fmaf(x[i], p.scale_log2, -m_run));
+      sum += e[i];
+    }
+    pa = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
+    pbb = pack_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
+    return sum;
+  };
+
+  auto iter = [&](int s, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
     if (issues(s)) gather(s + kCStages - 1);
     const bool refill = (s & 31) == 0 && (s >> 5) + 1 < nchunks;
     int32_t nxt[4];
     if (refill) load_idx((s >> 5) + 1, nxt);
     if (active) {
-      // slot mask of this wave's query block
-      const int slot = s * kCStep + lane;
-      const int c = cidx[(s >> 5) & 1][(s & 31) * kCStep + lane];
-      const bool ok = slot < cnt_mine && ((tbits[blk][c >> 12] >> ((c >> 7) & 31)) & 1u) == 0;
-      const uint64_t mcur = __ballot(ok);
-      if (mcur != 0ull) {  // uniform per wave
-        const char* kb8 = (const char*)kst[st];
-        f32x16 sc[2];
+      const bool has_next = s + 1 < nsteps;
+      const uint64_t m_next = has_next ? mask_of(s + 1) : 0ull;
+      const bool cur_on = m_cur != 0ull;
+      if (cur_on && !started) {
+        m_run = row_max(sc);
+        started = true;
+        lo_ready = false;
+      }
+      if (cur_on && !lo_ready) ls_lo = half_exps(sc[0], p_lo[0], p_lo[1]);
+      bf16x8 pb[4];
+      float ls = 0.f;
+      if (has_next && cur_on) {
+        // block 1: MFMA t of S_{s+1} beside score t of the second key half of S_s
+        bf16x8 kr[4];
+        kr[0] = kread(s + 1, 0);
+        kr[1] = kread(s + 1, 1);
+        kr[2] = kread(s + 1, 2);
+        const f32x16 zero = {};
+        float e[16];
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-          for (int v = 0; v < 16; ++v) sc[kb2][v] = 0.f;
-#pragma unroll
-          for (int kk = 0; kk < 8; ++kk)
-            sc[kb2] = mfma32(as_bf16x8(*(const u32x4*)(kb8 + k_off[kk] + kb2 * 8192)), qf[kk], sc[kb2]);
+        for (int t = 0; t < 16; ++t) {
+          sn[t & 1] = mfma32(kr[t & 3], qf[t >> 1], t < 2 ? zero : sn[t & 1]);
+          if (t + 3 < 16) kr[(t + 3) & 3] = kread(s + 1, t + 3);
+          e[t] = fast_exp2(fmaf(sc[1][t], p.scale_log2, -m_run));
+          ls += e[t];
+          if ((t & 7) == 7)
+            pb[2 + (t >> 3)] = pack_bf16x8(e[t - 7], e[t - 6], e[t - 5], e[t - 4], e[t - 3], e[t - 2], e[t - 1], e[t]);
+          __builtin_amdgcn_sched_barrier(0);
         }
-        if (mcur != ~0ull) {  // a partial step: slots past the block or in a listed tile
+      } else {
+        if (has_next) {
 #pragma unroll
           for (int kb2 = 0; kb2 < 2; ++kb2) {
-            const uint32_t mh = (uint32_t)(mcur >> (32 * kb2));
-            // register v < 8 holds slot 8lg + v, v >= 8 slot 16 + 8lg + (v - 8)
-            const uint32_t bits = ((mh >> (8 * lg)) & 0xffu) | (((mh >> (16 + 8 * lg)) & 0xffu) << 8);
+            f32x16 acc = {};
 #pragma unroll
-            for (int v = 0; v < 16; ++v)
-              if (!((bits >> v) & 1u)) sc[kb2][v] = -INFINITY;
+            for (int kk = 0; kk < 8; ++kk) acc = mfma32(kread(s + 1, 2 * kk + kb2), qf[kk], acc);
+            sn[kb2] = acc;
           }
         }
-        // Lazy running max: set from the first counted step, raised only when
-        // a step's probabilities sum past kSumLimit (any value keeps the
-        // result exact; it only has to keep the exps in range).
-        auto row_max = [&]() -> float {
-          float mx = -INFINITY;
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kb2][v]);
-          return fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
-        };
-        if (!started) {
-          m_run = row_max();
-          started = true;
-        }
-        bf16x8 pb[4];
-        float ls = 0.f;
-        auto exps = [&]() {
-          ls = 0.f;
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int f = 0; f < 2; ++f) {
-              float x[8];
-#pragma unroll
-              for (int i = 0; i < 8; ++i) {
-                x[i] = fast_exp2(fmaf(sc[kb2][8 * f + i], p.scale_log2, -m_run));
-                ls += x[i];
-              }
-              pb[2 * kb2 + f] = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
-            }
-        };
-        exps();
-        if (__any(!(ls <= kColSumLimit))) {  // rare: raise the running max and redo the step
-          const float m_new = fmaxf(m_run, row_max());
+        if (cur_on) ls = half_exps(sc[1], pb[2], pb[3]);
+      }
+      if (cur_on) {
+        pb[0] = p_lo[0];
+        pb[1] = p_lo[1];
+        ls += ls_lo;
+        if (__any(!(ls <= kColSumLimit))) {  // rare: raise the running max, redo the step's exps
+          const float m_new = fmaxf(m_run, row_max(sc));
           const float alpha = fast_exp2(m_run - m_new);
 #pragma unroll
           for (int db = 0; db < 4; ++db)
@@ -267,33 +346,71 @@ __global__ __launch_bounds__(kColThreads, 1) void col_attn_kernel(ColArgs p) {
             for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
           l_run *= alpha;
           m_run = m_new;
-          exps();
+          ls = half_exps(sc[0], pb[0], pb[1]) + half_exps(sc[1], pb[2], pb[3]);
         }
         l_run += ls;
-        __attribute__((address_space(3))) char* vb8 = (__attribute__((address_space(3))) char*)vst[st];
+      }
+      // block 2: PV MFMA u beside the masking of scores 2u, 2u+1 of S_{s+1}
+      // and the exp of its score u (first key half)
+      const bool mask_next = has_next && m_next != ~0ull;
+      const bool next_lo = has_next && m_next != 0ull && started;
+      const uint32_t nb0 = lane_bits(m_next, 0), nb1 = lane_bits(m_next, 1);
+      float lsn = 0.f;
+      if (cur_on && next_lo) {
+        bf16x8 vr[4];
+        vr[0] = vread(s, 0);
+        vr[1] = vread(s, 1);
+        vr[2] = vread(s, 2);
+        float e[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-          const int db = u & 3, f = u >> 2;
-          const int off = v_base[db] + (32 * (f >> 1) + 16 * (f & 1)) * 256;
-          const bf16x4 lo =
-              __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4c*)(vb8 + off)));
-          const bf16x4 hi = __builtin_bit_cast(
-              bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4c*)(vb8 + off + 4 * 256)));
-          o[db] = mfma32(__builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7), pb[f], o[db]);
+          o[u & 3] = mfma32(vr[u & 3], pb[u >> 2], o[u & 3]);
+          if (u + 3 < 16) vr[(u + 3) & 3] = vread(s, u + 3);
+          if (mask_next) {
+#pragma unroll
+            for (int i = 2 * u; i < 2 * u + 2; ++i) {
+              const uint32_t bits = (i >> 4) ? nb1 : nb0;
+              if (!((bits >> (i & 15)) & 1u)) sn[i >> 4][i & 15] = -INFINITY;
+            }
+          }
+          e[u] = fast_exp2(fmaf(sn[0][u], p.scale_log2, -m_run));
+          lsn += e[u];
+          if ((u & 7) == 7)
+            p_lo[u >> 3] = pack_bf16x8(e[u - 7], e[u - 6], e[u - 5], e[u - 4], e[u - 3], e[u - 2], e[u - 1], e[u]);
+          __builtin_amdgcn_sched_barrier(0);
         }
+      } else {
+        if (cur_on) {
+#pragma unroll
+          for (int u = 0; u < 16; ++u) o[u & 3] = mfma32(vread(s, u), pb[u >> 2], o[u & 3]);
+        }
+        if (mask_next) {
+#pragma unroll
+          for (int i = 0; i < 32; ++i) {
+            const uint32_t bits = (i >> 4) ? nb1 : nb0;
+            if (!((bits >> (i & 15)) & 1u)) sn[i >> 4][i & 15] = -INFINITY;
+          }
+        }
+        if (next_lo) lsn = half_exps(sn[0], p_lo[0], p_lo[1]);
       }
+      ls_lo = lsn;
+      lo_ready = next_lo;
+      m_cur = m_next;
     }
     if (refill) store_idx((s >> 5) + 1, nxt);
-    // step s+1's rows must have landed; later gathers (4 per issuing step) may stay in flight
-    const int ahead = (issues(s) ? 1 : 0) + (s >= 1 && issues(s - 1) ? 1 : 0);
-    if (ahead == 2)
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-    else if (ahead == 1)
+    // K_{s+2} and V_{s+1} must have landed: only this iteration's gather may stay in flight
+    if (issues(s))
       asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
     else
       wait_dma();
     __syncthreads();
+  };
+  int s = 0;
+  for (; s + 1 < nsteps; s += 2) {
+    iter(s, sa, sb);
+    iter(s + 1, sb, sa);
   }
+  if (s < nsteps) iter(s, sa, sb);
 
   if (!active) return;
   // merge with the tile softmax of the same row
