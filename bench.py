@@ -57,6 +57,8 @@ def parse():
                     help="C_struct vs JSD routing agreement and routing cost on the five synthetic layers")
     ap.add_argument("--agreement-out", default="", help="also write the agreement report as JSON to this path")
     ap.add_argument("--tau-jsd", type=float, default=0.1, help="JSD distance threshold of the agreement report")
+    ap.add_argument("--token-chain", action="store_true",
+                    help="time only the token-granular chain (forced VS, alpha 1.25) on --workload (profiling runs)")
     return ap.parse_args()
 
 
@@ -611,6 +613,16 @@ def main():
         return
     if args.agreement:
         agreement(torch, B, synth, args)
+        return
+    if args.token_chain:
+        w = synth.workload(args.workload)
+        x = synth.make_inputs(w, device="cuda")
+        dims = B.make_dims(w.num_q_heads, w.num_kv_heads, w.seq_len)
+        tb = B.CrispBuffers(dims, tokens=True)
+        c = B.make_cfg(tau=0.5, alpha=1.25, gamma_pe=0.95, route_override=B.ROUTE_FORCE_VS)
+        r = timed_token_chain(torch, B, x, dims, tb, c, args.steps, args.warmup)
+        r["gathered_columns"] = int(tb.col_below.sum().item())
+        print(json.dumps({"workload": w.name, "token_chain": r}))
         return
     if args.calibrate_copy:
         src = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
