@@ -390,10 +390,15 @@ def cpu_baseline(q, k, v, dims, res, cfg_kw):
     lists = {qb: O.pe_row_select(qbar, kbar, qb, dims.scale, ocfg.gamma_pe) for qb in rows}
     t_rows = time.perf_counter() - t0
     t_pe_head = t_rows / sum(qb + 1 for qb in rows) * (N * (N + 1) / 2)
-    att_rows = rows[:2]
-    t0 = time.perf_counter()
-    O.attention_rows(q, k, v, lists, dims.scale, att_rows)
-    t_att = time.perf_counter() - t0
+    # attention of sampled query blocks, one at a time, until about 10 s of CPU work
+    att_rows, t_att = [], 0.0
+    for qb in rows:
+        t0 = time.perf_counter()
+        O.attention_rows(q, k, v, lists, dims.scale, [qb])
+        t_att += time.perf_counter() - t0
+        att_rows.append(qb)
+        if t_att >= 10.0:
+            break
     tiles_sampled = sum(len(lists[qb]) for qb in att_rows)
     tiles = res["crisp"]["tiles"]
     total_s = t_head * hq + t_pe_head * res["crisp"]["heads_pe"] + t_att / tiles_sampled * tiles
