@@ -17,7 +17,8 @@
 //                two key blocks covered by each kept slash band, compacted in
 //                ascending order.
 // Pooled-Estimation heads ("Key Contributions" item 2; gamma = 0.95 on PE):
-//   pe_pool    - mean of each 128-row block of q (PE heads) and k.
+//   pe_pool    - mean of each 128-row block of q (PE heads) and k (KV groups
+//                holding a PE head).
 //   pe_select  - per (head, query block): pooled logits against kb <= qb,
 //                softmax, radix select of the shortest prefix reaching
 //                gamma, plus qb.
@@ -188,7 +189,7 @@ __global__ __launch_bounds__(kVsThreads) void vs_select_kernel(VsArgs p) {
 }
 
 __global__ __launch_bounds__(256) void pe_pool_kernel(const __bf16* q, const __bf16* k, const int32_t* route,
-                                                      float* qbar, float* kbar, int hq, int n) {
+                                                      float* qbar, float* kbar, int hq, int qpg, int n) {
   __shared__ float part[16][kHeadDim];
   const int kb = blockIdx.x, which = blockIdx.y, tid = threadIdx.x;
   const int nblk = n / kBlock;
@@ -200,6 +201,10 @@ __global__ __launch_bounds__(256) void pe_pool_kernel(const __bf16* q, const __b
     dst = qbar + (size_t)which * nblk * kHeadDim;
   } else {
     const int g = which - hq;
+    // pooled keys are only read by the Pooled-Estimation heads of the group
+    bool any_pe = false;
+    for (int t = 0; t < qpg; ++t) any_pe |= route[g * qpg + t] == 0;
+    if (!any_pe) return;
     src = k + (size_t)g * n * kHeadDim;
     dst = kbar + (size_t)g * nblk * kHeadDim;
   }
@@ -707,7 +712,8 @@ hipError_t launch_select(const __bf16* q, const __bf16* k, const float* amap, co
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
 
-  hipLaunchKernelGGL(pe_pool_kernel, dim3(N, hq + hkv), dim3(256), 0, stream, q, k, route, b.qbar, b.kbar, hq, n);
+  hipLaunchKernelGGL(pe_pool_kernel, dim3(N, hq + hkv), dim3(256), 0, stream, q, k, route, b.qbar, b.kbar, hq,
+                     hq / hkv, n);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   PeArgs pa;

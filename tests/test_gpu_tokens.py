@@ -184,3 +184,38 @@ def test_token_chain_is_deterministic():
     for h in range(hq):
         k = int(b1.ncols[h])
         assert torch.equal(b1.cols[h, :k], b2.cols[h, :k])
+
+
+@pytest.mark.parametrize("hq,hkv,n", [(2, 1, 256), (2, 1, 384), (4, 2, 1152)])
+def test_token_chain_small_layers(hq, hkv, n):
+    """The shortest layers (two and three key blocks, an odd block count):
+    fewer candidate columns than k_min, so the top-up decides, and query
+    block pairs with a missing second block."""
+    x = _inputs(hq, hkv, n, 61 + n)
+    cfg = B.make_cfg(route_override=B.ROUTE_FORCE_VS)
+    dims, bufs = _token_chain(x, cfg)
+    N = n // BLK
+    cols = bufs.cols.cpu().numpy()
+    ncols = bufs.ncols.cpu().numpy()
+    count = bufs.blocks["count"].cpu().numpy()
+    idx = bufs.blocks["idx"].cpu().numpy()
+    smask = bufs.blocks["s_mask"].cpu().numpy()
+    out = bufs.out.cpu().numpy()
+    for h in range(hq):
+        g = h * hkv // hq
+        q, k, v = to64(x.q[h]), to64(x.k[g]), to64(x.v[g])
+        A, _ = O.proxy_map(q[n - BLK:], k, dims.scale)
+        c, dg = O.token_scores(A)
+        _, sl = O.pooled_scores(c, dg)
+        kept = cols[h, :ncols[h]]
+        # min(1024, n) columns in all: every candidate is kept when n <= 1024
+        check_token_cols(c, cfg.alpha, 8 * BLK, 0, kept, float(bufs.blocks["floor_v"][h]))
+        if n <= 8 * BLK:
+            assert ncols[h] == n - BLK
+        lists = gpu_lists(count, idx, h, N)
+        vb = np.zeros(N, dtype=bool)
+        vb[0] = True
+        assert lists == O.vs_lists(vb, smask[h].astype(bool))
+        ref = O.attention_rows_mixed(q, k, v, lists, kept.tolist(), dims.scale, range(N))
+        for qb in range(N):
+            check_attention(out[h, qb * BLK:(qb + 1) * BLK], ref[qb][0], f"n {n} head {h} qb {qb}")
