@@ -393,39 +393,75 @@ __global__ __launch_bounds__(kPeThreads) void pe_select_kernel(PeArgs p) {
   if (tid == 0) p.count[(size_t)h * N + qb] = total;
 }
 
-// One workgroup per (head, 64 query blocks): the head's two masks are staged
-// in LDS as bytes once, then each wavefront builds whole rows, deciding 64
-// key blocks per ballot and writing the kept ones in ascending order.
-constexpr int kExpandRows = 64;
+// One workgroup per (head, 256 query blocks), one thread per query block.
+// The head's kept vertical blocks V and slash bands S are compacted once
+// into ascending LDS lists; the list of qb is the merge of {v in V : v <= qb}
+// with the tiles qb - s - 1, qb - s of the bands s in S taken from the widest
+// band down (an ascending sequence in which neighbouring bands repeat one
+// block), dropping repeats and blocks below 0.
+constexpr int kExpandRows = 256;
 constexpr int kMaxBlocks = 4096;  // n <= 524288
 
 __global__ __launch_bounds__(256) void vs_expand_kernel(const int32_t* route, const int32_t* vmask,
                                                         const int32_t* smask, int32_t* count, int32_t* idx, int nblk) {
-  __shared__ uint8_t vm[kMaxBlocks], sm[kMaxBlocks];
-  const int N = nblk, h = blockIdx.y, qb0 = blockIdx.x * kExpandRows;
+  __shared__ int32_t vl[kMaxBlocks], sl[kMaxBlocks];
+  __shared__ int scan_tmp[8];
+  const int N = nblk, h = blockIdx.y, tid = threadIdx.x;
   if (route[h] != 1) return;
-  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
-  for (int i = tid; i < N; i += 256) {
-    vm[i] = vmask[(size_t)h * N + i] != 0;
-    sm[i] = smask[(size_t)h * N + i] != 0;
+  // ascending compaction of both masks, 256 blocks per round
+  int nv = 0, ns = 0;
+  for (int b0 = 0; b0 < N; b0 += 256) {
+    const int b = b0 + tid;
+    const int fv = (b < N && vmask[(size_t)h * N + b] != 0) ? 1 : 0;
+    const int fs = (b < N && smask[(size_t)h * N + b] != 0) ? 1 : 0;
+    int tv, ts;
+    const int pv = block_exclusive_scan(fv, scan_tmp, tid, 256, &tv);
+    const int ps = block_exclusive_scan(fs, scan_tmp, tid, 256, &ts);
+    if (fv) vl[nv + pv] = b;
+    if (fs) sl[ns + ps] = b;
+    nv += tv;
+    ns += ts;
   }
   __syncthreads();
-  const uint64_t below = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-  for (int r = wv; r < kExpandRows; r += 4) {
-    const int qb = qb0 + r;
-    if (qb >= N) break;
-    int32_t* out = idx + (size_t)h * ((size_t)N * (N + 1) / 2) + (size_t)qb * (qb + 1) / 2;
-    int total = 0;
-    for (int kb0 = 0; kb0 <= qb; kb0 += 64) {
-      const int kb = kb0 + lane;
-      bool f = false;
-      if (kb <= qb) f = vm[kb] | sm[qb - kb] | (kb < qb ? sm[qb - kb - 1] : 0);
-      const uint64_t bal = __ballot(f);
-      if (f) out[total + __popcll(bal & below)] = kb;
-      total += __popcll(bal);
+  const int qb = blockIdx.x * kExpandRows + tid;
+  if (qb >= N) return;
+  int32_t* out = idx + (size_t)h * ((size_t)N * (N + 1) / 2) + (size_t)qb * (qb + 1) / 2;
+  constexpr int kNone = 0x7fffffff;
+  int a = 0;           // next vertical block
+  int bi = ns - 1;     // next band, widest first
+  int ph = 0;          // 0: block qb - s - 1, 1: block qb - s
+  auto next_b = [&]() -> int {  // next slash tile >= 0, or kNone
+    while (bi >= 0) {
+      const int e = qb - sl[bi] - 1 + ph;
+      if (ph == 1) {
+        ph = 0;
+        --bi;
+      } else {
+        ph = 1;
+      }
+      if (e >= 0) return e;
     }
-    if (lane == 0) count[(size_t)h * N + qb] = total;
+    return kNone;
+  };
+  int va = (a < nv && vl[a] <= qb) ? vl[a] : kNone;
+  int vb = next_b();
+  int last = -1, pos = 0;
+  while (va != kNone || vb != kNone) {
+    int e;
+    if (va <= vb) {
+      e = va;
+      ++a;
+      va = (a < nv && vl[a] <= qb) ? vl[a] : kNone;
+    } else {
+      e = vb;
+      vb = next_b();
+    }
+    if (e != last) {
+      out[pos++] = e;
+      last = e;
+    }
   }
+  count[(size_t)h * N + qb] = pos;
 }
 
 // ---------------------------------------------------------------------------
