@@ -205,13 +205,27 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
         const int t = 2 * half + kb2;
         float a[16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          a[v] = fast_exp2(fmaf(s[kb2][v], p.scale_log2, neg_lse));
-          if (kMass) {
-            if (t < w || (t == w && l32 >= acc_key(v, lg)))
-              lo += a[v];
+        for (int v = 0; v < 16; ++v) a[v] = fast_exp2(fmaf(s[kb2][v], p.scale_log2, neg_lse));
+        if (kMass) {
+          if (t == w) {  // the diagonal sub-tile: split by row >= column
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              if (l32 >= acc_key(v, lg))
+                lo += a[v];
+              else
+                up += a[v];
+            }
+          } else {  // wave-uniform: the whole sub-tile on one side
+            float t8[8];
+#pragma unroll
+            for (int v = 0; v < 8; ++v) t8[v] = a[v] + a[v + 8];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) t8[v] += t8[v + 4];
+            const float sum = (t8[0] + t8[2]) + (t8[1] + t8[3]);
+            if (t < w)
+              lo += sum;
             else
-              up += a[v];
+              up += sum;
           }
         }
         if (kCols) {
