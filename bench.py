@@ -386,7 +386,7 @@ def cpu_baseline(q, k, v, dims, res, cfg_kw):
     del A
     t0 = time.perf_counter()
     qbar, kbar = O.pe_pool(q), O.pe_pool(k)
-    rows = [N - 1 - 7 * i for i in range(24)]
+    rows = [N - 1 - 7 * i for i in range(48)]
     lists = {qb: O.pe_row_select(qbar, kbar, qb, dims.scale, ocfg.gamma_pe) for qb in rows}
     t_rows = time.perf_counter() - t0
     t_pe_head = t_rows / sum(qb + 1 for qb in rows) * (N * (N + 1) / 2)

@@ -505,9 +505,14 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
 
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / l_tot;
-  const size_t orow = ((size_t)h * p.n + qpos) * kHeadDim;
-  if (p.out_fp32) {
-    float* out = (float*)p.out + orow;
+  // The output goes through LDS (the K/V stages are idle after the last
+  // barrier): each lane writes its row's values with 16-byte chunks
+  // XOR-swizzled by the row, then the workgroup stores whole rows, a 16-byte
+  // chunk per lane, consecutive lanes along a row.
+  char* ob = (char*)lds;
+  const int orow_l = 32 * w + l32;  // row within the query block
+  const size_t obase = ((size_t)h * p.n + (size_t)qb * kBlock) * kHeadDim;
+  if (p.out_fp32) {  // 512-byte rows, 32 chunks of 4 values
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -517,10 +522,17 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
         r[1] = o[db][4 * a + 1] * inv;
         r[2] = o[db][4 * a + 2] * inv;
         r[3] = o[db][4 * a + 3] * inv;
-        *(f32x4*)(out + 32 * db + 8 * a + 4 * lg) = r;
+        const int c = 8 * db + 2 * a + lg;
+        *(f32x4*)(ob + orow_l * 512 + ((c ^ (orow_l & 31)) << 4)) = r;
       }
-  } else {
-    __bf16* out = (__bf16*)p.out + orow;
+    __syncthreads();
+    float* out = (float*)p.out + obase;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int id = i * 256 + tid, row = id >> 5, c = id & 31;
+      *(f32x4*)(out + row * kHeadDim + 4 * c) = *(const f32x4*)(ob + row * 512 + ((c ^ (row & 31)) << 4));
+    }
+  } else {  // 256-byte rows, 16 chunks of 8 values; a lane holds half a chunk
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -530,8 +542,16 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
         r[1] = (__bf16)(o[db][4 * a + 1] * inv);
         r[2] = (__bf16)(o[db][4 * a + 2] * inv);
         r[3] = (__bf16)(o[db][4 * a + 3] * inv);
-        *(bf16x4*)(out + 32 * db + 8 * a + 4 * lg) = r;
+        const int c = 4 * db + a;
+        *(bf16x4*)(ob + orow_l * 256 + ((c ^ (orow_l & 15)) << 4) + 8 * lg) = r;
       }
+    __syncthreads();
+    __bf16* out = (__bf16*)p.out + obase;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int id = i * 256 + tid, row = id >> 4, c = id & 15;
+      *(u32x4*)(out + row * kHeadDim + 8 * c) = *(const u32x4*)(ob + row * 256 + ((c ^ (row & 15)) << 4));
+    }
   }
   if (p.lse != nullptr && lg == 0) p.lse[(size_t)h * p.n + qpos] = (m_run + fast_log2(l_tot)) * kLn2;
 }
