@@ -1,0 +1,52 @@
+"""Host-side checks of the benchmark's reporting helpers (no GPU)."""
+import sys
+import types
+
+import numpy as np
+import pytest
+import torch
+
+sys.argv = sys.argv[:1]
+import bench  # noqa: E402
+
+
+def test_spearman_matches_scipy_with_ties():
+    from scipy.stats import spearmanr
+
+    r = np.random.default_rng(3)
+    a = r.random(40).round(2).tolist()
+    b = (np.array(a) * 0.5 + r.random(40) * 0.3).round(2).tolist()
+    assert bench._spearman(a, b) == pytest.approx(spearmanr(a, b).statistic, abs=1e-12)
+    assert bench._spearman([1.0, 2.0], [2.0, 1.0]) is None
+
+
+def test_agreement_stats_hand_example():
+    c = [0.1, 0.6, 0.3, 0.55]   # C_struct >= 0.5: heads 1 and 3
+    d = [0.05, 0.5, 0.4, 0.2]   # JSD distances
+    st = bench.agreement_stats(c, d, 0.5, (0.1, 0.45))
+    assert st["vs_heads_cstruct"] == 2
+    # distance >= 0.1: heads 1, 2, 3 -> alike on 0, 1, 3
+    assert st["agreement_at"][0.1] == pytest.approx(0.75)
+    # distance >= 0.45: head 1 only -> alike on 0, 1, 2
+    assert st["agreement_at"][0.45] == pytest.approx(0.75)
+    # no threshold separates {1, 3} from {0, 2} (head 3's distance is below head 2's);
+    # the first threshold reaching the best is the distance 0.2
+    assert st["best_agreement"] == pytest.approx(0.75)
+    assert st["best_tau_jsd"] == 0.2
+
+
+def test_needle_recall_counts_listed_blocks_and_kept_columns():
+    N, B = 4, 128
+    # one sink head (0) of one KV group, needles at keys 130 (block 1) and 300 (block 2)
+    x = types.SimpleNamespace(q=torch.zeros(1, N * B, 1), k=torch.zeros(1, N * B, 1), sink_heads=[0],
+                              needle_pos={0: [130, 300]})
+    count = torch.zeros(1, N, dtype=torch.int32)
+    idx = torch.zeros(N * (N + 1) // 2, dtype=torch.int32)
+    last = (N - 1) * N // 2
+    count[0, N - 1] = 2
+    idx[last:last + 2] = torch.tensor([1, 3])  # the last query block lists key blocks 1 and 3
+    bufs = types.SimpleNamespace(blocks={"count": count, "idx": idx},
+                                 cols=torch.tensor([[300, 0, 0, 0]], dtype=torch.int32),
+                                 ncols=torch.tensor([1], dtype=torch.int32))
+    assert bench.needle_recall(x, bufs, N, tokens=False) == pytest.approx(0.5)
+    assert bench.needle_recall(x, bufs, N, tokens=True) == pytest.approx(1.0)
