@@ -449,12 +449,21 @@ def sweep(torch, B, synth, args):
             t = med(lambda: B.crisp_prefill(dims, cfg, x.q, x.k, x.v, bufs, dense_below=0), args.compare_steps)
             tiles = int(bufs.blocks["count"].sum().item())
             row[name] = {"ms": t, "tiles": tiles, "tile_frac": tiles / dense_tiles, "speedup": row["dense_ms"] / t}
+        del bufs
+        tb = B.CrispBuffers(dims, tokens=True)
+        ct = B.make_cfg(route_override=B.ROUTE_FORCE_VS, alpha=1.25)
+        t = med(lambda: B.crisp_prefill_tokens(dims, ct, x.q, x.k, x.v, tb), args.compare_steps)
+        row["tokens_alpha1.25"] = {"ms": t, "tiles": int(tb.blocks["count"].sum().item()),
+                                   "gathered_columns": int(tb.col_below.sum().item()),
+                                   "tile_frac": int(tb.blocks["count"].sum().item()) / dense_tiles,
+                                   "speedup": row["dense_ms"] / t}
         log(f"sweep n={n}: dense {row['dense_ms']:.3f} ms, " +
-            ", ".join(f"{nm} {row[nm]['ms']:.3f} ms" for nm, _ in chains))
+            ", ".join(f"{nm} {row[nm]['ms']:.3f} ms" for nm, _ in chains) +
+            f", tokens {row['tokens_alpha1.25']['ms']:.3f} ms")
         rows.append(row)
-        del x, bufs
+        del x, tb
         torch.cuda.empty_cache()
-    names = ["auto"] + [f"vs_alpha{a}" for a in SWEEP_ALPHAS]
+    names = ["auto"] + [f"vs_alpha{a}" for a in SWEEP_ALPHAS] + ["tokens_alpha1.25"]
     print("| n | dense ms | " + " | ".join(f"{nm} ms (speedup, tiles)" for nm in names) + " |")
     print("|---|---|" + "---|" * len(names))
     for r in rows:
