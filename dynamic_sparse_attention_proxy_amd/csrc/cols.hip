@@ -216,23 +216,6 @@ __global__ __launch_bounds__(kColThreads, 1) void col_attn_kernel(ColArgs p) {
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sc[kb2][v]);
     return fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
   };
-  // Probabilities of a step against m_run, packed as the PV B operands.
-  auto exps = [&](const f32x16 (&sc)[2], bf16x8 (&pb)[4]) -> float {
-    float ls = 0.f;
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-      for (int f = 0; f < 2; ++f) {
-        float x[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          x[i] = fast_exp2(fmaf(sc[kb2][8 * f + i], p.scale_log2, -m_run));
-          ls += x[i];
-        }
-        pb[2 * kb2 + f] = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
-      }
-    return ls;
-  };
 
   for (int s = 0; s < kCStages - 1 && s < nsteps; ++s) gather(s);
   // steps 0 and 1 must have landed: at most the gather of step 2 (4 per wave) outstanding
