@@ -343,13 +343,13 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
         if ((t & 3) == 0) dma1(vrs, dma_v, vdst, kb_v, j + 1, t >> 2, true);
       }
       e[t] = fast_exp2(fmaf(sc[1][t], p.scale_log2, neg_m));
-      ls += e[t];
       if (t & 1) {  // pack each pair as soon as it is complete
         pb[2 + (t >> 3)][(t & 7) - 1] = (__bf16)e[t - 1];
         pb[2 + (t >> 3)][t & 7] = (__bf16)e[t];
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    ls = sum_rounded(pb[3], sum_rounded(pb[2], ls));
     // The running max is only raised when it was too low for this step:
     // some lane's probabilities sum past kSumLimit (+inf included).  Every
     // probability then stays at most kSumLimit, far inside bf16 / fp32 range.
@@ -376,11 +376,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
         for (int f = 0; f < 2; ++f) {
           float x[8];
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            x[i] = fast_exp2(fmaf(sr[8 * f + i], p.scale_log2, neg_m));
-            ls += x[i];
-          }
+          for (int i = 0; i < 8; ++i) x[i] = fast_exp2(fmaf(sr[8 * f + i], p.scale_log2, neg_m));
           pb[2 * kb2 + f] = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+          ls = sum_rounded(pb[2 * kb2 + f], ls);
         }
       }
     }
@@ -416,7 +414,6 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
           if (kbase + acc_key((2 * u + 1) & 15, lg) > qpos) sn[u >> 3][(2 * u + 1) & 15] = -INFINITY;
         }
         e[u] = fast_exp2(fmaf(sn[0][u], p.scale_log2, neg_m));
-        lsn += e[u];
         if (u & 1) {
           p_lo[u >> 3][(u & 7) - 1] = (__bf16)e[u - 1];
           p_lo[u >> 3][u & 7] = (__bf16)e[u];
@@ -424,6 +421,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
       }
       __builtin_amdgcn_sched_barrier(0);
     }
+    if (kNext) lsn = sum_rounded(p_lo[1], sum_rounded(p_lo[0], lsn));
     ls_lo = lsn;
 
     if (kKAhead)
@@ -448,11 +446,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   for (int f = 0; f < 2; ++f) {
     float x[8];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      x[i] = fast_exp2(fmaf(sa[0][8 * f + i], p.scale_log2, neg_m));
-      ls_lo += x[i];
-    }
+    for (int i = 0; i < 8; ++i) x[i] = fast_exp2(fmaf(sa[0][8 * f + i], p.scale_log2, neg_m));
     p_lo[f] = pack_bf16x8(x[0], x[1], x[2], x[3], x[4], x[5], x[6], x[7]);
+    ls_lo = sum_rounded(p_lo[f], ls_lo);
   }
   __syncthreads();  // every wave has read K_0 before iteration 0 overwrites it
 

@@ -258,15 +258,12 @@ __global__ __launch_bounds__(kColThreads, 1) void col_attn_kernel(ColArgs p) {
   }
   // exps of one key half, packed as two PV B operands
   auto half_exps = [&](const f32x16& x, bf16x8& pa, bf16x8& pbb) -> float {
-    float e[16], sum = 0.f;
+    float e[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      e[i] = fast_exp2(fmaf(x[i], p.scale_log2, -m_run));
-      sum += e[i];
-    }
+    for (int i = 0; i < 16; ++i) e[i] = fast_exp2(fmaf(x[i], p.scale_log2, -m_run));
     pa = pack_bf16x8(e[0], e[1], e[2], e[3], e[4], e[5], e[6], e[7]);
     pbb = pack_bf16x8(e[8], e[9], e[10], e[11], e[12], e[13], e[14], e[15]);
-    return sum;
+    return sum_rounded(pbb, sum_rounded(pa, 0.f));  // the rounded values that enter PV
   };
 
   auto iter = [&](int s, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
@@ -299,11 +296,11 @@ __global__ __launch_bounds__(kColThreads, 1) void col_attn_kernel(ColArgs p) {
           sn[t & 1] = mfma32(kr[t & 3], qf[t >> 1], t < 2 ? zero : sn[t & 1]);
           if (t + 3 < 16) kr[(t + 3) & 3] = kread(s + 1, t + 3);
           e[t] = fast_exp2(fmaf(sc[1][t], p.scale_log2, -m_run));
-          ls += e[t];
           if ((t & 7) == 7)
             pb[2 + (t >> 3)] = pack_bf16x8(e[t - 7], e[t - 6], e[t - 5], e[t - 4], e[t - 3], e[t - 2], e[t - 1], e[t]);
           __builtin_amdgcn_sched_barrier(0);
         }
+        ls = sum_rounded(pb[3], sum_rounded(pb[2], 0.f));
       } else {
         if (has_next) {
 #pragma unroll
@@ -357,11 +354,11 @@ __global__ __launch_bounds__(kColThreads, 1) void col_attn_kernel(ColArgs p) {
             }
           }
           e[u] = fast_exp2(fmaf(sn[0][u], p.scale_log2, -m_run));
-          lsn += e[u];
           if ((u & 7) == 7)
             p_lo[u >> 3] = pack_bf16x8(e[u - 7], e[u - 6], e[u - 5], e[u - 4], e[u - 3], e[u - 2], e[u - 1], e[u]);
           __builtin_amdgcn_sched_barrier(0);
         }
+        lsn = sum_rounded(p_lo[1], sum_rounded(p_lo[0], 0.f));
       } else {
         if (cur_on) {
 #pragma unroll

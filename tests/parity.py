@@ -8,6 +8,10 @@ Tolerances (applied element by element):
     gamma cut); a gamma prefix may differ in length by one when the oracle's
     running sum crosses gamma within 1e-3 relative;
   * attention: max-abs 1e-2 and mean-abs 1e-3 against fp64, on identical lists.
+  * attention lse: the kernels sum the bf16-rounded probabilities that enter
+    the PV product (so a row is an exact weighted mean of V rows); each is
+    within a relative 2^-8 of the exact one, so the log of the sum is within
+    ln(1 + 2^-8) < 2^-8 of the oracle's, plus 2e-5 for the fp32 parts.
   * JSD routing signal: the pooled estimate 1e-4 relative per key block
     (fp32 logits, errors of order 1e-6 in the exponent); the divergence
     JSD = dist^2 within 2e-6 absolute plus 1e-4 relative (the kernel reads
@@ -29,6 +33,7 @@ REL_SEL = 1e-3
 REL_CSTRUCT = 1e-4
 ATTN_MAXABS = 1e-2
 ATTN_MEANABS = 1e-3
+LSE_ABS = 2.0 ** -8 + 2e-5
 REL_JSD_EST = 1e-4
 JSD_ABS = 2e-6
 JSD_REL = 1e-4
@@ -145,6 +150,11 @@ def check_pe_lists(qbar: np.ndarray, kbar: np.ndarray, scale: float, gamma: floa
         assert lists_gpu[qb] == sorted(got), "lists must be ascending without repeats"
         assert qb in got
         check_gamma_set(p, range(qb + 1), gamma, got, {qb})
+
+
+def check_lse(lse_gpu: np.ndarray, lse_ref: np.ndarray, what: str = ""):
+    err = np.abs(np.asarray(lse_gpu, dtype=np.float64) - lse_ref)
+    assert err.max() <= LSE_ABS, f"{what} lse max-abs {err.max()}"
 
 
 def check_attention(out_gpu: np.ndarray, out_ref: np.ndarray, what: str = ""):

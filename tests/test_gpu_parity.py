@@ -12,7 +12,8 @@ import torch
 from dynamic_sparse_attention_proxy_amd import binding as B
 from dynamic_sparse_attention_proxy_amd import synth
 from oracle import crisp_oracle as O
-from parity import (JSD_ABS, JSD_REL, REL_CSTRUCT, REL_JSD_EST, check_attention, check_gamma_set, check_noise_floor_mask, check_pe_lists,
+from parity import (JSD_ABS, JSD_REL, REL_CSTRUCT, REL_JSD_EST, check_attention, check_gamma_set, check_lse,
+                    check_noise_floor_mask, check_pe_lists,
                     check_route, gpu_lists, near, to64)
 
 pytestmark = pytest.mark.gpu
@@ -74,7 +75,7 @@ def test_dense_attention_single_head_4k():
     og, lg = out[0].cpu().numpy(), lse[0].cpu().numpy()
     for qb in range(32):
         check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"qb {qb}")
-        np.testing.assert_allclose(lg[qb * BLK:(qb + 1) * BLK], ref[qb][1], rtol=2e-5, atol=2e-5)
+        check_lse(lg[qb * BLK:(qb + 1) * BLK], ref[qb][1])
     # bf16 output is the fp32 result rounded once
     outb = torch.empty((1, 4096, 128), dtype=torch.bfloat16, device="cuda")
     B.crisp_dense_attn(dims, x.q, x.k, x.v, outb)
@@ -150,9 +151,9 @@ def test_attention_raises_running_max_mid_row(where):
         for qb in range(N):
             rows = slice(qb * BLK, (qb + 1) * BLK)
             check_attention(og[rows], ref[qb][0], f"{where} sparse h {h} qb {qb}")
-            np.testing.assert_allclose(lg[rows], ref[qb][1], rtol=2e-5, atol=2e-5)
+            check_lse(lg[rows], ref[qb][1])
             check_attention(dg[rows], dref[qb][0], f"{where} dense h {h} qb {qb}")
-            np.testing.assert_allclose(dl[rows], dref[qb][1], rtol=2e-5, atol=2e-5)
+            check_lse(dl[rows], dref[qb][1])
     # the planted keys dominate the rows that see them
     assert float(lse[0, planted[-1] + 1]) > 20.0
 
@@ -183,7 +184,7 @@ def test_sparse_attention_matches_oracle_on_given_lists(hq, hkv, n, kind):
         og, lg = out[h].cpu().numpy(), lse[h].cpu().numpy()
         for qb in range(N):
             check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"h {h} qb {qb}")
-            np.testing.assert_allclose(lg[qb * BLK:(qb + 1) * BLK], ref[qb][1], rtol=2e-5, atol=2e-5)
+            check_lse(lg[qb * BLK:(qb + 1) * BLK], ref[qb][1])
     if kind == "full":
         dense = torch.empty_like(out)
         B.crisp_dense_attn(dims, x.q, x.k, x.v, dense)

@@ -9,7 +9,8 @@ import torch
 from dynamic_sparse_attention_proxy_amd import binding as B
 from dynamic_sparse_attention_proxy_amd import synth
 from oracle import crisp_oracle as O
-from parity import check_attention, check_noise_floor_mask, check_token_cols, gpu_lists, to64
+from parity import (check_attention, check_lse, check_noise_floor_mask, check_pe_lists, check_token_cols, gpu_lists,
+                    to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -125,7 +126,7 @@ def test_token_chain_attention_matches_oracle():
         for qb in qbs:
             rows = slice(qb * BLK, (qb + 1) * BLK)
             check_attention(out[h, rows], ref[qb][0], f"head {h} qb {qb}")
-            np.testing.assert_allclose(lse[h, rows], ref[qb][1], rtol=2e-5, atol=2e-5)
+            check_lse(lse[h, rows], ref[qb][1])
 
 
 @pytest.mark.parametrize("ncol,n", [(1, 2048), (64, 2048), (200, 2176), (3000, 8192)])
@@ -172,7 +173,7 @@ def test_column_kernel_on_given_lists_and_columns(ncol, n):
         for qb in qbs:
             rows = slice(qb * BLK, (qb + 1) * BLK)
             check_attention(og[h, rows], ref[qb][0], f"head {h} qb {qb}")
-            np.testing.assert_allclose(lg[h, rows], ref[qb][1], rtol=2e-5, atol=2e-5)
+            check_lse(lg[h, rows], ref[qb][1])
 
 
 def test_token_chain_is_deterministic():
@@ -221,3 +222,41 @@ def test_token_chain_small_layers(hq, hkv, n):
         ref = O.attention_rows_mixed(q, k, v, lists, kept.tolist(), dims.scale, range(N))
         for qb in range(N):
             check_attention(out[h, qb * BLK:(qb + 1) * BLK], ref[qb][0], f"n {n} head {h} qb {qb}")
+
+
+def test_token_chain_with_mixed_routes():
+    """Route auto on the graded-structure family (tau 0.2): some heads go
+    Vertical-Slash and get kept columns, the others Pooled-Estimation with
+    no columns; lists, columns and the attention of sampled query blocks
+    against the oracle, head by head."""
+    n = 8192
+    x = synth.make_routing_family(seq_len=n, device="cuda")
+    hq, hkv = x.q.shape[0], x.k.shape[0]
+    cfg = B.make_cfg(tau=0.2)
+    dims, bufs = _token_chain(x, cfg)
+    N = n // BLK
+    route = bufs.route.cpu().numpy()
+    assert 0 < int(route.sum()) < hq, "the family must mix both routes"
+    cols = bufs.cols.cpu().numpy()
+    ncols = bufs.ncols.cpu().numpy()
+    below = bufs.col_below.cpu().numpy()
+    count = bufs.blocks["count"].cpu().numpy()
+    idx = bufs.blocks["idx"].cpu().numpy()
+    out = bufs.out.cpu().numpy()
+    qbs = [0, 1, 31, N - 1]
+    for h in range(hq):
+        g = h * hkv // hq
+        q, k, v = to64(x.q[h]), to64(x.k[g]), to64(x.v[g])
+        lists = gpu_lists(count, idx, h, N)
+        if route[h] == B.ROUTE_PE:
+            assert ncols[h] == 0 and not below[h].any()
+            check_pe_lists(O.pe_pool(q), O.pe_pool(k), dims.scale, cfg.gamma_pe, lists, qbs)
+            kept = []
+        else:
+            A, _ = O.proxy_map(q[n - BLK:], k, dims.scale)
+            c, _ = O.token_scores(A)
+            kept = cols[h, :ncols[h]].tolist()
+            check_token_cols(c, cfg.alpha, 8 * BLK, 0, kept, float(bufs.blocks["floor_v"][h]))
+        ref = O.attention_rows_mixed(q, k, v, lists, kept, dims.scale, qbs)
+        for qb in qbs:
+            check_attention(out[h, qb * BLK:(qb + 1) * BLK], ref[qb][0], f"head {h} qb {qb}")
