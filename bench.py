@@ -549,8 +549,8 @@ def agreement(torch, B, synth, args):
         hq, hkv, n = w.num_q_heads, w.num_kv_heads, w.seq_len
         dims = B.make_dims(hq, hkv, n)
         cfg = B.make_cfg()
-        N = n // 128
-        mass = torch.empty((2, hq, N), dtype=torch.float32, device="cuda")
+        N = B.num_blocks(n)
+        mass = torch.empty((4, hq, N), dtype=torch.float32, device="cuda")
         partials = torch.empty(B.crisp_proxy_scratch_bytes(dims), dtype=torch.uint8, device="cuda")
         cs = torch.empty(hq, dtype=torch.float32, device="cuda")
         rt = torch.empty(hq, dtype=torch.int32, device="cuda")

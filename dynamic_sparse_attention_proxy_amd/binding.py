@@ -117,6 +117,12 @@ def _stream(stream) -> ctypes.c_void_p:
     return ctypes.c_void_p(stream.cuda_stream)
 
 
+def num_blocks(seq_len: int, block: int = 128) -> int:
+    """Key/query blocks of a sequence: the last one is partial when `block`
+    does not divide `seq_len`."""
+    return -(-seq_len // block)
+
+
 def make_dims(num_q_heads: int, num_kv_heads: int, seq_len: int, head_dim: int = 128, block: int = 128,
               scale: Optional[float] = None) -> crisp_dims:
     if scale is None:
@@ -250,11 +256,11 @@ class CrispBuffers:
                  with_map: bool = False, tokens: bool = False):
         dev = torch.device("cuda") if device is None else torch.device(device)
         hq, n = dims.num_q_heads, dims.seq_len
-        N = n // dims.block
+        N = num_blocks(n, dims.block)
         f32, i32 = torch.float32, torch.int32
         self.dims = dims
         self.attn_map = torch.empty((hq, dims.block, n), dtype=f32, device=dev) if with_map else None
-        self.block_mass = torch.empty((2, hq, N), dtype=f32, device=dev)
+        self.block_mass = torch.empty((4, hq, N), dtype=f32, device=dev)
         self.row_lse = torch.empty((hq, dims.block), dtype=f32, device=dev)
         self.partials = torch.empty(crisp_proxy_scratch_bytes(dims), dtype=torch.uint8, device=dev)
         self.c_struct = torch.empty((hq,), dtype=f32, device=dev)

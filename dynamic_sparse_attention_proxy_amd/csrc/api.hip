@@ -22,9 +22,10 @@ crisp_status check_dims(const crisp_dims* d) {
   if (d->head_dim != 128 || d->block != 128) return CRISP_ERR_SHAPE;
   if (d->num_q_heads <= 0 || d->num_kv_heads <= 0) return CRISP_ERR_SHAPE;
   if (d->num_q_heads % d->num_kv_heads != 0) return CRISP_ERR_SHAPE;
-  if (d->seq_len < 2 * d->block || d->seq_len % d->block != 0 || d->seq_len > kMaxSeqLen) return CRISP_ERR_SHAPE;
+  // any length: a partial last block holds the n - 128 (N-1) last positions
+  if (d->seq_len < 2 * d->block || d->seq_len > kMaxSeqLen) return CRISP_ERR_SHAPE;
   // grid sizes (Hq * N workgroups) must fit the launch limits comfortably
-  if ((long long)d->num_q_heads * (d->seq_len / d->block) > (1LL << 30)) return CRISP_ERR_SHAPE;
+  if ((long long)d->num_q_heads * crisp::nblocks(d->seq_len) > (1LL << 30)) return CRISP_ERR_SHAPE;
   if (!(d->scale > 0.f) || !isfinite(d->scale)) return CRISP_ERR_PARAM;
   return CRISP_OK;
 }
@@ -261,7 +262,7 @@ size_t crisp_select_workspace_bytes(const crisp_dims* dims) {
 
 size_t crisp_list_capacity(const crisp_dims* dims) {
   if (check_dims(dims) != CRISP_OK) return 0;
-  const size_t N = (size_t)dims->seq_len / dims->block;
+  const size_t N = (size_t)crisp::nblocks(dims->seq_len);
   return (size_t)dims->num_q_heads * (N * (N + 1) / 2);
 }
 
@@ -299,7 +300,7 @@ const char* crisp_status_string(crisp_status status) {
   switch (status) {
     case CRISP_OK: return "ok";
     case CRISP_ERR_NULL: return "a required pointer is NULL";
-    case CRISP_ERR_SHAPE: return "unsupported dimensions (need d = 128, block = 128, n % 128 == 0, 256 <= n <= 524288, Hq % Hkv == 0)";
+    case CRISP_ERR_SHAPE: return "unsupported dimensions (need d = 128, block = 128, 256 <= n <= 524288, Hq % Hkv == 0)";
     case CRISP_ERR_PARAM: return "a method parameter is out of range";
     case CRISP_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case CRISP_ERR_WORKSPACE: return "workspace or scratch buffer too small";
@@ -309,6 +310,6 @@ const char* crisp_status_string(crisp_status status) {
   return "unknown status";
 }
 
-int32_t crisp_abi_version(void) { return (2 << 16) | 2; }
+int32_t crisp_abi_version(void) { return (3 << 16) | 0; }
 
 }  // extern "C"

@@ -16,6 +16,11 @@
 // Rows of the K operand are loaded in a permuted order chosen so that the
 // accumulator registers 0..7 / 8..15 of lane group g hold keys 8g..8g+7 and
 // 16+8g..16+8g+7, the 8 contiguous keys each PV k-group needs.
+//
+// When 128 does not divide n the last block holds fewer than 128 positions
+// (kRagged): its K and V rows past n are read as copies of row n-1 (finite,
+// and never weighted: every key past n lies past every real query), query
+// rows past n are computed from row n-1 and not stored.
 
 #include <type_traits>
 
@@ -51,7 +56,7 @@ struct AttnArgs {
 // Key index (0..31) held by accumulator register v of lane group lg.
 __device__ __forceinline__ int acc_key(int v, int lg) { return (v < 8) ? (8 * lg + v) : (16 + 8 * lg + (v - 8)); }
 
-template <bool kDense>
+template <bool kDense, bool kRagged>
 __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   // 32 KiB of V stages (tiles 0-1) then 48 KiB of K stages (tiles 2-4): two
   // workgroups fill a CU's 160 KiB.  With V first, every stage offset of a
@@ -85,10 +90,11 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
 
   // Q rows as the B operand of K.Q^T: query row 32w + l32, d = 16kk + 8lg + [0, 8).
   const int qpos = qb * kBlock + 32 * w + l32;
+  const int qrow = kRagged ? min(qpos, p.n - 1) : qpos;
   bf16x8 qf[8];
 #pragma unroll
   for (int kk = 0; kk < 8; ++kk)
-    qf[kk] = as_bf16x8(*(const u32x4*)(qh + (size_t)qpos * kHeadDim + 16 * kk + 8 * lg));
+    qf[kk] = as_bf16x8(*(const u32x4*)(qh + (size_t)qrow * kHeadDim + 16 * kk + 8 * lg));
 
   f32x16 o[4];
 #pragma unroll
@@ -146,13 +152,26 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   // instruction's immediate offset (1024 i) then moves both the global read
   // and the LDS destination.  Otherwise `off` is the lane's offset for i.
   auto dma1 = [&](__amdgpu_buffer_rsrc_t rs, int off, __bf16* stage, int kb, int step, int i, bool imm) {
-    const int soff = key0_of(kb, step) * (kHeadDim * 2);
+    const int key0 = key0_of(kb, step);
+    int soff = key0 * (kHeadDim * 2);
     // one wait state between writing M0 and the DMA that reads it
 #define CRISP_DMA(OFF)                                                                        \
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, %3 offen offset:" #OFF " lds" \
                :                                                                              \
                : "s"(lds_addr), "v"(off), "s"(rs), "s"(soff)                                  \
                : "memory", "m0")
+    if (kRagged && key0 + kStep > p.n) {
+      // a tile past row n-1: the whole row offset goes to the lane, clamped
+      // to the last row (the lane's 16-byte chunk within its row is kept)
+      const int off_i = imm ? off + 1024 * i : off;
+      const int r = 16 * w + 4 * i + (lane >> 4);
+      off = min(key0 + r, p.n - 1) * (kHeadDim * 2) + (off_i & 255);
+      soff = 0;
+      const unsigned lds_addr =
+          (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)(stage + (16 * wu + 4 * i) * kHeadDim);
+      CRISP_DMA(0);
+      return;
+    }
     if (imm) {
       const unsigned lds_addr =
           (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)(stage + 16 * wu * kHeadDim);
@@ -227,7 +246,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   // One key half (keys key0 + 32 kb2 .. +31) of a step's scores, with the
   // K operand read from global memory in the layout the LDS path gives.
   auto qk_half_global = [&](int key0, int kb2) -> f32x16 {
-    const __bf16* krow_g = kg + (size_t)(key0 + 32 * kb2 + krow) * kHeadDim + 8 * lg;
+    const int kr = key0 + 32 * kb2 + krow;
+    const __bf16* krow_g = kg + (size_t)(kRagged ? min(kr, p.n - 1) : kr) * kHeadDim + 8 * lg;
     f32x16 s = {};
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk) s = mfma32(as_bf16x8(*(const u32x4*)(krow_g + 16 * kk)), qf[kk], s);
@@ -508,6 +528,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   char* ob = (char*)lds;
   const int orow_l = 32 * w + l32;  // row within the query block
   const size_t obase = ((size_t)h * p.n + (size_t)qb * kBlock) * kHeadDim;
+  const int rows_out = kRagged ? min(kBlock, p.n - qb * kBlock) : kBlock;  // rows of the block inside [0, n)
   if (p.out_fp32) {  // 512-byte rows, 32 chunks of 4 values
 #pragma unroll
     for (int db = 0; db < 4; ++db)
@@ -526,7 +547,8 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       const int id = i * 256 + tid, row = id >> 5, c = id & 31;
-      *(f32x4*)(out + row * kHeadDim + 4 * c) = *(const f32x4*)(ob + row * 512 + ((c ^ (row & 31)) << 4));
+      if (!kRagged || row < rows_out)
+        *(f32x4*)(out + row * kHeadDim + 4 * c) = *(const f32x4*)(ob + row * 512 + ((c ^ (row & 31)) << 4));
     }
   } else {  // 256-byte rows, 16 chunks of 8 values; a lane holds half a chunk
 #pragma unroll
@@ -546,10 +568,12 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const int id = i * 256 + tid, row = id >> 4, c = id & 15;
-      *(u32x4*)(out + row * kHeadDim + 8 * c) = *(const u32x4*)(ob + row * 256 + ((c ^ (row & 15)) << 4));
+      if (!kRagged || row < rows_out)
+        *(u32x4*)(out + row * kHeadDim + 8 * c) = *(const u32x4*)(ob + row * 256 + ((c ^ (row & 15)) << 4));
     }
   }
-  if (p.lse != nullptr && lg == 0) p.lse[(size_t)h * p.n + qpos] = (m_run + fast_log2(l_tot)) * kLn2;
+  if (p.lse != nullptr && lg == 0 && (!kRagged || qpos < p.n))
+    p.lse[(size_t)h * p.n + qpos] = (m_run + fast_log2(l_tot)) * kLn2;
 }
 
 }  // namespace
@@ -566,16 +590,21 @@ hipError_t launch_attention(const __bf16* q, const __bf16* k, const __bf16* v, c
   a.out = out;
   a.lse = lse;
   a.n = n;
-  a.nblk = n / kBlock;
+  a.nblk = nblocks(n);
   a.qpg = hq / hkv;
   a.scale_log2 = scale * kLog2e;
   a.out_fp32 = out_fp32;
   a.map = make_row_map(hq, hkv, a.nblk);
   const unsigned grid = (unsigned)hq * (unsigned)a.nblk;
-  if (dense)
-    hipLaunchKernelGGL(fa_fwd_kernel<true>, dim3(grid), dim3(256), 0, stream, a);
+  const bool ragged = n % kBlock != 0;
+  if (dense && ragged)
+    hipLaunchKernelGGL((fa_fwd_kernel<true, true>), dim3(grid), dim3(256), 0, stream, a);
+  else if (dense)
+    hipLaunchKernelGGL((fa_fwd_kernel<true, false>), dim3(grid), dim3(256), 0, stream, a);
+  else if (ragged)
+    hipLaunchKernelGGL((fa_fwd_kernel<false, true>), dim3(grid), dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL(fa_fwd_kernel<false>, dim3(grid), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((fa_fwd_kernel<false, false>), dim3(grid), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -21,7 +21,9 @@
 // layout the tile kernel uses.  Column indices are staged in LDS 2048 at a
 // time (two halves, the next one loaded while the current one is used);
 // each wave turns "before its block and not in its listed tiles" into the
-// step's 64-bit slot mask with one ballot.
+// step's 64-bit slot mask with one ballot.  In a partial last block (128
+// does not divide n) the query rows past n-1 are computed from row n-1 and
+// not written; every gathered column lies below the pair's blocks.
 
 #include "common.h"
 #include "internal.h"
@@ -125,7 +127,8 @@ __global__ __launch_bounds__(kColThreads, 1) void col_attn_kernel(ColArgs p) {
   if (active) {
 #pragma unroll
     for (int kk = 0; kk < 8; ++kk)
-      qf[kk] = as_bf16x8(*(const u32x4*)(p.q + (size_t)h * nd + (size_t)qpos * kHeadDim + 16 * kk + 8 * lg));
+      qf[kk] = as_bf16x8(
+          *(const u32x4*)(p.q + (size_t)h * nd + (size_t)min(qpos, p.n - 1) * kHeadDim + 16 * kk + 8 * lg));
   }
 
   const __amdgpu_buffer_rsrc_t krs =
@@ -396,6 +399,7 @@ __global__ __launch_bounds__(kColThreads, 1) void col_attn_kernel(ColArgs p) {
   // merge with the tile softmax of the same row
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   if (!(l_tot > 0.f)) return;  // no counted column for this row
+  if (qpos >= p.n) return;     // a row of a partial last block past n
   const size_t row = (size_t)h * p.n + qpos;
   const float lt = p.lse[row] * kLog2e;
   const float lc = m_run + fast_log2(l_tot);
@@ -434,7 +438,7 @@ hipError_t launch_col_attention(const __bf16* q, const __bf16* k, const __bf16* 
   a.out = out;
   a.lse = lse;
   a.n = n;
-  a.nblk = n / kBlock;
+  a.nblk = nblocks(n);
   a.qpg = hq / hkv;
   a.scale_log2 = scale * kLog2e;
   const int npairs = (a.nblk + 1) / 2;

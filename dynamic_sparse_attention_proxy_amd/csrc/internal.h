@@ -8,20 +8,26 @@
 
 namespace crisp {
 
+// Blocks of 128 positions, aligned at position 0; the last one holds
+// n - 128 (N - 1) positions when 128 does not divide n.
+__host__ __device__ inline int nblocks(int n) { return (n + 127) / 128; }
+
 // Proxy: keys per workgroup of the two proxy passes.
 constexpr int kProxyChunk = 1024;
 inline int proxy_chunks(int n) { return (n + kProxyChunk - 1) / kProxyChunk; }
 inline size_t proxy_scratch_bytes(int hq, int n) {
   // per (head, chunk, row): running max and sum; per (head, row): log2-sum-exp;
-  // per (head, key block, row): the row's mass below / above the tile
-  // diagonal against its running max (16 bytes)
+  // per (head, key block, row): the row's mass in the three slash bands of
+  // the block and its running max (16 bytes); per (head, row): the row's
+  // mass in key block N-2 that lies in the recency window
   return (size_t)hq * proxy_chunks(n) * 128 * 2 * sizeof(float) + (size_t)hq * 128 * sizeof(float) +
-         (size_t)hq * (n / 128) * 128 * 4 * sizeof(float);
+         (size_t)hq * nblocks(n) * 128 * 4 * sizeof(float) + (size_t)hq * 128 * sizeof(float);
 }
 
 // amap and/or mass (at least one non-null): the proxy map and the block
-// masses [2][Hq][N] (on/below, above each tile's diagonal).  colmass
-// [Hq][n] (the column masses) may only be given with mass and without amap.
+// masses [4][Hq][N] (per key block kb the mass in slash bands N-1-kb,
+// N-2-kb, N-3-kb, and the mass on the last 128 keys).  colmass [Hq][n] (the
+// column masses) may only be given with mass and without amap.
 hipError_t launch_proxy(const __bf16* q, const __bf16* k, float* amap, float* mass, float* colmass, float* row_lse,
                         void* scratch, int hq, int hkv, int n, float scale, hipStream_t stream);
 
@@ -31,8 +37,7 @@ hipError_t launch_route(const float* amap, const float* mass, float* c_struct, i
                         int sink_width, int recency_width, float tau, int route_override, hipStream_t stream);
 
 struct SelectBuffers {
-  float* lo;      // [Hq][N] lower-triangle tile sums of the proxy map
-  float* up;      // [Hq][N] strict upper-triangle tile sums
+  float* mass;    // [4][Hq][N] block masses summed from the proxy map
   float* vscore;  // [Hq][N]
   float* sscore;  // [Hq][N]
   float* floor_v; // [Hq]

@@ -12,11 +12,11 @@
 // Three kernels:
 //   jsd_qpool:  qbar[h] = mean of the head's last 128 query rows (fp32).
 //   jsd_logits: one wave per (KV group, key block) mean-pools the block's
-//               128 keys and scores it against qbar of every query head of
+//               keys (128, or fewer in a partial last block) and scores it against qbar of every query head of
 //               the group: logit2[h][kb] = scale * log2(e) * <qbar, kbar>.
 //               This is the pass that reads all of K (HBM-bound).
 //   jsd_final:  per head, softmax of the logits, the block-summed proxy
-//               (lo + up) / 128 from the block masses, their divergence and
+//               (lo + up + up2) / 128 from the block masses, their divergence and
 //               the route.
 //
 // The divergence is evaluated as sum_kb (s/2) f(delta) with s the midpoint
@@ -73,6 +73,7 @@ __global__ __launch_bounds__(256) void jsd_logits_kernel(const __bf16* k, const 
   const int kb = blockIdx.x * kJWaves + wave, g = blockIdx.y;
   if (kb >= nblk) return;
   const int dc = lane & 15, rg = lane >> 4;
+  const int rows = min(kBlock, n - kb * kBlock);  // fewer in a partial last block
   const __bf16* src = k + ((size_t)g * n + (size_t)kb * kBlock + rg) * kHeadDim + 8 * dc;
   float acc[8];
 #pragma unroll
@@ -81,7 +82,11 @@ __global__ __launch_bounds__(256) void jsd_logits_kernel(const __bf16* k, const 
   for (int half = 0; half < 2; ++half) {
     u32x4 x[16];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) x[i] = *(const u32x4*)(src + (size_t)(4 * (16 * half + i)) * kHeadDim);
+    for (int i = 0; i < 16; ++i) {
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      const int r = 4 * (16 * half + i) + rg;
+      x[i] = r < rows ? *(const u32x4*)(src + (size_t)(4 * (16 * half + i)) * kHeadDim) : zero;
+    }
 #pragma unroll
     for (int i = 0; i < 16; ++i)
 #pragma unroll
@@ -96,7 +101,7 @@ __global__ __launch_bounds__(256) void jsd_logits_kernel(const __bf16* k, const 
     acc[e] += __shfl_xor(acc[e], 16);
     acc[e] += __shfl_xor(acc[e], 32);
   }
-  const float sc = scale_log2 * (1.f / kBlock);
+  const float sc = scale_log2 / (float)rows;
   for (int j = rg; j < qpg; j += 4) {
     const int h = g * qpg + j;
     const f32x4* qv = (const f32x4*)(qbar + (size_t)h * kHeadDim + 8 * dc);
@@ -132,6 +137,7 @@ __global__ __launch_bounds__(kFinalThreads) void jsd_final_kernel(const float* l
   const float* l = logit2 + (size_t)h * nblk;
   const float* lo = mass + (size_t)h * nblk;
   const float* up = mass + ((size_t)hq + h) * nblk;
+  const float* up2 = mass + ((size_t)2 * hq + h) * nblk;
   float m = -INFINITY;
   for (int b = tid; b < nblk; b += kFinalThreads) m = fmaxf(m, l[b]);
   m = block_max_f(m, red, tid, kFinalThreads);
@@ -143,7 +149,7 @@ __global__ __launch_bounds__(kFinalThreads) void jsd_final_kernel(const float* l
   for (int b = tid; b < nblk; b += kFinalThreads) {
     const float p = fast_exp2(l[b] - m) * inv_z;
     if (estimate != nullptr) estimate[(size_t)h * nblk + b] = p;
-    const float a = (lo[b] + up[b]) * (1.f / kBlock);
+    const float a = (lo[b] + up[b] + up2[b]) * (1.f / kBlock);
     const float t = a + p;
     if (t > 0.f) acc += 0.25f * t * jsd_f((a - p) / t);  // (s / 2) f(delta), s = t / 2
   }
@@ -158,13 +164,13 @@ __global__ __launch_bounds__(kFinalThreads) void jsd_final_kernel(const float* l
 }  // namespace
 
 size_t jsd_workspace_bytes(int hq, int n) {
-  return (size_t)hq * kHeadDim * sizeof(float) + (size_t)hq * (n / kBlock) * sizeof(float);
+  return (size_t)hq * kHeadDim * sizeof(float) + (size_t)hq * nblocks(n) * sizeof(float);
 }
 
 hipError_t launch_route_jsd(const __bf16* q, const __bf16* k, const float* mass, float* js_dist, int32_t* route,
                             float* estimate, void* workspace, int hq, int hkv, int n, float scale, float tau_jsd,
                             hipStream_t stream) {
-  const int nblk = n / kBlock, qpg = hq / hkv;
+  const int nblk = nblocks(n), qpg = hq / hkv;
   float* qbar = (float*)workspace;
   float* logit2 = qbar + (size_t)hq * kHeadDim;
   hipLaunchKernelGGL(jsd_qpool_kernel, dim3(hq), dim3(256), 0, stream, q, qbar, n);

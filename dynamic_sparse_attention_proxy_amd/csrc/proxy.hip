@@ -27,8 +27,19 @@
 //   block's masses are complete inside one workgroup.
 // Route: C_struct = mean over rows of the mass on the first sink_width and
 //   the last recency_width columns (from the map, or from the block masses
-//   of key blocks 0 and N-1 when both widths are 128); VS when
-//   C_struct >= tau.
+//   when both widths are 128); VS when C_struct >= tau.
+//
+// Block masses: proxy row r (position n-128+r) against key j lies at offset
+// n-128+r-j, in slash band (offset) / 128.  With t = n - 128 (N-1) positions
+// in the last key block, entry (r, column c) of key block kb lies in band
+// N-1-kb + floor((r - c + t - 128) / 128): band N-1-kb ("lo"), N-2-kb ("up")
+// or, only when t < 128, N-3-kb ("up2").  Against the 32 rows of wave w, the
+// 32 columns of sub-tile st give r - c + t - 128 = D + (l32 - cc) with
+// D = 32 (w - st) + t - 128, so a sub-tile lies in one band or straddles one
+// band edge (0 or -128), which a per-element compare splits.  With t = 128
+// this is the tile diagonal: below for st < w, above for st > w, split for
+// st = w.  The fourth plane is the mass on the last 128 keys: all of block
+// N-1, and the columns c >= t of block N-2.
 
 #include "common.h"
 #include "internal.h"
@@ -45,17 +56,59 @@ struct ProxyArgs {
   const __bf16* q;
   const __bf16* k;
   float* amap;
-  float* mass;   // [2][Hq][N]: on/below, above the tile diagonal
+  float* mass;   // [4][Hq][N]: slash bands N-1-kb, N-2-kb, N-3-kb of each key block; its recency mass
   float* colmass;  // [Hq][n]: column mass, the map's column sums over the rows / 128
   float* part;   // [Hq][128][chunks][2]
-  f32x4* bpart;  // [Hq][N][128]: per row and key block, (below, above, max) in base 2 against that max
+  f32x4* bpart;  // [Hq][N][128]: per row and key block, (lo, up, up2, max) in base 2 against that max
+  float* rpart;  // [Hq][128]: per row, the recency part of key block N-2 against its bpart max
   float* lse2;   // [Hq][128]
   float* row_lse;
   int n;
+  int nblk;
+  int tlast;     // positions in the last key block, 1..128
   int qpg;
   int nchunks;
   float scale_log2;
 };
+
+// Band class of sub-tile st against the rows of wave w (see the top):
+// 0, 1, 2 = wholly in band lo, up, up2; 3 = split at edge 0 (lo / up);
+// 4 = split at edge -128 (up / up2).  D = 32 (w - st) + tlast - 128.
+__device__ __forceinline__ int band_class(int D) {
+  if (D - 31 >= 0) return 0;
+  if (D + 31 < -128) return 2;
+  if (D + 31 < 0 && D - 31 >= -128) return 1;
+  return D + 31 >= 0 ? 3 : 4;
+}
+
+// Adds this lane's 16 values of a sub-tile of class `cls` into the three
+// band sums; x = l32 + D - edge decides a split sub-tile per element (the
+// upper band when x >= the element's column).
+template <typename KeyOf>
+__device__ __forceinline__ void add_bands(const float (&e)[16], float tot, int cls, int x, KeyOf key_of,
+                                          float& b0, float& b1, float& b2) {
+  if (cls < 3) {
+    if (cls == 0) b0 += tot;
+    else if (cls == 1) b1 += tot;
+    else b2 += tot;
+    return;
+  }
+  float hi = 0.f, lo = 0.f;
+#pragma unroll
+  for (int v = 0; v < 16; ++v) {
+    if (x >= key_of(v))
+      hi += e[v];
+    else
+      lo += e[v];
+  }
+  if (cls == 3) {
+    b0 += hi;
+    b1 += lo;
+  } else {
+    b1 += hi;
+    b2 += lo;
+  }
+}
 
 __device__ __forceinline__ void merge_ml(float& m, float& l, float mo, float lo) {
   const float M = fmaxf(m, mo);
@@ -87,10 +140,10 @@ __device__ __forceinline__ float rows_sum_scatter(const float (&a)[16], int l32)
 
 // kPass 0: row statistics.  kPass 1: map (kMap) and/or block masses (kMass),
 // and the column masses (kCols).
-template <int kPass, bool kMap, bool kMass, bool kCols = false>
+template <int kPass, bool kMap, bool kMass, bool kCols, bool kRagged>
 __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
   __shared__ __attribute__((aligned(1024))) __bf16 ks[kPStages][kPStep * kHeadDim];
-  __shared__ float part[4][kProxyChunk / kBlock][2];  // masses per wave and key block of the chunk
+  __shared__ float part[4][kProxyChunk / kBlock][4];  // masses per wave and key block of the chunk
   // column masses of a step per wave, by step parity: summed over the waves
   // by the first 64 threads in the next step (after its barrier)
   __shared__ float colpart[kCols ? 2 : 1][4][kPStep];
@@ -102,7 +155,8 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
   const int chunk = blockIdx.x, h = blockIdx.y, g = h / p.qpg;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, lg = lane >> 5;
   const int kbeg = chunk * kProxyChunk, kend = min(p.n, kbeg + kProxyChunk);
-  const int nsteps = (kend - kbeg) / kPStep;  // whole key blocks: even, >= 2
+  // whole key blocks (even, >= 2): a partial last block runs both steps
+  const int nsteps = 2 * ((kend - kbeg + kBlock - 1) / kBlock);
   const int pos0 = p.n - kBlock;
   const int row = 32 * w + l32;
 
@@ -125,12 +179,16 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
   }
   const int wu = __builtin_amdgcn_readfirstlane(w);
   auto dma_tile = [&](int stage, int step) {
-    const int soff = (kbeg + step * kPStep) * (kHeadDim * 2);
+    const int key0 = kbeg + step * kPStep;
+    const bool past = kRagged && key0 + kPStep > p.n;  // rows past n read row n-1 (masked: past every proxy row)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      lds_dma_16B(krs, dma_k[i], soff,
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * w + 4 * i + (lane >> 4);
+      const int voff = past ? min(key0 + r, p.n - 1) * (kHeadDim * 2) + (dma_k[i] & 255) : dma_k[i];
+      lds_dma_16B(krs, voff, past ? 0 : key0 * (kHeadDim * 2),
                   (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)(ks[stage] + (16 * wu + 4 * i) *
                                                                                               kHeadDim));
+    }
   };
   // K operand of this lane: row l32 of each 32-key half, logical chunk 2 kk + lg.
   int k_off[8];
@@ -151,6 +209,8 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
   float neg_lse = 0.f;           // pass 2
   if (kPass == 1) neg_lse = -p.lse2[h * kBlock + row];
   float lo = 0.f, up = 0.f;      // this lane's masses of the current key block (pass 2: final; pass 1: against m)
+  float up2 = 0.f, rc = 0.f;     // kRagged: band N-3-kb, and the recency part of key block N-2
+  auto key_of = [&](int v) { return acc_key(v, lg); };
 
   dma_tile(0, 0);
   dma_tile(1, 1);
@@ -170,7 +230,9 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
           if (key0 + 32 * kb2 + acc_key(v, lg) > pos0 + row) s[kb2][v] = -INFINITY;
     }
     if (kPass == 0) {
-      if (j == 0) {  // key kbeg <= pos0 is visible to every row
+      // the running max starts at the first step's max: -inf only for a lane
+      // that sees none of the chunk's first keys, and then none later either
+      if (j == 0) {
         float mx = -INFINITY;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -183,16 +245,40 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
       // diagonal (sub-tile t of the key block against row group w: all below
       // when t < w, all above when t > w, split by row >= column when equal)
       const int half = (key0 >> 6) & 1;
-      float ls = 0.f, bl = 0.f, bu = 0.f;
+      const int kbk = key0 >> 7;  // key block of this step
+      float ls = 0.f, bl = 0.f, bu = 0.f, bu2 = 0.f, brc = 0.f;
       auto step_sums = [&](float nm) {
-        ls = bl = bu = 0.f;
+        ls = bl = bu = bu2 = brc = 0.f;
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2) {
           const int t = 2 * half + kb2;
           float e[16];
 #pragma unroll
           for (int v = 0; v < 16; ++v) e[v] = fast_exp2(fmaf(s[kb2][v], p.scale_log2, nm));
-          if (kMass && t == w) {
+          if (kRagged) {
+            float t8[8];
+#pragma unroll
+            for (int v = 0; v < 8; ++v) t8[v] = e[v] + e[v + 8];
+#pragma unroll
+            for (int v = 0; v < 4; ++v) t8[v] += t8[v + 4];
+            const float sum = (t8[0] + t8[2]) + (t8[1] + t8[3]);
+            ls += sum;
+            if (kMass) {
+              const int D = 32 * (w - t) + p.tlast - kBlock;
+              const int cls = band_class(D);
+              add_bands(e, sum, cls, l32 + D - (cls == 4 ? -kBlock : 0), key_of, bl, bu, bu2);
+              if (kbk == p.nblk - 2) {  // keys >= n - 128: columns >= R of this sub-tile
+                const int R = pos0 - key0 - 32 * kb2;
+                if (R <= 0) {
+                  brc += sum;
+                } else if (R < 32) {
+#pragma unroll
+                  for (int v = 0; v < 16; ++v)
+                    if (acc_key(v, lg) >= R) brc += e[v];
+                }
+              }
+            }
+          } else if (kMass && t == w) {
             float dl = 0.f, du = 0.f;
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
@@ -234,6 +320,10 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
           l *= r;
           lo *= r;
           up *= r;
+          if (kRagged) {
+            up2 *= r;
+            rc *= r;
+          }
           m = m_new;
           step_sums(-m);
         }
@@ -242,33 +332,66 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
       if (kMass) {
         lo += bl;
         up += bu;
-        if (half == 1) {  // end of a key block: this row's two parts, against a common max
+        if (kRagged) {
+          up2 += bu2;
+          rc += brc;
+        }
+        if (half == 1) {  // end of a key block: this row's parts, against a common max
           const float mo = __shfl_xor(m, 32), loo = __shfl_xor(lo, 32), upo = __shfl_xor(up, 32);
+          const float up2o = kRagged ? __shfl_xor(up2, 32) : 0.f, rco = kRagged ? __shfl_xor(rc, 32) : 0.f;
           const float M = fmaxf(m, mo);
-          const float a = fast_exp2(m - M), b = fast_exp2(mo - M);
+          // M = -inf: the row sees no key of this chunk yet (a partial last
+          // chunk that starts past the row), and every part is 0
+          const bool none = M == -INFINITY;
+          const float a = none ? 0.f : fast_exp2(m - M), b = none ? 0.f : fast_exp2(mo - M);
           if (lg == 0) {
             f32x4 rec;
             rec[0] = lo * a + loo * b;
             rec[1] = up * a + upo * b;
-            rec[2] = M;
-            rec[3] = 0.f;
-            p.bpart[((size_t)h * (p.n / kBlock) + (key0 >> 7)) * kBlock + row] = rec;
+            rec[2] = kRagged ? up2 * a + up2o * b : 0.f;
+            rec[3] = M;
+            p.bpart[((size_t)h * p.nblk + kbk) * kBlock + row] = rec;
+            if (kRagged && kbk == p.nblk - 2) p.rpart[h * kBlock + row] = rc * a + rco * b;
           }
           lo = 0.f;
           up = 0.f;
+          up2 = 0.f;
+          rc = 0.f;
         }
       }
     } else {
       // sub-tile t (32 keys) of the key block against row group w: all
       // below the diagonal when t < w, all above when t > w, split when equal
+      // (with 128 | n; band_class in general)
       const int half = (key0 >> 6) & 1;
+      const int kbk = key0 >> 7;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         const int t = 2 * half + kb2;
         float a[16];
 #pragma unroll
         for (int v = 0; v < 16; ++v) a[v] = fast_exp2(fmaf(s[kb2][v], p.scale_log2, neg_lse));
-        if (kMass) {
+        if (kMass && kRagged) {
+          float t8[8];
+#pragma unroll
+          for (int v = 0; v < 8; ++v) t8[v] = a[v] + a[v + 8];
+#pragma unroll
+          for (int v = 0; v < 4; ++v) t8[v] += t8[v + 4];
+          const float sum = (t8[0] + t8[2]) + (t8[1] + t8[3]);
+          const int D = 32 * (w - t) + p.tlast - kBlock;
+          const int cls = band_class(D);
+          add_bands(a, sum, cls, l32 + D - (cls == 4 ? -kBlock : 0), key_of, lo, up, up2);
+          if (kbk == p.nblk - 2) {
+            const int R = pos0 - key0 - 32 * kb2;
+            if (R <= 0) {
+              rc += sum;
+            } else if (R < 32) {
+#pragma unroll
+              for (int v = 0; v < 16; ++v)
+                if (acc_key(v, lg) >= R) rc += a[v];
+            }
+          }
+        } else if (kMass) {
           if (t == w) {  // the diagonal sub-tile: split by row >= column
 #pragma unroll
             for (int v = 0; v < 16; ++v) {
@@ -315,12 +438,18 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
           for (int i = 0; i < 4; ++i) {
             const int r = 8 * i + rr;
             const f32x4 o = *(const f32x4*)(tbuf + (32 * w + r) * kTStride + cc);
-            __builtin_nontemporal_store(
-                o, (f32x4*)(p.amap + ((size_t)h * kBlock + 32 * w + r) * p.n + key0 + 32 * kb2 + cc));
+            float* dst = p.amap + ((size_t)h * kBlock + 32 * w + r) * p.n + key0 + 32 * kb2 + cc;
+            if (kRagged) {  // rows of n floats are not 16-byte aligned; no column past n
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                if (key0 + 32 * kb2 + cc + e < p.n) __builtin_nontemporal_store(o[e], dst + e);
+            } else {
+              __builtin_nontemporal_store(o, (f32x4*)dst);
+            }
           }
         }
       }
-      if (kCols && j > 0 && tid < kPStep) {  // the previous step's column masses
+      if (kCols && j > 0 && tid < kPStep && key0 - kPStep + tid < p.n) {  // the previous step's column masses
         const float* cp = &colpart[(j - 1) & 1][0][tid];
         p.colmass[(size_t)h * p.n + key0 - kPStep + tid] =
             (cp[0] + cp[kPStep] + cp[2 * kPStep] + cp[3 * kPStep]) * (1.f / kBlock);
@@ -330,13 +459,21 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
         for (int o = 1; o < 64; o <<= 1) {
           lo += __shfl_xor(lo, o);
           up += __shfl_xor(up, o);
+          if (kRagged) {
+            up2 += __shfl_xor(up2, o);
+            rc += __shfl_xor(rc, o);
+          }
         }
         if (lane == 0) {
           part[w][(key0 - kbeg) >> 7][0] = lo;
           part[w][(key0 - kbeg) >> 7][1] = up;
+          part[w][(key0 - kbeg) >> 7][2] = kRagged ? up2 : 0.f;
+          part[w][(key0 - kbeg) >> 7][3] = kRagged ? rc : 0.f;
         }
         lo = 0.f;
         up = 0.f;
+        up2 = 0.f;
+        rc = 0.f;
       }
     }
     if (ahead)
@@ -356,20 +493,30 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
       dst[1] = l;
     }
   } else {
-    if (kCols && tid < kPStep) {  // the last step's column masses
+    const int klast = kbeg + (nsteps - 1) * kPStep;  // first key of the last step
+    if (kCols && tid < kPStep && klast + tid < p.n) {  // the last step's column masses
       const float* cp = &colpart[(nsteps - 1) & 1][0][tid];
-      p.colmass[(size_t)h * p.n + kend - kPStep + tid] =
+      p.colmass[(size_t)h * p.n + klast + tid] =
           (cp[0] + cp[kPStep] + cp[2 * kPStep] + cp[3 * kPStep]) * (1.f / kBlock);
     }
   }
   if (kPass == 1 && kMass) {
     // the loop's last barrier orders every wave's parked sums before this
-    const int nkb = (kend - kbeg) >> 7;
-    if (tid < 2 * nkb) {
-      const int jb = tid >> 1, which = tid & 1;
-      const float v = part[0][jb][which] + part[1][jb][which] + part[2][jb][which] + part[3][jb][which];
-      const int N = p.n / kBlock, hq = gridDim.y;
-      p.mass[((size_t)which * hq + h) * N + (kbeg >> 7) + jb] = v;
+    const int nkb = nsteps >> 1;
+    if (tid < 4 * nkb) {
+      const int jb = tid >> 2, which = tid & 3, kb = (kbeg >> 7) + jb;
+      const int N = p.nblk, hq = gridDim.y;
+      float v;
+      if (which < 3) {
+        v = part[0][jb][which] + part[1][jb][which] + part[2][jb][which] + part[3][jb][which];
+      } else if (kb == N - 1) {  // the recency window holds every visible key of the last block
+        v = 0.f;
+#pragma unroll
+        for (int c = 0; c < 3; ++c) v += part[0][jb][c] + part[1][jb][c] + part[2][jb][c] + part[3][jb][c];
+      } else {
+        v = part[0][jb][3] + part[1][jb][3] + part[2][jb][3] + part[3][jb][3];
+      }
+      p.mass[((size_t)which * hq + h) * N + kb] = v;
     }
   }
 }
@@ -395,32 +542,39 @@ __global__ __launch_bounds__(256) void proxy_combine_kernel(ProxyArgs p) {
   }
 }
 
-// Block masses from the stats pass's per-row parts: for w in (below, above),
-// mass[w][h][kb] = sum over the 128 rows of part_w * 2^(max - lse2).  One
-// workgroup per (head, 8 key blocks), 32 lanes per key block.
+// Block masses from the stats pass's per-row parts: for each band plane,
+// mass[c][h][kb] = sum over the 128 rows of part_c * 2^(max - lse2); the
+// recency plane is the whole of block N-1 and the rows' recency parts of
+// block N-2.  One workgroup per (head, 8 key blocks), 32 lanes per key block.
 __global__ __launch_bounds__(256) void mass_combine_kernel(ProxyArgs p) {
   const int h = blockIdx.y, hq = gridDim.y, tid = threadIdx.x;
-  const int N = p.n / kBlock;
+  const int N = p.nblk;
   const int kb = blockIdx.x * 8 + (tid >> 5), li = tid & 31;
-  float lo = 0.f, up = 0.f;
+  float lo = 0.f, up = 0.f, up2 = 0.f, rc = 0.f;
   if (kb < N) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = li + 32 * i;
       const f32x4 rec = p.bpart[((size_t)h * N + kb) * kBlock + r];
-      const float wgt = fast_exp2(rec[2] - p.lse2[h * kBlock + r]);
+      const float wgt = fast_exp2(rec[3] - p.lse2[h * kBlock + r]);
       lo += rec[0] * wgt;
       up += rec[1] * wgt;
+      up2 += rec[2] * wgt;
+      if (p.tlast < kBlock && kb == N - 2) rc += p.rpart[h * kBlock + r] * wgt;
     }
   }
 #pragma unroll
   for (int o = 16; o >= 1; o >>= 1) {
     lo += __shfl_xor(lo, o);
     up += __shfl_xor(up, o);
+    up2 += __shfl_xor(up2, o);
+    rc += __shfl_xor(rc, o);
   }
   if (kb < N && li == 0) {
     p.mass[(size_t)h * N + kb] = lo;
     p.mass[((size_t)hq + h) * N + kb] = up;
+    p.mass[((size_t)2 * hq + h) * N + kb] = up2;
+    p.mass[((size_t)3 * hq + h) * N + kb] = kb == N - 1 ? lo + up + up2 : rc;
   }
 }
 
@@ -452,14 +606,16 @@ __global__ __launch_bounds__(256) void route_kernel(const float* amap, float* c_
 }
 
 // C_struct from the block masses when sink and recency widths are both one
-// block: the mass of key blocks 0 and N-1 over the 128 rows.
+// block: the mass of key block 0 (the first 128 keys) and the recency plane
+// (the last 128 keys: block N-1 and the tail of block N-2) over the 128 rows.
 __global__ void route_mass_kernel(const float* mass, float* c_struct, int32_t* route, int hq, int nblk, float tau,
                                   int override_mode) {
   const int h = blockIdx.x * blockDim.x + threadIdx.x;
   if (h >= hq) return;
-  const float* lo = mass + (size_t)h * nblk;
-  const float* up = mass + ((size_t)hq + h) * nblk;
-  const float c = (lo[0] + up[0] + lo[nblk - 1] + up[nblk - 1]) / (float)kBlock;
+  const size_t plane = (size_t)hq * nblk;
+  const float* m0 = mass + (size_t)h * nblk;
+  const float* rec = m0 + 3 * plane;
+  const float c = (m0[0] + m0[plane] + m0[2 * plane] + rec[nblk - 2] + rec[nblk - 1]) / (float)kBlock;
   c_struct[h] = c;
   route[h] = override_mode == 1 ? 1 : override_mode == 2 ? 0 : (c >= tau ? 1 : 0);
 }
@@ -475,36 +631,54 @@ hipError_t launch_proxy(const __bf16* q, const __bf16* k, float* amap, float* ma
   a.mass = mass;
   a.colmass = colmass;
   a.nchunks = proxy_chunks(n);
+  a.nblk = nblocks(n);
+  a.tlast = n - kBlock * (a.nblk - 1);
   a.part = (float*)scratch;
   a.lse2 = a.part + (size_t)hq * a.nchunks * kBlock * 2;
   a.bpart = (f32x4*)(a.lse2 + (size_t)hq * kBlock);
+  a.rpart = (float*)(a.bpart + (size_t)hq * a.nblk * kBlock);
   a.row_lse = row_lse;
   a.n = n;
   a.qpg = hq / hkv;
   a.scale_log2 = scale * kLog2e;
+  const bool ragged = a.tlast != kBlock;
+  const dim3 grid(a.nchunks, hq);
   // Block masses alone come out of the stats pass (per-row parts against the
   // running max) and one small combine: no second pass over K.
   const bool one_pass = mass != nullptr && amap == nullptr && colmass == nullptr;
-  if (one_pass)
-    hipLaunchKernelGGL((proxy_pass_kernel<0, false, true>), dim3(a.nchunks, hq), dim3(256), 0, stream, a);
+  if (one_pass && ragged)
+    hipLaunchKernelGGL((proxy_pass_kernel<0, false, true, false, true>), grid, dim3(256), 0, stream, a);
+  else if (one_pass)
+    hipLaunchKernelGGL((proxy_pass_kernel<0, false, true, false, false>), grid, dim3(256), 0, stream, a);
+  else if (ragged)
+    hipLaunchKernelGGL((proxy_pass_kernel<0, false, false, false, true>), grid, dim3(256), 0, stream, a);
   else
-    hipLaunchKernelGGL((proxy_pass_kernel<0, false, false>), dim3(a.nchunks, hq), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL((proxy_pass_kernel<0, false, false, false, false>), grid, dim3(256), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(proxy_combine_kernel, dim3(hq * kBlock / 4), dim3(256), 0, stream, a);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (one_pass) {
-    hipLaunchKernelGGL(mass_combine_kernel, dim3((n / kBlock + 7) / 8, hq), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(mass_combine_kernel, dim3((a.nblk + 7) / 8, hq), dim3(256), 0, stream, a);
     return hipGetLastError();
   }
-  const dim3 grid(a.nchunks, hq);
-  if (colmass != nullptr)  // with the block masses, without the map
-    hipLaunchKernelGGL((proxy_pass_kernel<1, false, true, true>), grid, dim3(256), 0, stream, a);
-  else if (mass != nullptr)  // the map and the block masses
-    hipLaunchKernelGGL((proxy_pass_kernel<1, true, true>), grid, dim3(256), 0, stream, a);
-  else
-    hipLaunchKernelGGL((proxy_pass_kernel<1, true, false>), grid, dim3(256), 0, stream, a);
+  if (colmass != nullptr) {  // with the block masses, without the map
+    if (ragged)
+      hipLaunchKernelGGL((proxy_pass_kernel<1, false, true, true, true>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((proxy_pass_kernel<1, false, true, true, false>), grid, dim3(256), 0, stream, a);
+  } else if (mass != nullptr) {  // the map and the block masses
+    if (ragged)
+      hipLaunchKernelGGL((proxy_pass_kernel<1, true, true, false, true>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((proxy_pass_kernel<1, true, true, false, false>), grid, dim3(256), 0, stream, a);
+  } else {
+    if (ragged)
+      hipLaunchKernelGGL((proxy_pass_kernel<1, true, false, false, true>), grid, dim3(256), 0, stream, a);
+    else
+      hipLaunchKernelGGL((proxy_pass_kernel<1, true, false, false, false>), grid, dim3(256), 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -512,7 +686,7 @@ hipError_t launch_route(const float* amap, const float* mass, float* c_struct, i
                         int sink_width, int recency_width, float tau, int route_override, hipStream_t stream) {
   if (mass != nullptr)
     hipLaunchKernelGGL(route_mass_kernel, dim3((hq + 63) / 64), dim3(64), 0, stream, mass, c_struct, route, hq,
-                       n / kBlock, tau, route_override);
+                       nblocks(n), tau, route_override);
   else
     hipLaunchKernelGGL(route_kernel, dim3(hq), dim3(256), 0, stream, amap, c_struct, route, n, sink_width,
                        recency_width, tau, route_override);

@@ -32,38 +32,62 @@ namespace {
 
 constexpr int kAlign = 256;
 
-__global__ __launch_bounds__(256) void tile_sums_kernel(const float* amap, float* lo_out, float* up_out, int n,
-                                                        int nblk) {
+// Block masses from the proxy map: per (head, key block), the mass in each
+// of the tile's slash bands and on the last 128 keys.  Entry (row r, column
+// c) of key block kb lies r - c + t - 128 offsets into band N-1-kb (t: the
+// positions of the last block): band N-1-kb when that is >= 0, N-2-kb when
+// >= -128, else N-3-kb.  With 128 | n: on/below the diagonal, above it.
+template <bool kRagged>
+__global__ __launch_bounds__(256) void tile_sums_kernel(const float* amap, float* mass, int n, int nblk, int hq) {
   __shared__ float red[8];
   const int kb = blockIdx.x, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float* base = amap + (size_t)h * kBlock * n + (size_t)kb * kBlock;
   const int c0 = 4 * (lane & 31), rs = lane >> 5;
+  const int tl = n - kBlock * (nblk - 1);
   f32x4 x[16];
 #pragma unroll
-  for (int i = 0; i < 16; ++i) x[i] = *(const f32x4*)(base + (size_t)(32 * w + 2 * i + rs) * n + c0);
-  float lo = 0.f, up = 0.f;
+  for (int i = 0; i < 16; ++i) {
+    const float* src = base + (size_t)(32 * w + 2 * i + rs) * n + c0;
+    if (kRagged) {  // rows of n floats are not 16-byte aligned; no column past n
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[i][e] = kb * kBlock + c0 + e < n ? src[e] : 0.f;
+    } else {
+      x[i] = *(const f32x4*)src;
+    }
+  }
+  float b0 = 0.f, b1 = 0.f, b2 = 0.f, rc = 0.f;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     const int r = 32 * w + 2 * i + rs;
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      if (r >= c0 + e)
-        lo += x[i][e];
+      const int dlt = r - (c0 + e) + tl - kBlock;
+      if (dlt >= 0)
+        b0 += x[i][e];
+      else if (!kRagged || dlt >= -kBlock)
+        b1 += x[i][e];
       else
-        up += x[i][e];
+        b2 += x[i][e];
+      if (kRagged && kb == nblk - 2 && c0 + e >= tl) rc += x[i][e];
     }
   }
-  lo = block_sum_f(lo, red, tid, 256);
-  up = block_sum_f(up, red, tid, 256);
+  b0 = block_sum_f(b0, red, tid, 256);
+  b1 = block_sum_f(b1, red, tid, 256);
+  if (kRagged) {
+    b2 = block_sum_f(b2, red, tid, 256);
+    rc = block_sum_f(rc, red, tid, 256);
+  }
   if (tid == 0) {
-    lo_out[(size_t)h * nblk + kb] = lo;
-    up_out[(size_t)h * nblk + kb] = up;
+    const size_t plane = (size_t)hq * nblk, at = (size_t)h * nblk + kb;
+    mass[at] = b0;
+    mass[plane + at] = b1;
+    mass[2 * plane + at] = b2;
+    mass[3 * plane + at] = kb == nblk - 1 ? b0 + b1 + b2 : rc;
   }
 }
 
 struct VsArgs {
-  const float* lo;
-  const float* up;
+  const float* mass;  // [4][Hq][N] block masses
   const int32_t* route;
   float* vscore;
   float* sscore;
@@ -93,15 +117,18 @@ __global__ __launch_bounds__(kVsThreads) void vs_select_kernel(VsArgs p) {
   __shared__ float redf[20];
   __shared__ int redi[20];
   const int h = blockIdx.x, dir = blockIdx.y, tid = threadIdx.x;
-  const float* lo = p.lo + (size_t)h * N;
-  const float* up = p.up + (size_t)h * N;
+  const int hq = gridDim.x;
+  const float* lo = p.mass + (size_t)h * N;
+  const float* up = lo + (size_t)hq * N;
+  const float* up2 = up + (size_t)hq * N;
   float* xs = (dir == 0 ? p.vscore : p.sscore) + (size_t)h * N;
   for (int b = tid; b < N; b += kVsThreads) {
     float x;
-    if (dir == 0)
-      x = (lo[b] + up[b]) * (1.f / kBlock);
-    else
-      x = (lo[N - 1 - b] + (b <= N - 2 ? up[N - 2 - b] : 0.f)) * (1.f / kBlock);
+    if (dir == 0)  // vertical: the block's mass in all its bands
+      x = (lo[b] + up[b] + up2[b]) * (1.f / kBlock);
+    else  // slash band b: from key blocks N-1-b, N-2-b, N-3-b
+      x = (lo[N - 1 - b] + (b <= N - 2 ? up[N - 2 - b] : 0.f) + (b <= N - 3 ? up2[N - 3 - b] : 0.f)) *
+          (1.f / kBlock);
     xl[b] = x;
     xs[b] = x;
     mask[b] = 0;
@@ -192,7 +219,8 @@ __global__ __launch_bounds__(256) void pe_pool_kernel(const __bf16* q, const __b
                                                       float* qbar, float* kbar, int hq, int qpg, int n) {
   __shared__ float part[16][kHeadDim];
   const int kb = blockIdx.x, which = blockIdx.y, tid = threadIdx.x;
-  const int nblk = n / kBlock;
+  const int nblk = nblocks(n);
+  const int rows = min(kBlock, n - kb * kBlock);  // fewer in a partial last block
   const __bf16* src;
   float* dst;
   if (which < hq) {
@@ -214,8 +242,10 @@ __global__ __launch_bounds__(256) void pe_pool_kernel(const __bf16* q, const __b
   for (int e = 0; e < 8; ++e) acc[e] = 0.f;
   u32x4 x[8];
 #pragma unroll
-  for (int rr = 0; rr < 8; ++rr)
-    x[rr] = *(const u32x4*)(src + (size_t)(kb * kBlock + rg * 8 + rr) * kHeadDim + 8 * dc);
+  for (int rr = 0; rr < 8; ++rr) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    x[rr] = rg * 8 + rr < rows ? *(const u32x4*)(src + (size_t)(kb * kBlock + rg * 8 + rr) * kHeadDim + 8 * dc) : zero;
+  }
 #pragma unroll
   for (int rr = 0; rr < 8; ++rr)
 #pragma unroll
@@ -230,7 +260,7 @@ __global__ __launch_bounds__(256) void pe_pool_kernel(const __bf16* q, const __b
     float s = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += part[r][tid];
-    dst[(size_t)kb * kHeadDim + tid] = s * (1.f / kBlock);
+    dst[(size_t)kb * kHeadDim + tid] = s / (float)rows;
   }
 }
 
@@ -657,9 +687,10 @@ inline int host_pow2_ceil(int x) {
 }  // namespace
 
 size_t select_workspace_bytes(int hq, int hkv, int n) {
-  const size_t N = (size_t)n / kBlock;
+  const size_t N = (size_t)nblocks(n);
   size_t b = 0;
-  b += 4 * align_up(hq * N * sizeof(float));        // lo, up, vscore, sscore
+  b += align_up(4 * hq * N * sizeof(float));        // block masses from the map
+  b += 2 * align_up(hq * N * sizeof(float));        // vscore, sscore
   b += 2 * align_up(hq * sizeof(float));            // floors
   b += 2 * align_up(hq * N * sizeof(int32_t));      // masks
   b += 2 * align_up(hq * sizeof(int32_t));          // kept counts
@@ -669,7 +700,7 @@ size_t select_workspace_bytes(int hq, int hkv, int n) {
 }
 
 SelectBuffers carve_select_workspace(void* ws, int hq, int hkv, int n) {
-  const size_t N = (size_t)n / kBlock;
+  const size_t N = (size_t)nblocks(n);
   char* p = (char*)ws;
   SelectBuffers b;
   auto take = [&](size_t bytes) {
@@ -677,8 +708,7 @@ SelectBuffers carve_select_workspace(void* ws, int hq, int hkv, int n) {
     p += align_up(bytes);
     return (void*)r;
   };
-  b.lo = (float*)take(hq * N * sizeof(float));
-  b.up = (float*)take(hq * N * sizeof(float));
+  b.mass = (float*)take(4 * hq * N * sizeof(float));
   b.vscore = (float*)take(hq * N * sizeof(float));
   b.sscore = (float*)take(hq * N * sizeof(float));
   b.floor_v = (float*)take(hq * sizeof(float));
@@ -696,20 +726,19 @@ hipError_t launch_select(const __bf16* q, const __bf16* k, const float* amap, co
                          const SelectBuffers& b, int32_t* count, int32_t* idx, int hq, int hkv, int n, float scale,
                          float alpha, float gamma_pe, int kmin, int nf_stat, bool use_gamma, float gamma,
                          const TokenCols* tok, hipStream_t stream) {
-  const int N = n / kBlock;
+  const int N = nblocks(n);
   hipError_t e;
-  const float* lo = mass;
-  const float* up = mass + (size_t)hq * N;
   if (mass == nullptr) {
-    hipLaunchKernelGGL(tile_sums_kernel, dim3(N, hq), dim3(256), 0, stream, amap, b.lo, b.up, n, N);
+    if (n % kBlock != 0)
+      hipLaunchKernelGGL(tile_sums_kernel<true>, dim3(N, hq), dim3(256), 0, stream, amap, b.mass, n, N, hq);
+    else
+      hipLaunchKernelGGL(tile_sums_kernel<false>, dim3(N, hq), dim3(256), 0, stream, amap, b.mass, n, N, hq);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    lo = b.lo;
-    up = b.up;
+    mass = b.mass;
   }
 
   VsArgs va;
-  va.lo = lo;
-  va.up = up;
+  va.mass = mass;
   va.route = route;
   va.vscore = b.vscore;
   va.sscore = b.sscore;

@@ -16,8 +16,13 @@
  *       q        [Hq][n][d]   bf16, rotary embedding already applied
  *       k, v     [Hkv][n][d]  bf16, rotary embedding already applied (k)
  *     Query head h reads KV head h / (Hq / Hkv) (consecutive heads share).
- *   - Supported shapes: d = 128, block = 128, n a multiple of 128 with
- *     n >= 256, Hq a multiple of Hkv.  Anything else is CRISP_ERR_SHAPE.
+ *   - Supported shapes: d = 128, block = 128, 256 <= n <= 524288, Hq a
+ *     multiple of Hkv.  Anything else is CRISP_ERR_SHAPE.
+ *   - Blocks: N = ceil(n / 128) blocks of 128 positions from position 0;
+ *     when 128 does not divide n the last block holds the n - 128 (N-1)
+ *     last positions, and every quantity below covers only the positions
+ *     that exist (a partial block has fewer keys, query rows and offsets;
+ *     its pooled mean is over its rows).
  *   - Every pointer must be 16-byte aligned (CRISP_ERR_ALIGN otherwise).
  *   - The caller owns every buffer; the library allocates nothing.  Its only
  *     global state is a write-once per-device record of whether the device
@@ -72,7 +77,7 @@ typedef enum crisp_status {
 typedef struct crisp_dims {
   int32_t num_q_heads;  /* Hq */
   int32_t num_kv_heads; /* Hkv, divides Hq */
-  int32_t seq_len;      /* n, multiple of block, >= 2 * block */
+  int32_t seq_len;      /* n, 2 * block .. 524288 (any length) */
   int32_t head_dim;     /* d, must be 128 */
   int32_t block;        /* B, must be 128 */
   float scale;          /* softmax scale applied to q.k, > 0 (normally 1/sqrt(d)) */
@@ -93,7 +98,7 @@ typedef struct crisp_cfg {
   int32_t route_override;/* CRISP_ROUTE_AUTO / _FORCE_VS / _FORCE_PE */
 } crisp_cfg;
 
-/* Selection output.  With N = n / 128 blocks, the key-block list of query
+/* Selection output.  With N = ceil(n / 128) blocks, the key-block list of query
  * block qb of head h is idx[h * N(N+1)/2 + qb(qb+1)/2 + t], t < count[h*N+qb],
  * ascending, always holding qb (the diagonal).  Optional diagnostics may be
  * NULL; for PE heads the VS diagnostics are written as zeros. */
@@ -116,17 +121,23 @@ typedef struct crisp_blocks {
  * causally to all keys:
  *   attn_map[h][r][j] = softmax_j(scale * q[h][n-128+r] . k[g(h)][j]), j <= n-128+r,
  *   and 0 for j > n-128+r.                                 [Hq][128][n] fp32
- * block_mass: the map summed per 128x128 tile (key block kb, all 128 rows),
- * split at the tile's diagonal:                               [2][Hq][N] fp32
- *   block_mass[0][h][kb] = sum_{r >= c} attn_map[h][r][128 kb + c]
- *   block_mass[1][h][kb] = sum_{r <  c} attn_map[h][r][128 kb + c]
- * Every quantity routing and selection read from the map follows from
- * these (ai.info summary, "Methodology in Plain English": vertical mass per
- * key block, slash mass per offset band): the vertical score of kb is the
- * tile total over 128, and since proxy row r sits at offset
- * 128(N-1-kb) + r - c from key 128 kb + c, the lower part falls in slash
- * band N-1-kb and the upper part in band N-2-kb.  C_struct with one-block
- * sink and recency widths is (total of block 0 + total of block N-1) / 128.
+ * block_mass: the map summed per key block kb over all 128 rows, split by
+ * slash band and with the recency window apart:              [4][Hq][N] fp32
+ *   entry (r, j) lies at offset o = n-128+r-j, in slash band o / 128
+ *   block_mass[0][h][kb] = mass of key block kb in band N-1-kb
+ *   block_mass[1][h][kb] = mass of key block kb in band N-2-kb
+ *   block_mass[2][h][kb] = mass of key block kb in band N-3-kb
+ *   block_mass[3][h][kb] = mass of key block kb on keys j >= n-128
+ * No other band is reachable.  With 128 | n, entry (r, 128 kb + c) is at
+ * offset 128(N-1-kb) + r - c, so planes 0 and 1 are the tile's mass on/below
+ * (r >= c) and above its diagonal, plane 2 is zero and plane 3 is the total
+ * of block N-1.  Every quantity routing and selection read from the map
+ * follows from these (ai.info summary, "Methodology in Plain English":
+ * vertical mass per key block, slash mass per offset band): the vertical
+ * score of kb is its three band planes summed over 128, the slash score of
+ * band b is planes 0, 1, 2 of key blocks N-1-b, N-2-b, N-3-b over 128, and
+ * C_struct with one-block sink and recency widths is (block 0's bands +
+ * plane 3 of blocks N-2 and N-1) / 128.
  * Either output may be NULL, not both; computing only block_mass skips the
  * 4 * 128 * n * Hq bytes of the map.
  * row_lse (optional, [Hq][128] fp32): natural log of each row's sum of
@@ -259,13 +270,13 @@ CRISP_API crisp_status crisp_sparse_attn_cols(const crisp_dims* dims, const void
  * concentrated).  The pages give no formula; this computes, per query head h
  * of KV group g:
  *   qbar       = mean of q[h] rows n-128 .. n-1 (the proxy rows)
- *   kbar[kb]   = mean of k[g] rows 128kb .. 128kb+127
+ *   kbar[kb]   = mean of k[g] rows 128kb .. min(128kb+127, n-1)
  *   est[kb]    = softmax over all N key blocks of scale * qbar . kbar[kb]
- *   a[kb]      = (block_mass[0][h][kb] + block_mass[1][h][kb]) / 128, the
+ *   a[kb]      = (block_mass[0][h][kb] + [1][h][kb] + [2][h][kb]) / 128, the
  *                proxy map summed per key block and averaged over its rows
  *   js_dist[h] = sqrt(JSD(a, est)), natural log (0 .. sqrt(ln 2))
  *   route[h]   = CRISP_ROUTE_VS when js_dist >= tau_jsd, else CRISP_ROUTE_PE.
- * block_mass: [2][Hq][N] from crisp_proxy.  js_dist [Hq] fp32, route [Hq]
+ * block_mass: [4][Hq][N] from crisp_proxy.  js_dist [Hq] fp32, route [Hq]
  * int32; estimate (optional, [Hq][N] fp32) receives est.  tau_jsd >= 0,
  * finite (CRISP_ERR_PARAM otherwise).  `workspace` must hold
  * crisp_route_jsd_workspace_bytes(dims) bytes of device memory.  Reads all

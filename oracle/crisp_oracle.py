@@ -18,10 +18,13 @@ All arithmetic is float64.  Inputs arrive as float64 arrays that hold the
 exact values of the bf16 tensors the GPU sees.  Array conventions:
   q  : [Hq][n][d]      k, v : [Hkv][n][d]
   GQA group of query head h is g(h) = h * Hkv // Hq (consecutive heads share).
-  B  : block size (128); N = n / B blocks.
+  B  : block size (128); N = ceil(n / B) blocks, aligned at position 0.
+       When B does not divide n the last block holds the n - B (N-1) last
+       positions (reading R29); every quantity below stays defined token by
+       token, so a partial block only has fewer keys, rows or offsets.
 
 Where the pages leave a step open, the reading used here is named in the
-function's docstring with its tag (R1..R25); the same tags are listed with
+function's docstring with its tag (R1..R29); the same tags are listed with
 their justification in the repository's design notes.
 
 Parity pins: every function below is pinned by tests that do not reuse its
@@ -154,31 +157,45 @@ def token_scores(A: np.ndarray):
 
 def pooled_scores(c: np.ndarray, dg: np.ndarray, block: int = 128):
     """Block-pooled scores: v[kb] sums columns of key block kb; sl[s] sums
-    offsets 128s .. 128s+127 (reading R5)."""
+    offsets 128s .. 128s+127 (reading R5).  A partial last block or band
+    sums the entries it has (reading R29)."""
     n = c.shape[0]
-    N = n // block
-    v = c.reshape(N, block).sum(axis=1)
-    sl = dg.reshape(N, block).sum(axis=1)
+    N = -(-n // block)
+    v = np.array([c[b * block:(b + 1) * block].sum() for b in range(N)])
+    sl = np.array([dg[b * block:(b + 1) * block].sum() for b in range(N)])
     return v, sl
 
 
-def block_masses(A: np.ndarray, block: int = 128):
-    """Per key block kb, the proxy map's mass on and below the diagonal of
-    its tile (proxy row r, key 128 kb + c, r >= c) and above it (r < c).
-    Reading R5 pools offsets in bands of 128: row r against key 128 kb + c
-    lies at offset 128 (N-1-kb) + r - c, so these two parts are what the
-    tile gives to slash bands N-1-kb and N-2-kb, and their sum is the tile's
-    vertical mass."""
+def block_masses(A: np.ndarray, block: int = 128, recency_width: int = 128):
+    """Per key block kb, how the proxy map's mass in that block splits over
+    the slash bands, and how much of it lies in the recency window.
+
+    Reading R5 pools offsets in bands of 128: proxy row r (position
+    i_r = n - B + r) against key j lies at offset o = i_r - j, in band
+    o // 128.  Within key block kb every visible entry falls in band
+    N-1-kb, N-2-kb or N-3-kb (the last only when 128 does not divide n,
+    reading R29).  Returns four [N] arrays:
+      lo[kb]  = mass of block kb in band N-1-kb,
+      up[kb]  = mass of block kb in band N-2-kb,
+      up2[kb] = mass of block kb in band N-3-kb,
+      rec[kb] = mass of block kb on keys j >= n - recency_width.
+    lo + up + up2 is the block's vertical mass; with 128 | n, up2 = 0, lo is
+    the tile's mass on and below its diagonal (r >= column) and up the rest,
+    and rec is nonzero in block N-1 only."""
     B, n = A.shape
-    N = n // block
-    lo = np.zeros(N, dtype=np.float64)
-    up = np.zeros(N, dtype=np.float64)
-    for kb in range(N):
-        for r in range(B):
-            row = A[r, kb * block:(kb + 1) * block]
-            lo[kb] += row[: r + 1].sum()
-            up[kb] += row[r + 1:].sum()
-    return lo, up
+    N = -(-n // block)
+    planes = np.zeros(3 * N, dtype=np.float64)
+    rec = np.zeros(N, dtype=np.float64)
+    for r in range(B):
+        i = n - B + r
+        j = np.arange(i + 1)           # the keys row r sees
+        kb = j // block
+        d = (N - 1 - kb) - (i - j) // block
+        a = A[r, : i + 1]
+        planes += np.bincount(d * N + kb, weights=a, minlength=3 * N)
+        inw = j >= n - recency_width
+        rec += np.bincount(kb[inw], weights=a[inw], minlength=N)
+    return planes[:N], planes[N:2 * N], planes[2 * N:], rec
 
 
 # ---------------------------------------------------------------------------
@@ -286,9 +303,11 @@ def vs_gamma_select(x: np.ndarray, gamma: float, kmin: int):
 
 
 def pe_pool(x: np.ndarray, block: int = 128) -> np.ndarray:
-    """Mean of each block of `block` consecutive rows: [n][d] -> [N][d]."""
+    """Mean of each block of `block` consecutive rows: [n][d] -> [N][d].
+    A partial last block is the mean of the rows it has (reading R29)."""
     n, d = x.shape
-    return x.reshape(n // block, block, d).mean(axis=1)
+    N = -(-n // block)
+    return np.stack([x[b * block:(b + 1) * block].mean(axis=0) for b in range(N)])
 
 
 def pe_row_probs(qbar: np.ndarray, kbar: np.ndarray, qb: int, scale: float) -> np.ndarray:
@@ -347,13 +366,15 @@ def attention_rows(q: np.ndarray, k: np.ndarray, v: np.ndarray, lists: Sequence[
     """Block-sparse causal attention of one head for the query blocks `qbs`.
 
     For query i in block qb the key set is the union of the listed key
-    blocks, restricted to keys j <= i.  Returns {qb: (O [block][d], lse [block])}.
+    blocks, restricted to keys j <= i.  Returns {qb: (O [rows][d], lse [rows])}
+    over the block's rows (fewer than `block` in a partial last block).
     """
     out = {}
     for qb in qbs:
+        n = q.shape[0]
         kbs = sorted(set(int(t) for t in lists[qb]))
-        keys = np.concatenate([np.arange(kb * block, (kb + 1) * block) for kb in kbs])
-        rows = np.arange(qb * block, (qb + 1) * block)
+        keys = np.concatenate([np.arange(kb * block, min((kb + 1) * block, n)) for kb in kbs])
+        rows = np.arange(qb * block, min((qb + 1) * block, n))
         s = scale * (q[rows] @ k[keys].T)
         s[keys[None, :] > rows[:, None]] = -np.inf
         m = s.max(axis=1)
@@ -414,7 +435,7 @@ def select_head(q_h: np.ndarray, k_g: np.ndarray, cfg: OracleConfig, scale: floa
         g = cfg.gamma_pe if gamma is None else gamma
         qbar = pe_pool(q_h, B)
         kbar = pe_pool(k_g, B)
-        lists = [pe_row_select(qbar, kbar, qb, scale, g) for qb in range(n // B)]
+        lists = [pe_row_select(qbar, kbar, qb, scale, g) for qb in range(-(-n // B))]
     return HeadResult(c, rt, lse, v, sl, vmask, smask, fv, fs, lists, A=A if keep_map else None)
 
 
@@ -430,7 +451,7 @@ def run_layer(q: np.ndarray, k: np.ndarray, v: np.ndarray, cfg: OracleConfig,
         scale = 1.0 / math.sqrt(d)
     if heads is None:
         heads = range(Hq)
-    N = n // cfg.block
+    N = -(-n // cfg.block)
     qbs = list(range(N)) if attn_qbs is None else list(attn_qbs)
     res = {}
     for h in heads:
@@ -469,7 +490,8 @@ def jsd_actual(A: np.ndarray, block: int = 128) -> np.ndarray:
     """The per-query attention of the proxy rows, summed over each key block
     and averaged over the rows: a distribution over the N key blocks."""
     B, n = A.shape
-    return A.reshape(B, n // block, block).sum(axis=(0, 2)) / B
+    N = -(-n // block)
+    return np.array([A[:, b * block:(b + 1) * block].sum() for b in range(N)]) / B
 
 
 def js_divergence(p: np.ndarray, q: np.ndarray) -> float:
@@ -557,7 +579,7 @@ def token_vs_plan(c: np.ndarray, sl: np.ndarray, alpha: float, kmin_tokens: int,
     holds the retained sink columns and is always a tile.  Reading R28:
     every kept column outside key block 0 is read one by one, by every query
     block past it, on top of the tiles."""
-    N = c.shape[0] // block
+    N = -(-c.shape[0] // block)
     vmask, Tv = token_noise_floor_select(c, alpha, kmin_tokens, block, stat)
     smask, Ts = noise_floor_select(sl, alpha, kmin_blocks, stat)
     vblocks = np.zeros(N, dtype=bool)
@@ -573,14 +595,15 @@ def attention_rows_mixed(q: np.ndarray, k: np.ndarray, v: np.ndarray, lists: Seq
     lies in a listed key block of qb or is one of `cols`.  Each key counts
     once.  Returns {qb: (O [block][d], lse [block])}."""
     out = {}
+    n = q.shape[0]
     col_set = set(int(j) for j in cols)
     for qb in qbs:
         keys = set()
         for kb in lists[qb]:
-            keys.update(range(int(kb) * block, (int(kb) + 1) * block))
+            keys.update(range(int(kb) * block, min((int(kb) + 1) * block, n)))
         keys.update(j for j in col_set if j < (qb + 1) * block)
         keys = np.array(sorted(keys), dtype=np.int64)
-        rows = np.arange(qb * block, (qb + 1) * block)
+        rows = np.arange(qb * block, min((qb + 1) * block, n))
         s = scale * (q[rows] @ k[keys].T)
         s[keys[None, :] > rows[:, None]] = -np.inf
         m = s.max(axis=1)

@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert B.crisp_abi_version() >> 16 == 2
+    assert B.crisp_abi_version() >> 16 == 3
     lib = B.lib()
     for s in range(8):
         assert lib.crisp_status_string(s)
@@ -51,9 +51,13 @@ def test_sizes():
     ws = B.crisp_select_workspace_bytes(d)
     assert ws >= (32 + 8) * N * 128 * 4 + 4 * 32 * N * 4
     assert B.crisp_proxy_scratch_bytes(d) >= 32 * 128 * 4
-    bad = B.make_dims(32, 8, 1000)
+    bad = B.make_dims(32, 8, 255)
     assert B.crisp_list_capacity(bad) == 0
     assert B.crisp_select_workspace_bytes(bad) == 0
+    # a partial last block counts as a block
+    r = B.make_dims(4, 2, 1000)
+    assert B.crisp_list_capacity(r) == 4 * 8 * 9 // 2
+    assert B.crisp_proxy_scratch_bytes(r) >= 4 * 8 * 128 * 16
 
 
 def _dense(dims, q=P16, k=P16, v=P16, out=P16, fp32=0, lse=None):
@@ -61,8 +65,8 @@ def _dense(dims, q=P16, k=P16, v=P16, out=P16, fp32=0, lse=None):
 
 
 @pytest.mark.parametrize("hq,hkv,n,d,blk,status", [
-    (32, 8, 1000, 128, 128, 2),    # n not a multiple of the block
-    (32, 8, 128, 128, 128, 2),     # n below two blocks
+    (32, 8, 255, 128, 128, 2),     # n below two blocks
+    (32, 8, 128, 128, 128, 2),
     (32, 8, 4096, 64, 128, 2),     # head_dim
     (32, 8, 4096, 128, 64, 2),     # block
     (30, 8, 4096, 128, 128, 2),    # Hq % Hkv
@@ -214,7 +218,7 @@ def test_route_jsd_errors():
     lib = B.lib()
     ws = B.crisp_route_jsd_workspace_bytes(dims)
     assert ws >= 4 * 128 * 4 + 4 * 8 * 4
-    assert B.crisp_route_jsd_workspace_bytes(B.make_dims(4, 2, 1000)) == 0
+    assert B.crisp_route_jsd_workspace_bytes(B.make_dims(4, 2, 255)) == 0
 
     def call(tau=0.1, q=P16, k=P16, mass=P16, dist=P16, route=P16, est=None, w=P16, wb=ws):
         return lib.crisp_route_jsd(ctypes.byref(dims), tau, q, k, mass, dist, route, est, w, wb, None)
@@ -230,5 +234,5 @@ def test_route_jsd_errors():
     assert call(dist=P8) == 4
     assert call(est=P8) == 4
     assert call(wb=ws - 4) == 5
-    bad = B.crisp_dims(4, 2, 1000, 128, 128, 0.088)
+    bad = B.crisp_dims(4, 2, 255, 128, 128, 0.088)
     assert lib.crisp_route_jsd(ctypes.byref(bad), 0.1, P16, P16, P16, P16, P16, None, P16, ws, None) == 2

@@ -81,10 +81,10 @@ def test_layer_route_auto(widx):
         assert abs(float(jd[h]) ** 2 - d_o * d_o) <= JSD_ABS + JSD_REL * d_o * d_o, (h, jd[h], d_o)
         check_route(d_o, tau_jsd, int(jr[h]), r_o)
         if h in sampled:
-            lo_o, up_o = O.block_masses(A)
+            planes = O.block_masses(A)
             bm = bufs.block_mass[:, h].cpu().numpy().astype(np.float64)
-            np.testing.assert_allclose(bm[0], lo_o, rtol=1e-3, atol=1e-9)
-            np.testing.assert_allclose(bm[1], up_o, rtol=1e-3, atol=1e-9)
+            for c in range(4):
+                np.testing.assert_allclose(bm[c], planes[c], rtol=1e-3, atol=1e-9, err_msg=f"plane {c}")
         del A
     kcache.clear()
     for h in sampled:

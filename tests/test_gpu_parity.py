@@ -164,12 +164,16 @@ def test_attention_raises_running_max_mid_row(where):
     (4, 2, 1024, "diag"),      # local window only (N = 8: blocks dealt across XCDs)
     (7, 1, 384, "full"),       # 7:1 GQA, full lists = dense
     (8, 8, 1024, "random"),    # one KV head per query head
+    (2, 1, 300, "random"),     # partial last block of 44 rows (N = 3)
+    (4, 2, 1000, "full"),      # partial last block of 104 rows: full lists = dense
+    (3, 1, 1601, "random"),    # partial last block of a single row (N = 13)
+    (2, 2, 2110, "diag"),      # 62 rows: the last block's second 64-key step lies past n
 ])
 def test_sparse_attention_matches_oracle_on_given_lists(hq, hkv, n, kind):
     rng = np.random.default_rng(hq * 1000 + n)
     w = synth.custom(hq, hkv, n, seed=hq + n, needles=2)
     x = synth.make_inputs(w, device="cuda")
-    N = n // BLK
+    N = B.num_blocks(n)
     lists = [_random_lists(rng, N, kind) for _ in range(hq)]
     count, idx = _pack_lists(lists, hq, N)
     dims = B.make_dims(hq, hkv, n)
@@ -190,6 +194,15 @@ def test_sparse_attention_matches_oracle_on_given_lists(hq, hkv, n, kind):
         B.crisp_dense_attn(dims, x.q, x.k, x.v, dense)
         torch.cuda.synchronize()
         assert torch.equal(dense, out)
+    if n % BLK:
+        # rows past n are not written: canary rows after the last head survive
+        outc = torch.full((hq * n + BLK, 128), 7.0, dtype=torch.float32, device="cuda")
+        lsec = torch.full((hq * n + BLK,), 7.0, dtype=torch.float32, device="cuda")
+        B.crisp_sparse_attn(dims, x.q, x.k, x.v, count, idx, outc, lsec)
+        torch.cuda.synchronize()
+        assert torch.equal(outc[: hq * n].view(hq, n, 128), out)
+        assert torch.equal(lsec[: hq * n].view(hq, n), lse)
+        assert bool((outc[hq * n:] == 7.0).all()) and bool((lsec[hq * n:] == 7.0).all())
 
 
 # ---------------------------------------------------------------------------
@@ -209,11 +222,12 @@ def test_proxy_and_route_single_head_4k():
     for r in range(BLK):
         assert np.all(A_g[r, 4096 - BLK + r + 1:] == 0.0)
     np.testing.assert_allclose(bufs.row_lse[0].cpu().numpy(), lse_o, rtol=1e-5, atol=1e-5)
-    lo_o, up_o = O.block_masses(A_o)
+    planes_o = O.block_masses(A_o)
     bm = bufs.block_mass[:, 0].cpu().numpy().astype(np.float64)
-    np.testing.assert_allclose(bm[0], lo_o, rtol=1e-4, atol=1e-9)
-    np.testing.assert_allclose(bm[1], up_o, rtol=1e-4, atol=1e-9)
+    for c in range(4):
+        np.testing.assert_allclose(bm[c], planes_o[c], rtol=1e-4, atol=1e-9, err_msg=f"plane {c}")
     assert bm[1, -1] == 0.0  # the masked half of the diagonal tile
+    assert np.all(bm[2] == 0.0) and np.all(bm[3, :-1] == 0.0)
     c_o = O.c_struct(A_o)
     c_g = float(bufs.c_struct[0])
     assert abs(c_g - c_o) <= REL_CSTRUCT * c_o
@@ -224,7 +238,7 @@ TAU_JSD = 0.1
 
 
 @pytest.mark.parametrize("hq,hkv,n,family", [(1, 1, 4096, False), (8, 2, 4480, False), (14, 2, 2048, False),
-                                             (32, 8, 8192, True)])
+                                             (32, 8, 8192, True), (4, 2, 3000, False)])
 def test_jsd_routing_signal_matches_oracle(hq, hkv, n, family):
     """The comparison routing signal, and C_struct beside it, on the
     single-head 4k workload, a GQA layer whose 35 key blocks leave a partial
@@ -239,8 +253,8 @@ def test_jsd_routing_signal_matches_oracle(hq, hkv, n, family):
         x = synth.make_inputs(synth.custom(hq, hkv, n, seed=hq * 31 + n, needles=4), device="cuda")
     dims = B.make_dims(hq, hkv, n)
     cfg = B.make_cfg(tau=0.2)
-    N = n // BLK
-    mass = torch.empty((2, hq, N), dtype=torch.float32, device="cuda")
+    N = B.num_blocks(n)
+    mass = torch.empty((4, hq, N), dtype=torch.float32, device="cuda")
     partials = torch.empty(B.crisp_proxy_scratch_bytes(dims), dtype=torch.uint8, device="cuda")
     B.crisp_proxy(dims, x.q, x.k, None, partials=partials, block_mass=mass)
     cs = torch.empty(hq, dtype=torch.float32, device="cuda")
@@ -278,18 +292,22 @@ def test_jsd_routing_signal_matches_oracle(hq, hkv, n, family):
         assert 0 < int(rt_g.sum()) < hq and 0 < int(route_g.sum()) < hq
 
 
-@pytest.mark.parametrize("hq,hkv,n", [(1, 1, 4096), (8, 2, 4480), (4, 2, 256)])
+@pytest.mark.parametrize("hq,hkv,n", [(1, 1, 4096), (8, 2, 4480), (4, 2, 256), (4, 2, 1000), (2, 1, 1090),
+                                     (3, 1, 2100), (2, 2, 4097)])
 def test_one_pass_block_masses(hq, hkv, n):
     """Block masses alone come from the stats pass (each row's part per key
     block against its running max, then weighed by 2^(max - lse2)); with the
     map they come from the second pass.  Both against the oracle's
     definition and against each other, on a layer whose last 1024-key chunk
-    holds three key blocks and on the shortest layer."""
+    holds three key blocks, on the shortest layer, and on lengths with a
+    partial last block: 104 positions in one chunk; a last chunk of 66 keys
+    that starts past the first 62 proxy rows; 52 positions (its second
+    64-key step lies past n); a single position."""
     x = inputs(0) if hq == 1 else synth.make_inputs(synth.custom(hq, hkv, n, seed=n + 7, needles=4), device="cuda")
     dims = B.make_dims(hq, hkv, n)
-    N = n // BLK
+    N = B.num_blocks(n)
     part = torch.empty(B.crisp_proxy_scratch_bytes(dims), dtype=torch.uint8, device="cuda")
-    m1 = torch.empty((2, hq, N), dtype=torch.float32, device="cuda")
+    m1 = torch.empty((4, hq, N), dtype=torch.float32, device="cuda")
     m2 = torch.empty_like(m1)
     amap = torch.empty((hq, BLK, n), dtype=torch.float32, device="cuda")
     lse1 = torch.empty((hq, BLK), dtype=torch.float32, device="cuda")
@@ -301,12 +319,28 @@ def test_one_pass_block_masses(hq, hkv, n):
     np.testing.assert_allclose(lse1.cpu().numpy(), lse2.cpu().numpy(), rtol=1e-6, atol=1e-6)
     np.testing.assert_allclose(m1.cpu().numpy(), m2.cpu().numpy(), rtol=1e-5, atol=1e-10)
     g1 = m1.cpu().numpy().astype(np.float64)
+    g2 = m2.cpu().numpy().astype(np.float64)
+    amap_g = amap.cpu().numpy().astype(np.float64)
+    cfg = B.make_cfg()
+    cs = torch.empty(hq, dtype=torch.float32, device="cuda")
+    rt = torch.empty(hq, dtype=torch.int32, device="cuda")
+    cs_map = torch.empty_like(cs)
+    B.crisp_route(dims, cfg, None, cs, rt, block_mass=m1)
+    B.crisp_route(dims, cfg, amap, cs_map, rt)
+    torch.cuda.synchronize()
     for h in range(hq):
         A, _ = O.proxy_map(to64(x.q[h, n - BLK:]), to64(x.k[h * hkv // hq]), dims.scale)
-        lo, up = O.block_masses(A)
-        np.testing.assert_allclose(g1[0, h], lo, rtol=1e-4, atol=1e-9, err_msg=f"head {h} below")
-        np.testing.assert_allclose(g1[1, h], up, rtol=1e-4, atol=1e-9, err_msg=f"head {h} above")
-        assert g1[1, h, -1] == 0.0  # the masked half of the diagonal tile
+        assert np.abs(amap_g[h] - A).max() <= 1e-6, f"head {h} map"
+        planes = O.block_masses(A)
+        for c, name in enumerate(("band N-1-kb", "band N-2-kb", "band N-3-kb", "recency")):
+            np.testing.assert_allclose(g1[c, h], planes[c], rtol=1e-4, atol=1e-9, err_msg=f"head {h} {name}")
+            np.testing.assert_allclose(g2[c, h], planes[c], rtol=1e-4, atol=1e-9, err_msg=f"head {h} {name} 2p")
+        assert g1[1, h, -1] == 0.0 and g1[2, h, -1] == 0.0  # nothing of the last block lies past its band
+        if n % BLK == 0:
+            assert np.all(g1[2, h] == 0.0)
+        c_o = O.c_struct(A)
+        assert abs(float(cs[h]) - c_o) <= REL_CSTRUCT * c_o, (h, float(cs[h]), c_o)
+        assert abs(float(cs_map[h]) - c_o) <= REL_CSTRUCT * c_o, (h, float(cs_map[h]), c_o)
 
 
 @pytest.mark.parametrize("alpha,stat", [(1.25, B.NF_MEDIAN), (1.0, B.NF_MEDIAN), (1.25, B.NF_MEAN)])
@@ -405,6 +439,77 @@ def test_llama_32k_layer(override):
             og = bufs.out[h].cpu().numpy()
             for qb in qbs:
                 check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"h {h} qb {qb}")
+
+
+# ---------------------------------------------------------------------------
+# lengths that 128 does not divide: every step of the chain on a partial
+# last block
+# ---------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("n,mode,use_map", [
+    (5000, "auto", False),      # graded family: both routes; 8 positions in the last block
+    (5000, "auto", True),       # the same from the materialised map
+    (3333, "vs", False),        # forced VS; 5 positions, a last 1024-key chunk of 261 keys
+    (4160, "pe", False),        # forced PE; 64 positions
+    (3001, "gamma", False),     # gamma 0.95 comparison chain; a single position
+])
+def test_ragged_length_chain(n, mode, use_map):
+    """Route, selection and attention at lengths with a partial last block,
+    head by head against the oracle: C_struct and the route, the VS floors,
+    masks and lists, the PE lists (the last query block pooled over its own
+    rows), and the attention of query blocks that include the partial one."""
+    hq, hkv = 8, 2
+    if mode == "auto":
+        x = synth.make_routing_family(seq_len=n, num_q_heads=hq, num_kv_heads=hkv, device="cuda")
+    else:
+        x = synth.make_inputs(synth.custom(hq, hkv, n, seed=n, needles=4), device="cuda")
+    override = {"auto": B.ROUTE_AUTO, "vs": B.ROUTE_FORCE_VS, "pe": B.ROUTE_FORCE_PE, "gamma": B.ROUTE_FORCE_VS}[mode]
+    cfg = B.make_cfg(tau=0.2 if mode == "auto" else 0.5, route_override=override)
+    gamma = 0.95 if mode == "gamma" else None
+    print(f"[ragged] n={n} mode={mode} map={use_map}", flush=True)
+    dims, bufs = run_chain(x, cfg, gamma=gamma, use_map=use_map)
+    N = B.num_blocks(n)
+    assert n % BLK and N == n // BLK + 1
+    count = bufs.blocks["count"].cpu().numpy()
+    idx = bufs.blocks["idx"].cpu().numpy()
+    cs = bufs.c_struct.cpu().numpy()
+    rt = bufs.route.cpu().numpy()
+    out = bufs.out.cpu().numpy()
+    lse = bufs.lse.cpu().numpy()
+    qbs = [0, 1, N // 2, N - 2, N - 1]
+    for h in range(hq):
+        g = h * hkv // hq
+        q, k, v = to64(x.q[h]), to64(x.k[g]), to64(x.v[g])
+        A, _ = O.proxy_map(q[n - BLK:], k, dims.scale)
+        c_o = O.c_struct(A)
+        assert abs(cs[h] - c_o) <= REL_CSTRUCT * c_o, (h, cs[h], c_o)
+        check_route(c_o, cfg.tau, int(rt[h]), O.route(c_o, cfg.tau, override))
+        lists_g = gpu_lists(count, idx, h, N)
+        assert all(l[-1] == qb for qb, l in enumerate(lists_g))
+        if rt[h] == O.ROUTE_VS:
+            ct, dg = O.token_scores(A)
+            vs, sl = O.pooled_scores(ct, dg)
+            np.testing.assert_allclose(bufs.blocks["v_score"][h].cpu().numpy(), vs, rtol=1e-4, atol=1e-9)
+            np.testing.assert_allclose(bufs.blocks["s_score"][h].cpu().numpy(), sl, rtol=1e-4, atol=1e-9)
+            vm = bufs.blocks["v_mask"][h].cpu().numpy()
+            sm = bufs.blocks["s_mask"][h].cpu().numpy()
+            if gamma is None:
+                check_noise_floor_mask(vs, cfg.alpha, 8, 0, vm, float(bufs.blocks["floor_v"][h]))
+                check_noise_floor_mask(sl, cfg.alpha, 8, 0, sm, float(bufs.blocks["floor_s"][h]))
+            else:
+                for xs, m in ((vs, vm), (sl, sm)):
+                    check_gamma_set(xs, range(N), gamma, set(np.nonzero(m)[0].tolist()), {0}, extra_fill=8)
+            assert lists_g == O.vs_lists(vm.astype(bool), sm.astype(bool))
+        else:
+            check_pe_lists(O.pe_pool(q), O.pe_pool(k), dims.scale, gamma or cfg.gamma_pe, lists_g, qbs=qbs)
+        ref = O.attention_rows(q, k, v, lists_g, dims.scale, qbs)
+        for qb in qbs:
+            rows = slice(qb * BLK, min((qb + 1) * BLK, n))
+            check_attention(out[h, rows], ref[qb][0], f"n {n} h {h} qb {qb}")
+            check_lse(lse[h, rows], ref[qb][1])
+    if mode == "auto":
+        assert 0 < int(rt.sum()) < hq  # both routes occur
 
 
 @pytest.mark.parametrize("override", [B.ROUTE_AUTO, B.ROUTE_FORCE_VS])

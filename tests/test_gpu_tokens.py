@@ -43,11 +43,11 @@ def _token_chain(x, cfg):
 
 
 def test_column_masses_match_oracle_and_block_masses_agree():
-    for hq, hkv, n in [(1, 1, 4096), (8, 2, 4480)]:
+    for hq, hkv, n in [(1, 1, 4096), (8, 2, 4480), (2, 1, 3030), (2, 2, 1090)]:
         x = _inputs(hq, hkv, n, 41)
         dims = B.make_dims(hq, hkv, n)
-        N = n // BLK
-        mass = torch.empty((2, hq, N), dtype=torch.float32, device="cuda")
+        N = B.num_blocks(n)
+        mass = torch.empty((4, hq, N), dtype=torch.float32, device="cuda")
         mass_ref = torch.empty_like(mass)
         cm = torch.empty((hq, n), dtype=torch.float32, device="cuda")
         part = torch.empty(B.crisp_proxy_scratch_bytes(dims), dtype=torch.uint8, device="cuda")
@@ -75,7 +75,7 @@ def test_token_selection_matches_oracle(alpha, stat, kmin):
     x = _inputs(hq, hkv, n, 43)
     cfg = B.make_cfg(alpha=alpha, nf_stat=stat, kmin_blocks=kmin, route_override=B.ROUTE_FORCE_VS)
     dims, bufs = _token_chain(x, cfg)
-    N = n // BLK
+    N = B.num_blocks(n)
     cols = bufs.cols.cpu().numpy()
     ncols = bufs.ncols.cpu().numpy()
     below = bufs.col_below.cpu().numpy()
@@ -110,7 +110,7 @@ def test_token_chain_attention_matches_oracle():
     x = _inputs(hq, hkv, n, 47)
     cfg = B.make_cfg(route_override=B.ROUTE_FORCE_VS)
     dims, bufs = _token_chain(x, cfg)
-    N = n // BLK
+    N = B.num_blocks(n)
     cols = bufs.cols.cpu().numpy()
     ncols = bufs.ncols.cpu().numpy()
     count = bufs.blocks["count"].cpu().numpy()
@@ -136,7 +136,7 @@ def test_column_kernel_on_given_lists_and_columns(ncol, n):
     number of query blocks (a pair with one block), and more columns than
     one staged index chunk (2048)."""
     hq, hkv = 4, 2
-    N = n // BLK
+    N = B.num_blocks(n)
     x = _inputs(hq, hkv, n, 53 + ncol)
     dims = B.make_dims(hq, hkv, n)
     rng = np.random.default_rng(ncol)
@@ -189,15 +189,17 @@ def test_token_chain_is_deterministic():
         assert torch.equal(b1.cols[h, :k], b2.cols[h, :k])
 
 
-@pytest.mark.parametrize("hq,hkv,n", [(2, 1, 256), (2, 1, 384), (4, 2, 1152)])
+@pytest.mark.parametrize("hq,hkv,n", [(2, 1, 256), (2, 1, 384), (4, 2, 1152), (2, 1, 700), (4, 2, 3100),
+                                     (2, 2, 2049)])
 def test_token_chain_small_layers(hq, hkv, n):
     """The shortest layers (two and three key blocks, an odd block count):
     fewer candidate columns than k_min, so the top-up decides, and query
-    block pairs with a missing second block."""
+    block pairs with a missing second block; then lengths with a partial
+    last block (60, 28 and 1 positions)."""
     x = _inputs(hq, hkv, n, 61 + n)
     cfg = B.make_cfg(route_override=B.ROUTE_FORCE_VS)
     dims, bufs = _token_chain(x, cfg)
-    N = n // BLK
+    N = B.num_blocks(n)
     cols = bufs.cols.cpu().numpy()
     ncols = bufs.ncols.cpu().numpy()
     count = bufs.blocks["count"].cpu().numpy()
@@ -221,7 +223,7 @@ def test_token_chain_small_layers(hq, hkv, n):
         assert lists == O.vs_lists(vb, smask[h].astype(bool))
         ref = O.attention_rows_mixed(q, k, v, lists, kept.tolist(), dims.scale, range(N))
         for qb in range(N):
-            check_attention(out[h, qb * BLK:(qb + 1) * BLK], ref[qb][0], f"n {n} head {h} qb {qb}")
+            check_attention(out[h, qb * BLK:min((qb + 1) * BLK, n)], ref[qb][0], f"n {n} head {h} qb {qb}")
 
 
 def test_token_chain_with_mixed_routes():
@@ -234,7 +236,7 @@ def test_token_chain_with_mixed_routes():
     hq, hkv = x.q.shape[0], x.k.shape[0]
     cfg = B.make_cfg(tau=0.2)
     dims, bufs = _token_chain(x, cfg)
-    N = n // BLK
+    N = B.num_blocks(n)
     route = bufs.route.cpu().numpy()
     assert 0 < int(route.sum()) < hq, "the family must mix both routes"
     cols = bufs.cols.cpu().numpy()

@@ -183,40 +183,65 @@ def test_scores_sum_to_one_and_tile_triangle_identity():
     np.testing.assert_allclose(sl, sl_t, rtol=1e-12, atol=1e-18)
 
 
-def test_block_masses_give_vertical_slash_and_c_struct():
+@pytest.mark.parametrize("n", [1536, 1499, 300, 257])
+def test_block_masses_give_vertical_slash_and_c_struct(n):
     # block_masses is pinned by quantities computed along other routes: the
     # column sums (v), the diagonal loop (sl) and the slice sums (C_struct).
+    # 1499, 300 and 257 leave a partial last block (43, 44 and 1 positions).
     rng = _rng(16)
-    n, d = 1536, 64
+    d = 64
     A, _ = O.proxy_map(rng.standard_normal((B, d)), rng.standard_normal((n, d)), 0.3)
-    lo, up = O.block_masses(A)
+    lo, up, up2, rec = O.block_masses(A)
     v, sl = O.pooled_scores(*O.token_scores(A))
-    N = n // B
-    np.testing.assert_allclose((lo + up) / B, v, rtol=1e-12)
+    N = -(-n // B)
+    assert len(lo) == N
+    np.testing.assert_allclose((lo + up + up2) / B, v, rtol=1e-12)
     sl_b = np.zeros(N)
     for s in range(N):
-        sl_b[s] = lo[N - 1 - s] + (up[N - 2 - s] if s <= N - 2 else 0.0)
+        sl_b[s] = lo[N - 1 - s] + (up[N - 2 - s] if s <= N - 2 else 0.0) + (up2[N - 3 - s] if s <= N - 3 else 0.0)
     np.testing.assert_allclose(sl_b / B, sl, rtol=1e-12, atol=1e-18)
-    assert up[N - 1] == 0.0  # the masked half of the diagonal tile
-    c = (lo[0] + up[0] + lo[N - 1] + up[N - 1]) / B
+    # with 128 | n the tile splits at its diagonal only; with a partial last
+    # block its neighbour N-2 is fully visible and holds part of the window
+    if n % B == 0:
+        assert np.all(up2 == 0.0)
+        assert up[N - 1] == 0.0  # the masked half of the diagonal tile
+        assert np.all(rec[: N - 1] == 0.0)
+    else:
+        assert up2[: N - 2].sum() > 0.0
+        assert rec[N - 2] > 0.0
+    assert np.all(rec[: N - 2] == 0.0)
+    np.testing.assert_allclose(rec[N - 1], lo[N - 1] + up[N - 1] + up2[N - 1], rtol=1e-12)
+    c = (lo[0] + up[0] + up2[0] + rec.sum()) / B
     assert c == pytest.approx(O.c_struct(A), rel=1e-12)
 
 
-def test_block_masses_closed_form_at_zero_query():
+@pytest.mark.parametrize("n", [768, 700])
+def test_block_masses_closed_form_at_zero_query(n):
     # Q = 0: row r (position i_r = n - 128 + r) is uniform, 1/(i_r + 1), on
-    # keys 0..i_r.  A fully visible tile gives r + 1 columns on/below the
-    # diagonal and 127 - r above; the diagonal tile only the r + 1.
-    n = 768
-    N = n // B
+    # keys 0..i_r.  With t = n - 128 (N-1) positions in the last block, a
+    # fully visible tile has entry (r, column c) at offset
+    # 128 (N-1-kb) + (r + t - 128 - c): band N-1-kb for c <= r + t - 128,
+    # N-2-kb for r + t - 128 < c <= r + t, N-3-kb above.  Counting columns:
+    N = -(-n // B)
+    t = n - B * (N - 1)
     A, _ = O.proxy_map(np.zeros((B, 16)), _rng(17).standard_normal((n, 16)), 1.0)
-    lo, up = O.block_masses(A)
-    inv = np.array([1.0 / (n - B + r + 1) for r in range(B)])
+    lo, up, up2, rec = O.block_masses(A)
     r = np.arange(B)
-    for kb in range(N - 1):
-        assert lo[kb] == pytest.approx(float(((r + 1) * inv).sum()), rel=1e-12)
-        assert up[kb] == pytest.approx(float(((B - 1 - r) * inv).sum()), rel=1e-12)
-    assert lo[N - 1] == pytest.approx(float(((r + 1) * inv).sum()), rel=1e-12)
-    assert up[N - 1] == 0.0
+    inv = 1.0 / (n - B + r + 1)
+    n_lo = np.clip(r + t - B + 1, 0, B)
+    n_up = np.clip(r + t + 1, 0, B) - n_lo
+    n_up2 = B - n_lo - n_up
+    full = range(N - 2) if t < B else range(N - 1)
+    for kb in full:
+        assert lo[kb] == pytest.approx(float((n_lo * inv).sum()), rel=1e-12)
+        assert up[kb] == pytest.approx(float((n_up * inv).sum()), rel=1e-12)
+        assert up2[kb] == pytest.approx(float((n_up2 * inv).sum()), rel=1e-12, abs=1e-300)
+    # the last block: row r sees its first r + t - 127 keys, all in band 0
+    vis = np.clip(r + t - B + 1, 0, t)
+    assert lo[N - 1] == pytest.approx(float((vis * inv).sum()), rel=1e-12)
+    assert up[N - 1] == 0.0 and up2[N - 1] == 0.0
+    # recency window: keys n-128 .. i_r, r + 1 of them per row
+    assert rec.sum() == pytest.approx(float(((r + 1) * inv).sum()), rel=1e-12)
 
 
 def test_periodic_slash_closed_form():
@@ -443,15 +468,20 @@ def test_pe_two_level_closed_form():
     assert len(O.gamma_prefix(p, gamma)) == closed
 
 
-def test_pe_pool_means():
+@pytest.mark.parametrize("n", [4 * B, 3 * B + 29])
+def test_pe_pool_means(n):
     rng = _rng(9)
-    x = rng.standard_normal((4 * B, 5))
+    x = rng.standard_normal((n, 5))
     m = O.pe_pool(x)
+    assert m.shape == (4, 5)
     for b in range(4):
         acc = np.zeros(5)
+        cnt = 0
         for t in range(B):
-            acc += x[b * B + t]
-        np.testing.assert_allclose(m[b], acc / B, rtol=1e-13)
+            if b * B + t < n:
+                acc += x[b * B + t]
+                cnt += 1
+        np.testing.assert_allclose(m[b], acc / cnt, rtol=1e-13)
 
 
 # --------------------------------------------------------------------------
@@ -473,15 +503,17 @@ def _brute_dense(q, k, v, scale):
     return out, lse
 
 
-def test_all_blocks_equal_brute_force_dense():
+@pytest.mark.parametrize("n", [3 * B, 2 * B + 57])
+def test_all_blocks_equal_brute_force_dense(n):
     rng = _rng(10)
-    n, d = 3 * B, 16
+    d = 16
     q, k, v = (rng.standard_normal((n, d)) for _ in range(3))
     scale = 0.37
     res = O.attention_rows(q, k, v, O.dense_lists(3), scale, range(3))
     ref, ref_lse = _brute_dense(q, k, v, scale)
     for qb in range(3):
         Ob, lb = res[qb]
+        assert Ob.shape[0] == min(B, n - qb * B)
         np.testing.assert_allclose(Ob, ref[qb * B:(qb + 1) * B], rtol=1e-11, atol=1e-12)
         np.testing.assert_allclose(lb, ref_lse[qb * B:(qb + 1) * B], rtol=1e-12)
 
