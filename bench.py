@@ -57,6 +57,11 @@ def parse():
                     help="C_struct vs JSD routing agreement and routing cost on the five synthetic layers")
     ap.add_argument("--agreement-out", default="", help="also write the agreement report as JSON to this path")
     ap.add_argument("--tau-jsd", type=float, default=0.1, help="JSD distance threshold of the agreement report")
+    ap.add_argument("--counts", action="store_true",
+                    help="selected-block counts of the noise floor and gamma-cumulative selection per head and "
+                         "direction on --counts-workload, with the tiles and time of each chain")
+    ap.add_argument("--counts-workload", default="llama3.1-8b-256k")
+    ap.add_argument("--counts-out", default="", help="also write the counts report as JSON to this path")
     ap.add_argument("--token-chain", action="store_true",
                     help="time only the token-granular chain (forced VS, alpha 1.25) on --workload (profiling runs)")
     return ap.parse_args()
@@ -475,6 +480,67 @@ def sweep(torch, B, synth, args):
     return rows
 
 
+COUNT_CHAINS = (("route auto", None, None, None), ("noise floor alpha 1.25", 1.25, None, "vs"),
+                ("noise floor alpha 1.0", 1.0, None, "vs"), ("gamma 0.95", 1.25, 0.95, "vs"),
+                ("gamma 0.97", 1.25, 0.97, "vs"))
+
+
+def counts(torch, B, synth, args):
+    """Selected-block counts, noise floor against gamma-cumulative coverage.
+
+    Both rules run on every head's vertical and slash block scores (route
+    forced to Vertical-Slash), beside the route-auto chain: per head and
+    direction the kept blocks, and per chain the tiles the attention
+    computes and the layer's time.  The O(n) claim (ai.info "Key
+    Contributions" 3) shows as the gamma counts covering most of the N
+    blocks while the noise floor keeps a handful."""
+    w = synth.workload(args.counts_workload)
+    log(f"generating {w.name} on the GPU")
+    x = synth.make_inputs(w, device="cuda")
+    dims = B.make_dims(w.num_q_heads, w.num_kv_heads, w.seq_len)
+    bufs = B.CrispBuffers(dims, out_dtype=torch.bfloat16)
+    N = -(-w.seq_len // 128)
+    dense_tiles = w.num_q_heads * N * (N + 1) // 2
+    dense_ms = _med_ms(torch, lambda: B.crisp_dense_attn(dims, x.q, x.k, x.v, bufs.out), args.compare_steps)
+    rows = []
+    for name, alpha, gamma, route in COUNT_CHAINS:
+        kw = {} if route is None else {"route_override": B.ROUTE_FORCE_VS, "alpha": alpha}
+        cfg = B.make_cfg(**kw)
+        t = _med_ms(torch, lambda: B.crisp_prefill(dims, cfg, x.q, x.k, x.v, bufs, gamma=gamma, dense_below=0),
+                    args.compare_steps)
+        tiles = int(bufs.blocks["count"].sum().item())
+        routes = bufs.route.cpu().tolist()
+        r = {"chain": name, "ms": t, "tiles": tiles, "tile_frac": tiles / dense_tiles, "speedup": dense_ms / t,
+             "heads_vs": int(sum(routes)), "n_v": bufs.blocks["n_v"].cpu().tolist(),
+             "n_s": bufs.blocks["n_s"].cpu().tolist()}
+        rows.append(r)
+        log(f"counts {w.name} {name}: {t:.2f} ms, {tiles} tiles ({100 * r['tile_frac']:.1f}%)")
+    sink = set(range(w.num_sink_heads))
+    print(f"Workload {w.name}: {w.num_q_heads} query / {w.num_kv_heads} KV heads, n = {w.seq_len}, N = {N} "
+          f"blocks of 128; dense causal tiles {dense_tiles}; dense kernel {dense_ms:.2f} ms\n")
+    print("| chain | VS heads | ms | speedup vs dense | tiles | of causal | mean vertical blocks | "
+          "mean slash blocks |")
+    print("|---|---|---|---|---|---|---|---|")
+    for r in rows:
+        # vertical/slash counts mean something only when every head took the VS route
+        cells = ("-", "-") if r["chain"] == "route auto" else \
+            (f"{sum(r['n_v']) / len(r['n_v']):.1f}", f"{sum(r['n_s']) / len(r['n_s']):.1f}")
+        print(f"| {r['chain']} | {r['heads_vs']} | {r['ms']:.2f} | {r['speedup']:.2f}x | {r['tiles']} | "
+              f"{100 * r['tile_frac']:.2f}% | {cells[0]} | {cells[1]} |")
+    per = [r for r in rows if r["chain"] != "route auto"]
+    print("\nKept blocks per head, vertical / slash (of N = %d per direction)\n" % N)
+    print("| head | kind | " + " | ".join(r["chain"] for r in per) + " |")
+    print("|---|---|" + "---|" * len(per))
+    for h in range(w.num_q_heads):
+        kind = "sink" if h in sink else "diffuse"
+        print(f"| {h} | {kind} | " + " | ".join(f"{r['n_v'][h]} / {r['n_s'][h]}" for r in per) + " |")
+    if args.counts_out:
+        with open(args.counts_out, "w") as f:
+            json.dump({"workload": w.name, "dense_ms": dense_ms, "dense_tiles": dense_tiles, "rows": rows}, f,
+                      indent=1)
+    return rows
+
+
 AGREEMENT_WORKLOADS = (0, 1, 2, 3, 4, "family-32k", "family-512k")
 AGREEMENT_TAUS = (0.2, 0.5)
 AGREEMENT_TAU_JSDS = (0.1, 0.2, 0.3, 0.4, 0.5)
@@ -627,6 +693,9 @@ def main():
         return
     if args.agreement:
         agreement(torch, B, synth, args)
+        return
+    if args.counts:
+        counts(torch, B, synth, args)
         return
     if args.token_chain:
         w = synth.workload(args.workload)
