@@ -72,6 +72,7 @@ def _dense(dims, q=P16, k=P16, v=P16, out=P16, fp32=0, lse=None):
     (30, 8, 4096, 128, 128, 2),    # Hq % Hkv
     (32, 0, 4096, 128, 128, 2),
     (32, 8, 1 << 21, 128, 128, 2), # beyond the supported length
+    (32, 8, 524289, 128, 128, 2),  # one position past the longest layer
 ])
 def test_shape_errors(hq, hkv, n, d, blk, status):
     dims = B.crisp_dims(hq, hkv, n, d, blk, 0.088)
