@@ -69,6 +69,7 @@ struct ProxyArgs {
   int qpg;
   int nchunks;
   float scale_log2;
+  RowMap map;    // workgroup id -> (head, key chunk), over the chunks as blocks
 };
 
 // Band class of sub-tile st against the rows of wave w (see the top):
@@ -152,7 +153,12 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
   // distinct banks
   constexpr int kTStride = 36;
   __shared__ __attribute__((aligned(16))) float tbuf[kMap ? 4 * 32 * kTStride : 1];
-  const int chunk = blockIdx.x, h = blockIdx.y, g = h / p.qpg;
+  // The heads of a KV group read the same K chunk: the row map deals them
+  // to one XCD on consecutive slots, so K comes from that XCD's L2 once per
+  // group instead of from HBM once per head.
+  int chunk, h;
+  map_row(p.map, blockIdx.x, &h, &chunk);
+  const int g = h / p.qpg;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l32 = lane & 31, lg = lane >> 5;
   const int kbeg = chunk * kProxyChunk, kend = min(p.n, kbeg + kProxyChunk);
   // whole key blocks (even, >= 2): a partial last block runs both steps
@@ -505,7 +511,7 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
     const int nkb = nsteps >> 1;
     if (tid < 4 * nkb) {
       const int jb = tid >> 2, which = tid & 3, kb = (kbeg >> 7) + jb;
-      const int N = p.nblk, hq = gridDim.y;
+      const int N = p.nblk, hq = p.map.hq;
       float v;
       if (which < 3) {
         v = part[0][jb][which] + part[1][jb][which] + part[2][jb][which] + part[3][jb][which];
@@ -642,7 +648,8 @@ hipError_t launch_proxy(const __bf16* q, const __bf16* k, float* amap, float* ma
   a.qpg = hq / hkv;
   a.scale_log2 = scale * kLog2e;
   const bool ragged = a.tlast != kBlock;
-  const dim3 grid(a.nchunks, hq);
+  a.map = make_row_map(hq, hkv, a.nchunks);
+  const dim3 grid(a.nchunks * hq);
   // Block masses alone come out of the stats pass (per-row parts against the
   // running max) and one small combine: no second pass over K.
   const bool one_pass = mass != nullptr && amap == nullptr && colmass == nullptr;
