@@ -345,24 +345,31 @@ __global__ __launch_bounds__(kPeThreads) void pe_select_kernel(PeArgs p) {
   const int tid = threadIdx.x, l16 = tid & 15, grp = tid >> 4, lane = tid & 63;
   const int g = h / p.qpg;
 
-  // pooled logits (base 2): 16 lanes per key block, 8 dims each
+  // pooled logits (base 2): 16 lanes per key block, 8 dims each; four
+  // groups of 16 key blocks per iteration, their loads issued together
   const float* qv = p.qbar + ((size_t)h * N + qb) * kHeadDim + 8 * l16;
   const f32x4 qa = *(const f32x4*)qv, qc = *(const f32x4*)(qv + 4);
   const float* kbase = p.kbar + (size_t)g * N * kHeadDim + 8 * l16;
-  for (int kb0 = 0; kb0 < L; kb0 += 16) {
-    const int kb = kb0 + grp;
-    float dot = 0.f;
-    if (kb < L) {
-      const f32x4 ka = *(const f32x4*)(kbase + (size_t)kb * kHeadDim);
-      const f32x4 kc = *(const f32x4*)(kbase + (size_t)kb * kHeadDim + 4);
-      dot = qa[0] * ka[0] + qa[1] * ka[1] + qa[2] * ka[2] + qa[3] * ka[3] + qc[0] * kc[0] + qc[1] * kc[1] +
-            qc[2] * kc[2] + qc[3] * kc[3];
+  constexpr int kPeUnroll = 4;
+  for (int kb0 = 0; kb0 < L; kb0 += 16 * kPeUnroll) {
+    f32x4 ka[kPeUnroll], kc[kPeUnroll];
+#pragma unroll
+    for (int u = 0; u < kPeUnroll; ++u) {
+      const int kb = min(kb0 + 16 * u + grp, L - 1);  // rows past the causal range: a valid row, result unused
+      ka[u] = *(const f32x4*)(kbase + (size_t)kb * kHeadDim);
+      kc[u] = *(const f32x4*)(kbase + (size_t)kb * kHeadDim + 4);
     }
-    dot += __shfl_xor(dot, 1);
-    dot += __shfl_xor(dot, 2);
-    dot += __shfl_xor(dot, 4);
-    dot += __shfl_xor(dot, 8);
-    if (kb < L && l16 == 0) pr[kb] = dot * p.scale_log2;
+#pragma unroll
+    for (int u = 0; u < kPeUnroll; ++u) {
+      const int kb = kb0 + 16 * u + grp;
+      float dot = qa[0] * ka[u][0] + qa[1] * ka[u][1] + qa[2] * ka[u][2] + qa[3] * ka[u][3] + qc[0] * kc[u][0] +
+                  qc[1] * kc[u][1] + qc[2] * kc[u][2] + qc[3] * kc[u][3];
+      dot += __shfl_xor(dot, 1);
+      dot += __shfl_xor(dot, 2);
+      dot += __shfl_xor(dot, 4);
+      dot += __shfl_xor(dot, 8);
+      if (kb < L && l16 == 0) pr[kb] = dot * p.scale_log2;
+    }
   }
   __syncthreads();
   float mx = -INFINITY;
