@@ -367,6 +367,26 @@ def mfma_ceiling(torch):
     return probe.crisp_probe_mfma_bf16_flops(nblocks, iters) / (ms[2] * 1e-3) / 1e12
 
 
+def _host_cpu():
+    """CPU model, logical CPU count and BLAS thread pools of the host."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        import numpy  # noqa: F401  (loads the BLAS whose pools are listed)
+        from threadpoolctl import threadpool_info
+        blas = [f"{i.get('internal_api')}:{i.get('num_threads')}" for i in threadpool_info()]
+    except Exception:  # pragma: no cover
+        blas = []
+    return {"cpu_model": model, "logical_cpus": os.cpu_count(), "blas_threads": blas}
+
+
 def cpu_baseline(q, k, v, dims, res, cfg_kw):
     """The fp64 oracle on a bounded sample of the same layer (head 0), scaled
     to ms/layer: per-head proxy/route/scores x Hq, pooled-estimation rows by
@@ -408,6 +428,7 @@ def cpu_baseline(q, k, v, dims, res, cfg_kw):
     tiles = res["crisp"]["tiles"]
     total_s = t_head * hq + t_pe_head * res["crisp"]["heads_pe"] + t_att / tiles_sampled * tiles
     return {"value": round(total_s * 1e3, 1), "unit": "ms", "cores": int(threads), "kind": "oracle",
+            "host": _host_cpu(),
             "sample": (f"head 0 of {res['workload']}: proxy map, C_struct and vertical/slash scores in full, "
                        f"{len(rows)} pooled-estimation rows, attention of query blocks {att_rows} "
                        f"({tiles_sampled} tiles); scaled to {hq} heads, N(N+1)/2 pooled pairs per PE head "
