@@ -187,6 +187,60 @@ def test_layer_forced_vertical_slash(widx):
             check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"{w.name} VS h {h} qb {qb}")
 
 
+@pytest.mark.parametrize("mode", ["auto", "vs"])
+def test_longest_layer_with_partial_last_block(mode):
+    """The 512k Llama workload cut 37 positions short of the longest
+    supported layer, so the last key and query block hold 91 positions:
+    C_struct and route of sampled heads, the selection of a sampled head and
+    the attention of sampled query blocks, the partial one included, against
+    the oracle on the GPU's lists."""
+    w = synth.workload(4)
+    n = w.seq_len - 37
+    print(f"[fullsize] {w.name} cut to n={n}, {mode}", flush=True)
+    x = synth.make_inputs(w, device="cuda", seq_len=n)
+    override = B.ROUTE_AUTO if mode == "auto" else B.ROUTE_FORCE_VS
+    cfg = B.make_cfg(route_override=override)
+    dims, bufs = _run(x, cfg)
+    hq, hkv = w.num_q_heads, w.num_kv_heads
+    N = B.num_blocks(n)
+    assert N == n // BLK + 1 == 4096
+    qpg = hq // hkv
+    cs = bufs.c_struct.cpu().numpy()
+    rt = bufs.route.cpu().numpy()
+    count = bufs.blocks["count"].cpu().numpy()
+    idx = bufs.blocks["idx"].cpu().numpy()
+    for h in (0, hq - 1):
+        g = h // qpg
+        q, k, v = to64(x.q[h]), to64(x.k[g]), to64(x.v[g])
+        A, _ = O.proxy_map(q[n - BLK:], k, dims.scale)
+        c_o = O.c_struct(A)
+        assert abs(cs[h] - c_o) <= REL_CSTRUCT * c_o, (h, cs[h], c_o)
+        check_route(c_o, cfg.tau, int(rt[h]), O.route(c_o, cfg.tau, override))
+        lists = gpu_lists(count, idx, h, N)
+        assert all(l[-1] == qb for qb, l in enumerate(lists))
+        qbs = _sample_qbs(N, 4000 + h)
+        if rt[h] == O.ROUTE_VS:
+            ct, dg = O.token_scores(A)
+            vs, sl = O.pooled_scores(ct, dg)
+            np.testing.assert_allclose(bufs.blocks["v_score"][h].cpu().numpy(), vs, rtol=1e-3, atol=1e-9)
+            np.testing.assert_allclose(bufs.blocks["s_score"][h].cpu().numpy(), sl, rtol=1e-3, atol=1e-9)
+            vm = bufs.blocks["v_mask"][h].cpu().numpy()
+            sm = bufs.blocks["s_mask"][h].cpu().numpy()
+            check_noise_floor_mask(vs, cfg.alpha, 8, 0, vm, float(bufs.blocks["floor_v"][h]))
+            check_noise_floor_mask(sl, cfg.alpha, 8, 0, sm, float(bufs.blocks["floor_s"][h]))
+            assert lists == O.vs_lists(vm.astype(bool), sm.astype(bool))
+        else:
+            check_pe_lists(O.pe_pool(q), O.pe_pool(k), dims.scale, cfg.gamma_pe, lists, qbs=qbs)
+        del A
+        ref = O.attention_rows(q, k, v, lists, dims.scale, qbs)
+        og = bufs.out[h].cpu().numpy()
+        lg = bufs.lse[h].cpu().numpy()
+        for qb in qbs:
+            rows = slice(qb * BLK, min((qb + 1) * BLK, n))
+            check_attention(og[rows], ref[qb][0], f"n {n} {mode} h {h} qb {qb}")
+            check_lse(lg[rows], ref[qb][1])
+
+
 def test_gamma_comparison_256k_counts():
     """Llama 256k layer: noise-floor vs gamma = 0.95 selection on every head's
     Vertical-Slash scores; sampled heads checked against the oracle."""
