@@ -50,3 +50,18 @@ def test_needle_recall_counts_listed_blocks_and_kept_columns():
                                  ncols=torch.tensor([1], dtype=torch.int32))
     assert bench.needle_recall(x, bufs, N, tokens=False) == pytest.approx(0.5)
     assert bench.needle_recall(x, bufs, N, tokens=True) == pytest.approx(1.0)
+
+
+@pytest.mark.parametrize("gpus", ["2", "8"])
+def test_bench_refuses_more_than_one_gpu(gpus):
+    """The layer is timed on one GPU; asking for more exits with status 2 and
+    says so, before touching torch or a GPU."""
+    import os
+    import subprocess
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, os.path.join(root, "bench.py"), "--gpus", gpus],
+                       capture_output=True, text=True, timeout=120, cwd=root)
+    assert r.returncode == 2
+    assert "one GPU" in r.stderr
+    assert r.stdout == ""
