@@ -567,3 +567,44 @@ def test_chain_is_deterministic():
         assert gpu_lists(c, i1, h, 256) == gpu_lists(c, i2, h, 256)
     assert torch.equal(b1.out, b2.out)
     assert torch.equal(b1.lse, b2.lse)
+
+
+@pytest.mark.parametrize("n", [2048, 2000])
+def test_full_coverage_is_the_dense_kernel(n):
+    """gamma_PE = 1 keeps every block (no shorter prefix reaches the whole
+    mass), so every pooled-estimation list is 0..qb and the sparse kernel's
+    output and log-sum-exp equal the dense kernel's bit for bit; the same
+    for the gamma comparison chain at gamma = 1 on Vertical-Slash heads."""
+    hq, hkv = 4, 2
+    x = synth.make_inputs(synth.custom(hq, hkv, n, seed=n + 3, needles=3), device="cuda")
+    dims = B.make_dims(hq, hkv, n)
+    N = B.num_blocks(n)
+    dense = torch.empty((hq, n, 128), dtype=torch.float32, device="cuda")
+    dlse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    B.crisp_dense_attn(dims, x.q, x.k, x.v, dense, dlse)
+    for override, gamma in ((B.ROUTE_FORCE_PE, None), (B.ROUTE_FORCE_VS, 1.0)):
+        cfg = B.make_cfg(gamma_pe=1.0, route_override=override)
+        print(f"[full coverage] n={n} override={override} gamma={gamma}", flush=True)
+        bufs = B.CrispBuffers(dims, out_dtype=torch.float32)
+        B.crisp_prefill(dims, cfg, x.q, x.k, x.v, bufs, gamma=gamma, dense_below=0)
+        torch.cuda.synchronize()
+        count = bufs.blocks["count"].cpu().numpy()
+        idx = bufs.blocks["idx"].cpu().numpy()
+        for h in range(hq):
+            assert gpu_lists(count, idx, h, N) == [list(range(qb + 1)) for qb in range(N)], (override, h)
+        assert torch.equal(bufs.out, dense)
+        assert torch.equal(bufs.lse, dlse)
+
+
+@pytest.mark.parametrize("tau,expect", [(0.0, 1), (1.0, 0)])
+def test_route_threshold_extremes(tau, expect):
+    """C_struct lies in [0, 1] and is below 1 whenever any key outside the
+    sink and recency columns is visible: tau = 0 routes every head to
+    Vertical-Slash, tau = 1 every head to pooled estimation."""
+    hq, hkv, n = 8, 2, 3000
+    x = synth.make_routing_family(seq_len=n, num_q_heads=hq, num_kv_heads=hkv, device="cuda")
+    cfg = B.make_cfg(tau=tau)
+    dims, bufs = run_chain(x, cfg)
+    cs = bufs.c_struct.cpu().numpy()
+    assert np.all((cs >= 0.0) & (cs < 1.0))
+    assert np.all(bufs.route.cpu().numpy() == expect)
