@@ -31,3 +31,46 @@ def test_routing_family_is_seeded_and_graded():
     rec24 = proxy(24)[:, -128:].sum() / 128
     assert rec24 > 5 * rec0, (rec0, rec24)
     assert np.isfinite(a.q.float().numpy()).all()
+
+
+def test_workload_inputs_are_seeded():
+    """Same workload and seed: the same bf16 bits; another seed: other bits."""
+    w = synth.custom(4, 2, 1024, seed=9, needles=3)
+    a, b = synth.make_inputs(w), synth.make_inputs(w)
+    for x, y in ((a.q, b.q), (a.k, b.k), (a.v, b.v)):
+        assert x.dtype == torch.bfloat16 and torch.equal(x, y)
+    assert a.q.shape == (4, 1024, 128) and a.k.shape == (2, 1024, 128) and a.v.shape == (2, 1024, 128)
+    c = synth.make_inputs(synth.custom(4, 2, 1024, seed=10, needles=3))
+    assert not torch.equal(a.q, c.q) and not torch.equal(a.k, c.k)
+
+
+def test_workload_structure_matches_its_analytic_values():
+    """Two sink-dominant heads (group 0) and two diffuse heads (group 1):
+    - diffuse queries are the N(0,1) draws scaled by 0.3, sink-head queries
+      carry +1.5 u on top (per-component variance 1 + 1.5^2/128), so the
+      ratio of their RMS is 0.3 / sqrt(1 + 2.25/128) = 0.297;
+    - the sink keys 0..3 of group 0 carry +8 u (RoPE keeps norms): mean
+      squared norm 128 + 64, against 128 for group 1's first keys;
+    - the rows are close to uniform (scores of RMS about 1 or 0.3), so every
+      head's C_struct is close to the uniform-row value
+      (1/128) sum_r (128 + r + 1) / (n - 127 + r), about 192.5 / (n - 63.5)."""
+    n = 4096
+    w = synth.custom(4, 2, n, seed=3, sink_frac=0.5, needles=4)
+    assert w.num_sink_heads == 2
+    x = synth.make_inputs(w)
+    q = x.q.double()
+    rms = [float(q[h].pow(2).mean().sqrt()) for h in range(4)]
+    ratio = (rms[2] + rms[3]) / (rms[0] + rms[1])
+    assert abs(ratio - 0.3 / math.sqrt(1 + 2.25 / 128)) < 0.01, rms
+    k = x.k.double()
+    sink_norm2 = float(k[0, :4].pow(2).sum(-1).mean())
+    plain_norm2 = float(k[1, :4].pow(2).sum(-1).mean())
+    assert 192 - 35 < sink_norm2 < 192 + 35, sink_norm2
+    assert 128 - 35 < plain_norm2 < 128 + 35, plain_norm2
+    uniform = sum((128 + r + 1) / (n - 127 + r) for r in range(128)) / 128
+    assert abs(uniform - 192.5 / (n - 63.5)) < 5e-3 * uniform  # the closed form is first order
+    scale = 1.0 / math.sqrt(128)
+    for h in range(4):
+        A, _ = O.proxy_map(q[h, n - 128:].numpy(), k[h // 2].numpy(), scale)
+        c = O.c_struct(A)
+        assert abs(c - uniform) < 0.15 * uniform, (h, c, uniform)
