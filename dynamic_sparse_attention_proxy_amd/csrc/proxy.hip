@@ -88,10 +88,13 @@ __device__ __forceinline__ int band_class(int D) {
 template <typename KeyOf>
 __device__ __forceinline__ void add_bands(const float (&e)[16], float tot, int cls, int x, KeyOf key_of,
                                           float& b0, float& b1, float& b2) {
+  // Every band takes a predicated add: a branch that picks which of
+  // b0 / b1 / b2 to update becomes a pointer select, and the three sums are
+  // then kept in scratch memory, whose waits also cover the K prefetch.
   if (cls < 3) {
-    if (cls == 0) b0 += tot;
-    else if (cls == 1) b1 += tot;
-    else b2 += tot;
+    b0 += cls == 0 ? tot : 0.f;
+    b1 += cls == 1 ? tot : 0.f;
+    b2 += cls == 2 ? tot : 0.f;
     return;
   }
   float hi = 0.f, lo = 0.f;
@@ -102,13 +105,10 @@ __device__ __forceinline__ void add_bands(const float (&e)[16], float tot, int c
     else
       lo += e[v];
   }
-  if (cls == 3) {
-    b0 += hi;
-    b1 += lo;
-  } else {
-    b1 += hi;
-    b2 += lo;
-  }
+  const bool c3 = cls == 3;
+  b0 += c3 ? hi : 0.f;
+  b1 += c3 ? lo : hi;
+  b2 += c3 ? 0.f : lo;
 }
 
 __device__ __forceinline__ void merge_ml(float& m, float& l, float mo, float lo) {
@@ -305,10 +305,9 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
             const float sum = (t8[0] + t8[2]) + (t8[1] + t8[3]);
             ls += sum;
             if (kMass) {
-              if (t < w)
-                bl += sum;
-              else
-                bu += sum;
+              // predicated (see add_bands): the sub-tile is wholly below or above
+              bl += t < w ? sum : 0.f;
+              bu += t < w ? 0.f : sum;
             }
           }
         }
@@ -413,10 +412,8 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
 #pragma unroll
             for (int v = 0; v < 4; ++v) t8[v] += t8[v + 4];
             const float sum = (t8[0] + t8[2]) + (t8[1] + t8[3]);
-            if (t < w)
-              lo += sum;
-            else
-              up += sum;
+            lo += t < w ? sum : 0.f;  // predicated (see add_bands)
+            up += t < w ? 0.f : sum;
           }
         }
         if (kCols) {
