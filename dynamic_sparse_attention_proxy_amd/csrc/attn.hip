@@ -136,6 +136,11 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
     if (b - chunk_base >= 64) {
       chunk_base = b;
       chunk = __builtin_amdgcn_raw_buffer_load_b32(lrs, lane * 4, b * 4, 0);
+      // Wait here, in the rare reload (a full s_waitcnt the compiler sees),
+      // so that no load of `chunk` is pending at the lookups: otherwise the
+      // compiler puts a vmcnt(0) before every readlane below, and that wait
+      // also drains the K/V DMA in flight, which it cannot see.
+      __builtin_amdgcn_s_waitcnt(0);
     }
     return min(max(__builtin_amdgcn_readlane(chunk, b - chunk_base), 0), qb);
   };
