@@ -130,6 +130,13 @@ __global__ __launch_bounds__(kColThreads, 1) void col_attn_kernel(ColArgs p) {
       qf[kk] = as_bf16x8(
           *(const u32x4*)(p.q + (size_t)h * nd + (size_t)min(qpos, p.n - 1) * kHeadDim + 16 * kk + 8 * lg));
   }
+  // Q lands here, once, in a wait the compiler sees.  Its first use sits
+  // under `active`, so without this the loads count as pending in the loop
+  // and the compiler waits for them (vmcnt(7) .. vmcnt(0)) before the QK
+  // MFMAs of every step; those waits also cover the column gathers in
+  // flight, which it cannot see (measured without effect on the 512k token
+  // chain: the gathers have landed by then).
+  __builtin_amdgcn_s_waitcnt(0);
 
   const __amdgpu_buffer_rsrc_t krs =
       __builtin_amdgcn_make_buffer_rsrc((void*)(p.k + (size_t)g * nd), 0, (int)(nd * 2), kBufferFlags);
