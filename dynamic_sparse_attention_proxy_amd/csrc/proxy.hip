@@ -218,6 +218,10 @@ __global__ __launch_bounds__(256) void proxy_pass_kernel(ProxyArgs p) {
   float up2 = 0.f, rc = 0.f;     // kRagged: band N-3-kb, and the recency part of key block N-2
   auto key_of = [&](int v) { return acc_key(v, lg); };
 
+  // Q and the row log-sum-exp land here, in a wait the compiler sees: left
+  // pending into the loop, the compiler would wait for them before the QK
+  // MFMAs of every step, and those waits also cover the K DMA in flight.
+  __builtin_amdgcn_s_waitcnt(0);
   dma_tile(0, 0);
   dma_tile(1, 1);
   wait_dma();
