@@ -65,3 +65,19 @@ def test_bench_refuses_more_than_one_gpu(gpus):
     assert r.returncode == 2
     assert "one GPU" in r.stderr
     assert r.stdout == ""
+
+
+def test_traffic_record_matches_the_attention_kernel():
+    """The HBM counters the bench line reports as `traffic` were taken on the
+    attention kernel as committed (hash of attn.hip and common.h); after a
+    kernel change they must be taken again, or the bench reports null."""
+    import json
+    import os
+
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    with open(os.path.join(root, "profiles", "sparse_attn_traffic.json")) as f:
+        rec = json.load(f)
+    assert rec["kernel_sha"] == bench.kernel_sha()
+    assert rec["workload"] == "llama3.1-8b-512k"
+    assert rec["hbm_bytes_per_launch"] == rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
+    assert rec["hbm_bytes_per_launch"] > rec["algorithmic_bytes_per_launch"] > 0
