@@ -810,3 +810,81 @@ def test_mixed_attention_brute_force_and_reductions():
     for qb in range(N):
         np.testing.assert_allclose(allc[qb][0], dense[qb][0], rtol=1e-12, atol=1e-12)
         np.testing.assert_allclose(allc[qb][1], dense[qb][1], rtol=1e-12, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# whole layer: the per-head loop and the GQA head -> KV group map
+# --------------------------------------------------------------------------
+
+
+def _gqa_layer(hq, hkv, n, d, beta):
+    """KV group 0 carries a sink (keys 0..3 = 8u, every other key 0) and
+    constant values 3; its query heads have every row = beta u.  KV group
+    1 has zero keys and values whose coordinate 0 is 10 + position (the
+    rest 10); its query heads are zero.  Further groups repeat group 1 with
+    values shifted by 100 g."""
+    u = np.zeros(d)
+    u[1] = 1.0
+    q = np.zeros((hq, n, d))
+    k = np.zeros((hkv, n, d))
+    v = np.zeros((hkv, n, d))
+    qpg = hq // hkv
+    k[0, :4] = 8.0 * u
+    v[0] = 3.0
+    for h in range(qpg):  # consecutive heads share a group (the configs' GQA reading)
+        q[h] = beta * u
+    for g in range(1, hkv):
+        v[g] = 10.0 + 100.0 * (g - 1)
+        v[g, :, 0] += np.arange(n)
+    return q, k, v
+
+
+@pytest.mark.parametrize("hq,hkv", [(8, 2), (14, 2), (12, 3)])
+def test_run_layer_maps_heads_to_groups_and_blocks(hq, hkv):
+    n, d, scale, beta = 4 * B, 16, 0.25, 4.0
+    q, k, v = _gqa_layer(hq, hkv, n, d, beta)
+    qpg = hq // hkv
+    # gamma_pe = 1 and kmin >= N keep every block on either route, so every
+    # output has a closed form whatever the route
+    cfg = O.OracleConfig(tau=0.5, gamma_pe=1.0, kmin_blocks=8)
+    qbs = [3, 1]
+    heads = list(range(hq))[::-1]
+    res = O.run_layer(q, k, v, cfg, scale=scale, heads=heads, attn_qbs=qbs)
+    assert sorted(res) == list(range(hq))
+    e8 = math.exp(scale * beta * 8.0)  # sink logit 8 for group-0 heads
+    # group 0: 4 sink keys of weight e8, every other visible key weight 1;
+    # C_struct = mean over rows of (4 e8 + 124 + (r + 1)) / (4 e8 + i_r - 3)
+    c_sink = sum((4 * e8 + 124 + r + 1) / (4 * e8 + (n - B + r) - 3) for r in range(B)) / B
+    # zero queries: uniform rows, C_struct = mean of (129 + r) / (n - 127 + r)
+    c_flat = sum((129 + r) / (n - 127 + r) for r in range(B)) / B
+    assert c_sink > 0.9 and c_flat < 0.5
+    for h in range(hq):
+        g = h // qpg
+        hr = res[h]
+        assert sorted(hr.attn) == sorted(qbs)
+        if g == 0:
+            assert hr.route == O.ROUTE_VS
+            assert hr.c_struct == pytest.approx(c_sink, rel=1e-12)
+        else:
+            assert hr.route == O.ROUTE_PE
+            assert hr.c_struct == pytest.approx(c_flat, rel=1e-12)
+        assert hr.lists == O.dense_lists(4)
+        for qb in qbs:
+            out, lse = hr.attn[qb]
+            rows = np.arange(qb * B, (qb + 1) * B)
+            if g == 0:
+                np.testing.assert_allclose(out, 3.0, rtol=1e-13)
+                # the row's logits: 8 on the sink keys, 0 elsewhere
+                want_lse = np.log(4 * e8 + (rows + 1 - 4))
+            else:
+                # zero queries: the running mean of the group's values
+                want = np.full((B, d), 10.0 + 100.0 * (g - 1))
+                want[:, 0] += rows / 2.0
+                np.testing.assert_allclose(out, want, rtol=1e-13)
+                want_lse = np.log(rows + 1.0)
+            np.testing.assert_allclose(lse, want_lse, rtol=1e-13)
+    # a subset of heads and no attention
+    sub = O.run_layer(q, k, v, cfg, scale=scale, heads=[qpg - 1, qpg], attn_qbs=[])
+    assert sorted(sub) == [qpg - 1, qpg]
+    assert sub[qpg - 1].route == O.ROUTE_VS and sub[qpg].route == O.ROUTE_PE
+    assert sub[qpg].attn == {}
