@@ -77,6 +77,10 @@ _SIGS = {
     "crisp_sparse_attn": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P,
                                          _P]),
     "crisp_dense_attn": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, ctypes.c_int32, _P, _P]),
+    "crisp_prefill": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), ctypes.c_int32, _P, _P,
+                                     _P, ctypes.POINTER(crisp_blocks), _P, _P, _P, _P, ctypes.c_int32, _P, _P,
+                                     ctypes.c_size_t, _P]),
+    "crisp_prefill_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(crisp_dims)]),
     "crisp_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "crisp_abi_version": (ctypes.c_int32, []),
 }
@@ -142,6 +146,10 @@ def crisp_proxy_scratch_bytes(dims: crisp_dims) -> int:
 
 def crisp_select_workspace_bytes(dims: crisp_dims) -> int:
     return int(lib().crisp_select_workspace_bytes(ctypes.byref(dims)))
+
+
+def crisp_prefill_workspace_bytes(dims: crisp_dims) -> int:
+    return int(lib().crisp_prefill_workspace_bytes(ctypes.byref(dims)))
 
 
 def crisp_list_capacity(dims: crisp_dims) -> int:
@@ -262,10 +270,16 @@ class CrispBuffers:
         self.attn_map = torch.empty((hq, dims.block, n), dtype=f32, device=dev) if with_map else None
         self.block_mass = torch.empty((4, hq, N), dtype=f32, device=dev)
         self.row_lse = torch.empty((hq, dims.block), dtype=f32, device=dev)
-        self.partials = torch.empty(crisp_proxy_scratch_bytes(dims), dtype=torch.uint8, device=dev)
+        # one buffer for the one-call layer; the step-by-step calls use its
+        # start as the proxy scratch and, from the scratch size rounded up to
+        # 256 bytes, the selection workspace (crisp.h guarantees the room)
+        self.prefill_workspace = torch.empty(crisp_prefill_workspace_bytes(dims), dtype=torch.uint8, device=dev)
+        ps, ws = crisp_proxy_scratch_bytes(dims), crisp_select_workspace_bytes(dims)
+        off = -(-ps // 256) * 256
+        self.partials = self.prefill_workspace[:ps]
+        self.workspace = self.prefill_workspace[off:off + ws]
         self.c_struct = torch.empty((hq,), dtype=f32, device=dev)
         self.route = torch.empty((hq,), dtype=i32, device=dev)
-        self.workspace = torch.empty(crisp_select_workspace_bytes(dims), dtype=torch.uint8, device=dev)
         self.blocks = {"count": torch.empty((hq, N), dtype=i32, device=dev),
                        "idx": torch.empty((crisp_list_capacity(dims),), dtype=i32, device=dev)}
         if diagnostics:
@@ -292,25 +306,32 @@ class CrispBuffers:
 # Context-length gate (ai.info summary: "Main Findings" puts the crossover
 # where sparse prefill starts to pay between 8K and 64K, and "Why This
 # Matters" suggests gating sparse prefill on a context-length threshold).
-# Below this many tokens the route-auto chain does not recover the cost of
-# proxy, routing and selection on MI355X (measured Llama-3.1-8B-shaped
-# layers: 0.90x of dense at 8k, 1.02x at 16k, 1.00-1.04x from 32k to 512k),
-# so a layer this short runs the dense kernel instead.
-DENSE_BELOW = 16384
+# The gate lives in the library's crisp_prefill; None here asks for its
+# default, CRISP_DENSE_BELOW_DEFAULT (16384 tokens).
+DENSE_BELOW = 16384  # the library default, mirrored for reporting and tests
 
 
 def crisp_prefill(dims: crisp_dims, cfg: crisp_cfg, q, k, v, bufs: CrispBuffers, gamma: Optional[float] = None,
-                  stream=None, use_map: bool = False, dense_below: int = DENSE_BELOW):
-    """One layer's path: proxy -> route -> select (or the gamma comparison
-    chain when `gamma` is given) -> block-sparse attention, all on `stream`.
+                  stream=None, use_map: bool = False, dense_below: Optional[int] = None):
+    """One layer's path on `stream`.
 
-    Routing and selection read the block masses, unless `use_map` asks for
-    the materialised map (bufs must then hold one); with a map in bufs the
-    proxy fills both.  A layer shorter than `dense_below` tokens runs the
-    dense kernel only (pass 0 to always run the chain); the comparison chain
-    (`gamma`) is never gated."""
-    if gamma is None and dims.seq_len < dense_below:
-        crisp_dense_attn(dims, q, k, v, bufs.out, bufs.lse, stream)
+    With no map in `bufs` and no `gamma`, this is the library's one-call
+    layer (crisp_prefill in the C ABI): below the context-length gate
+    (`dense_below` tokens, None for the library default) the dense kernel
+    alone, else proxy -> route -> select -> block-sparse attention on the
+    block masses.  With a map in bufs (CrispBuffers(with_map=True)) or a
+    `gamma` (the gamma-cumulative comparison chain), the same steps are
+    called one by one and never gated; routing and selection then read the
+    block masses unless `use_map` asks for the materialised map."""
+    if gamma is None and bufs.attn_map is None and not use_map:
+        b = _blocks(bufs.blocks)
+        out_fp32 = 1 if bufs.out.dtype == torch.float32 else 0
+        ws = bufs.prefill_workspace
+        _check("crisp_prefill", lib().crisp_prefill(ctypes.byref(dims), ctypes.byref(cfg),
+                                                    -1 if dense_below is None else int(dense_below), _ptr(q),
+                                                    _ptr(k), _ptr(v), ctypes.byref(b), _ptr(bufs.block_mass),
+                                                    _ptr(bufs.c_struct), _ptr(bufs.route), _ptr(bufs.out), out_fp32,
+                                                    _ptr(bufs.lse), _ptr(ws), ws.numel(), _stream(stream)))
         return bufs.out
     if use_map and bufs.attn_map is None:
         raise ValueError("use_map needs CrispBuffers(with_map=True)")

@@ -30,7 +30,6 @@ FLAGS = [
     "-fvisibility=hidden",
     "-Wall",
     "-Wno-unused-command-line-argument",
-    "-fno-honor-nans",  # inputs are finite; lets fmaxf map to v_max3 without canonicalisation
     "-Wno-inline-asm",  # the LDS-DMA asm names m0, which it sets itself
     # packed fp32 ops stay off: ordinary float code only
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
@@ -38,9 +37,20 @@ FLAGS = [
 ]
 
 
+# Kernel sources may assume finite floats (fmaxf then maps to v_max3 with no
+# canonicalisation); the host-side argument validation in api.hip must see
+# NaNs, so it is built without the flag.
+KERNEL_ONLY_FLAGS = ["-fno-honor-nans"]
+HOST_VALIDATION_SOURCES = ("api.hip",)
+
+
+def flags_for(src):
+    return FLAGS + ([] if src in HOST_VALIDATION_SOURCES else KERNEL_ONLY_FLAGS)
+
+
 def _compile(src):
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC] + flags_for(src) + ["-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     out = "\n".join(line for line in (r.stdout + r.stderr).splitlines()
                     if "packed-fp32-ops" not in line)

@@ -17,6 +17,20 @@ constexpr int kMaxDevices = 64;
 
 bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
 
+// Finite, decided on the bit pattern (exponent not all ones), so that a NaN
+// or an infinity is rejected even where a compiler flag lets the compiler
+// assume that floats are never NaN.
+bool finite_bits(float x) {
+  uint32_t b;
+  memcpy(&b, &x, sizeof b);
+  return (b & 0x7f800000u) != 0x7f800000u;
+}
+// lo <= x <= hi (or lo < x when lo_open), for finite x only.
+bool in_range(float x, float lo, float hi, bool lo_open = false) {
+  if (!finite_bits(x)) return false;
+  return (lo_open ? x > lo : x >= lo) && x <= hi;
+}
+
 crisp_status check_dims(const crisp_dims* d) {
   if (d == nullptr) return CRISP_ERR_NULL;
   if (d->head_dim != 128 || d->block != 128) return CRISP_ERR_SHAPE;
@@ -26,15 +40,15 @@ crisp_status check_dims(const crisp_dims* d) {
   if (d->seq_len < 2 * d->block || d->seq_len > kMaxSeqLen) return CRISP_ERR_SHAPE;
   // grid sizes (Hq * N workgroups) must fit the launch limits comfortably
   if ((long long)d->num_q_heads * crisp::nblocks(d->seq_len) > (1LL << 30)) return CRISP_ERR_SHAPE;
-  if (!(d->scale > 0.f) || !isfinite(d->scale)) return CRISP_ERR_PARAM;
+  if (!in_range(d->scale, 0.f, 3.0e38f, true)) return CRISP_ERR_PARAM;
   return CRISP_OK;
 }
 
 crisp_status check_cfg(const crisp_dims* d, const crisp_cfg* c) {
   if (c == nullptr) return CRISP_ERR_NULL;
-  if (!(c->tau >= 0.f && c->tau <= 1.f)) return CRISP_ERR_PARAM;
-  if (!(c->alpha > 0.f) || !isfinite(c->alpha)) return CRISP_ERR_PARAM;
-  if (!(c->gamma_pe > 0.f && c->gamma_pe <= 1.f)) return CRISP_ERR_PARAM;
+  if (!in_range(c->tau, 0.f, 1.f)) return CRISP_ERR_PARAM;
+  if (!in_range(c->alpha, 0.f, 3.0e38f, true)) return CRISP_ERR_PARAM;
+  if (!in_range(c->gamma_pe, 0.f, 1.f, true)) return CRISP_ERR_PARAM;
   if (c->kmin_blocks < 1) return CRISP_ERR_PARAM;
   if (c->sink_width < 1 || c->sink_width > d->seq_len / 2) return CRISP_ERR_PARAM;
   if (c->recency_width < 1 || c->recency_width > d->seq_len / 2) return CRISP_ERR_PARAM;
@@ -83,18 +97,8 @@ crisp_status check_map_or_mass(const void* attn_map, const void* block_mass) {
   return check_opt(block_mass);
 }
 
-crisp_status select_common(const crisp_dims* dims, const crisp_cfg* cfg, bool use_gamma, float gamma, const void* q,
-                           const void* k, const float* attn_map, const float* block_mass, const int32_t* route,
-                           const crisp_blocks* out, void* workspace, size_t workspace_bytes,
-                           const crisp::TokenCols* tok, void* stream) {
-  CRISP_TRY(check_dims(dims));
-  CRISP_TRY(check_cfg(dims, cfg));
-  if (use_gamma && !(gamma > 0.f && gamma <= 1.f)) return CRISP_ERR_PARAM;
+crisp_status check_blocks(const crisp_blocks* out) {
   if (out == nullptr) return CRISP_ERR_NULL;
-  CRISP_TRY(check_ptr(q));
-  CRISP_TRY(check_ptr(k));
-  CRISP_TRY(check_map_or_mass(attn_map, block_mass));
-  CRISP_TRY(check_ptr(route));
   CRISP_TRY(check_ptr(out->count));
   CRISP_TRY(check_ptr(out->idx));
   CRISP_TRY(check_opt(out->v_score));
@@ -105,10 +109,15 @@ crisp_status select_common(const crisp_dims* dims, const crisp_cfg* cfg, bool us
   CRISP_TRY(check_opt(out->s_mask));
   CRISP_TRY(check_opt(out->n_v));
   CRISP_TRY(check_opt(out->n_s));
-  CRISP_TRY(check_ptr(workspace));
+  return CRISP_OK;
+}
+
+// Selection launch after validation: carves the workspace and points the
+// optional diagnostics the caller gave at its own buffers.
+crisp_status select_launch(const crisp_dims* dims, const crisp_cfg* cfg, bool use_gamma, float gamma, const void* q,
+                           const void* k, const float* attn_map, const float* block_mass, const int32_t* route,
+                           const crisp_blocks* out, void* workspace, const crisp::TokenCols* tok, void* stream) {
   const int hq = dims->num_q_heads, hkv = dims->num_kv_heads, n = dims->seq_len;
-  if (workspace_bytes < crisp::select_workspace_bytes(hq, hkv, n)) return CRISP_ERR_WORKSPACE;
-  CRISP_TRY(check_device());
   crisp::SelectBuffers b = crisp::carve_select_workspace(workspace, hq, hkv, n);
   if (out->v_score) b.vscore = out->v_score;
   if (out->s_score) b.sscore = out->s_score;
@@ -122,6 +131,60 @@ crisp_status select_common(const crisp_dims* dims, const crisp_cfg* cfg, bool us
                                        out->idx,
                                        hq, hkv, n, dims->scale, cfg->alpha, cfg->gamma_pe, cfg->kmin_blocks,
                                        cfg->nf_stat, use_gamma, gamma, tok, (hipStream_t)stream));
+}
+
+crisp_status select_common(const crisp_dims* dims, const crisp_cfg* cfg, bool use_gamma, float gamma, const void* q,
+                           const void* k, const float* attn_map, const float* block_mass, const int32_t* route,
+                           const crisp_blocks* out, void* workspace, size_t workspace_bytes,
+                           const crisp::TokenCols* tok, void* stream) {
+  CRISP_TRY(check_dims(dims));
+  CRISP_TRY(check_cfg(dims, cfg));
+  if (use_gamma && !in_range(gamma, 0.f, 1.f, true)) return CRISP_ERR_PARAM;
+  CRISP_TRY(check_blocks(out));
+  CRISP_TRY(check_ptr(q));
+  CRISP_TRY(check_ptr(k));
+  CRISP_TRY(check_map_or_mass(attn_map, block_mass));
+  CRISP_TRY(check_ptr(route));
+  CRISP_TRY(check_ptr(workspace));
+  if (workspace_bytes < crisp::select_workspace_bytes(dims->num_q_heads, dims->num_kv_heads, dims->seq_len))
+    return CRISP_ERR_WORKSPACE;
+  CRISP_TRY(check_device());
+  return select_launch(dims, cfg, use_gamma, gamma, q, k, attn_map, block_mass, route, out, workspace, tok, stream);
+}
+
+// The one-call layer's workspace: the proxy scratch first (so that a buffer
+// of this size also serves the step-by-step calls, the selection workspace
+// starting at the proxy scratch rounded up to 256 bytes), then the selection
+// workspace, then the block masses, C_struct and routes.
+constexpr size_t kCarve = 256;
+size_t round_carve(size_t x) { return (x + kCarve - 1) / kCarve * kCarve; }
+
+struct PrefillCarve {
+  void* partials;
+  void* select_ws;
+  float* mass;
+  float* c_struct;
+  int32_t* route;
+  size_t bytes;
+};
+
+PrefillCarve carve_prefill(void* ws, int hq, int hkv, int n) {
+  PrefillCarve c;
+  const size_t N = (size_t)crisp::nblocks(n);
+  const uintptr_t p = (uintptr_t)ws;  // integer arithmetic: ws may be NULL when only the size is wanted
+  size_t off = 0;
+  c.partials = (void*)(p + off);
+  off += round_carve(crisp::proxy_scratch_bytes(hq, n));
+  c.select_ws = (void*)(p + off);
+  off += round_carve(crisp::select_workspace_bytes(hq, hkv, n));
+  c.mass = (float*)(p + off);
+  off += round_carve(4 * (size_t)hq * N * sizeof(float));
+  c.c_struct = (float*)(p + off);
+  off += round_carve((size_t)hq * sizeof(float));
+  c.route = (int32_t*)(p + off);
+  off += round_carve((size_t)hq * sizeof(int32_t));
+  c.bytes = off;
+  return c;
 }
 
 crisp_status attn_common(const crisp_dims* dims, const void* q, const void* k, const void* v, const int32_t* count,
@@ -208,7 +271,7 @@ crisp_status crisp_route_jsd(const crisp_dims* dims, float tau_jsd, const void* 
                              const float* block_mass, float* js_dist, int32_t* route, float* estimate,
                              void* workspace, size_t workspace_bytes, void* stream) {
   CRISP_TRY(check_dims(dims));
-  if (!(tau_jsd >= 0.f) || !isfinite(tau_jsd)) return CRISP_ERR_PARAM;
+  if (!in_range(tau_jsd, 0.f, 3.0e38f)) return CRISP_ERR_PARAM;
   CRISP_TRY(check_ptr(q));
   CRISP_TRY(check_ptr(k));
   CRISP_TRY(check_ptr(block_mass));
@@ -296,6 +359,51 @@ crisp_status crisp_dense_attn(const crisp_dims* dims, const void* q, const void*
   return attn_common(dims, q, k, v, nullptr, nullptr, out, out_is_fp32, lse, true, stream);
 }
 
+size_t crisp_prefill_workspace_bytes(const crisp_dims* dims) {
+  if (check_dims(dims) != CRISP_OK) return 0;
+  return carve_prefill(nullptr, dims->num_q_heads, dims->num_kv_heads, dims->seq_len).bytes;
+}
+
+crisp_status crisp_prefill(const crisp_dims* dims, const crisp_cfg* cfg, int32_t dense_below, const void* q,
+                           const void* k, const void* v, const crisp_blocks* blocks, float* block_mass,
+                           float* c_struct, int32_t* route, void* out, int32_t out_is_fp32, float* lse,
+                           void* workspace, size_t workspace_bytes, void* stream) {
+  CRISP_TRY(check_dims(dims));
+  CRISP_TRY(check_cfg(dims, cfg));
+  // routing reads the block masses, which resolve whole key blocks only
+  if (cfg->sink_width != dims->block || cfg->recency_width != dims->block) return CRISP_ERR_PARAM;
+  CRISP_TRY(check_ptr(q));
+  CRISP_TRY(check_ptr(k));
+  CRISP_TRY(check_ptr(v));
+  CRISP_TRY(check_blocks(blocks));
+  CRISP_TRY(check_opt(block_mass));
+  CRISP_TRY(check_opt(c_struct));
+  CRISP_TRY(check_opt(route));
+  CRISP_TRY(check_ptr(out));
+  CRISP_TRY(check_opt(lse));
+  if (out_is_fp32 != 0 && out_is_fp32 != 1) return CRISP_ERR_PARAM;
+  CRISP_TRY(check_ptr(workspace));
+  const int hq = dims->num_q_heads, hkv = dims->num_kv_heads, n = dims->seq_len;
+  const PrefillCarve w = carve_prefill(workspace, hq, hkv, n);
+  if (workspace_bytes < w.bytes) return CRISP_ERR_WORKSPACE;
+  CRISP_TRY(check_device());
+  const int gate = dense_below < 0 ? CRISP_DENSE_BELOW_DEFAULT : dense_below;
+  const hipStream_t st = (hipStream_t)stream;
+  if (n < gate)
+    return launched(crisp::launch_attention((const __bf16*)q, (const __bf16*)k, (const __bf16*)v, nullptr, nullptr,
+                                            out, out_is_fp32, lse, hq, hkv, n, dims->scale, true, st));
+  float* mass = block_mass ? block_mass : w.mass;
+  float* cs = c_struct ? c_struct : w.c_struct;
+  int32_t* rt = route ? route : w.route;
+  CRISP_TRY(launched(crisp::launch_proxy((const __bf16*)q, (const __bf16*)k, nullptr, mass, nullptr, nullptr,
+                                         w.partials, hq, hkv, n, dims->scale, st)));
+  CRISP_TRY(launched(crisp::launch_route(nullptr, mass, cs, rt, hq, n, cfg->sink_width, cfg->recency_width, cfg->tau,
+                                         cfg->route_override, st)));
+  CRISP_TRY(select_launch(dims, cfg, false, 0.f, q, k, nullptr, mass, rt, blocks, w.select_ws, nullptr, stream));
+  return launched(crisp::launch_attention((const __bf16*)q, (const __bf16*)k, (const __bf16*)v, blocks->count,
+                                          blocks->idx, out, out_is_fp32, lse, hq, hkv, n, dims->scale, false, st));
+}
+
 const char* crisp_status_string(crisp_status status) {
   switch (status) {
     case CRISP_OK: return "ok";
@@ -310,6 +418,6 @@ const char* crisp_status_string(crisp_status status) {
   return "unknown status";
 }
 
-int32_t crisp_abi_version(void) { return (3 << 16) | 0; }
+int32_t crisp_abi_version(void) { return (3 << 16) | 1; }
 
 }  // extern "C"

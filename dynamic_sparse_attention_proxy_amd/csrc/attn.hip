@@ -125,24 +125,29 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
 
   // List entries: 64 at a time in one VGPR (lane i holds entry c0 + i),
   // picked out with readlane; a chunk is reloaded only when a block past it
-  // is needed.  Entries past `cnt` read as 0, and every entry is clamped to
-  // [0, qb], so reads stay inside the head's rows.
+  // is needed.  The entry's whole byte offset goes in the lane offset, which
+  // the buffer's range check covers, so entries past `cnt` read as 0.  The
+  // last entry is taken as the diagonal block qb and every other entry is
+  // clamped to [0, qb-1]: reads stay inside the head's rows, and only the
+  // two masked steps of the diagonal block ever see a key past a query,
+  // whatever the list holds.
   const __amdgpu_buffer_rsrc_t lrs =
       __builtin_amdgcn_make_buffer_rsrc((void*)list, 0, kDense ? 0 : cnt * 4, kBufferFlags);
   int chunk_base = 0;
   int chunk = kDense ? 0 : __builtin_amdgcn_raw_buffer_load_b32(lrs, lane * 4, 0, 0);
   auto block_at = [&](int b) -> int {
     if (kDense) return b;
+    if (b >= cnt - 1) return qb;
     if (b - chunk_base >= 64) {
       chunk_base = b;
-      chunk = __builtin_amdgcn_raw_buffer_load_b32(lrs, lane * 4, b * 4, 0);
+      chunk = __builtin_amdgcn_raw_buffer_load_b32(lrs, (b + lane) * 4, 0, 0);
       // Wait here, in the rare reload (a full s_waitcnt the compiler sees),
       // so that no load of `chunk` is pending at the lookups: otherwise the
       // compiler puts a vmcnt(0) before every readlane below, and that wait
       // also drains the K/V DMA in flight, which it cannot see.
       __builtin_amdgcn_s_waitcnt(0);
     }
-    return min(max(__builtin_amdgcn_readlane(chunk, b - chunk_base), 0), qb);
+    return min(max(__builtin_amdgcn_readlane(chunk, b - chunk_base), 0), qb - 1);
   };
   auto key0_of = [&](int kb, int step) -> int { return kb * kBlock + (step & 1) * kStep; };
 

@@ -95,10 +95,12 @@ __global__ __launch_bounds__(kColThreads, 1) void col_attn_kernel(ColArgs p) {
   __syncthreads();
   for (int b = 0; b < (has_b ? 2 : 1); ++b) {
     const int qq = b ? qb2 : qa;
-    const int tc = min(max(p.count[(size_t)h * N + qq], 0), qq + 1);
+    // the tile kernel's reading of a list: the last entry is the diagonal
+    // block, every other entry clamped to [0, qq-1]
+    const int tc = min(max(p.count[(size_t)h * N + qq], 1), qq + 1);
     const int32_t* list = p.idx + (size_t)h * ((size_t)N * (N + 1) / 2) + (size_t)qq * (qq + 1) / 2;
     for (int t = tid; t < tc; t += kColThreads) {
-      const int kb = min(max(list[t], 0), qq);
+      const int kb = t == tc - 1 ? qq : min(max(list[t], 0), qq - 1);
       atomicOr(&tbits[b][kb >> 5], 1u << (kb & 31));
     }
   }

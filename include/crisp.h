@@ -203,7 +203,12 @@ CRISP_API size_t crisp_list_capacity(const crisp_dims* dims);
  * i in block qb the keys are every j <= i lying in a key block of qb's list:
  *   out[h][i] = sum_j softmax_j(scale * q[h][i] . k[g][j]) v[g][j]
  * count/idx: the lists produced by crisp_select (entries must satisfy
- * 0 <= kb <= qb, strictly ascending, last entry qb; count >= 1).
+ * 0 <= kb <= qb, strictly ascending, last entry qb; count >= 1).  A list
+ * that breaks this is read defensively: count is clamped to [1, qb+1], the
+ * last entry is taken as qb whatever it holds, and every other entry is
+ * clamped to [0, qb-1].  So no key after a query is ever weighted and every
+ * read stays inside the head's rows; the result is only meaningful for a
+ * well-formed list (a repeated entry counts its keys twice).
  * out: [Hq][n][d], bf16 when out_is_fp32 = 0, fp32 otherwise.
  * lse (optional, [Hq][n] fp32): natural log of each row's sum of exp. */
 CRISP_API crisp_status crisp_sparse_attn(const crisp_dims* dims, const void* q, const void* k, const void* v,
@@ -286,6 +291,44 @@ CRISP_API crisp_status crisp_route_jsd(const crisp_dims* dims, float tau_jsd, co
                              void* workspace, size_t workspace_bytes, void* stream);
 
 CRISP_API size_t crisp_route_jsd_workspace_bytes(const crisp_dims* dims);
+
+/* One layer in one call, with the context-length gate (ai.info summary,
+ * "Main Findings": the point where sparse prefill starts to pay lies between
+ * 8K and 64K tokens; "Why This Matters": gate sparse prefill on a
+ * context-length threshold).
+ *   n <  gate: crisp_dense_attn alone (blocks, block_mass, c_struct and route
+ *              are then not written);
+ *   n >= gate: crisp_proxy (block masses only) -> crisp_route (from the block
+ *              masses) -> crisp_select -> crisp_sparse_attn, in that order on
+ *              `stream`.
+ * gate = dense_below, or CRISP_DENSE_BELOW_DEFAULT when dense_below < 0;
+ * dense_below = 0 always runs the sparse chain.  The default is the length
+ * from which the route-auto chain recovers its proxy, routing and selection
+ * cost on MI355X (Llama-3.1-8B-shaped layers: 0.90x of the dense kernel at
+ * 8K tokens, 1.00x or better from 16K on).
+ * cfg: as crisp_route / crisp_select; sink_width and recency_width must be
+ * 128 (routing reads the block masses; CRISP_ERR_PARAM otherwise).
+ * blocks: as crisp_select (count and idx required, diagnostics optional).
+ * block_mass ([4][Hq][N] fp32), c_struct ([Hq] fp32), route ([Hq] int32):
+ * optional copies of the intermediate results (NULL: kept in the workspace).
+ * out, out_is_fp32, lse: as crisp_sparse_attn.
+ * workspace: crisp_prefill_workspace_bytes(dims) bytes of device memory.
+ * That size is at least crisp_proxy_scratch_bytes rounded up to a multiple
+ * of 256 plus crisp_select_workspace_bytes, so one buffer can also serve the
+ * step-by-step calls (proxy scratch at its start, selection workspace at
+ * that rounded offset).
+ * Every argument is validated before anything is launched, whichever branch
+ * the gate takes.  A launch failure part-way returns CRISP_ERR_LAUNCH with
+ * the earlier steps already enqueued. */
+#define CRISP_DENSE_BELOW_DEFAULT 16384
+
+CRISP_API crisp_status crisp_prefill(const crisp_dims* dims, const crisp_cfg* cfg, int32_t dense_below,
+                                     const void* q, const void* k, const void* v, const crisp_blocks* blocks,
+                                     float* block_mass, float* c_struct, int32_t* route, void* out,
+                                     int32_t out_is_fp32, float* lse, void* workspace, size_t workspace_bytes,
+                                     void* stream);
+
+CRISP_API size_t crisp_prefill_workspace_bytes(const crisp_dims* dims);
 
 /* Static description of a status code. */
 CRISP_API const char* crisp_status_string(crisp_status status);

@@ -333,21 +333,24 @@ def pe_row_select(qbar: np.ndarray, kbar: np.ndarray, qb: int, scale: float, gam
 # ---------------------------------------------------------------------------
 
 
-def vs_lists(vmask: np.ndarray, smask: np.ndarray) -> List[List[int]]:
+def vs_list_row(vmask: np.ndarray, smask: np.ndarray, qb: int) -> List[int]:
+    """Key-block list of query block qb: the kept vertical blocks up to qb
+    and the two key blocks each kept slash band covers, ascending."""
     N = vmask.shape[0]
-    lists = []
-    for qb in range(N):
-        sel = set()
-        for kb in range(qb + 1):
-            if vmask[kb]:
-                sel.add(kb)
-        for s in range(N):
-            if smask[s]:
-                for kb in (qb - s, qb - s - 1):
-                    if 0 <= kb <= qb:
-                        sel.add(kb)
-        lists.append(sorted(sel))
-    return lists
+    sel = set()
+    for kb in range(qb + 1):
+        if vmask[kb]:
+            sel.add(kb)
+    for s in range(N):
+        if smask[s]:
+            for kb in (qb - s, qb - s - 1):
+                if 0 <= kb <= qb:
+                    sel.add(kb)
+    return sorted(sel)
+
+
+def vs_lists(vmask: np.ndarray, smask: np.ndarray) -> List[List[int]]:
+    return [vs_list_row(vmask, smask, qb) for qb in range(vmask.shape[0])]
 
 
 def dense_lists(N: int) -> List[List[int]]:

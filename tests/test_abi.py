@@ -26,7 +26,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 16
+    assert len(names) == 18
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -38,6 +38,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_abi_version_and_status_strings():
     assert B.crisp_abi_version() >> 16 == 3
+    assert B.crisp_abi_version() & 0xffff >= 1  # crisp_prefill
     lib = B.lib()
     for s in range(8):
         assert lib.crisp_status_string(s)
@@ -94,9 +95,13 @@ def test_pointer_and_param_errors():
     assert lib.crisp_proxy(None, P16, P16, P16, None, None, P16, 1 << 30, None) == 1
 
 
+NAN, INF = float("nan"), float("inf")
+
+
 @pytest.mark.parametrize("field,value", [
     ("tau", 1.5), ("tau", -0.1), ("alpha", 0.0), ("gamma_pe", 0.0), ("gamma_pe", 1.01), ("kmin_blocks", 0),
     ("sink_width", 0), ("recency_width", 600), ("nf_stat", 2), ("route_override", 3),
+    ("tau", NAN), ("alpha", NAN), ("alpha", INF), ("gamma_pe", NAN), ("tau", -INF),
 ])
 def test_cfg_errors(field, value):
     dims = B.make_dims(4, 2, 1024)
@@ -109,6 +114,25 @@ def test_cfg_errors(field, value):
     blocks.idx = P16
     assert lib.crisp_select(ctypes.byref(dims), ctypes.byref(cfg), P16, P16, P16, None, P16, ctypes.byref(blocks), P16,
                             1 << 40, None) == 3
+
+
+@pytest.mark.parametrize("value", [NAN, INF, -INF, 0.0, -0.5])
+def test_non_finite_scale_and_thresholds_are_param_errors(value):
+    """NaN and infinite method parameters are rejected before any launch
+    (CRISP_ERR_PARAM), never passed on to the kernels."""
+    lib = B.lib()
+    dims = B.crisp_dims(4, 2, 1024, 128, 128, value)
+    assert _dense(dims) == 3
+    good = B.make_dims(4, 2, 1024)
+    cfg = B.make_cfg()
+    blocks = B.crisp_blocks()
+    blocks.count = P16
+    blocks.idx = P16
+    assert lib.crisp_select_gamma(ctypes.byref(good), ctypes.byref(cfg), value, P16, P16, P16, None, P16,
+                                  ctypes.byref(blocks), P16, 1 << 40, None) == 3
+    if value != 0.0:  # a JSD threshold of 0 is allowed
+        assert lib.crisp_route_jsd(ctypes.byref(good), ctypes.c_float(value), P16, P16, P16, P16, P16, None, P16,
+                                   1 << 40, None) == 3
 
 
 def test_select_errors():
@@ -191,31 +215,92 @@ def test_row_map_is_a_bijection(tmp_path_factory, hq, hkv, nblk, sanitized):
     assert r.returncode == 0, r.stdout + r.stderr
 
 
-def test_prefill_context_length_gate(monkeypatch):
-    """crisp_prefill runs the dense kernel alone below DENSE_BELOW tokens and
-    the four-call chain from there on; dense_below=0 always runs the chain
-    and the gamma comparison chain is never gated."""
+def test_prefill_marshalling_and_composed_chains(monkeypatch):
+    """The binding's crisp_prefill hands the default layer to the library's
+    one-call crisp_prefill (dense_below None -> -1, the library default);
+    with a gamma, or a map in the buffers, it calls the steps one by one and
+    never gates."""
     import types
 
+    seen = []
+
+    class FakeLib:
+        def crisp_prefill(self, dims, cfg, dense_below, *rest):
+            seen.append(dense_below)
+            return 0
+
+    monkeypatch.setattr(B, "_lib", FakeLib())
     calls = []
     for name in ("crisp_proxy", "crisp_route", "crisp_select", "crisp_select_gamma", "crisp_sparse_attn",
                  "crisp_dense_attn"):
         monkeypatch.setattr(B, name, lambda *a, _n=name, **kw: calls.append(_n))
-    bufs = types.SimpleNamespace(out=None, lse=None, attn_map=None, block_mass=None, row_lse=None, partials=None,
-                                 c_struct=None, route=None, blocks={"count": None, "idx": None}, workspace=None)
+    import torch
+
+    bufs = types.SimpleNamespace(out=torch.empty(1), lse=None, attn_map=None, block_mass=None, row_lse=None,
+                                 partials=None, c_struct=None, route=None, blocks={"count": None, "idx": None},
+                                 workspace=None, prefill_workspace=torch.empty(16, dtype=torch.uint8))
+    monkeypatch.setattr(B, "_stream", lambda s: None)
     cfg = B.make_cfg()
-    chain = ["crisp_proxy", "crisp_route", "crisp_select", "crisp_sparse_attn"]
-    for n, expect in ((B.DENSE_BELOW // 2, ["crisp_dense_attn"]), (B.DENSE_BELOW - 128, ["crisp_dense_attn"]),
-                      (B.DENSE_BELOW, chain), (4 * B.DENSE_BELOW, chain)):
-        calls.clear()
+    for n in (1024, B.DENSE_BELOW, 4 * B.DENSE_BELOW):
         B.crisp_prefill(B.make_dims(32, 8, n), cfg, None, None, None, bufs)
-        assert calls == expect, (n, calls)
-    calls.clear()
     B.crisp_prefill(B.make_dims(32, 8, 1024), cfg, None, None, None, bufs, dense_below=0)
-    assert calls == chain
-    calls.clear()
+    B.crisp_prefill(B.make_dims(32, 8, 1024), cfg, None, None, None, bufs, dense_below=4096)
+    assert seen == [-1, -1, -1, 0, 4096] and calls == []
     B.crisp_prefill(B.make_dims(32, 8, 1024), cfg, None, None, None, bufs, gamma=0.95)
     assert calls == ["crisp_proxy", "crisp_route", "crisp_select_gamma", "crisp_sparse_attn"]
+    calls.clear()
+    bufs.attn_map = torch.empty(1)
+    B.crisp_prefill(B.make_dims(32, 8, 1024), cfg, None, None, None, bufs, use_map=True)
+    assert calls == ["crisp_proxy", "crisp_route", "crisp_select", "crisp_sparse_attn"]
+    assert len(seen) == 5
+
+
+def test_prefill_gate_default_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+CRISP_DENSE_BELOW_DEFAULT\s+(\d+)", text)
+    assert m and int(m.group(1)) == B.DENSE_BELOW
+
+
+def test_prefill_validation():
+    """The one-call layer validates every argument before any launch,
+    whichever way the gate goes; a valid call reaches the device check (6)."""
+    lib = B.lib()
+    dims = B.make_dims(4, 2, 1024)
+    ws = B.crisp_prefill_workspace_bytes(dims)
+    ps, ss = B.crisp_proxy_scratch_bytes(dims), B.crisp_select_workspace_bytes(dims)
+    assert ws >= -(-ps // 256) * 256 + ss
+    assert B.crisp_prefill_workspace_bytes(B.make_dims(4, 2, 255)) == 0
+    blocks = B.crisp_blocks()
+    blocks.count = P16
+    blocks.idx = P16
+
+    def call(dims=dims, cfg=None, gate=-1, q=P16, k=P16, v=P16, blk=blocks, mass=None, cs=None, rt=None, out=P16,
+             fp32=0, lse=None, w=P16, wb=ws):
+        cfg = cfg or B.make_cfg()
+        return lib.crisp_prefill(ctypes.byref(dims), ctypes.byref(cfg), gate, q, k, v,
+                                 None if blk is None else ctypes.byref(blk), mass, cs, rt, out, fp32, lse, w, wb,
+                                 None)
+
+    assert call() == 6
+    assert call(gate=0) == 6
+    assert call(gate=1 << 30) == 6
+    assert call(mass=P16, cs=P16, rt=P16, lse=P16, fp32=1) == 6
+    assert call(v=None) == 1
+    assert call(blk=None) == 1
+    assert call(out=None) == 1
+    assert call(w=None) == 1
+    assert call(mass=P8) == 4
+    assert call(rt=P8) == 4
+    assert call(lse=P8) == 4
+    assert call(wb=ws - 1) == 5
+    assert call(fp32=2) == 3
+    assert call(cfg=B.make_cfg(sink_width=64)) == 3
+    assert call(cfg=B.make_cfg(tau=float("nan"))) == 3
+    assert call(dims=B.crisp_dims(4, 2, 1024, 128, 128, float("nan"))) == 3
+    # the gate does not skip validation: a short layer with a bad list pointer fails too
+    b2 = B.crisp_blocks()
+    b2.count = P16
+    assert call(blk=b2, gate=1 << 30) == 1
 
 
 def test_route_jsd_errors():

@@ -286,3 +286,182 @@ def test_gamma_count_grows_with_n_noise_floor_flat():
     print(f"[counts] mean vertical blocks kept, n = 32k/256k/512k: noise floor {nf_counts}, gamma {g_counts}")
     assert g_counts[0] < g_counts[1] < g_counts[2]
     assert max(nf_counts) - min(nf_counts) <= 2.0
+
+
+@pytest.mark.parametrize("widx", [2, 4])
+def test_dense_kernel_at_full_size(widx):
+    """The dense kernel, every speedup's denominator, at the sizes the
+    benchmark times it: the Qwen-shaped 128k and the Llama-shaped 512k
+    layers, fp32 output and lse of two heads on sampled query blocks
+    against the oracle's dense causal attention."""
+    w = synth.workload(widx)
+    print(f"[fullsize] {w.name} dense kernel", flush=True)
+    x = synth.make_inputs(w, device="cuda")
+    hq, hkv, n = w.num_q_heads, w.num_kv_heads, w.seq_len
+    N = n // BLK
+    qpg = hq // hkv
+    dims = B.make_dims(hq, hkv, n)
+    out = torch.empty((hq, n, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    B.crisp_dense_attn(dims, x.q, x.k, x.v, out, lse)
+    torch.cuda.synchronize()
+    for h in (0, hq - 1):
+        g = h // qpg
+        q, k, v = to64(x.q[h]), to64(x.k[g]), to64(x.v[g])
+        qbs = _sample_qbs(N, 500 + widx * 10 + h)
+        ref = O.attention_rows(q, k, v, {qb: list(range(qb + 1)) for qb in qbs}, dims.scale, qbs)
+        og = out[h].cpu().numpy()
+        lg = lse[h].cpu().numpy()
+        for qb in qbs:
+            check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"dense {w.name} h {h} qb {qb}")
+            check_lse(lg[qb * BLK:(qb + 1) * BLK], ref[qb][1])
+
+
+@pytest.mark.parametrize("gamma", [0.95, 0.97])
+def test_gamma_chains_512k(gamma):
+    """The gamma-cumulative comparison chains of the 512k Llama layer, in
+    the benchmark's launch configuration (every head Vertical-Slash): the
+    vertical and slash sets of a sink-dominant and a diffuse head against
+    the oracle's gamma selection, their lists on sampled query blocks, and
+    the attention of those blocks."""
+    w = synth.workload(4)
+    print(f"[fullsize] {w.name} gamma {gamma}", flush=True)
+    x = synth.make_inputs(w, device="cuda")
+    cfg = B.make_cfg(route_override=B.ROUTE_FORCE_VS)
+    dims, bufs = _run(x, cfg, gamma=gamma)
+    hq, hkv, n = w.num_q_heads, w.num_kv_heads, w.seq_len
+    N = n // BLK
+    qpg = hq // hkv
+    count = bufs.blocks["count"].cpu().numpy()
+    idx = bufs.blocks["idx"].cpu().numpy()
+    for h in (0, hq - 1):  # a sink-dominant head and a diffuse one
+        g = h // qpg
+        q, k, v = to64(x.q[h]), to64(x.k[g]), to64(x.v[g])
+        A, _ = O.proxy_map(q[n - BLK:], k, dims.scale)
+        ct, dg = O.token_scores(A)
+        del A
+        vs, ss = O.pooled_scores(ct, dg)
+        np.testing.assert_allclose(bufs.blocks["v_score"][h].cpu().numpy(), vs, rtol=1e-3, atol=1e-9)
+        np.testing.assert_allclose(bufs.blocks["s_score"][h].cpu().numpy(), ss, rtol=1e-3, atol=1e-9)
+        masks = {}
+        for key, nkey, xs in (("v_mask", "n_v", vs), ("s_mask", "n_s", ss)):
+            m = bufs.blocks[key][h].cpu().numpy()
+            got = set(np.nonzero(m)[0].tolist())
+            check_gamma_set(xs, range(N), gamma, got, {0}, extra_fill=8)
+            assert int(bufs.blocks[nkey][h]) == len(got)
+            masks[key] = m.astype(bool)
+        lists = gpu_lists(count, idx, h, N)
+        qbs = _sample_qbs(N, 900 + int(gamma * 100) + h)
+        for qb in qbs:
+            assert lists[qb] == O.vs_list_row(masks["v_mask"], masks["s_mask"], qb), (h, qb)
+        ref = O.attention_rows(q, k, v, lists, dims.scale, qbs)
+        og = bufs.out[h].cpu().numpy()
+        lg = bufs.lse[h].cpu().numpy()
+        for qb in qbs:
+            check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"gamma {gamma} h {h} qb {qb}")
+            check_lse(lg[qb * BLK:(qb + 1) * BLK], ref[qb][1])
+
+
+def _every_head(x, dims, cfg, bufs, oracle_head, rows_per_head):
+    """Selection of every head against the oracle: the route, the
+    Vertical-Slash masks (and lists of sampled query blocks) of VS heads,
+    and the pooled-estimation lists of PE heads on `rows_per_head` query
+    blocks (all of them when None)."""
+    hq, n = dims.num_q_heads, dims.seq_len
+    N = B.num_blocks(n)
+    count = bufs.blocks["count"].cpu().numpy()
+    idx = bufs.blocks["idx"].cpu().numpy()
+    rt = bufs.route.cpu().numpy()
+    cs = bufs.c_struct.cpu().numpy()
+    vms = bufs.blocks["v_mask"].cpu().numpy()
+    sms = bufs.blocks["s_mask"].cpu().numpy()
+    fv = bufs.blocks["floor_v"].cpu().numpy()
+    fs = bufs.blocks["floor_s"].cpu().numpy()
+    for h in range(hq):
+        hr, qbar, kbar = oracle_head(h)
+        assert abs(cs[h] - hr.c_struct) <= REL_CSTRUCT * hr.c_struct, (h, cs[h], hr.c_struct)
+        check_route(hr.c_struct, cfg.tau, int(rt[h]), hr.route)
+        assert int(rt[h]) == hr.route  # far from tau on these layers
+        lists = gpu_lists(count, idx, h, N)
+        qbs = range(N) if rows_per_head is None else _sample_qbs(N, 7000 + h)[:rows_per_head]
+        if hr.route == O.ROUTE_VS:
+            check_noise_floor_mask(hr.v, cfg.alpha, cfg.kmin_blocks, cfg.nf_stat, vms[h], float(fv[h]))
+            check_noise_floor_mask(hr.sl, cfg.alpha, cfg.kmin_blocks, cfg.nf_stat, sms[h], float(fs[h]))
+            for qb in _sample_qbs(N, 8000 + h):
+                assert lists[qb] == O.vs_list_row(vms[h].astype(bool), sms[h].astype(bool), qb), (h, qb)
+        else:
+            check_pe_lists(qbar, kbar, dims.scale, cfg.gamma_pe, lists, qbs=qbs)
+
+
+@pytest.mark.parametrize("override", [B.ROUTE_AUTO, B.ROUTE_FORCE_VS])
+def test_llama_32k_every_head_through_run_layer(override):
+    """Every head of the Llama-shaped 32k layer against the oracle's whole-
+    layer driver (its own head-to-group map): route and C_struct, noise-floor
+    masks of VS heads, and the pooled-estimation lists of every query block
+    of PE heads; attention of sampled blocks of four heads."""
+    w = synth.workload(1)
+    print(f"[fullsize] {w.name} every head, override {override}", flush=True)
+    x = synth.make_inputs(w, device="cuda")
+    cfg = B.make_cfg(route_override=override)
+    dims, bufs = _run(x, cfg)
+    q, k, v = to64(x.q), to64(x.k), to64(x.v)
+    ocfg = O.OracleConfig(route_override=override)
+    res = O.run_layer(q, k, v, ocfg, scale=dims.scale, attn_qbs=[])
+    hq, hkv = w.num_q_heads, w.num_kv_heads
+    N = w.seq_len // BLK
+
+    def oracle_head(h):
+        g = h * hkv // hq
+        return res[h], O.pe_pool(q[h]), O.pe_pool(k[g])
+
+    _every_head(x, dims, cfg, bufs, oracle_head, None)
+    count = bufs.blocks["count"].cpu().numpy()
+    idx = bufs.blocks["idx"].cpu().numpy()
+    for h in (0, 9, 22, 31):
+        qbs = _sample_qbs(N, 300 + h)
+        sub = O.run_layer(q, k, v, ocfg, scale=dims.scale, heads=[h], attn_qbs=qbs)[h]
+        g = h * hkv // hq
+        lists = gpu_lists(count, idx, h, N)
+        ref = O.attention_rows(q[h], k[g], v[g], lists, dims.scale, qbs)
+        og = bufs.out[h].cpu().numpy()
+        for qb in qbs:
+            check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"32k h {h} qb {qb}")
+            if lists[qb] == sub.lists[qb]:  # identical sets: the oracle's own attention too
+                check_attention(og[qb * BLK:(qb + 1) * BLK], sub.attn[qb][0], f"32k oracle lists h {h} qb {qb}")
+
+
+@pytest.mark.parametrize("override", [B.ROUTE_AUTO, B.ROUTE_FORCE_VS])
+def test_qwen_128k_every_head(override):
+    """Every head of the Qwen-shaped 128k layer (GQA 7:1): route and
+    C_struct, noise-floor masks and sampled lists of VS heads, and the
+    pooled-estimation lists of 16 sampled query blocks of every PE head."""
+    w = synth.workload(2)
+    print(f"[fullsize] {w.name} every head, override {override}", flush=True)
+    x = synth.make_inputs(w, device="cuda")
+    cfg = B.make_cfg(route_override=override)
+    dims, bufs = _run(x, cfg)
+    hq, hkv, n = w.num_q_heads, w.num_kv_heads, w.seq_len
+    qpg = hq // hkv
+    ocfg = O.OracleConfig(route_override=override)
+    cache = {}
+
+    def oracle_head(h):
+        g = h // qpg
+        if cache.get("g") != g:
+            cache.clear()
+            cache["g"] = g
+            cache["k"] = to64(x.k[g])
+            cache["kbar"] = O.pe_pool(cache["k"])
+        qh = to64(x.q[h])
+        A, lse = O.proxy_map(qh[n - BLK:], cache["k"], dims.scale)
+        c = O.c_struct(A)
+        rt = O.route(c, ocfg.tau, ocfg.route_override)
+        vs = ss = None
+        if rt == O.ROUTE_VS:
+            ct, dg = O.token_scores(A)
+            vs, ss = O.pooled_scores(ct, dg)
+        del A
+        hr = O.HeadResult(c, rt, lse, vs, ss, None, None, 0.0, 0.0, [])
+        return hr, (O.pe_pool(qh) if rt == O.ROUTE_PE else None), cache["kbar"]
+
+    _every_head(x, dims, cfg, bufs, oracle_head, 16)

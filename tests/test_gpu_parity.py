@@ -608,3 +608,95 @@ def test_route_threshold_extremes(tau, expect):
     cs = bufs.c_struct.cpu().numpy()
     assert np.all((cs >= 0.0) & (cs < 1.0))
     assert np.all(bufs.route.cpu().numpy() == expect)
+
+
+def test_malformed_lists_never_weight_future_keys():
+    """Lists that break the contract are read defensively: the count is
+    clamped to [1, qb+1], the last entry taken as the diagonal block and
+    every other entry clamped to [0, qb-1].  The output must equal the
+    oracle's attention on the list so read, so no key past a query is ever
+    weighted (a diagonal entry anywhere but last would otherwise be computed
+    without the causal mask)."""
+    hq, hkv, n = 2, 1, 1024
+    N = 8
+    x = synth.make_inputs(synth.custom(hq, hkv, n, seed=404, needles=2), device="cuda")
+    dims = B.make_dims(hq, hkv, n)
+    # (count, stored entries, list as read)
+    rows = [(0, [], [0]),
+            (2, [1, 0], [0, 1]),
+            (2, [2, 2], [1, 2]),
+            (2, [7, 1], [2, 3]),
+            (4, [0, 2, 4, 3], [0, 2, 3, 4]),
+            (9, [0, 1, 2, 3, 4, 5], [0, 1, 2, 3, 4, 5]),
+            (2, [-3, 6], [0, 6]),
+            (2, [3, 5], [3, 7])]
+    count = np.zeros((hq, N), np.int32)
+    idx = np.full(hq * N * (N + 1) // 2, 99, np.int32)
+    for h in range(hq):
+        base = h * N * (N + 1) // 2
+        for qb, (c, stored, _) in enumerate(rows):
+            count[h, qb] = c
+            s = base + qb * (qb + 1) // 2
+            idx[s:s + len(stored)] = stored
+    out = torch.empty((hq, n, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    B.crisp_sparse_attn(dims, x.q, x.k, x.v, torch.from_numpy(count).cuda(), torch.from_numpy(idx).cuda(), out, lse)
+    torch.cuda.synchronize()
+    read = [r[2] for r in rows]
+    for h in range(hq):
+        ref = O.attention_rows(to64(x.q[h]), to64(x.k[0]), to64(x.v[0]), read, dims.scale, range(N))
+        og, lg = out[h].cpu().numpy(), lse[h].cpu().numpy()
+        for qb in range(N):
+            check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"malformed h {h} qb {qb}")
+            check_lse(lg[qb * BLK:(qb + 1) * BLK], ref[qb][1])
+
+
+@pytest.mark.parametrize("gate", ["gated", "ungated"])
+def test_one_call_layer_through_the_c_abi(gate):
+    """crisp_prefill of the C ABI on a 4k layer: below its context-length
+    gate it runs the dense kernel alone (selection outputs untouched, output
+    equal to the oracle's dense causal attention); with the gate at the
+    layer's length it runs the whole chain (routes, C_struct, selection and
+    attention against the oracle's whole-layer driver)."""
+    hq, hkv, n = 4, 2, 4096
+    N = n // BLK
+    x = synth.make_inputs(synth.custom(hq, hkv, n, seed=515, needles=3), device="cuda")
+    dims = B.make_dims(hq, hkv, n)
+    cfg = B.make_cfg()
+    bufs = B.CrispBuffers(dims, out_dtype=torch.float32)
+    bufs.blocks["count"].fill_(-7)
+    bufs.route.fill_(-7)
+    print(f"[prefill] {gate}", flush=True)
+    B.crisp_prefill(dims, cfg, x.q, x.k, x.v, bufs, dense_below=None if gate == "gated" else n)
+    torch.cuda.synchronize()
+    q, k, v = to64(x.q), to64(x.k), to64(x.v)
+    if gate == "gated":
+        assert n < B.DENSE_BELOW
+        assert bool((bufs.blocks["count"] == -7).all()) and bool((bufs.route == -7).all())
+        for h in range(hq):
+            g = h * hkv // hq
+            ref = O.attention_rows(q[h], k[g], v[g], O.dense_lists(N), dims.scale, range(N))
+            og, lg = bufs.out[h].cpu().numpy(), bufs.lse[h].cpu().numpy()
+            for qb in range(N):
+                check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"gated h {h} qb {qb}")
+                check_lse(lg[qb * BLK:(qb + 1) * BLK], ref[qb][1])
+        return
+    res = O.run_layer(q, k, v, _cfg_oracle(cfg), scale=dims.scale)
+    count = bufs.blocks["count"].cpu().numpy()
+    idx = bufs.blocks["idx"].cpu().numpy()
+    for h in range(hq):
+        hr = res[h]
+        g = h * hkv // hq
+        c_g = float(bufs.c_struct[h])
+        assert abs(c_g - hr.c_struct) <= REL_CSTRUCT * hr.c_struct
+        check_route(hr.c_struct, cfg.tau, int(bufs.route[h]), hr.route)
+        lists = gpu_lists(count, idx, h, N)
+        if int(bufs.route[h]) == O.ROUTE_PE:
+            check_pe_lists(O.pe_pool(q[h]), O.pe_pool(k[g]), dims.scale, cfg.gamma_pe, lists)
+        ref = O.attention_rows(q[h], k[g], v[g], lists, dims.scale, range(N))
+        og, lg = bufs.out[h].cpu().numpy(), bufs.lse[h].cpu().numpy()
+        for qb in range(N):
+            check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"chain h {h} qb {qb}")
+            check_lse(lg[qb * BLK:(qb + 1) * BLK], ref[qb][1])
+            if lists[qb] == hr.lists[qb]:
+                check_attention(og[qb * BLK:(qb + 1) * BLK], hr.attn[qb][0], f"chain oracle h {h} qb {qb}")

@@ -25,7 +25,7 @@ pytestmark = pytest.mark.skipif(not os.path.exists(HIPCC), reason="needs hipcc f
 
 def _report(src, out_dir):
     obj = os.path.join(out_dir, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC] + bld.FLAGS + ["-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(bld.CSRC, src),
+    cmd = [HIPCC] + bld.flags_for(src) + ["-Rpass-analysis=kernel-resource-usage", "-c", os.path.join(bld.CSRC, src),
                                  "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-2000:]
