@@ -265,6 +265,31 @@ __device__ inline float block_sum_f(float x, float* lds_tmp, int tid, int nthrea
   return r;
 }
 
+// block_sum_f and block_max_f with one barrier: each wave's lane 0 writes
+// its partial to lds_tmp[wave], and every thread then combines the partials
+// in wave order, so every thread gets the value block_sum_f / block_max_f
+// return.  lds_tmp must not be written again until every thread has read it
+// (use a separate array for each reduction between two other barriers).
+__device__ inline float block_sum_f1(float x, float* lds_tmp, int tid, int nthreads) {
+  const int lane = tid & 63, wid = tid >> 6, nw = (nthreads + 63) >> 6;
+  const float s = wave_sum(x);
+  if (lane == 0) lds_tmp[wid] = s;
+  __syncthreads();
+  float acc = 0.f;
+  for (int w = 0; w < nw; ++w) acc += lds_tmp[w];
+  return acc;
+}
+
+__device__ inline float block_max_f1(float x, float* lds_tmp, int tid, int nthreads) {
+  const int lane = tid & 63, wid = tid >> 6, nw = (nthreads + 63) >> 6;
+  const float s = wave_max(x);
+  if (lane == 0) lds_tmp[wid] = s;
+  __syncthreads();
+  float acc = -INFINITY;
+  for (int w = 0; w < nw; ++w) acc = fmaxf(acc, lds_tmp[w]);
+  return acc;
+}
+
 __device__ inline float block_max_f(float x, float* lds_tmp, int tid, int nthreads) {
   const int lane = tid & 63, wid = tid >> 6, nw = (nthreads + 63) >> 6;
   float s = wave_max(x);

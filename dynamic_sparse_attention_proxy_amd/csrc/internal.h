@@ -46,7 +46,7 @@ struct SelectBuffers {
   int32_t* smask; // [Hq][N]
   int32_t* n_v;   // [Hq]
   int32_t* n_s;   // [Hq]
-  float* qbar;    // [Hq][N][128]
+  int32_t* kept;  // [2][Hq] kept blocks per direction (workspace only)
   float* kbar;    // [Hkv][N][128]
 };
 

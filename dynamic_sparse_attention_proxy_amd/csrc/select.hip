@@ -14,14 +14,17 @@
 //                above it plus block 0, top up to k_min; or, for the
 //                comparison chain, the shortest gamma-coverage prefix.
 //   vs_expand  - per (head, query block): kept vertical blocks <= qb and the
-//                two key blocks covered by each kept slash band, compacted in
-//                ascending order.
+//                two key blocks covered by each kept slash band, flagged per
+//                key block and compacted in ascending order by one wave.
 // Pooled-Estimation heads ("Key Contributions" item 2; gamma = 0.95 on PE):
-//   pe_pool    - mean of each 128-row block of q (PE heads) and k (KV groups
-//                holding a PE head).
-//   pe_select  - per (head, query block): pooled logits against kb <= qb,
-//                softmax, radix select of the shortest prefix reaching
-//                gamma, plus qb.
+//   pe_pool    - mean of each 128-row block of k (KV groups holding a PE head).
+//   pe_logits  - per (head, 16 query blocks): mean of each query block of q,
+//                then the pooled logits against every kb <= qb, each pooled
+//                key read once for the 16 rows; a row's logits are written
+//                into its own list row, which has exactly qb + 1 entries.
+//   pe_select  - per (head, query block): the row's logits, softmax, radix
+//                select of the shortest prefix reaching gamma, plus qb; the
+//                list then overwrites the logits.
 
 #include "common.h"
 #include "internal.h"
@@ -97,6 +100,7 @@ struct VsArgs {
   int32_t* smask;
   int32_t* n_v;
   int32_t* n_s;
+  int32_t* kept;  // [2][Hq] kept blocks per direction (read by the list expansion)
   int nblk;
   int pw2;  // power of two >= nblk
   float alpha;
@@ -141,6 +145,7 @@ __global__ __launch_bounds__(kVsThreads) void vs_select_kernel(VsArgs p) {
     if (tid == 0) {
       floor_out[h] = 0.f;
       nsel_out[h] = 0;
+      p.kept[dir * hq + h] = 0;
     }
     return;
   }
@@ -171,6 +176,7 @@ __global__ __launch_bounds__(kVsThreads) void vs_select_kernel(VsArgs p) {
       mask[0] = 1;
       floor_out[h] = T;
       nsel_out[h] = take + 1;
+      p.kept[dir * hq + h] = take + 1;
     }
   } else {
     // gamma-cumulative coverage over all N blocks, then block 0 and k_min.
@@ -209,33 +215,28 @@ __global__ __launch_bounds__(kVsThreads) void vs_select_kernel(VsArgs p) {
       }
       floor_out[h] = key_value(keys[cut]);
       nsel_out[h] = cnt;
+      p.kept[dir * hq + h] = cnt;
     }
   }
   __syncthreads();
   for (int b = tid; b < N; b += kVsThreads) mask_out[b] = mask[b];
 }
 
-__global__ __launch_bounds__(256) void pe_pool_kernel(const __bf16* q, const __bf16* k, const int32_t* route,
-                                                      float* qbar, float* kbar, int hq, int qpg, int n) {
+// Mean of the 128 rows of a block, summed in a fixed order: 8 consecutive
+// rows per thread (16 row groups), then the 16 group sums in order.  The
+// query blocks pooled inside pe_logits_kernel follow the same order.
+__global__ __launch_bounds__(256) void pe_pool_kernel(const __bf16* k, const int32_t* route, float* kbar, int qpg,
+                                                      int n) {
   __shared__ float part[16][kHeadDim];
-  const int kb = blockIdx.x, which = blockIdx.y, tid = threadIdx.x;
+  const int kb = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
   const int nblk = nblocks(n);
   const int rows = min(kBlock, n - kb * kBlock);  // fewer in a partial last block
-  const __bf16* src;
-  float* dst;
-  if (which < hq) {
-    if (route[which] != 0) return;
-    src = q + (size_t)which * n * kHeadDim;
-    dst = qbar + (size_t)which * nblk * kHeadDim;
-  } else {
-    const int g = which - hq;
-    // pooled keys are only read by the Pooled-Estimation heads of the group
-    bool any_pe = false;
-    for (int t = 0; t < qpg; ++t) any_pe |= route[g * qpg + t] == 0;
-    if (!any_pe) return;
-    src = k + (size_t)g * n * kHeadDim;
-    dst = kbar + (size_t)g * nblk * kHeadDim;
-  }
+  // pooled keys are only read by the Pooled-Estimation heads of the group
+  bool any_pe = false;
+  for (int t = 0; t < qpg; ++t) any_pe |= route[g * qpg + t] == 0;
+  if (!any_pe) return;
+  const __bf16* src = k + (size_t)g * n * kHeadDim;
+  float* dst = kbar + (size_t)g * nblk * kHeadDim;
   const int dc = tid & 15, rg = tid >> 4;
   float acc[8];
 #pragma unroll
@@ -264,20 +265,171 @@ __global__ __launch_bounds__(256) void pe_pool_kernel(const __bf16* q, const __b
   }
 }
 
-struct PeArgs {
-  const float* qbar;
+// Pooled logit of one (query block, key block) pair: 16 partial dot products
+// over 8 consecutive dimensions each (one fma chain in dimension order),
+// combined as a balanced binary tree of neighbours,
+//   ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7)) + ((p8+p9)+...+(p14+p15)).
+__device__ __forceinline__ float dot8(f32x4 qa, f32x4 qc, f32x4 ka, f32x4 kc) {
+  float d = qa[0] * ka[0];
+  d = fmaf(qa[1], ka[1], d);
+  d = fmaf(qa[2], ka[2], d);
+  d = fmaf(qa[3], ka[3], d);
+  d = fmaf(qc[0], kc[0], d);
+  d = fmaf(qc[1], kc[1], d);
+  d = fmaf(qc[2], kc[2], d);
+  return fmaf(qc[3], kc[3], d);
+}
+
+constexpr int kPeTile = 16;  // query blocks per pe_logits workgroup
+
+struct PeLogitArgs {
+  const __bf16* q;
   const float* kbar;
+  const int32_t* route;
+  int32_t* idx;
+  int hq;
+  int qpg;
+  int n;
+  int nblk;
+  float scale_log2;
+};
+
+// One workgroup per (head, 16 consecutive query blocks) of a PE head,
+// heaviest (last) tiles first.  The 16 pooled query rows go to LDS; thread t
+// then owns key block c0 + t of each 256-block chunk and computes its logit
+// against all 16 rows, reading each pooled key once.  The logit of
+// (qb, kb), in base 2, is stored as float bits at entry kb of qb's list row.
+__global__ __launch_bounds__(256) void pe_logits_kernel(PeLogitArgs p) {
+  constexpr int kPoolBatch = 4;  // query blocks pooled per round, their loads issued together
+  __shared__ float part[kPoolBatch][16][kHeadDim];
+  __shared__ __attribute__((aligned(16))) float qs[kPeTile][kHeadDim];
+  const int N = p.nblk, tiles = (N + kPeTile - 1) / kPeTile;
+  const int h = blockIdx.x % p.hq, tile = tiles - 1 - (int)blockIdx.x / p.hq;
+  if (p.route[h] != 0) return;
+  const int qb0 = tile * kPeTile, nt = min(kPeTile, N - qb0), qbmax = qb0 + nt - 1;
+  const int tid = threadIdx.x, dc = tid & 15, rg = tid >> 4;
+  const __bf16* qh = p.q + (size_t)h * p.n * kHeadDim;
+  // Pooled query rows in pe_pool_kernel's order; rows past the last block
+  // are zeros, computed and not stored.
+  for (int t0 = 0; t0 < kPeTile; t0 += kPoolBatch) {
+    u32x4 x[kPoolBatch][8];
+#pragma unroll
+    for (int u = 0; u < kPoolBatch; ++u) {
+      const int qb = qb0 + t0 + u;
+      const int rows = t0 + u < nt ? min(kBlock, p.n - qb * kBlock) : 0;
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr) {
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        x[u][rr] = rg * 8 + rr < rows
+                       ? *(const u32x4*)(qh + (size_t)(qb * kBlock + rg * 8 + rr) * kHeadDim + 8 * dc)
+                       : zero;
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < kPoolBatch; ++u) {
+      float acc[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[e] = 0.f;
+#pragma unroll
+      for (int rr = 0; rr < 8; ++rr)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          acc[2 * j] += bf16lo_to_f(x[u][rr][j]);
+          acc[2 * j + 1] += bf16hi_to_f(x[u][rr][j]);
+        }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) part[u][rg][8 * dc + e] = acc[e];
+    }
+    __syncthreads();
+    if (tid < kHeadDim) {
+#pragma unroll
+      for (int u = 0; u < kPoolBatch; ++u) {
+        const int t = t0 + u;
+        const int rows = t < nt ? min(kBlock, p.n - (qb0 + t) * kBlock) : 0;
+        float s = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s += part[u][r][tid];
+        qs[t][tid] = rows > 0 ? s / (float)rows : 0.f;
+      }
+    }
+    __syncthreads();
+  }
+  const float* kbase = p.kbar + (size_t)(h / p.qpg) * N * kHeadDim;
+  int32_t* idx_h = p.idx + (size_t)h * ((size_t)N * (N + 1) / 2);
+  // Thread t owns key blocks c0 + 2t and c0 + 2t + 1 of each 512-block
+  // chunk: every pooled-query read from LDS feeds both.  Slices are taken
+  // two at a time, (2m, 2m+1), whose partials are paired at once; the pair
+  // sums then fold into the tree by m, one uniform branch per pair: levels
+  // st[.][0] = pairs, [1] = quads, [2] = halves.
+  for (int c0 = 0; c0 <= qbmax; c0 += 512) {
+    const int kb0 = c0 + 2 * tid;
+    // rows past the causal range read a valid row, results unused
+    const float* kr0 = kbase + (size_t)min(kb0, qbmax) * kHeadDim;
+    const float* kr1 = kbase + (size_t)min(kb0 + 1, qbmax) * kHeadDim;
+    float st0[kPeTile][3], st1[kPeTile][3];
+#pragma unroll 1
+    for (int m = 0; m < 8; ++m) {
+      f32x4 k0[4], k1[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        k0[u] = *(const f32x4*)(kr0 + 16 * m + 4 * u);
+        k1[u] = *(const f32x4*)(kr1 + 16 * m + 4 * u);
+      }
+      float v0[kPeTile], v1[kPeTile];
+#pragma unroll
+      for (int t = 0; t < kPeTile; ++t) {
+        const f32x4 qa = *(const f32x4*)&qs[t][16 * m], qc = *(const f32x4*)&qs[t][16 * m + 4];
+        const f32x4 qe = *(const f32x4*)&qs[t][16 * m + 8], qg = *(const f32x4*)&qs[t][16 * m + 12];
+        v0[t] = dot8(qa, qc, k0[0], k0[1]) + dot8(qe, qg, k0[2], k0[3]);
+        v1[t] = dot8(qa, qc, k1[0], k1[1]) + dot8(qe, qg, k1[2], k1[3]);
+      }
+      if ((m & 1) == 0) {
+#pragma unroll
+        for (int t = 0; t < kPeTile; ++t) {
+          st0[t][0] = v0[t];
+          st1[t][0] = v1[t];
+        }
+      } else if ((m & 2) == 0) {
+#pragma unroll
+        for (int t = 0; t < kPeTile; ++t) {
+          st0[t][1] = st0[t][0] + v0[t];
+          st1[t][1] = st1[t][0] + v1[t];
+        }
+      } else if ((m & 4) == 0) {
+#pragma unroll
+        for (int t = 0; t < kPeTile; ++t) {
+          st0[t][2] = st0[t][1] + (st0[t][0] + v0[t]);
+          st1[t][2] = st1[t][1] + (st1[t][0] + v1[t]);
+        }
+      } else {
+#pragma unroll
+        for (int t = 0; t < kPeTile; ++t) {
+          st0[t][2] = st0[t][2] + (st0[t][1] + (st0[t][0] + v0[t]));
+          st1[t][2] = st1[t][2] + (st1[t][1] + (st1[t][0] + v1[t]));
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < kPeTile; ++t) {
+      const int qb = qb0 + t;
+      float* dst = (float*)idx_h + (size_t)qb * (qb + 1) / 2;
+      if (t < nt && kb0 <= qb) dst[kb0] = st0[t][2] * p.scale_log2;
+      if (t < nt && kb0 + 1 <= qb) dst[kb0 + 1] = st1[t][2] * p.scale_log2;
+    }
+  }
+}
+
+struct PeArgs {
   const int32_t* route;
   int32_t* count;
   int32_t* idx;
   int hq;
-  int qpg;
   int nblk;
-  float scale_log2;
   float gamma;
 };
 
 constexpr int kPeThreads = 256;
+constexpr int kMaxBlocks = 4096;  // n <= 524288
 constexpr float kFixOne = 2147483648.0f;  // 2^31: probabilities as 32-bit fixed point (a row sums to <= 2^31)
 
 // Wave 0 of a workgroup: the smallest digit d with
@@ -317,6 +469,69 @@ __device__ inline void find_digit(const uint32_t* hist, uint32_t below, uint32_t
   if (lane == 0 && best == 256) *d_out = 256;
 }
 
+// The gamma cut's histogram bins hold (mass << 16) | count: masses are
+// 2^-31 fixed point and a row's total is at most 2^31, counts at most 4096,
+// so neither part overflows into the other.
+constexpr int kCountBits = 16;
+
+// find_digit over the mass parts of packed bins, also returning the number
+// of keys in the chosen bin.
+__device__ inline void find_digit_packed(const uint64_t* hist, uint32_t below, uint32_t target, int lane, int* d_out,
+                                         uint32_t* below_out, uint32_t* count_out) {
+  uint32_t s[4], c[4], tot = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    const uint64_t v = hist[4 * lane + b];
+    s[b] = (uint32_t)(v >> kCountBits);
+    c[b] = (uint32_t)(v & ((1u << kCountBits) - 1));
+    tot += s[b];
+  }
+  uint32_t incl = tot;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t y = __shfl_up(incl, o);
+    if (lane >= o) incl += y;
+  }
+  uint32_t run = below + incl - tot;
+  int cand = 256;
+  uint32_t cand_below = 0, cand_count = 0;
+#pragma unroll
+  for (int b = 0; b < 4; ++b) {
+    if (cand == 256 && run + s[b] >= target) {
+      cand = 4 * lane + b;
+      cand_below = run;
+      cand_count = c[b];
+    }
+    run += s[b];
+  }
+  int best = cand;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) best = min(best, __shfl_xor(best, o));
+  if (cand == best && cand < 256) {
+    *d_out = cand;
+    *below_out = cand_below;
+    *count_out = cand_count;
+  }
+  if (lane == 0 && best == 256) *d_out = 256;
+}
+
+// Adds `val` to bin `digit` for the valid lanes of a wave (all lanes must be
+// active).  The lanes sharing the first valid lane's digit are summed in
+// registers and added with one atomic: a row's probabilities are alike, so
+// most lanes fall in one bin of the high digits.  Integer sums, so the bins
+// do not depend on the grouping.
+__device__ __forceinline__ void hist_add_packed(uint64_t* hist, bool valid, uint32_t digit, uint64_t val, int lane) {
+  const uint64_t any = __ballot(valid);
+  if (any == 0) return;  // no valid lane in the wave (a uniform branch)
+  const uint32_t lead = __builtin_amdgcn_readlane(digit, (int)__builtin_ctzll(any));
+  const bool same = valid && digit == lead;
+  uint64_t sum = same ? val : 0ull;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+  if (lane == (int)__builtin_ctzll(__ballot(same))) atomicAdd((unsigned long long*)&hist[lead], sum);
+  if (valid && !same) atomicAdd((unsigned long long*)&hist[digit], val);
+}
+
 // One workgroup per (head, query block) of a Pooled-Estimation head.
 // The kept set is the shortest prefix, in (descending probability, ascending
 // block) order, whose mass reaches gamma.  That order is the ascending order
@@ -330,11 +545,12 @@ __device__ inline void find_digit(const uint32_t* hist, uint32_t below, uint32_t
 // sums are exact integers and the result deterministic.
 __global__ __launch_bounds__(kPeThreads) void pe_select_kernel(PeArgs p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  __shared__ float redf[8];
+  __shared__ float red_max[4], red_sum[4];
   __shared__ int redi[8];
-  __shared__ uint32_t hist[256];
+  __shared__ uint64_t hist2[2][256];
   __shared__ int sel_digit;
-  __shared__ uint32_t sel_below;
+  __shared__ uint32_t sel_below, sel_count;
+  __shared__ uint64_t sel_key;
   const int N = p.nblk;
   const int id = blockIdx.x;
   const int h = id % p.hq, qb = N - 1 - id / p.hq;
@@ -342,47 +558,41 @@ __global__ __launch_bounds__(kPeThreads) void pe_select_kernel(PeArgs p) {
   const int L = qb + 1;
   float* pr = (float*)smem;
   uint8_t* flags = (uint8_t*)(pr + N);
-  const int tid = threadIdx.x, l16 = tid & 15, grp = tid >> 4, lane = tid & 63;
-  const int g = h / p.qpg;
+  const int tid = threadIdx.x, lane = tid & 63;
 
-  // pooled logits (base 2): 16 lanes per key block, 8 dims each; four
-  // groups of 16 key blocks per iteration, their loads issued together
-  const float* qv = p.qbar + ((size_t)h * N + qb) * kHeadDim + 8 * l16;
-  const f32x4 qa = *(const f32x4*)qv, qc = *(const f32x4*)(qv + 4);
-  const float* kbase = p.kbar + (size_t)g * N * kHeadDim + 8 * l16;
-  constexpr int kPeUnroll = 4;
-  for (int kb0 = 0; kb0 < L; kb0 += 16 * kPeUnroll) {
-    f32x4 ka[kPeUnroll], kc[kPeUnroll];
-#pragma unroll
-    for (int u = 0; u < kPeUnroll; ++u) {
-      const int kb = min(kb0 + 16 * u + grp, L - 1);  // rows past the causal range: a valid row, result unused
-      ka[u] = *(const f32x4*)(kbase + (size_t)kb * kHeadDim);
-      kc[u] = *(const f32x4*)(kbase + (size_t)kb * kHeadDim + 4);
-    }
-#pragma unroll
-    for (int u = 0; u < kPeUnroll; ++u) {
-      const int kb = kb0 + 16 * u + grp;
-      float dot = qa[0] * ka[u][0] + qa[1] * ka[u][1] + qa[2] * ka[u][2] + qa[3] * ka[u][3] + qc[0] * kc[u][0] +
-                  qc[1] * kc[u][1] + qc[2] * kc[u][2] + qc[3] * kc[u][3];
-      dot += __shfl_xor(dot, 1);
-      dot += __shfl_xor(dot, 2);
-      dot += __shfl_xor(dot, 4);
-      dot += __shfl_xor(dot, 8);
-      if (kb < L && l16 == 0) pr[kb] = dot * p.scale_log2;
-    }
-  }
+  // the row's pooled logits (base 2), left in its list row by pe_logits_kernel
+  int32_t* row = p.idx + (size_t)h * ((size_t)N * (N + 1) / 2) + (size_t)qb * (qb + 1) / 2;
+  for (int kb = tid; kb < L; kb += kPeThreads) pr[kb] = __int_as_float(row[kb]);
   __syncthreads();
   float mx = -INFINITY;
   for (int kb = tid; kb < L; kb += kPeThreads) mx = fmaxf(mx, pr[kb]);
-  mx = block_max_f(mx, redf, tid, kPeThreads);
+  mx = block_max_f1(mx, red_max, tid, kPeThreads);
   float loc = 0.f;
   for (int kb = tid; kb < L; kb += kPeThreads) {
     const float e = fast_exp2(pr[kb] - mx);
     pr[kb] = e;
     loc += e;
   }
-  const float sum = block_sum_f(loc, redf, tid, kPeThreads);
-  for (int i = tid; i < L; i += kPeThreads) pr[i] = pr[i] / sum;
+  const float sum = block_sum_f1(loc, red_sum, tid, kPeThreads);
+  // Thread t holds entries t + 256 u (u < U <= 16) of the row in registers
+  // for the radix passes: the high word of its key (the complemented
+  // probability bits) and its fixed-point mass.
+  const int U = (L + kPeThreads - 1) / kPeThreads;
+  uint32_t khi[kMaxBlocks / kPeThreads], mass[kMaxBlocks / kPeThreads];
+#pragma unroll
+  for (int u = 0; u < kMaxBlocks / kPeThreads; ++u) {
+    const int i = tid + kPeThreads * u;
+    khi[u] = 0xffffffffu;
+    mass[u] = 0;
+    if (u < U && i < L) {
+      const float pv = pr[i] / sum;
+      pr[i] = pv;
+      khi[u] = ~__float_as_uint(pv);
+      mass[u] = (uint32_t)(pv * kFixOne);
+    }
+  }
+  hist2[0][tid] = 0;
+  hist2[1][tid] = 0;
   __syncthreads();
 
   const uint32_t target = (uint32_t)(p.gamma * kFixOne);
@@ -394,15 +604,36 @@ __global__ __launch_bounds__(kPeThreads) void pe_select_kernel(PeArgs p) {
   for (int pass = 0; pass < 6; ++pass) {
     const int sh = kShift[pass];
     const uint64_t hi_mask = pass == 0 ? 0ull : ~((uint64_t(1) << (sh + 8)) - 1);
-    if (tid < 256) hist[tid] = 0;
-    __syncthreads();
-    for (int i = tid; i < L; i += kPeThreads) {
-      const uint64_t key = desc_key(pr[i], (uint32_t)i);
-      if ((key & hi_mask) == decided)
-        atomicAdd(&hist[(key >> sh) & 255], (uint32_t)(pr[i] * kFixOne));
+    // two histograms in turn: this pass's starts cleared, and the other one
+    // (last read before the previous pass's final barrier) is cleared for
+    // the next pass
+    uint64_t* hist = hist2[pass & 1];
+    if (pass > 0) hist2[(pass + 1) & 1][tid] = 0;
+    // a thread's matching entries, run by run of equal digits: a run goes
+    // to the histogram when the digit changes, the last one with the wave
+    uint32_t run_d = 0xffffffffu;
+    uint64_t run_v = 0;
+#pragma unroll
+    for (int u = 0; u < kMaxBlocks / kPeThreads; ++u) {
+      const int i = tid + kPeThreads * u;
+      if (u < U && i < L) {
+        const uint64_t key = ((uint64_t)khi[u] << 32) | (uint32_t)i;
+        if ((key & hi_mask) == decided) {
+          const uint32_t dg = (uint32_t)(key >> sh) & 255u;
+          const uint64_t v = ((uint64_t)mass[u] << kCountBits) | 1ull;
+          if (dg == run_d) {
+            run_v += v;
+          } else {
+            if (run_d != 0xffffffffu) atomicAdd((unsigned long long*)&hist[run_d], run_v);
+            run_d = dg;
+            run_v = v;
+          }
+        }
+      }
     }
+    hist_add_packed(hist, run_d != 0xffffffffu, run_d, run_v, lane);
     __syncthreads();
-    if (tid < 64) find_digit(hist, below, target, lane, &sel_digit, &sel_below);
+    if (tid < 64) find_digit_packed(hist, below, target, lane, &sel_digit, &sel_below, &sel_count);
     __syncthreads();
     const int d = sel_digit;
     if (d == 256) {  // the whole row never reaches gamma (rounding): keep everything
@@ -411,6 +642,20 @@ __global__ __launch_bounds__(kPeThreads) void pe_select_kernel(PeArgs p) {
     }
     below = sel_below;
     decided |= (uint64_t)d << sh;
+    if (sel_count == 1) {
+      // one key carries the digits fixed so far: it is the cut, whatever
+      // its remaining digits (the passes left would single it out)
+      const uint64_t m = ~((uint64_t(1) << sh) - 1);
+#pragma unroll
+      for (int u = 0; u < kMaxBlocks / kPeThreads; ++u) {
+        const int i = tid + kPeThreads * u;
+        const uint64_t key = ((uint64_t)khi[u] << 32) | (uint32_t)i;
+        if (u < U && i < L && (key & m) == decided) sel_key = key;
+      }
+      __syncthreads();
+      decided = sel_key;
+      break;
+    }
   }
 
   // ascending compaction of the kept blocks plus the diagonal one
@@ -424,27 +669,34 @@ __global__ __launch_bounds__(kPeThreads) void pe_select_kernel(PeArgs p) {
   }
   int total;
   int pos = block_exclusive_scan(c, redi, tid, kPeThreads, &total);
-  int32_t* out = p.idx + (size_t)h * ((size_t)N * (N + 1) / 2) + (size_t)qb * (qb + 1) / 2;
   for (int kb = beg; kb < end; ++kb)
-    if (flags[kb]) out[pos++] = kb;
+    if (flags[kb]) row[pos++] = kb;
   if (tid == 0) p.count[(size_t)h * N + qb] = total;
 }
 
-// One workgroup per (head, 256 query blocks), one thread per query block.
-// The head's kept vertical blocks V and slash bands S are compacted once
-// into ascending LDS lists; the list of qb is the merge of {v in V : v <= qb}
-// with the tiles qb - s - 1, qb - s of the bands s in S taken from the widest
-// band down (an ascending sequence in which neighbouring bands repeat one
-// block), dropping repeats and blocks below 0.
-constexpr int kExpandRows = 256;
-constexpr int kMaxBlocks = 4096;  // n <= 524288
+// The lists of a Vertical-Slash head are written by one of two kernels,
+// chosen per head from its kept counts (both kernels decide alike): a
+// thread-per-row merge when |V| + 2|S| <= N / 16 (its cost grows with the
+// kept blocks), otherwise a wave per row that walks the row's key blocks
+// and writes whole runs of the list at once (its cost grows with qb).
+__device__ __forceinline__ bool expand_is_sparse(int nv, int ns, int N) { return 16 * (nv + 2 * ns) <= N; }
 
-__global__ __launch_bounds__(256) void vs_expand_kernel(const int32_t* route, const int32_t* vmask,
-                                                        const int32_t* smask, int32_t* count, int32_t* idx, int nblk) {
+// Sparse heads: one workgroup per (head, 256 query blocks), one thread per
+// query block.  The head's kept vertical blocks V and slash bands S are
+// compacted once into ascending LDS lists; the list of qb is the merge of
+// {v in V : v <= qb} with the tiles qb - s - 1, qb - s of the bands s in S
+// taken from the widest band down (an ascending sequence in which
+// neighbouring bands repeat one block), dropping repeats and blocks below 0.
+// A thread's work grows with |V| + 2|S|, not with qb.
+constexpr int kExpandRows = 256;
+
+__global__ __launch_bounds__(256) void vs_expand_sparse_kernel(const int32_t* route, const int32_t* kept,
+                                                               const int32_t* vmask, const int32_t* smask,
+                                                               int32_t* count, int32_t* idx, int nblk) {
   __shared__ int32_t vl[kMaxBlocks], sl[kMaxBlocks];
   __shared__ int scan_tmp[8];
   const int N = nblk, h = blockIdx.y, tid = threadIdx.x;
-  if (route[h] != 1) return;
+  if (route[h] != 1 || !expand_is_sparse(kept[h], kept[gridDim.y + h], N)) return;
   // ascending compaction of both masks, 256 blocks per round
   int nv = 0, ns = 0;
   for (int b0 = 0; b0 < N; b0 += 256) {
@@ -501,6 +753,46 @@ __global__ __launch_bounds__(256) void vs_expand_kernel(const int32_t* route, co
   count[(size_t)h * N + qb] = pos;
 }
 
+
+// Dense heads: one wave per (head, query block), eight per workgroup.  Key block kb is in
+// the list of qb when vertical block kb is kept, or a kept slash band covers
+// it: band qb - kb (its tile qb - s) or band qb - kb - 1 (its tile
+// qb - s - 1).  The wave walks kb = 0 .. qb 64 at a time, flags each block
+// and writes the flagged ones at their rank (ballot and popcount), so the
+// list is ascending and every store instruction writes consecutive entries.
+constexpr int kExpandWaves = 8;
+
+__global__ __launch_bounds__(64 * kExpandWaves) void vs_expand_dense_kernel(const int32_t* route,
+                                                                            const int32_t* kept,
+                                                                            const int32_t* vmask,
+                                                                            const int32_t* smask, int32_t* count,
+                                                                            int32_t* idx, int nblk) {
+  __shared__ uint8_t vm[kMaxBlocks], sm[kMaxBlocks];
+  const int N = nblk, h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  if (route[h] != 1 || expand_is_sparse(kept[h], kept[gridDim.y + h], N)) return;
+  for (int b = tid; b < N; b += 64 * kExpandWaves) {
+    vm[b] = vmask[(size_t)h * N + b] != 0;
+    sm[b] = smask[(size_t)h * N + b] != 0;
+  }
+  __syncthreads();
+  const int qb = blockIdx.x * kExpandWaves + (tid >> 6);
+  if (qb >= N) return;
+  int32_t* out = idx + (size_t)h * ((size_t)N * (N + 1) / 2) + (size_t)qb * (qb + 1) / 2;
+  int pos = 0;
+  for (int c0 = 0; c0 <= qb; c0 += 64) {
+    const int kb = c0 + lane;
+    bool f = false;
+    if (kb <= qb) {
+      const int s = qb - kb;
+      f = vm[kb] || sm[s] || (s >= 1 && sm[s - 1]);
+    }
+    const uint64_t bal = __ballot(f);
+    if (f) out[pos + __popcll(bal & ((1ull << lane) - 1))] = kb;
+    pos += __popcll(bal);
+  }
+  if (lane == 0) count[(size_t)h * N + qb] = pos;
+}
+
 // ---------------------------------------------------------------------------
 // Token-granular vertical selection (ai-feeds summary, method module 2: keep
 // the tokens clearly above the noise floor).  One workgroup per VS head over
@@ -526,6 +818,7 @@ struct TokArgs {
   int32_t* vmask;      // [Hq][N]
   float* floor_v;      // [Hq]
   int32_t* n_v;        // [Hq]
+  int32_t* kept;       // [2][Hq] kept blocks per direction: vertical becomes block 0 only
   int n;
   int nblk;
   float alpha;
@@ -680,6 +973,7 @@ __global__ __launch_bounds__(kTokThreads) void tok_select_kernel(TokArgs p) {
     p.ncols[h] = kept_before;
     p.floor_v[h] = T;
     p.n_v[h] = kBlock + kept_before;
+    p.kept[h] = 1;
   }
 }
 
@@ -701,7 +995,7 @@ size_t select_workspace_bytes(int hq, int hkv, int n) {
   b += 2 * align_up(hq * sizeof(float));            // floors
   b += 2 * align_up(hq * N * sizeof(int32_t));      // masks
   b += 2 * align_up(hq * sizeof(int32_t));          // kept counts
-  b += align_up(hq * N * kHeadDim * sizeof(float)); // qbar
+  b += align_up(2 * hq * sizeof(int32_t));          // kept blocks per direction, for the list expansion
   b += align_up(hkv * N * kHeadDim * sizeof(float));// kbar
   return b;
 }
@@ -724,7 +1018,7 @@ SelectBuffers carve_select_workspace(void* ws, int hq, int hkv, int n) {
   b.smask = (int32_t*)take(hq * N * sizeof(int32_t));
   b.n_v = (int32_t*)take(hq * sizeof(int32_t));
   b.n_s = (int32_t*)take(hq * sizeof(int32_t));
-  b.qbar = (float*)take(hq * N * kHeadDim * sizeof(float));
+  b.kept = (int32_t*)take(2 * hq * sizeof(int32_t));
   b.kbar = (float*)take(hkv * N * kHeadDim * sizeof(float));
   return b;
 }
@@ -755,6 +1049,7 @@ hipError_t launch_select(const __bf16* q, const __bf16* k, const float* amap, co
   va.smask = b.smask;
   va.n_v = b.n_v;
   va.n_s = b.n_s;
+  va.kept = b.kept;
   va.nblk = N;
   va.pw2 = host_pow2_ceil(N);
   va.alpha = alpha;
@@ -775,6 +1070,7 @@ hipError_t launch_select(const __bf16* q, const __bf16* k, const float* amap, co
     ta.vmask = b.vmask;
     ta.floor_v = b.floor_v;
     ta.n_v = b.n_v;
+    ta.kept = b.kept;
     ta.n = n;
     ta.nblk = N;
     ta.alpha = alpha;
@@ -784,27 +1080,38 @@ hipError_t launch_select(const __bf16* q, const __bf16* k, const float* amap, co
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
 
-  hipLaunchKernelGGL(pe_pool_kernel, dim3(N, hq + hkv), dim3(256), 0, stream, q, k, route, b.qbar, b.kbar, hq,
-                     hq / hkv, n);
+  hipLaunchKernelGGL(pe_pool_kernel, dim3(N, hkv), dim3(256), 0, stream, k, route, b.kbar, hq / hkv, n);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  PeLogitArgs la;
+  la.q = q;
+  la.kbar = b.kbar;
+  la.route = route;
+  la.idx = idx;
+  la.hq = hq;
+  la.qpg = hq / hkv;
+  la.n = n;
+  la.nblk = N;
+  la.scale_log2 = scale * kLog2e;
+  hipLaunchKernelGGL(pe_logits_kernel, dim3(hq * ((N + kPeTile - 1) / kPeTile)), dim3(256), 0, stream, la);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   PeArgs pa;
-  pa.qbar = b.qbar;
-  pa.kbar = b.kbar;
   pa.route = route;
   pa.count = count;
   pa.idx = idx;
   pa.hq = hq;
-  pa.qpg = hq / hkv;
   pa.nblk = N;
-  pa.scale_log2 = scale * kLog2e;
   pa.gamma = use_gamma ? gamma : gamma_pe;
   const size_t pe_lds = (size_t)N * 4 + (size_t)N;
   hipLaunchKernelGGL(pe_select_kernel, dim3(hq * N), dim3(kPeThreads), pe_lds, stream, pa);
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
-  hipLaunchKernelGGL(vs_expand_kernel, dim3((N + kExpandRows - 1) / kExpandRows, hq), dim3(256), 0, stream, route,
-                     b.vmask, b.smask, count, idx, N);
+  hipLaunchKernelGGL(vs_expand_sparse_kernel, dim3((N + kExpandRows - 1) / kExpandRows, hq), dim3(256), 0, stream,
+                     route, b.kept, b.vmask, b.smask, count, idx, N);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(vs_expand_dense_kernel, dim3((N + kExpandWaves - 1) / kExpandWaves, hq), dim3(64 * kExpandWaves),
+                     0, stream, route, b.kept, b.vmask, b.smask, count, idx, N);
   return hipGetLastError();
 }
 
