@@ -73,6 +73,8 @@ _SIGS = {
     "crisp_select_gamma": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), ctypes.c_float, _P,
                                           _P, _P, _P, _P, ctypes.POINTER(crisp_blocks), _P, ctypes.c_size_t, _P]),
     "crisp_select_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(crisp_dims)]),
+    "crisp_select_noalloc": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), _P, _P, _P, _P,
+                                            _P, ctypes.POINTER(crisp_blocks), _P]),
     "crisp_list_capacity": (ctypes.c_size_t, [ctypes.POINTER(crisp_dims)]),
     "crisp_sparse_attn": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P,
                                          _P]),
@@ -205,6 +207,19 @@ def crisp_select(dims: crisp_dims, cfg: crisp_cfg, q, k, attn_map, route, out: d
                                               _ptr(attn_map), _ptr(block_mass), _ptr(route), ctypes.byref(b),
                                               _ptr(workspace), workspace.numel() * workspace.element_size(),
                                               _stream(stream)))
+
+
+# CRISP_NOALLOC_SCRATCH_BYTES of include/crisp.h: the largest selection
+# workspace crisp_select_noalloc serves from its static per-device scratch.
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def crisp_select_noalloc(dims: crisp_dims, cfg: crisp_cfg, q, k, attn_map, route, out: dict, stream=None,
+                         block_mass=None):
+    b = _blocks(out)
+    _check("crisp_select_noalloc", lib().crisp_select_noalloc(ctypes.byref(dims), ctypes.byref(cfg), _ptr(q), _ptr(k),
+                                                              _ptr(attn_map), _ptr(block_mass), _ptr(route),
+                                                              ctypes.byref(b), _stream(stream)))
 
 
 def crisp_select_gamma(dims: crisp_dims, cfg: crisp_cfg, gamma: float, q, k, attn_map, route, out: dict,

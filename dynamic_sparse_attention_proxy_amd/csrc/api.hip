@@ -90,6 +90,27 @@ crisp_status check_device() {
 
 crisp_status launched(hipError_t e) { return e == hipSuccess ? CRISP_OK : CRISP_ERR_LAUNCH; }
 
+// Selection workspace of crisp_select_noalloc: a file-scope device array,
+// one copy per device, held from the module's load to the process's end.
+// Host code never passes its name to a kernel (on the host it is only a
+// stand-in for the symbol): the device address comes from
+// hipGetSymbolAddress, once per device, and is kept in g_scratch_ptr.
+static __device__ __align__(256) unsigned char scratch[CRISP_NOALLOC_SCRATCH_BYTES];
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (NULL if it cannot be had).
+void* scratch_ptr() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* ptr = __atomic_load_n(&g_scratch_ptr[dev], __ATOMIC_ACQUIRE);
+  if (ptr == nullptr) {
+    // concurrent first calls on one device get the same address
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+    __atomic_store_n(&g_scratch_ptr[dev], ptr, __ATOMIC_RELEASE);
+  }
+  return ptr;
+}
+
 // The proxy's output: the map, the block masses, or both; at least one.
 crisp_status check_map_or_mass(const void* attn_map, const void* block_mass) {
   if (attn_map == nullptr && block_mass == nullptr) return CRISP_ERR_NULL;
@@ -291,6 +312,25 @@ crisp_status crisp_select(const crisp_dims* dims, const crisp_cfg* cfg, const vo
                           const crisp_blocks* out, void* workspace, size_t workspace_bytes, void* stream) {
   return select_common(dims, cfg, false, 0.f, q, k, attn_map, block_mass, route, out, workspace, workspace_bytes,
                        nullptr, stream);
+}
+
+crisp_status crisp_select_noalloc(const crisp_dims* dims, const crisp_cfg* cfg, const void* q, const void* k,
+                                  const float* attn_map, const float* block_mass, const int32_t* route,
+                                  const crisp_blocks* out, void* stream) {
+  CRISP_TRY(check_dims(dims));
+  CRISP_TRY(check_cfg(dims, cfg));
+  CRISP_TRY(check_blocks(out));
+  CRISP_TRY(check_ptr(q));
+  CRISP_TRY(check_ptr(k));
+  CRISP_TRY(check_map_or_mass(attn_map, block_mass));
+  CRISP_TRY(check_ptr(route));
+  if (crisp::select_workspace_bytes(dims->num_q_heads, dims->num_kv_heads, dims->seq_len) >
+      (size_t)CRISP_NOALLOC_SCRATCH_BYTES)
+    return CRISP_ERR_WORKSPACE;
+  CRISP_TRY(check_device());
+  void* ws = scratch_ptr();
+  if (ws == nullptr) return CRISP_ERR_DEVICE;
+  return select_launch(dims, cfg, false, 0.f, q, k, attn_map, block_mass, route, out, ws, nullptr, stream);
 }
 
 crisp_status crisp_select_tokens(const crisp_dims* dims, const crisp_cfg* cfg, const void* q, const void* k,

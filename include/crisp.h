@@ -24,9 +24,10 @@
  *     that exist (a partial block has fewer keys, query rows and offsets;
  *     its pooled mean is over its rows).
  *   - Every pointer must be 16-byte aligned (CRISP_ERR_ALIGN otherwise).
- *   - The caller owns every buffer; the library allocates nothing.  Its only
- *     global state is a write-once per-device record of whether the device
- *     is a gfx950, so calls are reentrant.
+ *   - The caller owns every buffer; the library allocates nothing.  Its
+ *     global state is write-once per device: whether the device is a gfx950,
+ *     and the address of the static scratch of crisp_select_noalloc.  Every
+ *     other call is reentrant.
  *   - Arguments are validated on the host before anything is launched; a
  *     failed validation returns an error and leaves all outputs untouched.
  *   - Work is enqueued asynchronously on `stream` (a hipStream_t, NULL for
@@ -194,6 +195,24 @@ CRISP_API crisp_status crisp_select_gamma(const crisp_dims* dims, const crisp_cf
                                 size_t workspace_bytes, void* stream);
 
 CRISP_API size_t crisp_select_workspace_bytes(const crisp_dims* dims);
+
+/* crisp_select without a workspace argument, for callers that cannot
+ * allocate device memory: code under HIP stream capture, tight serving
+ * loops, harnesses that forbid allocation.  Arguments, results and errors
+ * are those of crisp_select.  The workspace is a static per-device buffer
+ * inside the library of CRISP_NOALLOC_SCRATCH_BYTES (32 MiB), held on every
+ * device the library runs on until the process ends; a layer whose
+ * crisp_select_workspace_bytes exceeds it is CRISP_ERR_WORKSPACE (every
+ * layer up to 524288 tokens with up to 64 query and 8 KV heads fits).  The
+ * call allocates nothing and needs no zeroed memory: every kernel writes the
+ * scratch it reads.  The buffer is shared by every call on a device and
+ * keeps the last call's contents, so calls that overlap on one device (two
+ * streams, or two threads) race: serialise them. */
+#define CRISP_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+CRISP_API crisp_status crisp_select_noalloc(const crisp_dims* dims, const crisp_cfg* cfg, const void* q,
+                                            const void* k, const float* attn_map, const float* block_mass,
+                                            const int32_t* route, const crisp_blocks* out, void* stream);
 
 /* Number of int32 entries crisp_blocks.idx must hold: Hq * N(N+1)/2. */
 CRISP_API size_t crisp_list_capacity(const crisp_dims* dims);

@@ -26,7 +26,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 18
+    assert len(names) == 19
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -136,6 +136,40 @@ def test_non_finite_scale_and_thresholds_are_param_errors(value):
     if value != 0.0:  # a JSD threshold of 0 is allowed
         assert lib.crisp_route_jsd(ctypes.byref(good), ctypes.c_float(value), P16, P16, P16, P16, P16, None, P16,
                                    1 << 40, None) == 3
+
+
+def test_select_noalloc_validation():
+    """The allocation-free selection validates like crisp_select; a layer
+    whose selection workspace exceeds the static scratch is
+    CRISP_ERR_WORKSPACE before any device call, a fitting one reaches the
+    device check (no GPU here: 6)."""
+    lib = B.lib()
+    cfg = B.make_cfg()
+    blocks = B.crisp_blocks()
+    blocks.count = P16
+    blocks.idx = P16
+
+    def call(dims, q=P16, route=P16, mass=P16, blk=blocks, c=cfg):
+        return lib.crisp_select_noalloc(ctypes.byref(dims), ctypes.byref(c), q, P16, None, mass, route,
+                                        None if blk is None else ctypes.byref(blk), None)
+
+    text = open(HEADER).read()
+    m = re.search(r"#define\s+CRISP_NOALLOC_SCRATCH_BYTES\s+\((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == B.NOALLOC_SCRATCH_BYTES
+    for hq, hkv, n in ((32, 8, 524288), (64, 8, 524288), (28, 4, 131072), (4, 2, 1024)):
+        d = B.make_dims(hq, hkv, n)
+        assert B.crisp_select_workspace_bytes(d) <= B.NOALLOC_SCRATCH_BYTES
+        assert call(d) == 6
+    for hq, hkv, n in ((32, 32, 524288), (64, 16, 524288)):
+        d = B.make_dims(hq, hkv, n)
+        assert B.crisp_select_workspace_bytes(d) > B.NOALLOC_SCRATCH_BYTES
+        assert call(d) == 5
+    d = B.make_dims(4, 2, 1024)
+    assert call(d, q=None) == 1
+    assert call(d, route=P8) == 4
+    assert call(d, mass=None) == 1
+    assert call(d, blk=None) == 1
+    assert call(d, c=B.make_cfg(alpha=float("nan"))) == 3
 
 
 def test_select_errors():
