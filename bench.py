@@ -136,7 +136,8 @@ def run_workload(torch, B, synth, wname, args, cfg_kw, compare):
                                  block_mass=mass)
         if t is not None:
             t.append(ev())
-        B.crisp_sparse_attn(dims, x.q, x.k, x.v, bufs.blocks["count"], bufs.blocks["idx"], bufs.out, bufs.lse)
+        B.crisp_sparse_attn(dims, x.q, x.k, x.v, bufs.blocks["count"], bufs.blocks["idx"], bufs.out, bufs.lse,
+                            workspace=bufs.attn_workspace)
         if t is not None:
             t.append(ev())
             marks.append(t)
@@ -179,12 +180,12 @@ def run_workload(torch, B, synth, wname, args, cfg_kw, compare):
     log(f"{w.name}: map path proxy {res['map_path']['proxy_ms']:.3f} ms, select {res['map_path']['select_ms']:.3f} ms")
     # dense baseline
     for _ in range(args.warmup):
-        B.crisp_dense_attn(dims, x.q, x.k, x.v, bufs.out)
+        B.crisp_dense_attn(dims, x.q, x.k, x.v, bufs.out, workspace=bufs.attn_workspace)
     torch.cuda.synchronize()
     dt = Timer(torch)
     for _ in range(args.steps):
         with dt:
-            B.crisp_dense_attn(dims, x.q, x.k, x.v, bufs.out)
+            B.crisp_dense_attn(dims, x.q, x.k, x.v, bufs.out, workspace=bufs.attn_workspace)
     torch.cuda.synchronize()
     d_ms = dt.ms()
     res["dense"] = {"ms_per_layer": sum(d_ms) / len(d_ms), "ms_all": d_ms,
@@ -254,7 +255,8 @@ def timed_token_chain(torch, B, x, dims, tb, cfg, steps, warmup):
         B.crisp_select_tokens(dims, cfg, x.q, x.k, tb.block_mass, tb.col_mass, tb.route, tb.blocks, tb.cols,
                               tb.ncols, tb.col_below, tb.workspace)
         mark()
-        B.crisp_sparse_attn(dims, x.q, x.k, x.v, tb.blocks["count"], tb.blocks["idx"], tb.out, tb.lse)
+        B.crisp_sparse_attn(dims, x.q, x.k, x.v, tb.blocks["count"], tb.blocks["idx"], tb.out, tb.lse,
+                            workspace=tb.attn_workspace)
         mark()
         B.crisp_sparse_attn_cols(dims, x.q, x.k, x.v, tb.blocks["count"], tb.blocks["idx"], tb.cols, tb.col_below,
                                  tb.out, tb.lse)
@@ -467,7 +469,8 @@ def sweep(torch, B, synth, args):
         bufs = B.CrispBuffers(dims, out_dtype=torch.bfloat16)
         N = n // 128
         dense_tiles = base.num_q_heads * N * (N + 1) // 2
-        row = {"seq_len": n, "dense_ms": med(lambda: B.crisp_dense_attn(dims, x.q, x.k, x.v, bufs.out),
+        row = {"seq_len": n, "dense_ms": med(lambda: B.crisp_dense_attn(dims, x.q, x.k, x.v, bufs.out,
+                                                                         workspace=bufs.attn_workspace),
                                              args.compare_steps)}
         chains = [("auto", B.make_cfg())] + [(f"vs_alpha{a}", B.make_cfg(route_override=B.ROUTE_FORCE_VS, alpha=a))
                                              for a in SWEEP_ALPHAS]
@@ -522,7 +525,8 @@ def counts(torch, B, synth, args):
     bufs = B.CrispBuffers(dims, out_dtype=torch.bfloat16)
     N = -(-w.seq_len // 128)
     dense_tiles = w.num_q_heads * N * (N + 1) // 2
-    dense_ms = _med_ms(torch, lambda: B.crisp_dense_attn(dims, x.q, x.k, x.v, bufs.out), args.compare_steps)
+    dense_ms = _med_ms(torch, lambda: B.crisp_dense_attn(dims, x.q, x.k, x.v, bufs.out, workspace=bufs.attn_workspace),
+                       args.compare_steps)
     rows = []
     for name, alpha, gamma, route in COUNT_CHAINS:
         kw = {} if route is None else {"route_override": B.ROUTE_FORCE_VS, "alpha": alpha}

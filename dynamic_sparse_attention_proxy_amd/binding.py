@@ -77,8 +77,10 @@ _SIGS = {
                                             _P, ctypes.POINTER(crisp_blocks), _P]),
     "crisp_list_capacity": (ctypes.c_size_t, [ctypes.POINTER(crisp_dims)]),
     "crisp_sparse_attn": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, _P, _P, ctypes.c_int32, _P,
-                                         _P]),
-    "crisp_dense_attn": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, ctypes.c_int32, _P, _P]),
+                                         _P, ctypes.c_size_t, _P]),
+    "crisp_dense_attn": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, ctypes.c_int32, _P, _P,
+                                        ctypes.c_size_t, _P]),
+    "crisp_attn_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(crisp_dims)]),
     "crisp_prefill": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), ctypes.c_int32, _P, _P,
                                      _P, ctypes.POINTER(crisp_blocks), _P, _P, _P, _P, ctypes.c_int32, _P, _P,
                                      ctypes.c_size_t, _P]),
@@ -252,16 +254,31 @@ def crisp_sparse_attn_cols(dims: crisp_dims, q, k, v, count, idx, cols, col_belo
                                                                   _stream(stream)))
 
 
-def crisp_sparse_attn(dims: crisp_dims, q, k, v, count, idx, out, lse=None, stream=None):
+def crisp_attn_workspace_bytes(dims: crisp_dims) -> int:
+    return int(lib().crisp_attn_workspace_bytes(ctypes.byref(dims)))
+
+
+def _attn_workspace(dims, out, workspace):
+    # the attention kernels' work queue; a fresh one per call unless given
+    if workspace is None:
+        workspace = torch.empty(crisp_attn_workspace_bytes(dims), dtype=torch.uint8, device=out.device)
+    return workspace
+
+
+def crisp_sparse_attn(dims: crisp_dims, q, k, v, count, idx, out, lse=None, stream=None, workspace=None):
     out_fp32 = 1 if out.dtype == torch.float32 else 0
+    ws = _attn_workspace(dims, out, workspace)
     _check("crisp_sparse_attn", lib().crisp_sparse_attn(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(count),
-                                                        _ptr(idx), _ptr(out), out_fp32, _ptr(lse), _stream(stream)))
+                                                        _ptr(idx), _ptr(out), out_fp32, _ptr(lse), _ptr(ws),
+                                                        ws.numel() * ws.element_size(), _stream(stream)))
 
 
-def crisp_dense_attn(dims: crisp_dims, q, k, v, out, lse=None, stream=None):
+def crisp_dense_attn(dims: crisp_dims, q, k, v, out, lse=None, stream=None, workspace=None):
     out_fp32 = 1 if out.dtype == torch.float32 else 0
+    ws = _attn_workspace(dims, out, workspace)
     _check("crisp_dense_attn", lib().crisp_dense_attn(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(out),
-                                                      out_fp32, _ptr(lse), _stream(stream)))
+                                                      out_fp32, _ptr(lse), _ptr(ws), ws.numel() * ws.element_size(),
+                                                      _stream(stream)))
 
 
 # --------------------------------------------------------------------------
@@ -316,6 +333,7 @@ class CrispBuffers:
             out_dtype = f32
         self.out = torch.empty((hq, n, dims.head_dim), dtype=out_dtype, device=dev)
         self.lse = torch.empty((hq, n), dtype=f32, device=dev)
+        self.attn_workspace = torch.empty(crisp_attn_workspace_bytes(dims), dtype=torch.uint8, device=dev)
 
 
 # Context-length gate (ai.info summary: "Main Findings" puts the crossover
@@ -359,7 +377,8 @@ def crisp_prefill(dims: crisp_dims, cfg: crisp_cfg, q, k, v, bufs: CrispBuffers,
     else:
         crisp_select_gamma(dims, cfg, gamma, q, k, amap, bufs.route, bufs.blocks, bufs.workspace, stream,
                            block_mass=mass)
-    crisp_sparse_attn(dims, q, k, v, bufs.blocks["count"], bufs.blocks["idx"], bufs.out, bufs.lse, stream)
+    crisp_sparse_attn(dims, q, k, v, bufs.blocks["count"], bufs.blocks["idx"], bufs.out, bufs.lse, stream,
+                      workspace=bufs.attn_workspace)
     return bufs.out
 
 
@@ -374,7 +393,8 @@ def crisp_prefill_tokens(dims: crisp_dims, cfg: crisp_cfg, q, k, v, bufs: CrispB
     crisp_route(dims, cfg, None, bufs.c_struct, bufs.route, stream, block_mass=bufs.block_mass)
     crisp_select_tokens(dims, cfg, q, k, bufs.block_mass, bufs.col_mass, bufs.route, bufs.blocks, bufs.cols,
                         bufs.ncols, bufs.col_below, bufs.workspace, stream)
-    crisp_sparse_attn(dims, q, k, v, bufs.blocks["count"], bufs.blocks["idx"], bufs.out, bufs.lse, stream)
+    crisp_sparse_attn(dims, q, k, v, bufs.blocks["count"], bufs.blocks["idx"], bufs.out, bufs.lse, stream,
+                      workspace=bufs.attn_workspace)
     crisp_sparse_attn_cols(dims, q, k, v, bufs.blocks["count"], bufs.blocks["idx"], bufs.cols, bufs.col_below,
                            bufs.out, bufs.lse, stream)
     return bufs.out

@@ -44,8 +44,18 @@ KERNEL_ONLY_FLAGS = ["-fno-honor-nans"]
 HOST_VALIDATION_SOURCES = ("api.hip",)
 
 
+# The attention kernel wraps each (head, query block) item in a loop over
+# claimed items.  Machine-level loop-invariant code motion would hoist the
+# constants of an item's prologue and epilogue out of that loop and hold them
+# in scalar registers across the item's main loop, which then spills; the
+# main loop itself gains nothing from it (its invariants are written outside
+# it already).
+PER_SOURCE_FLAGS = {"attn.hip": ["-mllvm", "-disable-machine-licm"]}
+
+
 def flags_for(src):
-    return FLAGS + ([] if src in HOST_VALIDATION_SOURCES else KERNEL_ONLY_FLAGS)
+    return (FLAGS + ([] if src in HOST_VALIDATION_SOURCES else KERNEL_ONLY_FLAGS)
+            + PER_SOURCE_FLAGS.get(src, []))
 
 
 def _compile(src):

@@ -186,6 +186,7 @@ struct PrefillCarve {
   float* mass;
   float* c_struct;
   int32_t* route;
+  int* queue;
   size_t bytes;
 };
 
@@ -204,12 +205,15 @@ PrefillCarve carve_prefill(void* ws, int hq, int hkv, int n) {
   off += round_carve((size_t)hq * sizeof(float));
   c.route = (int32_t*)(p + off);
   off += round_carve((size_t)hq * sizeof(int32_t));
+  c.queue = (int*)(p + off);
+  off += round_carve(crisp::kAttnQueueBytes);
   c.bytes = off;
   return c;
 }
 
 crisp_status attn_common(const crisp_dims* dims, const void* q, const void* k, const void* v, const int32_t* count,
-                         const int32_t* idx, void* out, int32_t out_is_fp32, float* lse, bool dense, void* stream) {
+                         const int32_t* idx, void* out, int32_t out_is_fp32, float* lse, bool dense, void* workspace,
+                         size_t workspace_bytes, void* stream) {
   CRISP_TRY(check_dims(dims));
   CRISP_TRY(check_ptr(q));
   CRISP_TRY(check_ptr(k));
@@ -221,10 +225,12 @@ crisp_status attn_common(const crisp_dims* dims, const void* q, const void* k, c
   CRISP_TRY(check_ptr(out));
   CRISP_TRY(check_opt(lse));
   if (out_is_fp32 != 0 && out_is_fp32 != 1) return CRISP_ERR_PARAM;
+  CRISP_TRY(check_ptr(workspace));
+  if (workspace_bytes < crisp::kAttnQueueBytes) return CRISP_ERR_WORKSPACE;
   CRISP_TRY(check_device());
   return launched(crisp::launch_attention((const __bf16*)q, (const __bf16*)k, (const __bf16*)v, count, idx, out,
                                           out_is_fp32, lse, dims->num_q_heads, dims->num_kv_heads, dims->seq_len,
-                                          dims->scale, dense, (hipStream_t)stream));
+                                          dims->scale, dense, (int*)workspace, (hipStream_t)stream));
 }
 
 }  // namespace
@@ -369,10 +375,15 @@ size_t crisp_list_capacity(const crisp_dims* dims) {
   return (size_t)dims->num_q_heads * (N * (N + 1) / 2);
 }
 
+size_t crisp_attn_workspace_bytes(const crisp_dims* dims) {
+  if (check_dims(dims) != CRISP_OK) return 0;
+  return crisp::kAttnQueueBytes;
+}
+
 crisp_status crisp_sparse_attn(const crisp_dims* dims, const void* q, const void* k, const void* v,
                                const int32_t* count, const int32_t* idx, void* out, int32_t out_is_fp32, float* lse,
-                               void* stream) {
-  return attn_common(dims, q, k, v, count, idx, out, out_is_fp32, lse, false, stream);
+                               void* workspace, size_t workspace_bytes, void* stream) {
+  return attn_common(dims, q, k, v, count, idx, out, out_is_fp32, lse, false, workspace, workspace_bytes, stream);
 }
 
 crisp_status crisp_sparse_attn_cols(const crisp_dims* dims, const void* q, const void* k, const void* v,
@@ -395,8 +406,10 @@ crisp_status crisp_sparse_attn_cols(const crisp_dims* dims, const void* q, const
 }
 
 crisp_status crisp_dense_attn(const crisp_dims* dims, const void* q, const void* k, const void* v, void* out,
-                              int32_t out_is_fp32, float* lse, void* stream) {
-  return attn_common(dims, q, k, v, nullptr, nullptr, out, out_is_fp32, lse, true, stream);
+                              int32_t out_is_fp32, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream) {
+  return attn_common(dims, q, k, v, nullptr, nullptr, out, out_is_fp32, lse, true, workspace, workspace_bytes,
+                     stream);
 }
 
 size_t crisp_prefill_workspace_bytes(const crisp_dims* dims) {
@@ -431,7 +444,7 @@ crisp_status crisp_prefill(const crisp_dims* dims, const crisp_cfg* cfg, int32_t
   const hipStream_t st = (hipStream_t)stream;
   if (n < gate)
     return launched(crisp::launch_attention((const __bf16*)q, (const __bf16*)k, (const __bf16*)v, nullptr, nullptr,
-                                            out, out_is_fp32, lse, hq, hkv, n, dims->scale, true, st));
+                                            out, out_is_fp32, lse, hq, hkv, n, dims->scale, true, w.queue, st));
   float* mass = block_mass ? block_mass : w.mass;
   float* cs = c_struct ? c_struct : w.c_struct;
   int32_t* rt = route ? route : w.route;
@@ -441,7 +454,8 @@ crisp_status crisp_prefill(const crisp_dims* dims, const crisp_cfg* cfg, int32_t
                                          cfg->route_override, st)));
   CRISP_TRY(select_launch(dims, cfg, false, 0.f, q, k, nullptr, mass, rt, blocks, w.select_ws, nullptr, stream));
   return launched(crisp::launch_attention((const __bf16*)q, (const __bf16*)k, (const __bf16*)v, blocks->count,
-                                          blocks->idx, out, out_is_fp32, lse, hq, hkv, n, dims->scale, false, st));
+                                          blocks->idx, out, out_is_fp32, lse, hq, hkv, n, dims->scale, false, w.queue,
+                                          st));
 }
 
 const char* crisp_status_string(crisp_status status) {
@@ -458,6 +472,6 @@ const char* crisp_status_string(crisp_status status) {
   return "unknown status";
 }
 
-int32_t crisp_abi_version(void) { return (3 << 16) | 1; }
+int32_t crisp_abi_version(void) { return (4 << 16) | 0; }
 
 }  // extern "C"

@@ -51,24 +51,29 @@ struct AttnArgs {
   float scale_log2;
   int out_fp32;
   RowMap map;
+  int* queue;  // 8 claim counters, zero at launch
+  int items;   // Hq * nblk
 };
 
 // Key index (0..31) held by accumulator register v of lane group lg.
 __device__ __forceinline__ int acc_key(int v, int lg) { return (v < 8) ? (8 * lg + v) : (16 + 8 * lg + (v - 8)); }
 
-template <bool kDense, bool kRagged>
-__global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
-  // 32 KiB of V stages (tiles 0-1) then 48 KiB of K stages (tiles 2-4): two
-  // workgroups fill a CU's 160 KiB.  With V first, every stage offset of a
-  // statically known stage fits the 16-bit immediate of an LDS read.
-  __shared__ __attribute__((aligned(1024))) __bf16 lds[2 + kKStages][kStep * kHeadDim];
+typedef __bf16 AttnLds[2 + kKStages][kStep * kHeadDim];
+
+// One (head, query block) item.  Leaves LDS in use until its last read of
+// the output staging; the caller synchronises before reusing it.
+template <bool kDense, bool kRagged, typename LoopEnd>
+__device__ __forceinline__ void attend(const AttnArgs& p, AttnLds& lds, int h, int qb, int w, LoopEnd&& loop_end) {
   auto kstage = [&](int i) -> __bf16* { return lds[2 + i]; };
   auto vstage = [&](int i) -> __bf16* { return lds[i]; };
 
-  int h, qb;
-  map_row(p.map, blockIdx.x, &h, &qb);
   const int g = h / p.qpg;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // w: the wave index (scalar).  The lane index comes from an asm statement
+  // the compiler may not move: otherwise it computes every offset derived
+  // from the thread index once, before the item loop, and keeps them all
+  // live (and spilled) across it.
+  const int lane = opaque_lane();
+  const int tid = 64 * w + lane;
   const int l32 = lane & 31, lg = lane >> 5;
 
   const size_t nd = (size_t)p.n * kHeadDim;
@@ -529,6 +534,7 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   kst = kst == 2 ? 0 : kst + 1;
   iter(j + 1, kb_cur, kb_cur, kb_cur, kb_cur, kst, 1, sb, sa, T{}, F{}, F{}, F{});
 
+  loop_end();
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = 1.f / l_tot;
   // The output goes through LDS (the K/V stages are idle after the last
@@ -586,11 +592,71 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
     p.lse[(size_t)h * p.n + qpos] = (m_run + fast_log2(l_tot)) * kLn2;
 }
 
+// Persistent workgroups, two per CU, take items from eight queues.  Queue x
+// holds the item ids x, x+8, x+16, ... in increasing order, which the row map
+// lays out so that the heads of a KV group stream the same K/V blocks side
+// by side; a workgroup serves the queue of the XCD it runs on (so those
+// heads share that XCD's L2) and, once it is empty, the others in turn.
+// Claiming items one at a time keeps every slot busy whatever the spread of
+// list lengths: the hardware dispatcher, which places workgroups in order,
+// leaves CUs idle behind a slow one, and XCDs that run slower than the rest
+// hand their last items to the others.  A claim is made when the previous
+// item starts, so its latency is hidden; every workgroup leaves once all
+// eight counters have passed the end of their queues.
+template <bool kDense, bool kRagged>
+__global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
+  // 32 KiB of V stages (tiles 0-1) then 48 KiB of K stages (tiles 2-4): two
+  // workgroups fill a CU's 160 KiB.  With V first, every stage offset of a
+  // statically known stage fits the 16-bit immediate of an LDS read.
+  __shared__ __attribute__((aligned(1024))) AttnLds lds;
+  // The next item id passes through the first word of V stage 1, which an
+  // item's first writes (K stages 0-2 and V stage 0) leave alone.
+  int* const next_slot = (int*)lds[1];
+  // Wave 0 claims (its first lane issues the atomic); the claim state is
+  // wave-uniform and stays in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const bool claimer = wave == 0;
+  int queue = __builtin_amdgcn_readfirstlane(xcd_id() & 7), tried = 0;
+  auto claim = [&]() -> int {
+    while (tried < 8) {
+      int old = 0;
+      if (opaque_lane() == 0) old = atomicAdd(p.queue + queue, 1);
+      const int id = 8 * __builtin_amdgcn_readfirstlane(old) + queue;
+      if (id < p.items) return id;
+      queue = (queue + 1) & 7;
+      ++tried;
+    }
+    return -1;
+  };
+  if (claimer) {
+    const int first = claim();
+    if (opaque_lane() == 0) next_slot[0] = first;
+  }
+  __syncthreads();
+  int item = next_slot[0];
+  while (item >= 0) {
+    int next = -1;
+    int h, qb;
+    map_row(p.map, item, &h, &qb);
+    attend<kDense, kRagged>(p, lds, h, qb, wave, [&] {
+      if (claimer) next = claim();
+    });
+    __syncthreads();
+    if (claimer && opaque_lane() == 0) next_slot[0] = next;
+    __syncthreads();
+    item = next_slot[0];
+  }
+}
+
+__global__ void clear_queue_kernel(int* queue) {
+  if (threadIdx.x < 8) queue[threadIdx.x] = 0;
+}
+
 }  // namespace
 
 hipError_t launch_attention(const __bf16* q, const __bf16* k, const __bf16* v, const int32_t* count,
                             const int32_t* idx, void* out, int out_fp32, float* lse, int hq, int hkv, int n,
-                            float scale, bool dense, hipStream_t stream) {
+                            float scale, bool dense, int* queue, hipStream_t stream) {
   AttnArgs a;
   a.q = q;
   a.k = k;
@@ -605,7 +671,14 @@ hipError_t launch_attention(const __bf16* q, const __bf16* k, const __bf16* v, c
   a.scale_log2 = scale * kLog2e;
   a.out_fp32 = out_fp32;
   a.map = make_row_map(hq, hkv, a.nblk);
-  const unsigned grid = (unsigned)hq * (unsigned)a.nblk;
+  a.queue = queue;
+  a.items = hq * a.nblk;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  const unsigned grid = (unsigned)min(a.items, 2 * max(cus, 1));
+  hipLaunchKernelGGL(clear_queue_kernel, dim3(1), dim3(64), 0, stream, queue);
   const bool ragged = n % kBlock != 0;
   if (dense && ragged)
     hipLaunchKernelGGL((fa_fwd_kernel<true, true>), dim3(grid), dim3(256), 0, stream, a);

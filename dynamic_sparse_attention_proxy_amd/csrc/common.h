@@ -57,6 +57,18 @@ __device__ __forceinline__ void wait_dma() { asm volatile("s_waitcnt vmcnt(0)" :
 // The same, except for the 4 most recently issued ones (loads complete in order).
 __device__ __forceinline__ void wait_dma_but_4() { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); }
 
+// Lane index (0..63) from an asm statement with side effects, recomputed
+// wherever it is written: a loop cannot hoist it or anything derived from it.
+__device__ __forceinline__ int opaque_lane() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// Index of the XCD (one of the 8 compute dies, each with its own L2) the
+// calling wave runs on: bits 0-3 of the XCC_ID hardware register (id 20).
+__device__ __forceinline__ int xcd_id() { return __builtin_amdgcn_s_getreg((3 << 11) | 20); }
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

@@ -84,6 +84,8 @@ hipError_t launch_col_attention(const __bf16* q, const __bf16* k, const __bf16* 
 
 hipError_t launch_attention(const __bf16* q, const __bf16* k, const __bf16* v, const int32_t* count,
                             const int32_t* idx, void* out, int out_fp32, float* lse, int hq, int hkv, int n,
-                            float scale, bool dense, hipStream_t stream);
+                            float scale, bool dense, int* queue, hipStream_t stream);
+// Device bytes of the attention kernels' work queue (the `queue` above).
+constexpr size_t kAttnQueueBytes = 256;
 
 }  // namespace crisp

@@ -229,16 +229,26 @@ CRISP_API size_t crisp_list_capacity(const crisp_dims* dims);
  * read stays inside the head's rows; the result is only meaningful for a
  * well-formed list (a repeated entry counts its keys twice).
  * out: [Hq][n][d], bf16 when out_is_fp32 = 0, fp32 otherwise.
- * lse (optional, [Hq][n] fp32): natural log of each row's sum of exp. */
+ * lse (optional, [Hq][n] fp32): natural log of each row's sum of exp.
+ * workspace: crisp_attn_workspace_bytes(dims) bytes of device memory, any
+ * contents; it holds the work queue the kernel's workgroups take (head,
+ * query block) items from, cleared by the call on `stream` (so two calls
+ * in flight at once need two workspaces).  Smaller: CRISP_ERR_WORKSPACE. */
 CRISP_API crisp_status crisp_sparse_attn(const crisp_dims* dims, const void* q, const void* k, const void* v,
                                const int32_t* count, const int32_t* idx, void* out, int32_t out_is_fp32,
-                               float* lse, void* stream);
+                               float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
 /* Dense causal attention with the same kernel and output conventions
  * (every key block 0..qb): the exact baseline the speedups are measured
- * against (ai.info summary, "Main Findings"). */
+ * against (ai.info summary, "Main Findings").  workspace: as
+ * crisp_sparse_attn. */
 CRISP_API crisp_status crisp_dense_attn(const crisp_dims* dims, const void* q, const void* k, const void* v, void* out,
-                              int32_t out_is_fp32, float* lse, void* stream);
+                              int32_t out_is_fp32, float* lse, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
+/* Bytes of the workspace crisp_sparse_attn and crisp_dense_attn take (0 for
+ * unsupported dims). */
+CRISP_API size_t crisp_attn_workspace_bytes(const crisp_dims* dims);
 
 /* Token-granular Vertical-Slash (ai-feeds summary, method module 2: keep
  * the tokens whose mass stands clearly above the noise floor; ai.info

@@ -26,7 +26,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 19
+    assert len(names) == 20
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -37,8 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert B.crisp_abi_version() >> 16 == 3
-    assert B.crisp_abi_version() & 0xffff >= 1  # crisp_prefill
+    assert B.crisp_abi_version() >> 16 == 4  # attention calls take a workspace
     lib = B.lib()
     for s in range(8):
         assert lib.crisp_status_string(s)
@@ -64,8 +63,8 @@ def test_sizes():
     assert B.crisp_proxy_scratch_bytes(r) >= 4 * 8 * 128 * 16
 
 
-def _dense(dims, q=P16, k=P16, v=P16, out=P16, fp32=0, lse=None):
-    return B.lib().crisp_dense_attn(ctypes.byref(dims), q, k, v, out, fp32, lse, None)
+def _dense(dims, q=P16, k=P16, v=P16, out=P16, fp32=0, lse=None, ws=P16, ws_bytes=1 << 20):
+    return B.lib().crisp_dense_attn(ctypes.byref(dims), q, k, v, out, fp32, lse, ws, ws_bytes, None)
 
 
 @pytest.mark.parametrize("hq,hkv,n,d,blk,status", [
@@ -92,7 +91,16 @@ def test_pointer_and_param_errors():
     bad_scale = B.crisp_dims(4, 2, 1024, 128, 128, -1.0)
     assert _dense(bad_scale) == 3
     lib = B.lib()
-    assert lib.crisp_sparse_attn(ctypes.byref(dims), P16, P16, P16, None, P16, P16, 0, None, None) == 1
+    assert lib.crisp_sparse_attn(ctypes.byref(dims), P16, P16, P16, None, P16, P16, 0, None, P16, 1 << 20,
+                                 None) == 1
+    # the attention work queue: required, and at least crisp_attn_workspace_bytes
+    need = B.crisp_attn_workspace_bytes(dims)
+    assert 32 <= need <= 4096
+    assert _dense(dims, ws=None) == 1
+    assert _dense(dims, ws_bytes=need - 1) == 5
+    assert lib.crisp_sparse_attn(ctypes.byref(dims), P16, P16, P16, P16, P16, P16, 0, None, P16, need - 1,
+                                 None) == 5
+    assert B.crisp_attn_workspace_bytes(B.make_dims(32, 8, 255)) == 0
     # proxy scratch too small
     assert lib.crisp_proxy(ctypes.byref(dims), P16, P16, P16, None, None, P16, 16, None) == 5
     assert lib.crisp_proxy(None, P16, P16, P16, None, None, P16, 1 << 30, None) == 1
@@ -275,7 +283,8 @@ def test_prefill_marshalling_and_composed_chains(monkeypatch):
 
     bufs = types.SimpleNamespace(out=torch.empty(1), lse=None, attn_map=None, block_mass=None, row_lse=None,
                                  partials=None, c_struct=None, route=None, blocks={"count": None, "idx": None},
-                                 workspace=None, prefill_workspace=torch.empty(16, dtype=torch.uint8))
+                                 workspace=None, prefill_workspace=torch.empty(16, dtype=torch.uint8),
+                                 attn_workspace=None)
     monkeypatch.setattr(B, "_stream", lambda s: None)
     cfg = B.make_cfg()
     for n in (1024, B.DENSE_BELOW, 4 * B.DENSE_BELOW):
@@ -305,7 +314,7 @@ def test_prefill_validation():
     dims = B.make_dims(4, 2, 1024)
     ws = B.crisp_prefill_workspace_bytes(dims)
     ps, ss = B.crisp_proxy_scratch_bytes(dims), B.crisp_select_workspace_bytes(dims)
-    assert ws >= -(-ps // 256) * 256 + ss
+    assert ws >= -(-ps // 256) * 256 + ss + B.crisp_attn_workspace_bytes(dims)
     assert B.crisp_prefill_workspace_bytes(B.make_dims(4, 2, 255)) == 0
     blocks = B.crisp_blocks()
     blocks.count = P16

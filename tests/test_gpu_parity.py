@@ -205,6 +205,50 @@ def test_sparse_attention_matches_oracle_on_given_lists(hq, hkv, n, kind):
         assert bool((outc[hq * n:] == 7.0).all()) and bool((lsec[hq * n:] == 7.0).all())
 
 
+def test_attention_work_queue():
+    """More (head, query block) items than the kernel's persistent
+    workgroups, with list lengths spread from 1 to qb + 1 so that queues
+    drain unevenly and workgroups take items from other XCDs' queues: every
+    row is written exactly as by a call on a fresh workspace, whatever the
+    workspace held before (the call clears its queue), on two calls in a
+    row, and sampled blocks match the oracle."""
+    hq, hkv, n = 8, 2, 16384
+    rng = np.random.default_rng(7)
+    x = synth.make_inputs(synth.custom(hq, hkv, n, seed=11, needles=2), device="cuda")
+    N = B.num_blocks(n)
+    lists = [_random_lists(rng, N, "random") for _ in range(hq)]
+    count, idx = _pack_lists(lists, hq, N)
+    dims = B.make_dims(hq, hkv, n)
+    wsb = B.crisp_attn_workspace_bytes(dims)
+    print(f"[work queue] hq={hq} n={n} items={hq * N} workspace={wsb}", flush=True)
+    outs = []
+    for fill in (0, 0x7F, 0xFF, 0x7F):
+        ws = torch.full((wsb,), fill, dtype=torch.uint8, device="cuda")
+        out = torch.full((hq, n, 128), float("nan"), dtype=torch.float32, device="cuda")
+        lse = torch.full((hq, n), float("nan"), dtype=torch.float32, device="cuda")
+        B.crisp_sparse_attn(dims, x.q, x.k, x.v, count, idx, out, lse, workspace=ws)
+        B.crisp_sparse_attn(dims, x.q, x.k, x.v, count, idx, out, lse, workspace=ws)
+        torch.cuda.synchronize()
+        assert not bool(out.isnan().any()) and not bool(lse.isnan().any()), fill
+        outs.append((out, lse))
+    for out, lse in outs[1:]:
+        assert torch.equal(out, outs[0][0]) and torch.equal(lse, outs[0][1])
+    out, lse = outs[0]
+    for h in (0, 5):
+        g = h * hkv // hq
+        qbs = [0, 1, N // 2, N - 2, N - 1]
+        ref = O.attention_rows(to64(x.q[h]), to64(x.k[g]), to64(x.v[g]), lists[h], dims.scale, qbs)
+        og, lg = out[h].cpu().numpy(), lse[h].cpu().numpy()
+        for qb in qbs:
+            check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"h {h} qb {qb}")
+            check_lse(lg[qb * BLK:(qb + 1) * BLK], ref[qb][1])
+    dense = torch.full((hq, n, 128), float("nan"), dtype=torch.float32, device="cuda")
+    ws = torch.full((wsb,), 0x55, dtype=torch.uint8, device="cuda")
+    B.crisp_dense_attn(dims, x.q, x.k, x.v, dense, workspace=ws)
+    torch.cuda.synchronize()
+    assert not bool(dense.isnan().any())
+
+
 # ---------------------------------------------------------------------------
 # proxy, route, selection on the single-head 4k workload
 # ---------------------------------------------------------------------------
