@@ -259,7 +259,7 @@ def timed_token_chain(torch, B, x, dims, tb, cfg, steps, warmup):
                             workspace=tb.attn_workspace)
         mark()
         B.crisp_sparse_attn_cols(dims, x.q, x.k, x.v, tb.blocks["count"], tb.blocks["idx"], tb.cols, tb.col_below,
-                                 tb.out, tb.lse)
+                                 tb.out, tb.lse, workspace=tb.attn_workspace)
         mark()
         if marks is not None:
             marks.append(t)

@@ -64,7 +64,8 @@ _SIGS = {
     "crisp_proxy_cols": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "crisp_select_tokens": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), _P, _P, _P, _P,
                                            _P, ctypes.POINTER(crisp_blocks), _P, _P, _P, _P, ctypes.c_size_t, _P]),
-    "crisp_sparse_attn_cols": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P]),
+    "crisp_sparse_attn_cols": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, _P, _P, _P, _P, _P, _P,
+                                              ctypes.c_size_t, _P]),
     "crisp_route_jsd": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.c_float, _P, _P, _P, _P, _P, _P, _P,
                                        ctypes.c_size_t, _P]),
     "crisp_route_jsd_workspace_bytes": (ctypes.c_size_t, [ctypes.POINTER(crisp_dims)]),
@@ -245,15 +246,6 @@ def crisp_select_tokens(dims: crisp_dims, cfg: crisp_cfg, q, k, block_mass, col_
                                                             _stream(stream)))
 
 
-def crisp_sparse_attn_cols(dims: crisp_dims, q, k, v, count, idx, cols, col_below, out, lse, stream=None):
-    if out.dtype != torch.float32:
-        raise TypeError("crisp_sparse_attn_cols updates an fp32 output in place")
-    _check("crisp_sparse_attn_cols", lib().crisp_sparse_attn_cols(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
-                                                                  _ptr(count), _ptr(idx), _ptr(cols),
-                                                                  _ptr(col_below), _ptr(out), _ptr(lse),
-                                                                  _stream(stream)))
-
-
 def crisp_attn_workspace_bytes(dims: crisp_dims) -> int:
     return int(lib().crisp_attn_workspace_bytes(ctypes.byref(dims)))
 
@@ -263,6 +255,17 @@ def _attn_workspace(dims, out, workspace):
     if workspace is None:
         workspace = torch.empty(crisp_attn_workspace_bytes(dims), dtype=torch.uint8, device=out.device)
     return workspace
+
+
+def crisp_sparse_attn_cols(dims: crisp_dims, q, k, v, count, idx, cols, col_below, out, lse, stream=None,
+                           workspace=None):
+    if out.dtype != torch.float32:
+        raise TypeError("crisp_sparse_attn_cols updates an fp32 output in place")
+    ws = _attn_workspace(dims, out, workspace)
+    _check("crisp_sparse_attn_cols", lib().crisp_sparse_attn_cols(ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v),
+                                                                  _ptr(count), _ptr(idx), _ptr(cols),
+                                                                  _ptr(col_below), _ptr(out), _ptr(lse), _ptr(ws),
+                                                                  ws.numel() * ws.element_size(), _stream(stream)))
 
 
 def crisp_sparse_attn(dims: crisp_dims, q, k, v, count, idx, out, lse=None, stream=None, workspace=None):
@@ -396,5 +399,5 @@ def crisp_prefill_tokens(dims: crisp_dims, cfg: crisp_cfg, q, k, v, bufs: CrispB
     crisp_sparse_attn(dims, q, k, v, bufs.blocks["count"], bufs.blocks["idx"], bufs.out, bufs.lse, stream,
                       workspace=bufs.attn_workspace)
     crisp_sparse_attn_cols(dims, q, k, v, bufs.blocks["count"], bufs.blocks["idx"], bufs.cols, bufs.col_below,
-                           bufs.out, bufs.lse, stream)
+                           bufs.out, bufs.lse, stream, workspace=bufs.attn_workspace)
     return bufs.out

@@ -388,7 +388,8 @@ crisp_status crisp_sparse_attn(const crisp_dims* dims, const void* q, const void
 
 crisp_status crisp_sparse_attn_cols(const crisp_dims* dims, const void* q, const void* k, const void* v,
                                     const int32_t* count, const int32_t* idx, const int32_t* cols,
-                                    const int32_t* col_below, float* out, float* lse, void* stream) {
+                                    const int32_t* col_below, float* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, void* stream) {
   CRISP_TRY(check_dims(dims));
   CRISP_TRY(check_ptr(q));
   CRISP_TRY(check_ptr(k));
@@ -399,10 +400,12 @@ crisp_status crisp_sparse_attn_cols(const crisp_dims* dims, const void* q, const
   CRISP_TRY(check_ptr(col_below));
   CRISP_TRY(check_ptr(out));
   CRISP_TRY(check_ptr(lse));
+  CRISP_TRY(check_ptr(workspace));
+  if (workspace_bytes < crisp::kAttnQueueBytes) return CRISP_ERR_WORKSPACE;
   CRISP_TRY(check_device());
   return launched(crisp::launch_col_attention((const __bf16*)q, (const __bf16*)k, (const __bf16*)v, count, idx, cols,
                                               col_below, out, lse, dims->num_q_heads, dims->num_kv_heads,
-                                              dims->seq_len, dims->scale, (hipStream_t)stream));
+                                              dims->seq_len, dims->scale, (int*)workspace, (hipStream_t)stream));
 }
 
 crisp_status crisp_dense_attn(const crisp_dims* dims, const void* q, const void* k, const void* v, void* out,
@@ -472,6 +475,6 @@ const char* crisp_status_string(crisp_status status) {
   return "unknown status";
 }
 
-int32_t crisp_abi_version(void) { return (4 << 16) | 0; }
+int32_t crisp_abi_version(void) { return (5 << 16) | 0; }
 
 }  // extern "C"

@@ -600,9 +600,13 @@ __device__ __forceinline__ void attend(const AttnArgs& p, AttnLds& lds, int h, i
 // Claiming items one at a time keeps every slot busy whatever the spread of
 // list lengths: the hardware dispatcher, which places workgroups in order,
 // leaves CUs idle behind a slow one, and XCDs that run slower than the rest
-// hand their last items to the others.  A claim is made when the previous
-// item starts, so its latency is hidden; every workgroup leaves once all
-// eight counters have passed the end of their queues.
+// hand their last items to the others.  The next item is claimed when the
+// current one's main loop ends, so the claim's latency hides behind the
+// output and items start in the order their slots free up, as under
+// hardware dispatch.  (Claiming it when the current item starts reorders
+// the items: heads of a group then stream their blocks further apart,
+// which measured 2.6 times the L2 misses and a 5% lower clock.)  Every
+// workgroup leaves once all eight counters have passed their queue ends.
 template <bool kDense, bool kRagged>
 __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   // 32 KiB of V stages (tiles 0-1) then 48 KiB of K stages (tiles 2-4): two
@@ -616,7 +620,9 @@ __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   // wave-uniform and stays in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
   const bool claimer = wave == 0;
-  int queue = __builtin_amdgcn_readfirstlane(xcd_id() & 7), tried = 0;
+  // The dispatcher deals workgroups to the XCDs round-robin, so workgroup b
+  // runs on XCD b mod 8 and starts with that XCD's queue.
+  int queue = (int)(blockIdx.x & 7), tried = 0;
   auto claim = [&]() -> int {
     while (tried < 8) {
       int old = 0;

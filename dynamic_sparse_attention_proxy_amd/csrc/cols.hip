@@ -56,22 +56,33 @@ struct ColArgs {
   int qpg;
   float scale_log2;
   RowMap map;                // over pairs of query blocks
+  int* queue;                // 8 claim counters, zero at launch
+  int items;                 // Hq * pairs
+};
+
+struct ColLds {
+  __bf16 kst[kCStages][kCStep * kHeadDim];
+  __bf16 vst[kCStages][kCStep * kHeadDim];
+  int32_t cidx[2][kIdxChunk];
+  uint32_t tbits[2][kMaxTiles / 32];
+  int next_item;
 };
 
 // Key slot (0..31 within a 32-key half) of accumulator register v of lane
 // group lg, for the permuted K-operand rows below.
 __device__ __forceinline__ int slot_of(int v, int lg) { return (v < 8) ? (8 * lg + v) : (16 + 8 * lg + (v - 8)); }
 
-__global__ __launch_bounds__(kColThreads, 1) void col_attn_kernel(ColArgs p) {
-  __shared__ __attribute__((aligned(1024))) __bf16 kst[kCStages][kCStep * kHeadDim];
-  __shared__ __attribute__((aligned(1024))) __bf16 vst[kCStages][kCStep * kHeadDim];
-  __shared__ __attribute__((aligned(16))) int32_t cidx[2][kIdxChunk];
-  __shared__ uint32_t tbits[2][kMaxTiles / 32];
-
-  int h, pi;
-  map_row(p.map, blockIdx.x, &h, &pi);
+// One (head, pair of query blocks) item.  Every wave returns having passed
+// the same barriers; the caller synchronises before reusing LDS.
+__device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int pi) {
+  auto& kst = L.kst;
+  auto& vst = L.vst;
+  auto& cidx = L.cidx;
+  auto& tbits = L.tbits;
   const int N = p.nblk;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  // The lane index comes from an asm statement the compiler may not hoist
+  // out of the item loop (see opaque_lane).
+  const int lane = opaque_lane(), w = (int)threadIdx.x >> 6, tid = 64 * w + lane;
   const int l32 = lane & 31, lg = lane >> 5;
   const int blk = w >> 2, wq = w & 3;
   const int qa = 2 * pi, qb2 = 2 * pi + 1;
@@ -425,17 +436,61 @@ __global__ __launch_bounds__(kColThreads, 1) void col_attn_kernel(ColArgs p) {
       const f32x4 t = *ptr;
       f32x4 r;
 #pragma unroll
-      for (int c = 0; c < 4; ++c) r[c] = (t[c] * w1 + o[db][4 * a + c] * wc) * inv;
+      for (int c = 0; c < 4; ++c) r[c] = fmaf(t[c], w1, o[db][4 * a + c] * wc) * inv;
       *ptr = r;
     }
   if (lg == 0) p.lse[row] = (M + fast_log2(denom)) * kLn2;
+}
+
+// Persistent workgroups, one per CU, take items from eight queues as the
+// tile kernel does (queue x holds item ids x, x+8, ..., heaviest first per
+// KV group; a workgroup starts with its XCD's queue, then takes from the
+// others).  Item costs spread from a few microseconds to milliseconds (the
+// kept columns below a pair grow with its position), which hardware
+// dispatch, placing workgroups in order, turns into idle CUs.  The next
+// item is claimed once the current one is done, so items start in the order
+// their CUs free up.
+__global__ __launch_bounds__(kColThreads, 1) void col_attn_kernel(ColArgs p) {
+  __shared__ __attribute__((aligned(1024))) ColLds L;
+  const int wave = __builtin_amdgcn_readfirstlane((int)threadIdx.x >> 6);
+  const bool claimer = wave == 0;
+  // workgroup b runs on XCD b mod 8 (round-robin dispatch)
+  int queue = (int)(blockIdx.x & 7), tried = 0;
+  auto claim = [&]() -> int {
+    while (tried < 8) {
+      int old = 0;
+      if (opaque_lane() == 0) old = atomicAdd(p.queue + queue, 1);
+      const int id = 8 * __builtin_amdgcn_readfirstlane(old) + queue;
+      if (id < p.items) return id;
+      queue = (queue + 1) & 7;
+      ++tried;
+    }
+    return -1;
+  };
+  for (;;) {
+    if (claimer) {
+      const int next = claim();
+      if (opaque_lane() == 0) L.next_item = next;
+    }
+    __syncthreads();
+    const int item = L.next_item;
+    if (item < 0) break;
+    int h, pi;
+    map_row(p.map, item, &h, &pi);
+    col_item(p, L, h, pi);
+    __syncthreads();
+  }
+}
+
+__global__ void clear_col_queue_kernel(int* queue) {
+  if (threadIdx.x < 8) queue[threadIdx.x] = 0;
 }
 
 }  // namespace
 
 hipError_t launch_col_attention(const __bf16* q, const __bf16* k, const __bf16* v, const int32_t* count,
                                 const int32_t* idx, const int32_t* cols, const int32_t* col_below, float* out,
-                                float* lse, int hq, int hkv, int n, float scale, hipStream_t stream) {
+                                float* lse, int hq, int hkv, int n, float scale, int* queue, hipStream_t stream) {
   ColArgs a;
   a.q = q;
   a.k = k;
@@ -452,7 +507,14 @@ hipError_t launch_col_attention(const __bf16* q, const __bf16* k, const __bf16* 
   a.scale_log2 = scale * kLog2e;
   const int npairs = (a.nblk + 1) / 2;
   a.map = make_row_map(hq, hkv, npairs);
-  hipLaunchKernelGGL(col_attn_kernel, dim3((unsigned)hq * (unsigned)npairs), dim3(kColThreads), 0, stream, a);
+  a.queue = queue;
+  a.items = hq * npairs;
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e == hipSuccess) e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(clear_col_queue_kernel, dim3(1), dim3(64), 0, stream, queue);
+  hipLaunchKernelGGL(col_attn_kernel, dim3((unsigned)min(a.items, max(cus, 1))), dim3(kColThreads), 0, stream, a);
   return hipGetLastError();
 }
 

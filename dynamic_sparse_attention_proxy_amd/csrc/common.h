@@ -65,10 +65,6 @@ __device__ __forceinline__ int opaque_lane() {
   return l;
 }
 
-// Index of the XCD (one of the 8 compute dies, each with its own L2) the
-// calling wave runs on: bits 0-3 of the XCC_ID hardware register (id 20).
-__device__ __forceinline__ int xcd_id() { return __builtin_amdgcn_s_getreg((3 << 11) | 20); }
-
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 __device__ __forceinline__ float fast_log2(float x) { return __builtin_amdgcn_logf(x); }
 

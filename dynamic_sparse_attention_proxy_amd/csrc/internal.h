@@ -80,12 +80,13 @@ hipError_t launch_route_jsd(const __bf16* q, const __bf16* k, const float* mass,
 // read and updated in place).
 hipError_t launch_col_attention(const __bf16* q, const __bf16* k, const __bf16* v, const int32_t* count,
                                 const int32_t* idx, const int32_t* cols, const int32_t* col_below, float* out,
-                                float* lse, int hq, int hkv, int n, float scale, hipStream_t stream);
+                                float* lse, int hq, int hkv, int n, float scale, int* queue, hipStream_t stream);
 
 hipError_t launch_attention(const __bf16* q, const __bf16* k, const __bf16* v, const int32_t* count,
                             const int32_t* idx, void* out, int out_fp32, float* lse, int hq, int hkv, int n,
                             float scale, bool dense, int* queue, hipStream_t stream);
-// Device bytes of the attention kernels' work queue (the `queue` above).
+// Device bytes of the attention kernels' work queues (the `queue` arguments
+// of launch_attention and launch_col_attention).
 constexpr size_t kAttnQueueBytes = 256;
 
 }  // namespace crisp

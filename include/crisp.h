@@ -246,8 +246,8 @@ CRISP_API crisp_status crisp_dense_attn(const crisp_dims* dims, const void* q, c
                               int32_t out_is_fp32, float* lse, void* workspace, size_t workspace_bytes,
                               void* stream);
 
-/* Bytes of the workspace crisp_sparse_attn and crisp_dense_attn take (0 for
- * unsupported dims). */
+/* Bytes of the workspace crisp_sparse_attn, crisp_dense_attn and
+ * crisp_sparse_attn_cols take (0 for unsupported dims). */
 CRISP_API size_t crisp_attn_workspace_bytes(const crisp_dims* dims);
 
 /* Token-granular Vertical-Slash (ai-feeds summary, method module 2: keep
@@ -291,10 +291,12 @@ CRISP_API crisp_status crisp_select_tokens(const crisp_dims* dims, const crisp_c
  * cols[h][0 .. col_below[h][qb]) that lie outside the listed tiles; the two
  * softmaxes are merged exactly and out/lse updated in place.  Column
  * entries are clamped to [0, 128 qb - 1] and counts to [0, n]; entries must
- * be distinct for the result to mean anything. */
+ * be distinct for the result to mean anything.  workspace: as
+ * crisp_sparse_attn (crisp_attn_workspace_bytes bytes, any contents). */
 CRISP_API crisp_status crisp_sparse_attn_cols(const crisp_dims* dims, const void* q, const void* k, const void* v,
                                     const int32_t* count, const int32_t* idx, const int32_t* cols,
-                                    const int32_t* col_below, float* out, float* lse, void* stream);
+                                    const int32_t* col_below, float* out, float* lse, void* workspace,
+                                    size_t workspace_bytes, void* stream);
 
 /* Comparison routing signal - FlexPrefill's Jensen-Shannon routing, the one
  * C_struct replaces (ai.info summary, "Key Contributions" items 1 and 2:

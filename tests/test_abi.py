@@ -37,7 +37,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_abi_version_and_status_strings():
-    assert B.crisp_abi_version() >> 16 == 4  # attention calls take a workspace
+    assert B.crisp_abi_version() >> 16 == 5  # every attention call takes a work-queue workspace
     lib = B.lib()
     for s in range(8):
         assert lib.crisp_status_string(s)
@@ -100,6 +100,10 @@ def test_pointer_and_param_errors():
     assert _dense(dims, ws_bytes=need - 1) == 5
     assert lib.crisp_sparse_attn(ctypes.byref(dims), P16, P16, P16, P16, P16, P16, 0, None, P16, need - 1,
                                  None) == 5
+    assert lib.crisp_sparse_attn_cols(ctypes.byref(dims), P16, P16, P16, P16, P16, P16, P16, P16, P16, None, 1 << 20,
+                                      None) == 1
+    assert lib.crisp_sparse_attn_cols(ctypes.byref(dims), P16, P16, P16, P16, P16, P16, P16, P16, P16, P16, need - 1,
+                                      None) == 5
     assert B.crisp_attn_workspace_bytes(B.make_dims(32, 8, 255)) == 0
     # proxy scratch too small
     assert lib.crisp_proxy(ctypes.byref(dims), P16, P16, P16, None, None, P16, 16, None) == 5

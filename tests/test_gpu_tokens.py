@@ -129,13 +129,15 @@ def test_token_chain_attention_matches_oracle():
             check_lse(lse[h, rows], ref[qb][1])
 
 
-@pytest.mark.parametrize("ncol,n", [(1, 2048), (64, 2048), (200, 2176), (3000, 8192)])
-def test_column_kernel_on_given_lists_and_columns(ncol, n):
+@pytest.mark.parametrize("ncol,n,hq,hkv", [(1, 2048, 4, 2), (64, 2048, 4, 2), (200, 2176, 4, 2), (3000, 8192, 4, 2),
+                                           (2500, 16384, 16, 4)])
+def test_column_kernel_on_given_lists_and_columns(ncol, n, hq, hkv):
     """crisp_sparse_attn_cols on random tile lists and random columns: some
     inside listed tiles, counts that leave partial 64-column steps, an odd
-    number of query blocks (a pair with one block), and more columns than
-    one staged index chunk (2048)."""
-    hq, hkv = 4, 2
+    number of query blocks (a pair with one block), more columns than one
+    staged index chunk (2048), and more (head, pair) items than CUs, so that
+    each persistent workgroup takes several and queues drain unevenly; a
+    workspace left full of garbage gives the same result."""
     N = B.num_blocks(n)
     x = _inputs(hq, hkv, n, 53 + ncol)
     dims = B.make_dims(hq, hkv, n)
@@ -161,9 +163,14 @@ def test_column_kernel_on_given_lists_and_columns(ncol, n):
     cd, idd, cold, bd = (torch.from_numpy(a).cuda() for a in (count, idx, cols, below))
     out = torch.empty((hq, n, 128), dtype=torch.float32, device="cuda")
     lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    print(f"[cols] hq={hq} n={n} ncol={ncol} items={hq * ((N + 1) // 2)}", flush=True)
     B.crisp_sparse_attn(dims, x.q, x.k, x.v, cd, idd, out, lse)
+    out2, lse2 = out.clone(), lse.clone()
     B.crisp_sparse_attn_cols(dims, x.q, x.k, x.v, cd, idd, cold, bd, out, lse)
+    junk = torch.full((B.crisp_attn_workspace_bytes(dims),), 0xFF, dtype=torch.uint8, device="cuda")
+    B.crisp_sparse_attn_cols(dims, x.q, x.k, x.v, cd, idd, cold, bd, out2, lse2, workspace=junk)
     torch.cuda.synchronize()
+    assert torch.equal(out, out2) and torch.equal(lse, lse2)
     og, lg = out.cpu().numpy(), lse.cpu().numpy()
     for h in range(hq):
         g = h * hkv // hq
