@@ -47,7 +47,7 @@ struct SelectBuffers {
   int32_t* n_v;   // [Hq]
   int32_t* n_s;   // [Hq]
   int32_t* kept;  // [2][Hq] kept blocks per direction (workspace only)
-  float* kbar;    // [Hkv][N][128]
+  float* kbar;    // [Hkv][N] pooled keys, 512 bytes each: bf16 hi[128] then lo[128]
 };
 
 size_t select_workspace_bytes(int hq, int hkv, int n);

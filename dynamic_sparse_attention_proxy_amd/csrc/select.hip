@@ -224,7 +224,9 @@ __global__ __launch_bounds__(kVsThreads) void vs_select_kernel(VsArgs p) {
 
 // Mean of the 128 rows of a block, summed in a fixed order: 8 consecutive
 // rows per thread (16 row groups), then the 16 group sums in order.  The
-// query blocks pooled inside pe_logits_kernel follow the same order.
+// query blocks pooled inside pe_logits_kernel follow the same order.  The
+// mean is kept as bf16 hi + lo (the rounding of the fp32 mean and of its
+// remainder).
 __global__ __launch_bounds__(256) void pe_pool_kernel(const __bf16* k, const int32_t* route, float* kbar, int qpg,
                                                       int n) {
   __shared__ float part[16][kHeadDim];
@@ -261,26 +263,17 @@ __global__ __launch_bounds__(256) void pe_pool_kernel(const __bf16* k, const int
     float s = 0.f;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s += part[r][tid];
-    dst[(size_t)kb * kHeadDim + tid] = s / (float)rows;
+    // stored as a bf16 pair, hi + lo (16 significant bits), the operands of
+    // the logit products: the block's 256-element row holds hi[128], lo[128]
+    const float m = s / (float)rows;
+    const __bf16 hi = (__bf16)m;
+    __bf16* row = (__bf16*)dst + (size_t)kb * 2 * kHeadDim;
+    row[tid] = hi;
+    row[kHeadDim + tid] = (__bf16)(m - (float)hi);
   }
 }
 
-// Pooled logit of one (query block, key block) pair: 16 partial dot products
-// over 8 consecutive dimensions each (one fma chain in dimension order),
-// combined as a balanced binary tree of neighbours,
-//   ((p0+p1)+(p2+p3))+((p4+p5)+(p6+p7)) + ((p8+p9)+...+(p14+p15)).
-__device__ __forceinline__ float dot8(f32x4 qa, f32x4 qc, f32x4 ka, f32x4 kc) {
-  float d = qa[0] * ka[0];
-  d = fmaf(qa[1], ka[1], d);
-  d = fmaf(qa[2], ka[2], d);
-  d = fmaf(qa[3], ka[3], d);
-  d = fmaf(qc[0], kc[0], d);
-  d = fmaf(qc[1], kc[1], d);
-  d = fmaf(qc[2], kc[2], d);
-  return fmaf(qc[3], kc[3], d);
-}
-
-constexpr int kPeTile = 16;  // query blocks per pe_logits workgroup
+constexpr int kPeTile = 64;  // query blocks per pe_logits workgroup
 
 struct PeLogitArgs {
   const __bf16* q;
@@ -294,15 +287,29 @@ struct PeLogitArgs {
   float scale_log2;
 };
 
-// One workgroup per (head, 16 consecutive query blocks) of a PE head,
-// heaviest (last) tiles first.  The 16 pooled query rows go to LDS; thread t
-// then owns key block c0 + t of each 256-block chunk and computes its logit
-// against all 16 rows, reading each pooled key once.  The logit of
+// One workgroup per (head, 64 consecutive query blocks) of a PE head,
+// heaviest (last) tiles first.  The 64 pooled query rows go to LDS.  The
+// pooled keys then stream through LDS 32 key blocks at a time (double
+// buffered, each read from L2 once per workgroup), and wave w computes the
+// logits of query rows 16w .. 16w+15 against them with bf16 matrix products
+// on split operands: with x = hi(x) + lo(x) (each bf16), the dot product is
+// taken as lo(q).hi(k) + hi(q).lo(k) + hi(q).hi(k), accumulated in fp32 by
+// v_mfma_f32_16x16x32_bf16 over the 128 dimensions (the dropped lo.lo term
+// and the split leave a relative error near 2^-16 of sum |q_d k_d|).  Lane l
+// supplies dimensions 32c + 8 (l / 16) .. +7 of query row 16w + l % 16 (A)
+// and of key block kb0 + l % 16 (B) for chunk c, and receives the logits of
+// rows 16w + 4 (l / 16) .. +3 against key block kb0 + l % 16.  The logit of
 // (qb, kb), in base 2, is stored as float bits at entry kb of qb's list row.
 __global__ __launch_bounds__(256) void pe_logits_kernel(PeLogitArgs p) {
   constexpr int kPoolBatch = 4;  // query blocks pooled per round, their loads issued together
-  __shared__ float part[kPoolBatch][16][kHeadDim];
+  constexpr int kKeyTile = 32;  // key blocks per LDS tile of pooled keys
+  // the pooling partials and, once the queries are pooled, the key tiles
+  // (double buffered) share one buffer: two workgroups fit a CU
+  __shared__ __attribute__((aligned(16))) float shared_u[2 * kKeyTile * kHeadDim];
   __shared__ __attribute__((aligned(16))) float qs[kPeTile][kHeadDim];
+  static_assert(kPoolBatch * 16 <= 2 * kKeyTile, "pooling partials fit the key-tile buffer");
+  auto& part = *(float (*)[kPoolBatch][16][kHeadDim])shared_u;
+  auto& kt = *(float (*)[2][kKeyTile][kHeadDim])shared_u;
   const int N = p.nblk, tiles = (N + kPeTile - 1) / kPeTile;
   const int h = blockIdx.x % p.hq, tile = tiles - 1 - (int)blockIdx.x / p.hq;
   if (p.route[h] != 0) return;
@@ -356,66 +363,78 @@ __global__ __launch_bounds__(256) void pe_logits_kernel(PeLogitArgs p) {
   }
   const float* kbase = p.kbar + (size_t)(h / p.qpg) * N * kHeadDim;
   int32_t* idx_h = p.idx + (size_t)h * ((size_t)N * (N + 1) / 2);
-  // Thread t owns key blocks c0 + 2t and c0 + 2t + 1 of each 512-block
-  // chunk: every pooled-query read from LDS feeds both.  Slices are taken
-  // two at a time, (2m, 2m+1), whose partials are paired at once; the pair
-  // sums then fold into the tree by m, one uniform branch per pair: levels
-  // st[.][0] = pairs, [1] = quads, [2] = halves.
-  for (int c0 = 0; c0 <= qbmax; c0 += 512) {
-    const int kb0 = c0 + 2 * tid;
-    // rows past the causal range read a valid row, results unused
-    const float* kr0 = kbase + (size_t)min(kb0, qbmax) * kHeadDim;
-    const float* kr1 = kbase + (size_t)min(kb0 + 1, qbmax) * kHeadDim;
-    float st0[kPeTile][3], st1[kPeTile][3];
-#pragma unroll 1
-    for (int m = 0; m < 8; ++m) {
-      f32x4 k0[4], k1[4];
+  const int lane = tid & 63, w = tid >> 6, li = lane & 15, kq = lane >> 4;
+  bf16x8 ahi[4], alo[4];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        k0[u] = *(const f32x4*)(kr0 + 16 * m + 4 * u);
-        k1[u] = *(const f32x4*)(kr1 + 16 * m + 4 * u);
-      }
-      float v0[kPeTile], v1[kPeTile];
+  for (int c = 0; c < 4; ++c)
 #pragma unroll
-      for (int t = 0; t < kPeTile; ++t) {
-        const f32x4 qa = *(const f32x4*)&qs[t][16 * m], qc = *(const f32x4*)&qs[t][16 * m + 4];
-        const f32x4 qe = *(const f32x4*)&qs[t][16 * m + 8], qg = *(const f32x4*)&qs[t][16 * m + 12];
-        v0[t] = dot8(qa, qc, k0[0], k0[1]) + dot8(qe, qg, k0[2], k0[3]);
-        v1[t] = dot8(qa, qc, k1[0], k1[1]) + dot8(qe, qg, k1[2], k1[3]);
-      }
-      if ((m & 1) == 0) {
+    for (int j = 0; j < 8; ++j) {
+      const float x = qs[16 * w + li][32 * c + 8 * kq + j];
+      const __bf16 hi = (__bf16)x;
+      ahi[c][j] = hi;
+      alo[c][j] = (__bf16)(x - (float)hi);
+    }
+  // A key tile is 32 rows of 512 bytes: thread t loads 16-byte pieces
+  // t + 256 e (e < 4); rows past the causal range read a valid row, results
+  // unused.  Tiles are loaded two ahead into registers (two sets in turn) and
+  // written to LDS one ahead, so a load has a whole tile's products to land.
+  auto load_tile = [&](int kb0, f32x4 (&r)[4]) {
 #pragma unroll
-        for (int t = 0; t < kPeTile; ++t) {
-          st0[t][0] = v0[t];
-          st1[t][0] = v1[t];
+    for (int e = 0; e < 4; ++e) {
+      const int piece = tid + 256 * e, row = piece >> 5;
+      r[e] = *(const f32x4*)(kbase + (size_t)min(kb0 + row, qbmax) * kHeadDim + 4 * (piece & 31));
+    }
+  };
+  auto store_tile = [&](int buf, const f32x4 (&r)[4]) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int piece = tid + 256 * e;
+      *(f32x4*)&kt[buf][piece >> 5][4 * (piece & 31)] = r[e];
+    }
+  };
+  const int wq0 = qb0 + 16 * w;  // this wave's first query row
+  auto products = [&](int kb0, int buf) {
+#pragma unroll
+    for (int sub = 0; sub < kKeyTile / 16; ++sub) {
+      const int kbs = kb0 + 16 * sub;
+      if (kbs <= qbmax && kbs <= wq0 + 15 && 16 * w < nt) {  // the wave has rows at or past these blocks
+        const __bf16* krow = (const __bf16*)&kt[buf][16 * sub + li][0];  // hi[128], lo[128]
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const bf16x8 bhi = *(const bf16x8*)(krow + 32 * c + 8 * kq);
+          const bf16x8 blo = *(const bf16x8*)(krow + kHeadDim + 32 * c + 8 * kq);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(alo[c], bhi, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[c], blo, acc, 0, 0, 0);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ahi[c], bhi, acc, 0, 0, 0);
         }
-      } else if ((m & 2) == 0) {
+        const int kb = kbs + li;
 #pragma unroll
-        for (int t = 0; t < kPeTile; ++t) {
-          st0[t][1] = st0[t][0] + v0[t];
-          st1[t][1] = st1[t][0] + v1[t];
-        }
-      } else if ((m & 4) == 0) {
-#pragma unroll
-        for (int t = 0; t < kPeTile; ++t) {
-          st0[t][2] = st0[t][1] + (st0[t][0] + v0[t]);
-          st1[t][2] = st1[t][1] + (st1[t][0] + v1[t]);
-        }
-      } else {
-#pragma unroll
-        for (int t = 0; t < kPeTile; ++t) {
-          st0[t][2] = st0[t][2] + (st0[t][1] + (st0[t][0] + v0[t]));
-          st1[t][2] = st1[t][2] + (st1[t][1] + (st1[t][0] + v1[t]));
+        for (int rr = 0; rr < 4; ++rr) {
+          const int t = 16 * w + 4 * kq + rr, qb = qb0 + t;
+          if (t < nt && kb <= qb) ((float*)idx_h)[(size_t)qb * (qb + 1) / 2 + kb] = acc[rr] * p.scale_log2;
         }
       }
     }
-#pragma unroll
-    for (int t = 0; t < kPeTile; ++t) {
-      const int qb = qb0 + t;
-      float* dst = (float*)idx_h + (size_t)qb * (qb + 1) / 2;
-      if (t < nt && kb0 <= qb) dst[kb0] = st0[t][2] * p.scale_log2;
-      if (t < nt && kb0 + 1 <= qb) dst[kb0 + 1] = st1[t][2] * p.scale_log2;
-    }
+  };
+  const int ntile = qbmax / kKeyTile + 1;
+  f32x4 r0[4], r1[4];
+  load_tile(0, r0);
+  if (ntile > 1) load_tile(kKeyTile, r1);
+  store_tile(0, r0);
+  __syncthreads();
+  for (int i = 0; i < ntile; i += 2) {
+    // tile i in buffer 0, tile i+1 in r1
+    if (i + 2 < ntile) load_tile((i + 2) * kKeyTile, r0);
+    products(i * kKeyTile, 0);
+    if (i + 1 < ntile) store_tile(1, r1);
+    __syncthreads();
+    if (i + 1 >= ntile) break;
+    // tile i+1 in buffer 1, tile i+2 in r0
+    if (i + 3 < ntile) load_tile((i + 3) * kKeyTile, r1);
+    products((i + 1) * kKeyTile, 1);
+    if (i + 2 < ntile) store_tile(0, r0);
+    __syncthreads();
   }
 }
 
