@@ -305,11 +305,15 @@ __global__ __launch_bounds__(256) void pe_logits_kernel(PeLogitArgs p) {
   constexpr int kKeyTile = 32;  // key blocks per LDS tile of pooled keys
   // the pooling partials and, once the queries are pooled, the key tiles
   // (double buffered) share one buffer: two workgroups fit a CU
-  __shared__ __attribute__((aligned(16))) float shared_u[2 * kKeyTile * kHeadDim];
-  __shared__ __attribute__((aligned(16))) float qs[kPeTile][kHeadDim];
+  // Rows of the pooled queries and of the key tiles are padded by 16 bytes:
+  // the products read 16 rows at one column offset, which with 512-byte rows
+  // all fall in the same LDS banks.
+  constexpr int kRow = kHeadDim + 4;
+  __shared__ __attribute__((aligned(16))) float shared_u[2 * kKeyTile * kRow];
+  __shared__ __attribute__((aligned(16))) float qs[kPeTile][kRow];
   static_assert(kPoolBatch * 16 <= 2 * kKeyTile, "pooling partials fit the key-tile buffer");
   auto& part = *(float (*)[kPoolBatch][16][kHeadDim])shared_u;
-  auto& kt = *(float (*)[2][kKeyTile][kHeadDim])shared_u;
+  auto& kt = *(float (*)[2][kKeyTile][kRow])shared_u;
   const int N = p.nblk, tiles = (N + kPeTile - 1) / kPeTile;
   const int h = blockIdx.x % p.hq, tile = tiles - 1 - (int)blockIdx.x / p.hq;
   if (p.route[h] != 0) return;
@@ -493,6 +497,17 @@ __device__ inline void find_digit(const uint32_t* hist, uint32_t below, uint32_t
 // so neither part overflows into the other.
 constexpr int kCountBits = 16;
 
+// Lane exchanges through ds_bpermute from a lane index l the caller takes
+// from opaque_lane() once per use site: the compiler would otherwise hoist
+// one address per offset out of the radix-pass loop and keep them all live
+// across it.
+__device__ __forceinline__ uint32_t lane_xor_u32(uint32_t x, int l, int o) {
+  return (uint32_t)__builtin_amdgcn_ds_bpermute((l ^ o) << 2, (int)x);
+}
+__device__ __forceinline__ uint32_t lane_up_u32(uint32_t x, int l, int o) {  // lanes below o keep x
+  return (uint32_t)__builtin_amdgcn_ds_bpermute((l >= o ? l - o : l) << 2, (int)x);
+}
+
 // find_digit over the mass parts of packed bins, also returning the number
 // of keys in the chosen bin.
 __device__ inline void find_digit_packed(const uint64_t* hist, uint32_t below, uint32_t target, int lane, int* d_out,
@@ -505,10 +520,11 @@ __device__ inline void find_digit_packed(const uint64_t* hist, uint32_t below, u
     c[b] = (uint32_t)(v & ((1u << kCountBits) - 1));
     tot += s[b];
   }
+  const int l = opaque_lane();
   uint32_t incl = tot;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t y = __shfl_up(incl, o);
+    const uint32_t y = lane_up_u32(incl, l, o);
     if (lane >= o) incl += y;
   }
   uint32_t run = below + incl - tot;
@@ -525,7 +541,7 @@ __device__ inline void find_digit_packed(const uint64_t* hist, uint32_t below, u
   }
   int best = cand;
 #pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) best = min(best, __shfl_xor(best, o));
+  for (int o = 32; o >= 1; o >>= 1) best = min(best, (int)lane_xor_u32((uint32_t)best, l, o));
   if (cand == best && cand < 256) {
     *d_out = cand;
     *below_out = cand_below;
@@ -562,7 +578,9 @@ __device__ __forceinline__ void hist_add_packed(uint64_t* hist, bool valid, uint
 // (< 4096, so key bits 16..31 are zero): 6 passes cover them.  Masses are
 // 2^-31 fixed point (truncated; at most 4096 x 2^-31 below the real sum), so
 // sums are exact integers and the result deterministic.
-__global__ __launch_bounds__(kPeThreads) void pe_select_kernel(PeArgs p) {
+// Five workgroups per CU (at most 102 registers): the kernel waits on memory
+// and barriers most of its time, and occupancy is what hides that.
+__global__ __launch_bounds__(kPeThreads, 5) void pe_select_kernel(PeArgs p) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   __shared__ float red_max[4], red_sum[4];
   __shared__ int redi[8];
