@@ -227,20 +227,30 @@ CRISP_API size_t crisp_list_capacity(const crisp_dims* dims);
  * last entry is taken as qb whatever it holds, and every other entry is
  * clamped to [0, qb-1].  So no key after a query is ever weighted and every
  * read stays inside the head's rows; the result is only meaningful for a
- * well-formed list (a repeated entry counts its keys twice).
+ * well-formed list (a repeated entry counts its keys twice, or once when
+ * the call takes the two-block schedule described below).
+ * Schedule: the call sums, over every head and pair of query blocks
+ * (2p, 2p+1), own = cA + cB and bound = min(cA + cB, 2p + 2) on the size
+ * of the union of the two lists.  When 2 sum(bound) <= 1.035 sum(own)
+ * (dense and near-dense lists) one workgroup walks the union of a pair's
+ * lists for both blocks and loads each K/V tile once; otherwise each
+ * (head, query block) is an item of its own.  Either way the result is the
+ * same exact attention, up to rounding.
  * out: [Hq][n][d], bf16 when out_is_fp32 = 0, fp32 otherwise.
  * lse (optional, [Hq][n] fp32): natural log of each row's sum of exp.
  * workspace: crisp_attn_workspace_bytes(dims) bytes of device memory, any
- * contents; it holds the work queue the kernel's workgroups take (head,
- * query block) items from, cleared by the call on `stream` (so two calls
+ * contents; it holds the work queue the kernel's workgroups take items
+ * from and the schedule sums, cleared by the call on `stream` (so two calls
  * in flight at once need two workspaces).  Smaller: CRISP_ERR_WORKSPACE. */
 CRISP_API crisp_status crisp_sparse_attn(const crisp_dims* dims, const void* q, const void* k, const void* v,
                                const int32_t* count, const int32_t* idx, void* out, int32_t out_is_fp32,
                                float* lse, void* workspace, size_t workspace_bytes, void* stream);
 
-/* Dense causal attention with the same kernel and output conventions
+/* Dense causal attention with the same kernels and output conventions
  * (every key block 0..qb): the exact baseline the speedups are measured
- * against (ai.info summary, "Main Findings").  workspace: as
+ * against (ai.info summary, "Main Findings").  It takes the schedule
+ * crisp_sparse_attn takes for full lists (two blocks per workgroup from 32
+ * blocks on), so the two agree bit for bit on full lists.  workspace: as
  * crisp_sparse_attn. */
 CRISP_API crisp_status crisp_dense_attn(const crisp_dims* dims, const void* q, const void* k, const void* v, void* out,
                               int32_t out_is_fp32, float* lse, void* workspace, size_t workspace_bytes,

@@ -249,6 +249,198 @@ def test_attention_work_queue():
     assert not bool(dense.isnan().any())
 
 
+def _long_short_lists(rng, N, kind):
+    """"long": each causal block kept with probability 0.995 (the diagonal
+    always), near-dense lists; "short": up to three
+    random blocks below the diagonal, plus the diagonal."""
+    out = []
+    for qb in range(N):
+        if kind == "long":
+            m = rng.random(qb + 1) < 0.995
+            m[qb] = True
+            out.append(np.flatnonzero(m).tolist())
+        else:
+            below = rng.choice(qb, size=min(qb, int(rng.integers(0, 4))), replace=False).tolist() if qb else []
+            out.append(sorted(below) + [qb])
+    return out
+
+
+def _schedule_sums(lists, N):
+    """Sums the schedule pass forms over every (head, pair of blocks): the
+    listed blocks cA + cB, and the bound min(cA + cB, 2p + 2) on the union."""
+    own = bound = 0
+    for hl in lists:
+        for qa in range(0, N, 2):
+            ca = len(hl[qa])
+            if qa + 1 < N:
+                cb = len(hl[qa + 1])
+                own += ca + cb
+                bound += min(ca + cb, qa + 2)
+            else:
+                own += ca
+                bound += ca
+    return own, bound
+
+
+def _two_block(own, bound):
+    """The launch rule: two blocks per workgroup when 2 bound <= 1.035 own."""
+    return 2000 * bound <= 1035 * own
+
+
+def _sums_left(ws):
+    """The schedule sums the call left in its workspace (bytes 64..79)."""
+    return tuple(int(t) for t in ws[64:80].view(torch.int64).cpu().tolist())
+
+
+@pytest.mark.parametrize("hq,hkv,n,kinds", [
+    (4, 2, 16384, "LLLL"),     # N = 128
+    (3, 1, 16512, "LLL"),      # N = 129: the last pair holds one block
+    (2, 1, 16321, "LL"),       # partial last block of 65 rows, the second block of its pair
+    (2, 2, 16257, "LL"),       # partial last block of one row
+    (7, 1, 16384, "LLLSLLL"),  # 7:1 GQA; one head of short lists
+])
+def test_two_block_attention_matches_oracle(hq, hkv, n, kinds):
+    """Near-dense lists go to the two-block kernel: the schedule sums the call
+    leaves in its workspace equal the ones formed here from the lists, and
+    they pick that kernel.  Rows of both blocks of sampled pairs (the first
+    two, the middle one, the last) match the oracle on their own lists, for
+    a short-list head too, whose blocks own few of the union's steps."""
+    rng = np.random.default_rng(n + 7 * hq)
+    x = synth.make_inputs(synth.custom(hq, hkv, n, seed=n + 1, needles=2), device="cuda")
+    N = B.num_blocks(n)
+    lists = [_long_short_lists(rng, N, "long" if c == "L" else "short") for c in kinds]
+    count, idx = _pack_lists(lists, hq, N)
+    dims = B.make_dims(hq, hkv, n)
+    ws = torch.full((B.crisp_attn_workspace_bytes(dims),), 0x5A, dtype=torch.uint8, device="cuda")
+    out = torch.full((hq, n, 128), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((hq, n), float("nan"), dtype=torch.float32, device="cuda")
+    print(f"[two-block] hq={hq} hkv={hkv} n={n} kinds={kinds}", flush=True)
+    B.crisp_sparse_attn(dims, x.q, x.k, x.v, count, idx, out, lse, workspace=ws)
+    torch.cuda.synchronize()
+    own, bound = _schedule_sums(lists, N)
+    assert _sums_left(ws) == (own, bound)
+    assert _two_block(own, bound)
+    qbs = sorted({0, 1, 2, 3, N // 2, N // 2 + 1, N - 2, N - 1} | {(N - 1) & ~1})
+    for h in range(hq):
+        g = h * hkv // hq
+        ref = O.attention_rows(to64(x.q[h]), to64(x.k[g]), to64(x.v[g]), lists[h], dims.scale, qbs)
+        og, lg = out[h].cpu().numpy(), lse[h].cpu().numpy()
+        for qb in qbs:
+            check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"two-block h {h} qb {qb}")
+            check_lse(lg[qb * BLK:(qb + 1) * BLK], ref[qb][1])
+
+
+def test_one_block_kernel_takes_short_lists():
+    """Short lists leave the two-block kernel unpaid: the sums pick the
+    one-block kernel, and the rows match the oracle."""
+    hq, hkv, n = 4, 2, 4096
+    rng = np.random.default_rng(3)
+    x = synth.make_inputs(synth.custom(hq, hkv, n, seed=5, needles=2), device="cuda")
+    N = B.num_blocks(n)
+    lists = [_long_short_lists(rng, N, "short") for _ in range(hq)]
+    count, idx = _pack_lists(lists, hq, N)
+    dims = B.make_dims(hq, hkv, n)
+    ws = torch.full((B.crisp_attn_workspace_bytes(dims),), 0xA5, dtype=torch.uint8, device="cuda")
+    out = torch.empty((hq, n, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    B.crisp_sparse_attn(dims, x.q, x.k, x.v, count, idx, out, lse, workspace=ws)
+    torch.cuda.synchronize()
+    own, bound = _schedule_sums(lists, N)
+    assert _sums_left(ws) == (own, bound)
+    assert not _two_block(own, bound)
+    for h in (0, 3):
+        g = h * hkv // hq
+        ref = O.attention_rows(to64(x.q[h]), to64(x.k[g]), to64(x.v[g]), lists[h], dims.scale, range(N))
+        og, lg = out[h].cpu().numpy(), lse[h].cpu().numpy()
+        for qb in range(N):
+            check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"one-block h {h} qb {qb}")
+            check_lse(lg[qb * BLK:(qb + 1) * BLK], ref[qb][1])
+
+
+def test_two_block_work_queue():
+    """The two-block kernel's items, (head, pair of blocks), outnumber its
+    workgroups: two calls in a row on workspaces of any contents write the
+    same rows, and sampled pairs match the oracle."""
+    hq, hkv, n = 8, 2, 16384
+    rng = np.random.default_rng(17)
+    x = synth.make_inputs(synth.custom(hq, hkv, n, seed=19, needles=2), device="cuda")
+    N = B.num_blocks(n)
+    lists = [_long_short_lists(rng, N, "long") for _ in range(hq)]
+    count, idx = _pack_lists(lists, hq, N)
+    dims = B.make_dims(hq, hkv, n)
+    wsb = B.crisp_attn_workspace_bytes(dims)
+    print(f"[two-block queue] hq={hq} n={n} pairs={hq * N // 2}", flush=True)
+    outs = []
+    for fill in (0, 0xFF, 0x7F):
+        ws = torch.full((wsb,), fill, dtype=torch.uint8, device="cuda")
+        out = torch.full((hq, n, 128), float("nan"), dtype=torch.float32, device="cuda")
+        lse = torch.full((hq, n), float("nan"), dtype=torch.float32, device="cuda")
+        B.crisp_sparse_attn(dims, x.q, x.k, x.v, count, idx, out, lse, workspace=ws)
+        B.crisp_sparse_attn(dims, x.q, x.k, x.v, count, idx, out, lse, workspace=ws)
+        torch.cuda.synchronize()
+        assert _two_block(*_sums_left(ws)), fill
+        assert not bool(out.isnan().any()) and not bool(lse.isnan().any()), fill
+        outs.append((out, lse))
+    for out, lse in outs[1:]:
+        assert torch.equal(out, outs[0][0]) and torch.equal(lse, outs[0][1])
+    out, lse = outs[0]
+    for h in (1, 6):
+        g = h * hkv // hq
+        qbs = [0, 1, 2, 3, N // 2, N // 2 + 1, N - 2, N - 1]
+        ref = O.attention_rows(to64(x.q[h]), to64(x.k[g]), to64(x.v[g]), lists[h], dims.scale, qbs)
+        og, lg = out[h].cpu().numpy(), lse[h].cpu().numpy()
+        for qb in qbs:
+            check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"h {h} qb {qb}")
+            check_lse(lg[qb * BLK:(qb + 1) * BLK], ref[qb][1])
+
+
+def test_two_block_malformed_lists():
+    """The two-block kernel reads each list as the one-block kernel does
+    (count clamped to [1, qb+1], last entry taken as qb, the others clamped
+    to [0, qb-1]) and walks the distinct blocks so read once each, so a
+    repeated entry counts once."""
+    hq, hkv, n = 2, 1, 16384
+    N = 128
+    rng = np.random.default_rng(23)
+    x = synth.make_inputs(synth.custom(hq, hkv, n, seed=29, needles=2), device="cuda")
+    dims = B.make_dims(hq, hkv, n)
+    lists = [_long_short_lists(rng, N, "long") for _ in range(hq)]
+    # qb: (count, stored entries, blocks as read)
+    bad = {5: (0, [], [5]),
+           6: (2, [7, 1], [5, 6]),
+           9: (4, [0, 2, 9, 3], [0, 2, 8, 9]),
+           12: (99, list(range(13)), list(range(13))),
+           13: (2, [-3, 6], [0, 13]),
+           20: (3, [4, 4, 20], [4, 20])}
+    count = np.zeros((hq, N), np.int32)
+    idx = np.full(hq * N * (N + 1) // 2, 77, np.int32)
+    read = []
+    for h in range(hq):
+        base = h * N * (N + 1) // 2
+        rh = []
+        for qb in range(N):
+            c, stored, r = bad[qb] if qb in bad else (len(lists[h][qb]), lists[h][qb], lists[h][qb])
+            count[h, qb] = c
+            s = base + qb * (qb + 1) // 2
+            idx[s:s + len(stored)] = stored
+            rh.append(r)
+        read.append(rh)
+    ws = torch.zeros(B.crisp_attn_workspace_bytes(dims), dtype=torch.uint8, device="cuda")
+    out = torch.empty((hq, n, 128), dtype=torch.float32, device="cuda")
+    lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    B.crisp_sparse_attn(dims, x.q, x.k, x.v, torch.from_numpy(count).cuda(), torch.from_numpy(idx).cuda(), out, lse,
+                        workspace=ws)
+    torch.cuda.synchronize()
+    assert _two_block(*_sums_left(ws))
+    qbs = sorted(set(q ^ b for q in bad for b in (0, 1)) | {0, 1, N - 2, N - 1})  # the bad blocks' pairs
+    for h in range(hq):
+        ref = O.attention_rows(to64(x.q[h]), to64(x.k[0]), to64(x.v[0]), read[h], dims.scale, qbs)
+        og, lg = out[h].cpu().numpy(), lse[h].cpu().numpy()
+        for qb in qbs:
+            check_attention(og[qb * BLK:(qb + 1) * BLK], ref[qb][0], f"malformed two-block h {h} qb {qb}")
+            check_lse(lg[qb * BLK:(qb + 1) * BLK], ref[qb][1])
+
+
 # ---------------------------------------------------------------------------
 # proxy, route, selection on the single-head 4k workload
 # ---------------------------------------------------------------------------
