@@ -356,4 +356,14 @@ __host__ __device__ inline void map_row(const RowMap& m, int id, int* h_out, int
   *qb_out = m.nblk - 1 - qi;
 }
 
+// Query blocks in runs of 16 per XCD: map_row deals XCD x the blocks x,
+// x+8, x+16, ... (counted from the last); this permutation of the query
+// block gives it 16x .. 16x+15, then 16(x+8) .. 16(x+8)+15, ... instead,
+// keeping each XCD's blocks in descending order (block count a multiple of
+// 128).
+__host__ __device__ inline int runs_of_16(int qb, int nblk) {
+  const int qi = nblk - 1 - qb, x = qi & 7, t = qi >> 3;
+  return nblk - 1 - (16 * (8 * (t >> 4) + x) + (t & 15));
+}
+
 }  // namespace crisp

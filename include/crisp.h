@@ -234,8 +234,10 @@ CRISP_API size_t crisp_list_capacity(const crisp_dims* dims);
  * of the union of the two lists.  When 2 sum(bound) <= 1.035 sum(own)
  * (dense and near-dense lists) one workgroup walks the union of a pair's
  * lists for both blocks and loads each K/V tile once; otherwise each
- * (head, query block) is an item of its own.  Either way the result is the
- * same exact attention, up to rounding.
+ * (head, query block) is an item of its own, dealt to the XCDs in runs of
+ * 16 adjacent query blocks when the lists hold at most 64 tiles per item on
+ * average and N is a multiple of 128.  Either way the result is the same
+ * exact attention, up to rounding.
  * out: [Hq][n][d], bf16 when out_is_fp32 = 0, fp32 otherwise.
  * lse (optional, [Hq][n] fp32): natural log of each row's sum of exp.
  * workspace: crisp_attn_workspace_bytes(dims) bytes of device memory, any

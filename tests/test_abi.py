@@ -247,10 +247,13 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
 @pytest.mark.skipif(shutil.which("hipcc") is None and not os.path.exists("/opt/rocm/bin/hipcc"),
                     reason="needs hipcc for a host build")
 @pytest.mark.parametrize("sanitized", [False, True])
-@pytest.mark.parametrize("hq,hkv,nblk", [(32, 8, 4096), (28, 4, 1024), (1, 1, 32), (3, 1, 5), (16, 16, 64), (4, 2, 3)])
-def test_row_map_is_a_bijection(tmp_path_factory, hq, hkv, nblk, sanitized):
-    """The workgroup map, also built with host AddressSanitizer and
-    UndefinedBehaviorSanitizer (host code only; any report aborts)."""
+@pytest.mark.parametrize("hq,hkv,nblk,runs", [(32, 8, 4096, False), (28, 4, 1024, False), (1, 1, 32, False),
+                                              (3, 1, 5, False), (16, 16, 64, False), (4, 2, 3, False),
+                                              (32, 8, 4096, True), (28, 4, 1024, True), (2, 1, 128, True)])
+def test_row_map_is_a_bijection(tmp_path_factory, hq, hkv, nblk, runs, sanitized):
+    """The workgroup map (and its deal in runs of 16 blocks), also built
+    with host AddressSanitizer and UndefinedBehaviorSanitizer (host code
+    only; any report aborts)."""
     exe = tmp_path_factory.getbasetemp() / ("row_map_check_san" if sanitized else "row_map_check")
     if not exe.exists():
         hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
@@ -260,7 +263,8 @@ def test_row_map_is_a_bijection(tmp_path_factory, hq, hkv, nblk, sanitized):
                      "-Xarch_host", "-fno-sanitize-recover=all"]
         subprocess.run([hipcc, *flags, "-std=c++17", os.path.join(ROOT, "tests", "cpp", "row_map_check.cpp"),
                         "-o", str(exe)], check=True, capture_output=True)
-    r = subprocess.run([str(exe), str(hq), str(hkv), str(nblk)], capture_output=True, text=True)
+    r = subprocess.run([str(exe), str(hq), str(hkv), str(nblk)] + (["runs"] if runs else []), capture_output=True,
+                       text=True)
     assert r.returncode == 0, r.stdout + r.stderr
 
 

@@ -292,6 +292,17 @@ def _sums_left(ws):
     return tuple(int(t) for t in ws[64:80].view(torch.int64).cpu().tolist())
 
 
+def _kernel_taken(ws):
+    """Which attention kernel took the items, from the decision words the
+    call left after the sums: "two", "one" or "runs"."""
+    w = [int(t) for t in ws[80:128].view(torch.int64).cpu().tolist()]
+    taken = [name for name, (a, b), runs_if_pays in (("two", w[0:2], True), ("one", w[2:4], False),
+                                                      ("runs", w[4:6], False))
+             if _two_block(a, b) == runs_if_pays]
+    assert len(taken) == 1, w
+    return taken[0]
+
+
 @pytest.mark.parametrize("hq,hkv,n,kinds", [
     (4, 2, 16384, "LLLL"),     # N = 128
     (3, 1, 16512, "LLL"),      # N = 129: the last pair holds one block
@@ -319,7 +330,7 @@ def test_two_block_attention_matches_oracle(hq, hkv, n, kinds):
     torch.cuda.synchronize()
     own, bound = _schedule_sums(lists, N)
     assert _sums_left(ws) == (own, bound)
-    assert _two_block(own, bound)
+    assert _two_block(own, bound) and _kernel_taken(ws) == "two"
     qbs = sorted({0, 1, 2, 3, N // 2, N // 2 + 1, N - 2, N - 1} | {(N - 1) & ~1})
     for h in range(hq):
         g = h * hkv // hq
@@ -330,10 +341,13 @@ def test_two_block_attention_matches_oracle(hq, hkv, n, kinds):
             check_lse(lg[qb * BLK:(qb + 1) * BLK], ref[qb][1])
 
 
-def test_one_block_kernel_takes_short_lists():
+@pytest.mark.parametrize("n,kernel", [(4096, "one"), (16384, "runs"), (16257, "runs"), (16512, "one")])
+def test_one_block_kernel_takes_short_lists(n, kernel):
     """Short lists leave the two-block kernel unpaid: the sums pick the
-    one-block kernel, and the rows match the oracle."""
-    hq, hkv, n = 4, 2, 4096
+    one-block kernel, dealt in runs of 16 query blocks per XCD when the block
+    count is a multiple of 128 (16384, and 16257 with a last block of one
+    row) and interleaved otherwise; every row matches the oracle."""
+    hq, hkv = 4, 2
     rng = np.random.default_rng(3)
     x = synth.make_inputs(synth.custom(hq, hkv, n, seed=5, needles=2), device="cuda")
     N = B.num_blocks(n)
@@ -341,14 +355,14 @@ def test_one_block_kernel_takes_short_lists():
     count, idx = _pack_lists(lists, hq, N)
     dims = B.make_dims(hq, hkv, n)
     ws = torch.full((B.crisp_attn_workspace_bytes(dims),), 0xA5, dtype=torch.uint8, device="cuda")
-    out = torch.empty((hq, n, 128), dtype=torch.float32, device="cuda")
-    lse = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    out = torch.full((hq, n, 128), float("nan"), dtype=torch.float32, device="cuda")
+    lse = torch.full((hq, n), float("nan"), dtype=torch.float32, device="cuda")
     B.crisp_sparse_attn(dims, x.q, x.k, x.v, count, idx, out, lse, workspace=ws)
     torch.cuda.synchronize()
     own, bound = _schedule_sums(lists, N)
     assert _sums_left(ws) == (own, bound)
-    assert not _two_block(own, bound)
-    for h in (0, 3):
+    assert not _two_block(own, bound) and _kernel_taken(ws) == kernel
+    for h in range(hq):
         g = h * hkv // hq
         ref = O.attention_rows(to64(x.q[h]), to64(x.k[g]), to64(x.v[g]), lists[h], dims.scale, range(N))
         og, lg = out[h].cpu().numpy(), lse[h].cpu().numpy()
@@ -378,7 +392,7 @@ def test_two_block_work_queue():
         B.crisp_sparse_attn(dims, x.q, x.k, x.v, count, idx, out, lse, workspace=ws)
         B.crisp_sparse_attn(dims, x.q, x.k, x.v, count, idx, out, lse, workspace=ws)
         torch.cuda.synchronize()
-        assert _two_block(*_sums_left(ws)), fill
+        assert _two_block(*_sums_left(ws)) and _kernel_taken(ws) == "two", fill
         assert not bool(out.isnan().any()) and not bool(lse.isnan().any()), fill
         outs.append((out, lse))
     for out, lse in outs[1:]:
