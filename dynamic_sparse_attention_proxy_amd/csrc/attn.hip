@@ -53,8 +53,9 @@ struct AttnArgs {
   RowMap map;
   int* queue;  // 8 claim counters, zero at launch
   int items;   // Hq * nblk, or Hq * pairs of blocks for the two-block kernel
-  // Sums written by the schedule pass (null: no choice to make); see
-  // two_block_pays.
+  // This kernel's pair of decision words, written by the decide pass (null:
+  // no choice to make): the one-block kernels run unless two_block_pays
+  // holds for them, the two-block kernel only if it does.
   const unsigned long long* sched;
 };
 
@@ -826,8 +827,8 @@ __host__ __device__ inline bool two_block_pays(unsigned long long own, unsigned 
 }
 
 // One-block kernel: four waves per (head, query block) item, two
-// workgroups per CU.  A launch that the schedule pass hands to the
-// two-block kernel ends here.
+// workgroups per CU.  A launch that the schedule hands to another kernel
+// ends here.
 template <bool kDense, bool kRagged>
 __global__ __launch_bounds__(256, 2) void fa_fwd_kernel(AttnArgs p) {
   // 32 KiB of V stages (tiles 0-1) then 48 KiB of K stages (tiles 2-4): two
