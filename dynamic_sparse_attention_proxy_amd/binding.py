@@ -61,6 +61,7 @@ _SIGS = {
     "crisp_proxy": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "crisp_proxy_scratch_bytes": (ctypes.c_size_t, [ctypes.POINTER(crisp_dims)]),
     "crisp_route": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), _P, _P, _P, _P, _P]),
+    "crisp_route_cols": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), _P, _P, _P, _P]),
     "crisp_proxy_cols": (ctypes.c_int, [ctypes.POINTER(crisp_dims), _P, _P, _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "crisp_select_tokens": (ctypes.c_int, [ctypes.POINTER(crisp_dims), ctypes.POINTER(crisp_cfg), _P, _P, _P, _P,
                                            _P, ctypes.POINTER(crisp_blocks), _P, _P, _P, _P, ctypes.c_size_t, _P]),
@@ -174,6 +175,11 @@ def crisp_proxy(dims: crisp_dims, q, k, attn_map, row_lse=None, partials=None, s
 def crisp_route(dims: crisp_dims, cfg: crisp_cfg, attn_map, c_struct, route, stream=None, block_mass=None):
     _check("crisp_route", lib().crisp_route(ctypes.byref(dims), ctypes.byref(cfg), _ptr(attn_map), _ptr(block_mass),
                                             _ptr(c_struct), _ptr(route), _stream(stream)))
+
+
+def crisp_route_cols(dims: crisp_dims, cfg: crisp_cfg, col_mass, c_struct, route, stream=None):
+    _check("crisp_route_cols", lib().crisp_route_cols(ctypes.byref(dims), ctypes.byref(cfg), _ptr(col_mass),
+                                                      _ptr(c_struct), _ptr(route), _stream(stream)))
 
 
 def crisp_proxy_cols(dims: crisp_dims, q, k, block_mass, col_mass, row_lse=None, partials=None, stream=None):

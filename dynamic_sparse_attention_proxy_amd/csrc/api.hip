@@ -289,6 +289,19 @@ crisp_status crisp_route(const crisp_dims* dims, const crisp_cfg* cfg, const flo
                                       (hipStream_t)stream));
 }
 
+crisp_status crisp_route_cols(const crisp_dims* dims, const crisp_cfg* cfg, const float* col_mass, float* c_struct,
+                              int32_t* route, void* stream) {
+  CRISP_TRY(check_dims(dims));
+  CRISP_TRY(check_cfg(dims, cfg));
+  CRISP_TRY(check_ptr(col_mass));
+  CRISP_TRY(check_ptr(c_struct));
+  CRISP_TRY(check_ptr(route));
+  CRISP_TRY(check_device());
+  return launched(crisp::launch_route_cols(col_mass, c_struct, route, dims->num_q_heads, dims->seq_len,
+                                           cfg->sink_width, cfg->recency_width, cfg->tau, cfg->route_override,
+                                           (hipStream_t)stream));
+}
+
 size_t crisp_route_jsd_workspace_bytes(const crisp_dims* dims) {
   if (check_dims(dims) != CRISP_OK) return 0;
   return crisp::jsd_workspace_bytes(dims->num_q_heads, dims->seq_len);
@@ -475,6 +488,6 @@ const char* crisp_status_string(crisp_status status) {
   return "unknown status";
 }
 
-int32_t crisp_abi_version(void) { return (5 << 16) | 0; }
+int32_t crisp_abi_version(void) { return (5 << 16) | 1; }
 
 }  // extern "C"

@@ -31,6 +31,10 @@ inline size_t proxy_scratch_bytes(int hq, int n) {
 hipError_t launch_proxy(const __bf16* q, const __bf16* k, float* amap, float* mass, float* colmass, float* row_lse,
                         void* scratch, int hq, int hkv, int n, float scale, hipStream_t stream);
 
+// From the column masses [Hq][n] (any widths).
+hipError_t launch_route_cols(const float* colmass, float* c_struct, int32_t* route, int hq, int n, int sink_width,
+                             int recency_width, float tau, int route_override, hipStream_t stream);
+
 // From the block masses when mass != nullptr (widths of one block), else
 // from the map.
 hipError_t launch_route(const float* amap, const float* mass, float* c_struct, int32_t* route, int hq, int n,

@@ -612,6 +612,23 @@ __global__ __launch_bounds__(256) void route_kernel(const float* amap, float* c_
   }
 }
 
+// C_struct from the column masses (the map's column sums over the rows /
+// 128), for any sink and recency widths: the same sum as route_kernel's,
+// over one row of column masses instead of the map's 128 rows.
+__global__ __launch_bounds__(256) void route_cols_kernel(const float* colmass, float* c_struct, int32_t* route, int n,
+                                                         int ws, int wr, float tau, int override_mode) {
+  __shared__ float red[8];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const float* c_h = colmass + (size_t)h * n;
+  float acc = 0.f;
+  for (int e = tid; e < ws + wr; e += 256) acc += c_h[e < ws ? e : n - wr + (e - ws)];
+  const float c = block_sum_f(acc, red, tid, 256);
+  if (tid == 0) {
+    c_struct[h] = c;
+    route[h] = override_mode == 1 ? 1 : override_mode == 2 ? 0 : (c >= tau ? 1 : 0);
+  }
+}
+
 // C_struct from the block masses when sink and recency widths are both one
 // block: the mass of key block 0 (the first 128 keys) and the recency plane
 // (the last 128 keys: block N-1 and the tail of block N-2) over the 128 rows.
@@ -687,6 +704,13 @@ hipError_t launch_proxy(const __bf16* q, const __bf16* k, float* amap, float* ma
     else
       hipLaunchKernelGGL((proxy_pass_kernel<1, true, false, false, false>), grid, dim3(256), 0, stream, a);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_route_cols(const float* colmass, float* c_struct, int32_t* route, int hq, int n, int sink_width,
+                             int recency_width, float tau, int route_override, hipStream_t stream) {
+  hipLaunchKernelGGL(route_cols_kernel, dim3(hq), dim3(256), 0, stream, colmass, c_struct, route, n, sink_width,
+                     recency_width, tau, route_override);
   return hipGetLastError();
 }
 

@@ -156,10 +156,21 @@ CRISP_API size_t crisp_proxy_scratch_bytes(const crisp_dims* dims);
  * proxy rows, so it lies in [0, 1]; route[h] = VS when C_struct >= tau, PE
  * otherwise, unless cfg->route_override forces one path.
  * Reads block_mass when it is non-NULL (then both widths must be 128,
- * CRISP_ERR_PARAM otherwise), else attn_map.
+ * CRISP_ERR_PARAM otherwise), else attn_map.  For other widths without the
+ * map, crisp_route_cols reads the column masses of crisp_proxy_cols.
  * c_struct [Hq] fp32, route [Hq] int32. */
 CRISP_API crisp_status crisp_route(const crisp_dims* dims, const crisp_cfg* cfg, const float* attn_map,
                          const float* block_mass, float* c_struct, int32_t* route, void* stream);
+
+/* Step 2 from the column masses (same pages as crisp_route): C_struct[h] =
+ * sum of col_mass[h][j] over the first sink_width and the last
+ * recency_width columns, any widths in 1..n/2 (cfg is checked as for
+ * crisp_route); route as crisp_route.  col_mass [Hq][n] fp32: the column
+ * masses crisp_proxy_cols writes (the map's column sums over its 128 rows,
+ * divided by 128).  c_struct [Hq] fp32, route [Hq] int32; all device
+ * pointers, 16-byte aligned. */
+CRISP_API crisp_status crisp_route_cols(const crisp_dims* dims, const crisp_cfg* cfg, const float* col_mass,
+                                        float* c_struct, int32_t* route, void* stream);
 
 /* Step 3 - block selection (ai.info summary, "Methodology in Plain English";
  * ai-feeds summary, method module 2).

@@ -26,7 +26,7 @@ def _declared():
 
 def test_library_exports_every_declared_symbol():
     names = _declared()
-    assert len(names) == 20
+    assert len(names) == 21
     lib = B.lib()
     for n in names:
         assert hasattr(lib, n), n
@@ -148,6 +148,34 @@ def test_non_finite_scale_and_thresholds_are_param_errors(value):
     if value != 0.0:  # a JSD threshold of 0 is allowed
         assert lib.crisp_route_jsd(ctypes.byref(good), ctypes.c_float(value), P16, P16, P16, P16, P16, None, P16,
                                    1 << 40, None) == 3
+
+
+def test_route_cols_validation():
+    """crisp_route_cols checks its pointers and the configuration like
+    crisp_route, takes any widths in 1..n/2, and reaches the device check
+    with valid arguments (no GPU here: 6)."""
+    lib = B.lib()
+    dims = B.make_dims(4, 2, 1024)
+
+    def call(cfg, colm=P16, c=P16, r=P16, d=dims):
+        return lib.crisp_route_cols(ctypes.byref(d), ctypes.byref(cfg), colm, c, r, None)
+
+    assert call(B.make_cfg(), colm=None) == 1
+    assert call(B.make_cfg(), c=None) == 1
+    assert call(B.make_cfg(), r=None) == 1
+    assert call(B.make_cfg(), colm=P8) == 4
+    assert call(B.make_cfg(tau=float("nan"))) == 3
+    bad = B.make_cfg()
+    bad.sink_width = 0
+    assert call(bad) == 3
+    bad = B.make_cfg()
+    bad.recency_width = 513
+    assert call(bad) == 3
+    for ws, wr in ((1, 1), (64, 200), (512, 512)):
+        cfg = B.make_cfg()
+        cfg.sink_width, cfg.recency_width = ws, wr
+        assert call(cfg) == 6
+    assert call(B.make_cfg(), d=B.make_dims(4, 3, 1024)) == 2
 
 
 def test_select_noalloc_validation():

@@ -9,8 +9,8 @@ import torch
 from dynamic_sparse_attention_proxy_amd import binding as B
 from dynamic_sparse_attention_proxy_amd import synth
 from oracle import crisp_oracle as O
-from parity import (check_attention, check_lse, check_noise_floor_mask, check_pe_lists, check_token_cols, gpu_lists,
-                    to64)
+from parity import (REL_CSTRUCT, check_attention, check_lse, check_noise_floor_mask, check_pe_lists, check_route,
+                    check_token_cols, gpu_lists, to64)
 
 pytestmark = pytest.mark.gpu
 
@@ -63,6 +63,45 @@ def test_column_masses_match_oracle_and_block_masses_agree():
             A, _ = O.proxy_map(to64(x.q[h, n - BLK:]), to64(x.k[g]), dims.scale)
             c, _ = O.token_scores(A)
             np.testing.assert_allclose(cg[h], c, rtol=1e-4, atol=1e-10, err_msg=f"head {h}")
+
+
+@pytest.mark.parametrize("hq,hkv,n", [(8, 2, 4096), (8, 2, 3030)])
+def test_route_from_column_masses_any_width(hq, hkv, n):
+    """crisp_route_cols on the column masses of crisp_proxy_cols: C_struct
+    of every head of the graded-structure family, for sink and recency
+    widths from one column to n/2, within 1e-4 of the oracle's C_struct on
+    the map, routes alike away from tau; at 128/128 it matches crisp_route
+    on the block masses."""
+    x = synth.make_routing_family(seq_len=n, num_q_heads=hq, num_kv_heads=hkv, device="cuda")
+    dims = B.make_dims(hq, hkv, n)
+    N = B.num_blocks(n)
+    mass = torch.empty((4, hq, N), dtype=torch.float32, device="cuda")
+    cm = torch.empty((hq, n), dtype=torch.float32, device="cuda")
+    part = torch.empty(B.crisp_proxy_scratch_bytes(dims), dtype=torch.uint8, device="cuda")
+    B.crisp_proxy_cols(dims, x.q, x.k, mass, cm, None, part)
+    maps = []
+    for h in range(hq):
+        A, _ = O.proxy_map(to64(x.q[h, n - BLK:]), to64(x.k[h * hkv // hq]), dims.scale)
+        maps.append(A)
+    for ws, wr in ((1, 1), (64, 200), (128, 128), (300, 1000), (n // 2, n // 2), (5, n // 2)):
+        cfg = B.make_cfg(tau=0.3)
+        cfg.sink_width, cfg.recency_width = ws, wr
+        c = torch.empty(hq, dtype=torch.float32, device="cuda")
+        r = torch.empty(hq, dtype=torch.int32, device="cuda")
+        print(f"[route cols] n={n} widths {ws}/{wr}", flush=True)
+        B.crisp_route_cols(dims, cfg, cm, c, r)
+        torch.cuda.synchronize()
+        cg, rg = c.cpu().numpy(), r.cpu().numpy()
+        for h in range(hq):
+            c_o = O.c_struct(maps[h], ws, wr)
+            assert abs(cg[h] - c_o) <= REL_CSTRUCT * c_o + 1e-7, (ws, wr, h, cg[h], c_o)
+            check_route(c_o, cfg.tau, int(rg[h]), O.route(c_o, cfg.tau))
+        if (ws, wr) == (128, 128):
+            cb = torch.empty_like(c)
+            rb = torch.empty_like(r)
+            B.crisp_route(dims, cfg, None, cb, rb, block_mass=mass)
+            torch.cuda.synchronize()
+            np.testing.assert_allclose(cb.cpu().numpy(), cg, rtol=1e-5)
 
 
 @pytest.mark.parametrize("alpha,stat,kmin", [(1.25, B.NF_MEDIAN, 8), (1.0, B.NF_MEDIAN, 8), (1.25, B.NF_MEAN, 8),
