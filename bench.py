@@ -97,6 +97,21 @@ class Timer:
         return [a.elapsed_time(b) for a, b in self.pairs]
 
 
+def _two_block_pays(own, bound):
+    return 2000 * bound <= 1035 * own
+
+
+def attn_schedule(torch, ws):
+    """Which attention kernel took the items of the last sparse call on the
+    workspace `ws`: the decision words after the schedule sums (bytes
+    80..127) give each kernel the pair its own launch test reads."""
+    w = [int(t) for t in ws[80:128].view(torch.int64).cpu().tolist()]
+    pays = [_two_block_pays(a, b) for a, b in (w[0:2], w[2:4], w[4:6])]
+    names = [n for n, p in zip(("two-block", "one-block", "one-block, runs of 16 blocks per XCD"),
+                                (pays[0], not pays[1], not pays[2])) if p]
+    return names[0] if len(names) == 1 else "unknown"
+
+
 def run_workload(torch, B, synth, wname, args, cfg_kw, compare):
     w = synth.workload(wname)
     log(f"generating {w.name} on the GPU")
@@ -168,7 +183,8 @@ def run_workload(torch, B, synth, wname, args, cfg_kw, compare):
                 "attn_ms_all": attn, "stage_ms": {k: {kk: round(vv, 4) for kk, vv in stats(v).items()}
                                                   for k, v in stage.items()},
                 "tiles": tiles, "tile_frac": tiles / (w.num_q_heads * N * (N + 1) / 2),
-                "heads_vs": int(sum(routes)), "heads_pe": len(routes) - int(sum(routes))}
+                "heads_vs": int(sum(routes)), "heads_pe": len(routes) - int(sum(routes)),
+                "attn_kernel": attn_schedule(torch, bufs.attn_workspace)}
 
     log(f"{w.name}: CRISP chain (route {args.route}), warmup {args.warmup}, steps {args.steps}")
     res["crisp"] = timed_chain(cfg, None, args.steps, args.warmup)
@@ -188,9 +204,13 @@ def run_workload(torch, B, synth, wname, args, cfg_kw, compare):
             B.crisp_dense_attn(dims, x.q, x.k, x.v, bufs.out, workspace=bufs.attn_workspace)
     torch.cuda.synchronize()
     d_ms = dt.ms()
+    # the dense call takes the rule the schedule pass applies to full lists
+    own = sum((qa + 1) + (qa + 2 if qa + 1 < N else 0) for qa in range(0, N, 2))
+    bound = sum(qa + 2 if qa + 1 < N else qa + 1 for qa in range(0, N, 2))
     res["dense"] = {"ms_per_layer": sum(d_ms) / len(d_ms), "ms_all": d_ms,
                     "ms": {kk: round(vv, 4) for kk, vv in stats(d_ms).items()},
-                    "tiles": w.num_q_heads * N * (N + 1) // 2}
+                    "tiles": w.num_q_heads * N * (N + 1) // 2,
+                    "attn_kernel": "two-block" if _two_block_pays(own, bound) else "one-block"}
     log(f"{w.name}: dense {res['dense']['ms_per_layer']:.2f} ms")
     # forced Vertical-Slash: the noise-floor selection on every head
     for alpha in (1.25, 1.0):

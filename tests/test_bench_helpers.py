@@ -81,3 +81,21 @@ def test_traffic_record_matches_the_attention_kernel():
     assert rec["workload"] == "llama3.1-8b-512k"
     assert rec["hbm_bytes_per_launch"] == rec["hbm_read_bytes_per_launch"] + rec["hbm_write_bytes_per_launch"]
     assert rec["hbm_bytes_per_launch"] > rec["algorithmic_bytes_per_launch"] > 0
+
+
+@pytest.mark.parametrize("taken", ["two-block", "one-block", "one-block, runs of 16 blocks per XCD"])
+def test_attn_schedule_reads_the_decision_words(taken):
+    """The bench reports which attention kernel took a call's items from the
+    decision words after the schedule sums: the two-block kernel runs when
+    its pair passes the two-block test, a one-block kernel when its pair
+    fails it ((1, 0) passes, (0, 1) fails)."""
+    go_two, stop_two = (1, 0), (0, 1)
+    go_one, stop_one = (0, 1), (1, 0)
+    words = {"two-block": go_two + stop_one + stop_one,
+             "one-block": stop_two + go_one + stop_one,
+             "one-block, runs of 16 blocks per XCD": stop_two + stop_one + go_one}[taken]
+    ws = torch.zeros(256, dtype=torch.uint8)
+    ws[80:128] = torch.tensor(words, dtype=torch.int64).view(torch.uint8)
+    assert bench.attn_schedule(torch, ws) == taken
+    ws[80:128] = torch.tensor(go_two + go_one + stop_one, dtype=torch.int64).view(torch.uint8)
+    assert bench.attn_schedule(torch, ws) == "unknown"
