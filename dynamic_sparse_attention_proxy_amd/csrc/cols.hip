@@ -37,6 +37,7 @@ constexpr int kCStages = 4;                 // K and V stages: three steps of lo
 constexpr int kIdxChunk = 32 * kCStep;      // column indices per staged half
 constexpr int kMaxTiles = 4096;             // key blocks per head (n <= 524288)
 constexpr int kColThreads = 512;
+constexpr int kColBits = (1 << 20) - 1;    // column index bits of a staged entry
 constexpr float kColSumLimit = 65536.f;     // a lane's step sum above this raises the running max
 typedef __bf16 gcc_bf16x4c __attribute__((__vector_size__(8)));
 typedef __attribute__((address_space(3))) gcc_bf16x4c lds_bf16x4c;
@@ -95,7 +96,6 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
   const int cnt_b = has_b ? min(max(p.col_below[(size_t)h * N + qb2], 0), p.n) : 0;
   const int cnt = max(cnt_a, cnt_b);
   if (cnt == 0) return;
-  const int cnt_mine = blk ? cnt_b : cnt_a;
   const int g = h / p.qpg;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int32_t* colh = p.cols + (size_t)h * p.n;
@@ -123,13 +123,24 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
       r[e] = slot < cnt ? min(max(colh[slot], 0), limit) : 0;
     }
   };
+  // Each staged entry carries, in bits 30 and 31, whether the slot does not
+  // count for block 2p or 2p+1: past the kept columns below that block, or
+  // inside one of its listed tiles (a column is below 2^19).
   auto store_idx = [&](int chunk, const int32_t (&r)[4]) {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) cidx[chunk & 1][4 * tid + e] = r[e];
+    for (int e = 0; e < 4; ++e) {
+      const int slot = chunk * kIdxChunk + 4 * tid + e;
+      const int c = r[e];
+      const uint32_t wb = (uint32_t)((c >> 7) & 31), word = (uint32_t)(c >> 12);
+      const bool off_a = slot >= cnt_a || ((tbits[0][word] >> wb) & 1u);
+      const bool off_b = slot >= cnt_b || ((tbits[1][word] >> wb) & 1u);
+      cidx[chunk & 1][4 * tid + e] = (int32_t)((uint32_t)c | ((uint32_t)off_a << 30) | ((uint32_t)off_b << 31));
+    }
   };
   {
     int32_t r[4];
     load_idx(0, r);
+    __syncthreads();  // the bitmaps are complete before store_idx reads them
     store_idx(0, r);
   }
   __syncthreads();
@@ -164,7 +175,7 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = 8 * w + 4 * i + (lane >> 4);
-      const int base = ci[r] * (kHeadDim * 2);
+      const int base = (ci[r] & kColBits) * (kHeadDim * 2);
       const unsigned ka =
           (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)(kst[st] + (8 * wu + 4 * i) * kHeadDim);
       const unsigned va =
@@ -207,10 +218,8 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
 
   // Slot mask of step s for this wave's query block.
   auto mask_of = [&](int s) -> uint64_t {
-    const int slot = s * kCStep + lane;
-    const int c = cidx[(s >> 5) & 1][(s & 31) * kCStep + lane];
-    const bool ok = slot < cnt_mine && ((tbits[blk][c >> 12] >> ((c >> 7) & 31)) & 1u) == 0;
-    return __ballot(ok);
+    const uint32_t e = (uint32_t)cidx[(s >> 5) & 1][(s & 31) * kCStep + lane];
+    return __ballot(((e >> (30 + blk)) & 1u) == 0);
   };
   auto kread = [&](int s, int t) -> bf16x8 {  // K operand of MFMA t (key half t & 1, d slice t / 2)
     const char* kb8 = (const char*)kst[s & (kCStages - 1)];
@@ -249,9 +258,9 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
   __syncthreads();
 
   // Iteration s: block 1 computes S_{s+1} = K_{s+1} Q^T (MFMA) beside the
-  // exps of the second key half of S_s (VALU); block 2 computes O += V_s P_s
-  // (MFMA) beside the masking of S_{s+1} and the exps of its first key half,
-  // carried to the next iteration in p_lo / ls_lo.  S_s arrives masked in
+  // exps of the second key half of S_s (VALU); S_{s+1} is masked if need be;
+  // block 2 computes O += V_s P_s (MFMA) beside the exps of S_{s+1}'s first
+  // key half, carried to the next iteration in p_lo / ls_lo.  S_s arrives masked in
   // `sc`.  Lazy running max: set from the first counted step and raised
   // (rare) when a step's probabilities sum past kColSumLimit, the step's
   // exps then redone from `sc`; any value keeps the result exact.
@@ -353,11 +362,20 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
         }
         l_run += ls;
       }
-      // block 2: PV MFMA u beside the masking of scores 2u, 2u+1 of S_{s+1}
-      // and the exp of its score u (first key half)
+      // S_{s+1}'s slots that do not count for this block, masked in a pass
+      // of its own: most steps need none, and a check per unit inside the
+      // block below cost more than the pass.
       const bool mask_next = has_next && m_next != ~0ull;
       const bool next_lo = has_next && m_next != 0ull && started;
-      const uint32_t nb0 = lane_bits(m_next, 0), nb1 = lane_bits(m_next, 1);
+      if (mask_next) {
+        const uint32_t nb0 = lane_bits(m_next, 0), nb1 = lane_bits(m_next, 1);
+#pragma unroll
+        for (int i = 0; i < 32; ++i) {
+          const uint32_t bits = (i >> 4) ? nb1 : nb0;
+          if (!((bits >> (i & 15)) & 1u)) sn[i >> 4][i & 15] = -INFINITY;
+        }
+      }
+      // block 2: PV MFMA u beside the exp of score u of S_{s+1} (first key half)
       float lsn = 0.f;
       if (cur_on && next_lo) {
         bf16x8 vr[4];
@@ -369,13 +387,6 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
         for (int u = 0; u < 16; ++u) {
           o[u & 3] = mfma32(vr[u & 3], pb[u >> 2], o[u & 3]);
           if (u + 3 < 16) vr[(u + 3) & 3] = vread(s, u + 3);
-          if (mask_next) {
-#pragma unroll
-            for (int i = 2 * u; i < 2 * u + 2; ++i) {
-              const uint32_t bits = (i >> 4) ? nb1 : nb0;
-              if (!((bits >> (i & 15)) & 1u)) sn[i >> 4][i & 15] = -INFINITY;
-            }
-          }
           e[u] = fast_exp2(fmaf(sn[0][u], p.scale_log2, -m_run));
           if ((u & 7) == 7)
             p_lo[u >> 3] = pack_bf16x8(e[u - 7], e[u - 6], e[u - 5], e[u - 4], e[u - 3], e[u - 2], e[u - 1], e[u]);
@@ -386,13 +397,6 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
         if (cur_on) {
 #pragma unroll
           for (int u = 0; u < 16; ++u) o[u & 3] = mfma32(vread(s, u), pb[u >> 2], o[u & 3]);
-        }
-        if (mask_next) {
-#pragma unroll
-          for (int i = 0; i < 32; ++i) {
-            const uint32_t bits = (i >> 4) ? nb1 : nb0;
-            if (!((bits >> (i & 15)) & 1u)) sn[i >> 4][i & 15] = -INFINITY;
-          }
         }
         if (next_lo) lsn = half_exps(sn[0], p_lo[0], p_lo[1]);
       }
