@@ -69,10 +69,6 @@ struct ColLds {
   int next_item;
 };
 
-// Key slot (0..31 within a 32-key half) of accumulator register v of lane
-// group lg, for the permuted K-operand rows below.
-__device__ __forceinline__ int slot_of(int v, int lg) { return (v < 8) ? (8 * lg + v) : (16 + 8 * lg + (v - 8)); }
-
 // One (head, pair of query blocks) item.  Every wave returns having passed
 // the same barriers; the caller synchronises before reusing LDS.
 __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int pi) {
