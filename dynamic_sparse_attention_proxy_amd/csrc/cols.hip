@@ -37,7 +37,7 @@ constexpr int kCStages = 4;                 // K and V stages: three steps of lo
 constexpr int kIdxChunk = 32 * kCStep;      // column indices per staged half
 constexpr int kMaxTiles = 4096;             // key blocks per head (n <= 524288)
 constexpr int kColThreads = 512;
-constexpr int kColBits = (1 << 20) - 1;    // column index bits of a staged entry
+constexpr int kColBits = (1 << 20) - 1;    // column index bits (entries hold them shifted by 8)
 constexpr float kColSumLimit = 65536.f;     // a lane's step sum above this raises the running max
 typedef __bf16 gcc_bf16x4c __attribute__((__vector_size__(8)));
 typedef __attribute__((address_space(3))) gcc_bf16x4c lds_bf16x4c;
@@ -119,9 +119,10 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
       r[e] = slot < cnt ? min(max(colh[slot], 0), limit) : 0;
     }
   };
-  // Each staged entry carries, in bits 30 and 31, whether the slot does not
-  // count for block 2p or 2p+1: past the kept columns below that block, or
-  // inside one of its listed tiles (a column is below 2^19).
+  // A staged entry holds the column times 256 (the byte offset of its K or V
+  // row; a column is below 2^19) and, in bits 30 and 31, whether the slot
+  // does not count for block 2p or 2p+1: past the kept columns below that
+  // block, or inside one of its listed tiles.
   auto store_idx = [&](int chunk, const int32_t (&r)[4]) {
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -130,7 +131,8 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
       const uint32_t wb = (uint32_t)((c >> 7) & 31), word = (uint32_t)(c >> 12);
       const bool off_a = slot >= cnt_a || ((tbits[0][word] >> wb) & 1u);
       const bool off_b = slot >= cnt_b || ((tbits[1][word] >> wb) & 1u);
-      cidx[chunk & 1][4 * tid + e] = (int32_t)((uint32_t)c | ((uint32_t)off_a << 30) | ((uint32_t)off_b << 31));
+      cidx[chunk & 1][4 * tid + e] =
+          (int32_t)(((uint32_t)c << 8) | ((uint32_t)off_a << 30) | ((uint32_t)off_b << 31));
     }
   };
   {
@@ -171,7 +173,7 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = 8 * w + 4 * i + (lane >> 4);
-      const int base = (ci[r] & kColBits) * (kHeadDim * 2);
+      const int base = ci[r] & (kColBits << 8);
       const unsigned ka =
           (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)(kst[st] + (8 * wu + 4 * i) * kHeadDim);
       const unsigned va =
