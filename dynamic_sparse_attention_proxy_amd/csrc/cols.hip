@@ -167,13 +167,15 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
   // Gather of step s: wave w fills rows 8w .. 8w+7 of the stage; lane L of
   // instruction i row r = 8w + 4i + L/16, chunk position L & 15, i.e. global
   // chunk (L & 15) ^ swz(r) of the row's column.
+  // this lane's byte address of its first gathered row's entry in a staged chunk
+  const char* ci_lane = (const char*)&cidx[0][0] + 4 * (8 * w + (lane >> 4));
   auto gather = [&](int s) {
     const int st = s & (kCStages - 1);
-    const int32_t* ci = cidx[(s >> 5) & 1] + (s & 31) * kCStep;
+    const int soff = ((s >> 5) & 1) * (kIdxChunk * 4) + (s & 31) * (kCStep * 4);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const int r = 8 * w + 4 * i + (lane >> 4);
-      const int base = ci[r] & (kColBits << 8);
+      const int base = *(const int32_t*)(ci_lane + soff + 16 * i) & (kColBits << 8);
       const unsigned ka =
           (unsigned)(uintptr_t)(__attribute__((address_space(3))) void*)(kst[st] + (8 * wu + 4 * i) * kHeadDim);
       const unsigned va =
@@ -215,8 +217,9 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
   auto issues = [&](int s) { return s + kCStages - 1 < nsteps; };
 
   // Slot mask of step s for this wave's query block.
+  const char* cm_lane = (const char*)&cidx[0][0] + 4 * lane;
   auto mask_of = [&](int s) -> uint64_t {
-    const uint32_t e = (uint32_t)cidx[(s >> 5) & 1][(s & 31) * kCStep + lane];
+    const uint32_t e = *(const uint32_t*)(cm_lane + ((s >> 5) & 1) * (kIdxChunk * 4) + (s & 31) * (kCStep * 4));
     return __ballot(((e >> (30 + blk)) & 1u) == 0);
   };
   auto kread = [&](int s, int t) -> bf16x8 {  // K operand of MFMA t (key half t & 1, d slice t / 2)
@@ -297,10 +300,14 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
   };
 
   auto iter = [&](int s, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+    // The next chunk of column indices, staged before this step's gather is
+    // issued (its wait then only drains the previous step's gather).
+    if ((s & 31) == 0 && (s >> 5) + 1 < nchunks) {
+      int32_t nxt[4];
+      load_idx((s >> 5) + 1, nxt);
+      store_idx((s >> 5) + 1, nxt);
+    }
     if (issues(s)) gather(s + kCStages - 1);
-    const bool refill = (s & 31) == 0 && (s >> 5) + 1 < nchunks;
-    int32_t nxt[4];
-    if (refill) load_idx((s >> 5) + 1, nxt);
     if (active) {
       const bool has_next = s + 1 < nsteps;
       const uint64_t m_next = has_next ? mask_of(s + 1) : 0ull;
@@ -402,7 +409,6 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
       lo_ready = next_lo;
       m_cur = m_next;
     }
-    if (refill) store_idx((s >> 5) + 1, nxt);
     // K_{s+2} and V_{s+1} must have landed: only this iteration's gather may stay in flight
     if (issues(s))
       asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
