@@ -261,15 +261,17 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
   // Iteration s: block 1 computes S_{s+1} = K_{s+1} Q^T (MFMA) beside the
   // exps of the second key half of S_s (VALU); S_{s+1} is masked if need be;
   // block 2 computes O += V_s P_s (MFMA) beside the exps of S_{s+1}'s first
-  // key half, carried to the next iteration in p_lo / ls_lo.  S_s arrives masked in
+  // key half, carried to the next iteration in pn / ls_lo (pc / ls_lo there:
+  // the two operand pairs swap roles from step to step, so no copy is
+  // made).  S_s arrives masked in
   // `sc`.  Lazy running max: set from the first counted step and raised
   // (rare) when a step's probabilities sum past kColSumLimit, the step's
   // exps then redone from `sc`; any value keeps the result exact.
   f32x16 sa[2], sb[2];
   uint64_t m_cur = 0;
-  bf16x8 p_lo[2];
+  bf16x8 p_lo_a[2], p_lo_b[2];
   float ls_lo = 0.f;
-  bool lo_ready = false;  // p_lo / ls_lo hold the first key half of S_s against m_run
+  bool lo_ready = false;  // pc / ls_lo hold the first key half of S_s against m_run
   if (active) {
     m_cur = mask_of(0);
 #pragma unroll
@@ -299,7 +301,7 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
     return sum_rounded(pbb, sum_rounded(pa, 0.f));  // the rounded values that enter PV
   };
 
-  auto iter = [&](int s, f32x16 (&sc)[2], f32x16 (&sn)[2]) {
+  auto iter = [&](int s, f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pc)[2], bf16x8 (&pn)[2]) {
     // The next chunk of column indices, staged before this step's gather is
     // issued (its wait then only drains the previous step's gather).
     if ((s & 31) == 0 && (s >> 5) + 1 < nchunks) {
@@ -317,7 +319,7 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
         started = true;
         lo_ready = false;
       }
-      if (cur_on && !lo_ready) ls_lo = half_exps(sc[0], p_lo[0], p_lo[1]);
+      if (cur_on && !lo_ready) ls_lo = half_exps(sc[0], pc[0], pc[1]);
       bf16x8 pb[4];
       float ls = 0.f;
       if (has_next && cur_on) {
@@ -351,8 +353,6 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
         if (cur_on) ls = half_exps(sc[1], pb[2], pb[3]);
       }
       if (cur_on) {
-        pb[0] = p_lo[0];
-        pb[1] = p_lo[1];
         ls += ls_lo;
         if (__any(!(ls <= kColSumLimit))) {  // rare: raise the running max, redo the step's exps
           const float m_new = fmaxf(m_run, row_max(sc));
@@ -363,7 +363,7 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
             for (int v = 0; v < 16; ++v) o[db][v] *= alpha;
           l_run *= alpha;
           m_run = m_new;
-          ls = half_exps(sc[0], pb[0], pb[1]) + half_exps(sc[1], pb[2], pb[3]);
+          ls = half_exps(sc[0], pc[0], pc[1]) + half_exps(sc[1], pb[2], pb[3]);
         }
         l_run += ls;
       }
@@ -390,20 +390,20 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
         float e[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
-          o[u & 3] = mfma32(vr[u & 3], pb[u >> 2], o[u & 3]);
+          o[u & 3] = mfma32(vr[u & 3], (u >> 2) < 2 ? pc[u >> 2] : pb[u >> 2], o[u & 3]);
           if (u + 3 < 16) vr[(u + 3) & 3] = vread(s, u + 3);
           e[u] = fast_exp2(fmaf(sn[0][u], p.scale_log2, -m_run));
           if ((u & 7) == 7)
-            p_lo[u >> 3] = pack_bf16x8(e[u - 7], e[u - 6], e[u - 5], e[u - 4], e[u - 3], e[u - 2], e[u - 1], e[u]);
+            pn[u >> 3] = pack_bf16x8(e[u - 7], e[u - 6], e[u - 5], e[u - 4], e[u - 3], e[u - 2], e[u - 1], e[u]);
           __builtin_amdgcn_sched_barrier(0);
         }
-        lsn = sum_rounded(p_lo[1], sum_rounded(p_lo[0], 0.f));
+        lsn = sum_rounded(pn[1], sum_rounded(pn[0], 0.f));
       } else {
         if (cur_on) {
 #pragma unroll
-          for (int u = 0; u < 16; ++u) o[u & 3] = mfma32(vread(s, u), pb[u >> 2], o[u & 3]);
+          for (int u = 0; u < 16; ++u) o[u & 3] = mfma32(vread(s, u), (u >> 2) < 2 ? pc[u >> 2] : pb[u >> 2], o[u & 3]);
         }
-        if (next_lo) lsn = half_exps(sn[0], p_lo[0], p_lo[1]);
+        if (next_lo) lsn = half_exps(sn[0], pn[0], pn[1]);
       }
       ls_lo = lsn;
       lo_ready = next_lo;
@@ -418,10 +418,10 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
   };
   int s = 0;
   for (; s + 1 < nsteps; s += 2) {
-    iter(s, sa, sb);
-    iter(s + 1, sb, sa);
+    iter(s, sa, sb, p_lo_a, p_lo_b);
+    iter(s + 1, sb, sa, p_lo_b, p_lo_a);
   }
-  if (s < nsteps) iter(s, sa, sb);
+  if (s < nsteps) iter(s, sa, sb, p_lo_a, p_lo_b);
 
   if (!active) return;
   // merge with the tile softmax of the same row
