@@ -25,6 +25,8 @@
 // does not divide n) the query rows past n-1 are computed from row n-1 and
 // not written; every gathered column lies below the pair's blocks.
 
+#include <type_traits>
+
 #include "common.h"
 #include "internal.h"
 
@@ -169,8 +171,7 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
   // chunk (L & 15) ^ swz(r) of the row's column.
   // this lane's byte address of its first gathered row's entry in a staged chunk
   const char* ci_lane = (const char*)&cidx[0][0] + 4 * (8 * w + (lane >> 4));
-  auto gather = [&](int s) {
-    const int st = s & (kCStages - 1);
+  auto gather = [&](int s, int st) {
     const int soff = ((s >> 5) & 1) * (kIdxChunk * 4) + (s & 31) * (kCStep * 4);
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
@@ -222,6 +223,8 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
     const uint32_t e = *(const uint32_t*)(cm_lane + ((s >> 5) & 1) * (kIdxChunk * 4) + (s & 31) * (kCStep * 4));
     return __ballot(((e >> (30 + blk)) & 1u) == 0);
   };
+  // Operand reads from the stage of a step: `s` need only equal the step
+  // modulo 4 (the loop below passes the stage itself, a constant).
   auto kread = [&](int s, int t) -> bf16x8 {  // K operand of MFMA t (key half t & 1, d slice t / 2)
     const char* kb8 = (const char*)kst[s & (kCStages - 1)];
     return as_bf16x8(*(const u32x4*)(kb8 + k_off[t >> 1] + (t & 1) * 8192));
@@ -250,7 +253,7 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
     return fmaxf(mx, __shfl_xor(mx, 32)) * p.scale_log2;
   };
 
-  for (int s = 0; s < kCStages - 1 && s < nsteps; ++s) gather(s);
+  for (int s = 0; s < kCStages - 1 && s < nsteps; ++s) gather(s, s);
   // steps 0 and 1 must have landed: at most the gather of step 2 (4 per wave) outstanding
   if (nsteps >= 3)
     asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
@@ -301,7 +304,8 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
     return sum_rounded(pbb, sum_rounded(pa, 0.f));  // the rounded values that enter PV
   };
 
-  auto iter = [&](int s, f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pc)[2], bf16x8 (&pn)[2]) {
+  auto iter = [&](int s, auto st_in, f32x16 (&sc)[2], f32x16 (&sn)[2], bf16x8 (&pc)[2], bf16x8 (&pn)[2]) {
+    const int st = st_in;  // stage of step s (s mod 4), a constant in the unrolled loop
     // The next chunk of column indices, staged before this step's gather is
     // issued (its wait then only drains the previous step's gather).
     if ((s & 31) == 0 && (s >> 5) + 1 < nchunks) {
@@ -309,7 +313,7 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
       load_idx((s >> 5) + 1, nxt);
       store_idx((s >> 5) + 1, nxt);
     }
-    if (issues(s)) gather(s + kCStages - 1);
+    if (issues(s)) gather(s + kCStages - 1, (st + kCStages - 1) & (kCStages - 1));
     if (active) {
       const bool has_next = s + 1 < nsteps;
       const uint64_t m_next = has_next ? mask_of(s + 1) : 0ull;
@@ -325,15 +329,15 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
       if (has_next && cur_on) {
         // block 1: MFMA t of S_{s+1} beside score t of the second key half of S_s
         bf16x8 kr[4];
-        kr[0] = kread(s + 1, 0);
-        kr[1] = kread(s + 1, 1);
-        kr[2] = kread(s + 1, 2);
+        kr[0] = kread(st + 1, 0);
+        kr[1] = kread(st + 1, 1);
+        kr[2] = kread(st + 1, 2);
         const f32x16 zero = {};
         float e[16];
 #pragma unroll
         for (int t = 0; t < 16; ++t) {
           sn[t & 1] = mfma32(kr[t & 3], qf[t >> 1], t < 2 ? zero : sn[t & 1]);
-          if (t + 3 < 16) kr[(t + 3) & 3] = kread(s + 1, t + 3);
+          if (t + 3 < 16) kr[(t + 3) & 3] = kread(st + 1, t + 3);
           e[t] = fast_exp2(fmaf(sc[1][t], p.scale_log2, -m_run));
           if ((t & 7) == 7)
             pb[2 + (t >> 3)] = pack_bf16x8(e[t - 7], e[t - 6], e[t - 5], e[t - 4], e[t - 3], e[t - 2], e[t - 1], e[t]);
@@ -346,7 +350,7 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
           for (int kb2 = 0; kb2 < 2; ++kb2) {
             f32x16 acc = {};
 #pragma unroll
-            for (int kk = 0; kk < 8; ++kk) acc = mfma32(kread(s + 1, 2 * kk + kb2), qf[kk], acc);
+            for (int kk = 0; kk < 8; ++kk) acc = mfma32(kread(st + 1, 2 * kk + kb2), qf[kk], acc);
             sn[kb2] = acc;
           }
         }
@@ -384,14 +388,14 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
       float lsn = 0.f;
       if (cur_on && next_lo) {
         bf16x8 vr[4];
-        vr[0] = vread(s, 0);
-        vr[1] = vread(s, 1);
-        vr[2] = vread(s, 2);
+        vr[0] = vread(st, 0);
+        vr[1] = vread(st, 1);
+        vr[2] = vread(st, 2);
         float e[16];
 #pragma unroll
         for (int u = 0; u < 16; ++u) {
           o[u & 3] = mfma32(vr[u & 3], (u >> 2) < 2 ? pc[u >> 2] : pb[u >> 2], o[u & 3]);
-          if (u + 3 < 16) vr[(u + 3) & 3] = vread(s, u + 3);
+          if (u + 3 < 16) vr[(u + 3) & 3] = vread(st, u + 3);
           e[u] = fast_exp2(fmaf(sn[0][u], p.scale_log2, -m_run));
           if ((u & 7) == 7)
             pn[u >> 3] = pack_bf16x8(e[u - 7], e[u - 6], e[u - 5], e[u - 4], e[u - 3], e[u - 2], e[u - 1], e[u]);
@@ -401,7 +405,7 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
       } else {
         if (cur_on) {
 #pragma unroll
-          for (int u = 0; u < 16; ++u) o[u & 3] = mfma32(vread(s, u), (u >> 2) < 2 ? pc[u >> 2] : pb[u >> 2], o[u & 3]);
+          for (int u = 0; u < 16; ++u) o[u & 3] = mfma32(vread(st, u), (u >> 2) < 2 ? pc[u >> 2] : pb[u >> 2], o[u & 3]);
         }
         if (next_lo) lsn = half_exps(sn[0], pn[0], pn[1]);
       }
@@ -416,12 +420,22 @@ __device__ __forceinline__ void col_item(const ColArgs& p, ColLds& L, int h, int
       wait_dma();
     __syncthreads();
   };
+  // Four steps per trip, one per stage, so that every stage's LDS offsets
+  // are instruction immediates; s is a multiple of 4 after the loop.
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  using S2 = std::integral_constant<int, 2>;
+  using S3 = std::integral_constant<int, 3>;
   int s = 0;
-  for (; s + 1 < nsteps; s += 2) {
-    iter(s, sa, sb, p_lo_a, p_lo_b);
-    iter(s + 1, sb, sa, p_lo_b, p_lo_a);
+  for (; s + 3 < nsteps; s += 4) {
+    iter(s, S0{}, sa, sb, p_lo_a, p_lo_b);
+    iter(s + 1, S1{}, sb, sa, p_lo_b, p_lo_a);
+    iter(s + 2, S2{}, sa, sb, p_lo_a, p_lo_b);
+    iter(s + 3, S3{}, sb, sa, p_lo_b, p_lo_a);
   }
-  if (s < nsteps) iter(s, sa, sb, p_lo_a, p_lo_b);
+  if (s < nsteps) iter(s, S0{}, sa, sb, p_lo_a, p_lo_b);
+  if (s + 1 < nsteps) iter(s + 1, S1{}, sb, sa, p_lo_b, p_lo_a);
+  if (s + 2 < nsteps) iter(s + 2, S2{}, sa, sb, p_lo_a, p_lo_b);
 
   if (!active) return;
   // merge with the tile softmax of the same row
